@@ -1,0 +1,98 @@
+"""Planted mistakes in the oracle, on the CPU: each mutant of oracle.c
+(a dropped term, a wrong sign or index, a transposed operand, a reversed
+tie rule) is compiled on its own and must fail at least one pin. This shows
+the pins constrain every step of the oracle rather than re-stating it."""
+import json
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rows.json")
+
+
+def _rows_golden_ok(lib):
+    with open(GOLDEN) as f:
+        for c in json.load(f)["cases"]:
+            st, idx, lcu = oracle.rows(c["cu_seqlens"], c["num_decode"], c["num_tokens"],
+                                       c.get("logits_indices"), lib=lib)
+            if st != 0 or idx.tolist() != c["gather_indices"] or lcu.tolist() != c["logits_cu_seqlens"]:
+                return False
+    return True
+
+
+def _head_integer_ok(lib):
+    hid = synth.small_int_bf16(1, (7, 48))
+    w = synth.small_int_bf16(2, (60, 48))
+    idx = np.array([6, 0, 3], dtype=np.int32)
+    Z = oracle.head(hid, w, idx, lib=lib)
+    hi = synth.bf16_bits_to_f32(hid).astype(np.int64)
+    wi = synth.bf16_bits_to_f32(w).astype(np.int64)
+    return np.array_equal(Z, (hi[idx] @ wi.T).astype(np.float64))
+
+
+def _head_one_hot_ok(lib):
+    T, H, V = 6, 16, 40
+    hid = np.zeros((T, H), dtype=np.float32)
+    cols = [0, 5, 15, 7, 1, 9]
+    for t, j in enumerate(cols):
+        hid[t, j] = 1.0
+    w = synth.normal_f32(synth.rng(3), (V, H))
+    Z = oracle.head(hid, w, np.arange(T, dtype=np.int32), lib=lib)
+    return all(np.array_equal(Z[t], w[:, j].astype(np.float64)) for t, j in enumerate(cols))
+
+
+def _closed_forms_ok(lib):
+    c, V = 3.5, 1000
+    lse, sel, ids, lp = oracle.reduce(np.full((1, V), c), np.array([2]), k=3, lib=lib)
+    if abs(lse[0] - (c + math.log(V))) > 1e-9 or ids[0].tolist() != [0, 1, 2]:
+        return False
+    if abs(sel[0] + math.log(V)) > 1e-9:
+        return False
+    a, b, n1, n2 = 2.0, -1.0, 3, 997
+    x = np.concatenate([np.full(n2, b), np.full(n1, a)])[None, :]
+    lse, _, ids, lp = oracle.reduce(x, None, k=4, lib=lib)
+    want = math.log(n1 * math.exp(a) + n2 * math.exp(b))
+    return (abs(lse[0] - want) <= 1e-12 and ids[0].tolist() == [n2, n2 + 1, n2 + 2, 0]
+            and abs(lp[0, 0] - (a - want)) <= 1e-12)
+
+
+def _all_pins_ok(lib):
+    return (_rows_golden_ok(lib) and _head_integer_ok(lib) and _head_one_hot_ok(lib)
+            and _closed_forms_ok(lib))
+
+
+MUTANTS = [
+    ("sampled row off by one", "if (idx_out) idx_out[s] = cu[s + 1] - 1;", "if (idx_out) idx_out[s] = cu[s + 1];"),
+    ("explicit count <= instead of <", "if (explicit_idx[r] < cu[s]) ++c;", "if (explicit_idx[r] <= cu[s]) ++c;"),
+    ("head drops the last term", "for (int64_t k = 0; k < H; ++k)", "for (int64_t k = 0; k < H - 1; ++k)"),
+    ("head transposed weight operand", "widen(W, wdt, v * wld + k)", "widen(W, wdt, k * wld + v)"),
+    ("exp of the negated difference", "s += exp(widen(logits, dt, base + v) - m);", "s += exp(m - widen(logits, dt, base + v));"),
+    ("lse drops the max", "l = m + log(s);", "l = log(s);"),
+    ("ties by descending id", "return (a->id < b->id) ? -1 : (a->id > b->id ? 1 : 0);", "return (a->id > b->id) ? -1 : (a->id < b->id ? 1 : 0);"),
+    ("logprob sign flipped", "topk_lp[r * K + i] = e[i].x - l;", "topk_lp[r * K + i] = l - e[i].x;"),
+    ("selected logprob adds lse", ": widen(logits, dt, base + t) - l;", ": widen(logits, dt, base + t) + l;"),
+]
+
+
+def test_unmutated_oracle_passes_the_pins():
+    assert _all_pins_ok(oracle.load())
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_fails_a_pin(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, name
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(mpath), "-o", so, "-lm"],
+                   check=True)
+    lib = oracle.load(so)
+    assert not _all_pins_ok(lib), f"mutant '{name}' survived every pin"
