@@ -1,0 +1,245 @@
+/*
+ * lmhead.h -- C ABI of the selective LM head and the on-device logprob
+ * reduction for AMD Instinct MI355X (gfx950).
+ *
+ * Two stages, each callable alone, plus a fused call:
+ *
+ *   lmhead_gather_project  gathers the sampled rows of a packed batch (the
+ *                          last row of every segment, which includes every
+ *                          decode row, or an explicit row list) and projects
+ *                          only those rows through the head
+ *                          [rows x hidden] . [hidden x vocab].
+ *   logprob_reduce         reduces each logits row on the device to a compact
+ *                          O(K+1) result: the row logsumexp, the selected
+ *                          token's logprob and the exact top-K ids and
+ *                          logprobs, exact ties listed by ascending id.
+ *   lmhead_logprobs        both, chunked, with the fp32 logits kept in a
+ *                          caller-provided workspace.
+ *
+ * Sources (the pages this implements):
+ *   [vllm-metal]  vllm-metal release v0.4.0.dev20260831001336 (selective
+ *                 logits for the paged text path), Summary: the sampled row
+ *                 of prefill segment j is cu_seqlens[num_decode + j + 1] - 1;
+ *                 decode rows are the leading one-token segments; an
+ *                 optional logits_indices replaces the sampled rows; pure
+ *                 decode is unchanged; logits_cu_seqlens describes the
+ *                 compacted logits layout.
+ *   [mlxcel]      mlxcel PR #1969, description: the head acts per position,
+ *                 so the row projected from a gathered hidden row equals the
+ *                 same row of the full projection.
+ *   [MTPLX]       MTPLX PR #532, Change: one float32 logsumexp per row; the
+ *                 vocabulary viewed as 64-logit blocks, the K blocks with
+ *                 the largest maxima kept, the exact top-K taken among their
+ *                 entries; float32(logit) - lse only at the survivors and the
+ *                 scored token; exact ties by ascending token id.
+ *   [openinfer]   openinfer issue #719, Suggested direction and Acceptance
+ *                 criteria: logsumexp, selected logprob and top-k computed
+ *                 while the logits stay on the GPU, returned as an O(k+1)
+ *                 result per row; no full-row device-to-host copy.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller. The library
+ *     allocates nothing, keeps no state between calls, never synchronises and
+ *     never copies to the host: all work is enqueued on `stream` (a
+ *     hipStream_t; NULL is the null stream) and the caller keeps every buffer
+ *     alive until that work completes. Calls on distinct outputs and
+ *     workspaces may run concurrently.
+ *   - Row pitches (`*_ld`) are in elements. Matrices are row-major.
+ *   - Argument errors visible on the host return a status BEFORE any HIP
+ *     call, so nothing is enqueued. A failed launch returns LMH_ERR_HIP.
+ *   - Errors that depend on device data are OR-ed into *device_error (an
+ *     int32 the caller zeroes beforehand; may be NULL) with the LMH_DEVERR_*
+ *     bits; the affected outputs are NaN (logits, logprobs) or -1 (indices).
+ *   - Logprob results are fp32: lse is an fp32 logsumexp of the row, and a
+ *     logprob is float32(logit) - lse rounded once. Top-K ids are exact:
+ *     order is value descending with exact ties (IEEE equality: -0 == +0,
+ *     -inf == -inf) by ascending token id. Rows containing +inf or NaN are
+ *     outside the contract.
+ */
+#ifndef LMHEAD_H
+#define LMHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LMH_OK = 0,
+    LMH_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    LMH_ERR_SHAPE = 2,     /* a size is negative/zero where it must not be, a   */
+                           /* row pitch is below the row width, or a size limit */
+                           /* below is exceeded                                 */
+    LMH_ERR_K = 3,         /* K < 0, K > vocab, or min(K, nb) * 64 > 8192       */
+    LMH_ERR_DTYPE = 4,     /* unsupported dtype or dtype combination           */
+    LMH_ERR_ALIGN = 5,     /* a base pointer or row pitch is not 16-B aligned   */
+    LMH_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the size function  */
+    LMH_ERR_HIP = 7        /* a HIP launch failed                               */
+} lmh_status;
+
+typedef enum { LMH_F32 = 0, LMH_BF16 = 1 } lmh_dtype;
+
+/* device_error bits */
+#define LMH_DEVERR_INDEX 1  /* a row index or selected id outside its range            */
+#define LMH_DEVERR_LAYOUT 2 /* cu_seqlens[0] != 0, cu_seqlens decreasing, cu_seqlens[S] */
+                            /* beyond num_tokens, a decode segment not one token long,   */
+                            /* or an empty segment in sampled mode                       */
+
+/* logits per prefilter block [MTPLX, Change] and the candidate bound */
+#define LMH_BLOCK 64
+#define LMH_MAX_CANDIDATES 8192
+/* largest vocabulary the reduction accepts when K > 0 (block maxima of a row
+ * are resolved in on-chip memory) */
+#define LMH_MAX_VOCAB_TOPK (8192 * LMH_BLOCK)
+
+/*
+ * lmhead_gather_project -- row gather + head projection [vllm-metal, mlxcel].
+ *
+ * hidden  [num_tokens][hidden_dim], pitch hidden_ld, dtype hidden_dt: the
+ *         packed, final-normed hidden states of one step.
+ * weight  [vocab][hidden_dim], pitch weight_ld, dtype weight_dt == hidden_dt:
+ *         the head, one row per token id (the transpose of the
+ *         [hidden x vocab] operand).
+ * cu_seqlens [num_segments + 1] int32: segment boundaries; the first
+ *         num_decode segments are decode rows (one token each).
+ * logits_indices [num_indices] int32 or NULL. NULL selects sampled mode:
+ *         R = num_segments rows, row s is cu_seqlens[s+1] - 1. Otherwise
+ *         R = num_indices rows taken as given (e.g. every prompt position).
+ * logits  [R][vocab], pitch logits_ld, dtype logits_dt (fp32, or bf16 rounded
+ *         to nearest even from the fp32 accumulator):
+ *         logits[r][v] = sum_k hidden[idx[r]][k] * weight[v][k].
+ *         bf16 inputs run on MFMA with fp32 accumulation; fp32 inputs on fp32
+ *         FMA. The result for a row does not depend on which other rows are
+ *         projected with it (bitwise).
+ * logits_cu_seqlens [num_segments + 1] int32 or NULL: sampled mode writes
+ *         0..num_segments; explicit mode writes, per segment s, the number of
+ *         logits rows whose source row lies before cu_seqlens[s].
+ * gather_indices [R] int32 or NULL: the source row of each logits row (-1 if
+ *         invalid).
+ * Requirements: num_tokens, hidden_dim, vocab > 0; num_segments >= 0;
+ *   0 <= num_decode <= num_segments; pitches >= widths. For bf16: hidden and
+ *   weight 16-B aligned, hidden_dim, hidden_ld and weight_ld multiples of 8.
+ *   logits 4-B (fp32) / 2-B (bf16) aligned.
+ * A row whose source index is outside [0, num_tokens) (or, in sampled mode,
+ * whose segment is malformed) is written as NaN and flagged.
+ */
+lmh_status lmhead_gather_project(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld,
+    const void* weight, lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    void* logits, lmh_dtype logits_dt, int64_t logits_ld,
+    int32_t* logits_cu_seqlens, int32_t* gather_indices,
+    int32_t* device_error, void* stream);
+
+/*
+ * logprob_reduce_workspace_size -- bytes of device workspace logprob_reduce
+ * needs for this shape (0 never; always a multiple of 256).
+ */
+size_t logprob_reduce_workspace_size(int64_t rows, int64_t vocab, int32_t k);
+
+/*
+ * logprob_reduce -- per-row logsumexp, selected logprob and exact top-K
+ * [MTPLX, openinfer].
+ *
+ * logits  [rows][vocab], pitch logits_ld, fp32 or bf16; 16-B aligned base
+ *         and pitch.
+ * selected_ids [rows] int32 or NULL (then selected_logprob is not written).
+ * k       0 <= k <= vocab and min(k, ceil(vocab/64)) * 64 <= 8192 (so k <= 128
+ *         at vocabularies above 8192). k = 0 computes lse and the selected
+ *         logprob only; topk_* may then be NULL.
+ * lse [rows], selected_logprob [rows], topk_ids [rows][k] (int32),
+ * topk_logprobs [rows][k] (fp32): outputs, written in full.
+ * Method: one coalesced pass over each row produces online (max, sum-exp)
+ * partials and the maximum of every 64-logit block; a second pass per row
+ * combines the partials in a fixed order, keeps the min(k, nb) blocks with
+ * the largest maxima (equal maxima by ascending block index) and takes the
+ * exact top-K among the entries of those blocks that are not below the k-th
+ * kept block maximum. No full-vocabulary log-softmax is formed.
+ * An all -inf row gives lse = -inf and NaN logprobs (ids 0..k-1); a selected
+ * id outside [0, vocab) gives NaN and LMH_DEVERR_INDEX. rows = 0 is a no-op
+ * (pointers may then be NULL) once the shape and K rules pass.
+ */
+lmh_status logprob_reduce(
+    const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab, int64_t logits_ld,
+    const int32_t* selected_ids, int32_t k,
+    float* lse, float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
+
+/*
+ * lmhead_logprobs_workspace_size -- bytes of device workspace lmhead_logprobs
+ * needs: room for one chunk of fp32 logits (chunk_rows x vocab, chunk_rows = 0
+ * meaning 256) plus the reduction's workspace for that chunk.
+ */
+size_t lmhead_logprobs_workspace_size(int64_t rows, int64_t vocab, int32_t k, int32_t chunk_rows);
+
+/*
+ * lmhead_logprobs -- fused gather + projection + reduction
+ * [vllm-metal, mlxcel, MTPLX, openinfer].
+ *
+ * Arguments as in lmhead_gather_project and logprob_reduce. The R selected
+ * rows are processed in chunks of chunk_rows (0 => 256, the chunk size of
+ * MTPLX PR #532, Motivation): each chunk is projected to fp32 logits in the
+ * workspace and reduced there, so no logits row leaves the device and at
+ * most one chunk of logits is resident. selected_ids is indexed by logits
+ * row (R entries). logits_debug, when not NULL, is an [R][vocab] fp32 buffer
+ * that receives the logits that were reduced (tests use it); the workspace
+ * then only holds the reduction's part.
+ */
+lmh_status lmhead_logprobs(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld,
+    const void* weight, lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    const int32_t* selected_ids, int32_t k,
+    float* lse, float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+    int32_t* logits_cu_seqlens, int32_t* gather_indices,
+    int32_t chunk_rows, float* logits_debug,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
+
+/* lmh_status_string -- static, human-readable name of a status code. */
+const char* lmh_status_string(lmh_status status);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostic entry points (tests and measurement). Same contracts as above.
+ * ------------------------------------------------------------------------- */
+
+/* Head kernel choices for lmh_debug_gather_project's `variant`. */
+#define LMH_HEAD_AUTO 0   /* weight streaming for R <= 64, tiled otherwise   */
+#define LMH_HEAD_STREAM 1 /* weight-streaming kernel (requires R <= 64)      */
+#define LMH_HEAD_TILED 2  /* LDS-tiled kernel                                */
+
+/*
+ * lmh_debug_gather_project -- lmhead_gather_project with the bf16 head kernel
+ * forced (tests use it to show both kernels give bitwise-identical rows).
+ * LMH_HEAD_STREAM with R > 64, or any non-auto variant with fp32 inputs,
+ * returns LMH_ERR_SHAPE.
+ */
+lmh_status lmh_debug_gather_project(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld,
+    const void* weight, lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    void* logits, lmh_dtype logits_dt, int64_t logits_ld,
+    int32_t* logits_cu_seqlens, int32_t* gather_indices,
+    int32_t* device_error, void* stream, int32_t variant);
+
+/*
+ * lmh_debug_reduce_stage1 -- only the streaming pass of logprob_reduce
+ * (partials and block maxima into the workspace); used to time that kernel
+ * alone. Same argument rules as logprob_reduce.
+ */
+lmh_status lmh_debug_reduce_stage1(
+    const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab, int64_t logits_ld,
+    int32_t k, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMHEAD_H */

@@ -1,0 +1,152 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every entry
+point the header declares, and rejects bad host-visible arguments with the
+documented status before any HIP call (so no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmhead.h")
+LIB = os.path.join(ROOT, "top_reduction_amd", "liblmhead.so")
+
+OK, NULL, SHAPE, K, DTYPE, ALIGN, WS, HIP = range(8)
+F32, BF16, BAD_DT = 0, 1, 7
+A = 0x10000  # a 256-aligned stand-in address; never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:lmh_status|size_t|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.skip("liblmhead.so is not built")
+    import top_reduction_amd
+    return top_reduction_amd.lib()
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    assert {"lmhead_gather_project", "logprob_reduce", "lmhead_logprobs",
+            "logprob_reduce_workspace_size", "lmhead_logprobs_workspace_size",
+            "lmh_status_string"} <= names
+
+
+def test_every_declared_symbol_is_exported(L):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(L):
+    for st in range(8):
+        assert L.lmh_status_string(st).decode().startswith("LMH_")
+
+
+def _project(L, **kw):
+    a = dict(hidden=A, hidden_dt=BF16, num_tokens=23, hidden_dim=64, hidden_ld=64, weight=A,
+             weight_dt=BF16, vocab=1000, weight_ld=64, cu=A, S=5, D=2, ex=None, nex=0,
+             logits=A, logits_dt=F32, logits_ld=1000, lcu=None, gidx=None, err=None)
+    a.update(kw)
+    return L.lmhead_gather_project(a["hidden"], a["hidden_dt"], a["num_tokens"], a["hidden_dim"],
+                                   a["hidden_ld"], a["weight"], a["weight_dt"], a["vocab"],
+                                   a["weight_ld"], a["cu"], a["S"], a["D"], a["ex"], a["nex"],
+                                   a["logits"], a["logits_dt"], a["logits_ld"], a["lcu"], a["gidx"],
+                                   a["err"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(hidden=None), NULL), (dict(weight=None), NULL), (dict(cu=None), NULL),
+    (dict(logits=None), NULL),
+    (dict(num_tokens=0), SHAPE), (dict(hidden_dim=0), SHAPE), (dict(vocab=0), SHAPE),
+    (dict(S=-1), SHAPE), (dict(D=6), SHAPE), (dict(D=-1), SHAPE),
+    (dict(hidden_ld=32), SHAPE), (dict(weight_ld=63), SHAPE), (dict(logits_ld=999), SHAPE),
+    (dict(ex=A, nex=-1), SHAPE),
+    (dict(hidden_dt=BAD_DT, weight_dt=BAD_DT), DTYPE), (dict(weight_dt=F32), DTYPE),
+    (dict(logits_dt=BAD_DT), DTYPE),
+    (dict(hidden=A + 8), ALIGN), (dict(weight=A + 2), ALIGN), (dict(hidden_dim=60, hidden_ld=64), ALIGN),
+    (dict(hidden_ld=68), ALIGN), (dict(logits=A + 2), ALIGN),
+])
+def test_gather_project_rejects(L, kw, want):
+    assert _project(L, **kw) == want
+
+
+def test_debug_variant_rules(L):
+    args = [A, BF16, 200, 64, 64, A, BF16, 1000, 64, A, 100, 0, None, 0, A, F32, 1000, None, None, None, None]
+    assert L.lmh_debug_gather_project(*args, 1) == SHAPE      # streaming head needs R <= 64
+    assert L.lmh_debug_gather_project(*args, 3) == SHAPE      # unknown variant
+    f32 = list(args)
+    f32[1] = f32[6] = F32
+    f32[9] = A
+    f32[10] = 5
+    assert L.lmh_debug_gather_project(*f32, 2) == SHAPE       # variants are bf16-only
+
+
+def _reduce(L, **kw):
+    a = dict(logits=A, dt=BF16, rows=256, vocab=248320, ld=248320, sel=A, k=20, lse=A, slp=A,
+             ids=A, lps=A, ws=A, wsb=1 << 30, err=None)
+    a.update(kw)
+    return L.logprob_reduce(a["logits"], a["dt"], a["rows"], a["vocab"], a["ld"], a["sel"], a["k"],
+                            a["lse"], a["slp"], a["ids"], a["lps"], a["ws"], a["wsb"], a["err"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(logits=None), NULL), (dict(lse=None), NULL), (dict(slp=None), NULL),
+    (dict(ids=None), NULL), (dict(lps=None), NULL),
+    (dict(rows=-1), SHAPE), (dict(vocab=0), SHAPE), (dict(ld=248319), SHAPE),
+    (dict(dt=BAD_DT), DTYPE),
+    (dict(logits=A + 8), ALIGN), (dict(ld=248324), ALIGN),
+    (dict(k=-1), K), (dict(k=129), K), (dict(vocab=100, ld=104, k=101), K),
+    (dict(vocab=9 * 8192 * 64, ld=9 * 8192 * 64, k=1), SHAPE),
+    (dict(ws=None), WS), (dict(wsb=1024), WS), (dict(ws=A + 16), WS),
+])
+def test_reduce_rejects(L, kw, want):
+    assert _reduce(L, **kw) == want
+
+
+def test_reduce_k_rule_small_vocab(L):
+    # V <= 8192: any K <= V passes the K rule (so the workspace check is reached)
+    assert _reduce(L, vocab=8192, ld=8192, k=8192, wsb=16) == WS
+    assert _reduce(L, vocab=8256, ld=8256, k=129, wsb=16) == K
+
+
+def test_reduce_zero_rows_is_a_noop(L):
+    assert _reduce(L, rows=0, logits=None, lse=None, slp=None, ids=None, lps=None, ws=None) == OK
+    assert _reduce(L, rows=0, k=129) == K
+
+
+def test_reduce_k0_needs_no_topk_buffers(L):
+    assert _reduce(L, k=0, ids=None, lps=None, wsb=16) == WS
+
+
+def test_workspace_sizes(L):
+    for rows, V, k in [(256, 248320, 128), (32, 151936, 5), (1, 1000, 0), (0, 64, 0)]:
+        n = L.logprob_reduce_workspace_size(rows, V, k)
+        assert n >= 256 and n % 256 == 0
+        nb = -(-V // 64)
+        assert n >= rows * nb * 2
+    a = L.lmhead_logprobs_workspace_size(1024, 128256, 20, 256)
+    b = L.lmhead_logprobs_workspace_size(40, 128256, 20, 256)
+    assert a >= 256 * 128256 * 4 and b >= 40 * 128256 * 4 and a > b
+
+
+def test_fused_rejects(L):
+    base = [A, BF16, 10272, 4096, 4096, A, BF16, 128256, 4096, A, 40, 32, None, 0,
+            A, 20, A, A, A, A, None, None, 0, None, A, 1 << 34, None, None]
+    bad = list(base)
+    bad[16] = None                      # lse
+    assert L.lmhead_logprobs(*bad) == NULL
+    bad = list(base)
+    bad[15] = 129                       # K rule
+    assert L.lmhead_logprobs(*bad) == K
+    bad = list(base)
+    bad[25] = 1024                      # workspace too small
+    assert L.lmhead_logprobs(*bad) == WS
+    bad = list(base)
+    bad[22] = -1                        # chunk_rows
+    assert L.lmhead_logprobs(*bad) == SHAPE

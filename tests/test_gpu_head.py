@@ -1,0 +1,178 @@
+"""GPU parity of lmhead_gather_project with the f64 oracle (vllm-metal
+release v0.4.0, Summary and Testing; mlxcel PR #1969).
+
+Bar: gather indices and logits_cu_seqlens bit-exact; head logits (bf16 in,
+fp32 accumulate) within 2e-3 of the oracle relative to the row's max |logit|;
+exact where the arithmetic is exact (small-integer inputs, one-hot rows);
+selective rows bitwise equal to the same rows of the full projection, and
+the weight-streaming and tiled kernels bitwise equal to each other."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_reduction_amd as lmh
+from helpers import bf16_bits, bf16_tensor, f32_tensor, i32_tensor
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _check_rows(proj, cu, nd, T, ex=None):
+    st, idx, lcu = oracle.rows(cu, nd, T, ex)
+    assert st == oracle.OK
+    torch.cuda.synchronize()
+    assert np.array_equal(proj.gather_indices.cpu().numpy(), idx)
+    assert np.array_equal(proj.logits_cu_seqlens.cpu().numpy(), lcu)
+    assert int(proj.device_error.item()) == 0
+    return idx
+
+
+def _close(z, z_ref, tol=TOL):
+    scale = np.abs(z_ref).max(axis=1, keepdims=True)
+    err = np.abs(z.astype(np.float64) - z_ref)
+    assert np.all(err <= tol * scale), float((err / scale).max())
+
+
+def test_tiny_fp32_batch():
+    d = synth.tiny_batch(1000)
+    T = d["hidden"].shape[0]
+    p = lmh.lmhead_gather_project(f32_tensor(d["hidden"]), f32_tensor(d["weight"]),
+                                  i32_tensor(d["cu_seqlens"]), d["num_decode"])
+    idx = _check_rows(p, d["cu_seqlens"], d["num_decode"], T)
+    assert idx.tolist() == [0, 1, 6, 13, 22]
+    _close(p.logits.cpu().numpy(), oracle.head(d["hidden"], d["weight"], idx), 1e-5)
+
+
+@pytest.mark.parametrize("variant", [lmh.LMH_HEAD_STREAM, lmh.LMH_HEAD_TILED])
+@pytest.mark.parametrize("H", [64, 96, 4096])
+def test_small_integers_exact(variant, H):
+    """bf16 entries in {-4..4}: every partial sum is an exact fp32 integer, so
+    the MFMA result must equal the oracle bit for bit."""
+    T, V = 50, 1000 + 17
+    hid = synth.small_int_bf16(11, (T, H))
+    w = synth.small_int_bf16(12, (V, H))
+    cu = synth.packed_cu_seqlens(3, [7, 9, 1, 30])
+    p = lmh.lmhead_gather_project(bf16_tensor(hid), bf16_tensor(w), i32_tensor(cu), 3, variant=variant)
+    idx = _check_rows(p, cu, 3, T)
+    assert np.array_equal(p.logits.cpu().numpy().astype(np.float64), oracle.head(hid, w, idx))
+
+
+def test_one_hot_rows_read_weight_columns():
+    H, V = 128, 3000
+    cols = [0, 1, 63, 64, 127, 5]
+    hid = np.zeros((len(cols), H), dtype=np.uint16)
+    for t, j in enumerate(cols):
+        hid[t, j] = 0x3F80                                   # 1.0
+    w = synth.normal_bf16(synth.rng(13), (V, H))
+    ex = np.arange(len(cols), dtype=np.int32)
+    p = lmh.lmhead_gather_project(bf16_tensor(hid), bf16_tensor(w), i32_tensor([0, len(cols)]), 0,
+                                  logits_indices=i32_tensor(ex))
+    z = p.logits.cpu().numpy()
+    wf = synth.bf16_bits_to_f32(w)
+    for t, j in enumerate(cols):
+        assert np.array_equal(z[t], wf[:, j])
+
+
+@pytest.mark.parametrize("R", [1, 17, 64, 65, 130])
+@pytest.mark.parametrize("V", [1000, 1001, 4096])
+def test_random_bf16_shapes(R, V):
+    """Ragged vocab tails, partial row tiles, both kernels (R <= 64 streams)."""
+    g = synth.rng(R * 7 + V)
+    H, T = 256, 300
+    hid = synth.normal_bf16(g, (T, H))
+    w = synth.normal_bf16(g, (V, H), H ** -0.5)
+    ex = g.integers(0, T, size=R).astype(np.int32)
+    cu = np.array([0, T], dtype=np.int32)
+    p = lmh.lmhead_gather_project(bf16_tensor(hid), bf16_tensor(w), i32_tensor(cu), 0,
+                                  logits_indices=i32_tensor(ex))
+    idx = _check_rows(p, cu, 0, T, ex)
+    _close(p.logits.cpu().numpy(), oracle.head(hid, w, idx))
+
+
+def test_bf16_output_is_rne_of_fp32():
+    g = synth.rng(14)
+    hid = synth.normal_bf16(g, (40, 512))
+    w = synth.normal_bf16(g, (5000, 512), 512 ** -0.5)
+    cu = synth.packed_cu_seqlens(40, [])
+    args = (bf16_tensor(hid), bf16_tensor(w), i32_tensor(cu), 40)
+    f = lmh.lmhead_gather_project(*args).logits
+    b = lmh.lmhead_gather_project(*args, out_dtype=torch.bfloat16).logits
+    assert np.array_equal(bf16_bits(b), synth.f32_to_bf16_bits(f.cpu().numpy()))
+
+
+def test_invalid_rows_are_nan_and_flagged():
+    g = synth.rng(15)
+    hid = synth.normal_bf16(g, (10, 64))
+    w = synth.normal_bf16(g, (300, 64))
+    ex = np.array([0, 10, -3, 9], dtype=np.int32)
+    p = lmh.lmhead_gather_project(bf16_tensor(hid), bf16_tensor(w), i32_tensor([0, 10]), 0,
+                                  logits_indices=i32_tensor(ex))
+    torch.cuda.synchronize()
+    z = p.logits.cpu().numpy()
+    assert np.all(np.isfinite(z[[0, 3]])) and np.all(np.isnan(z[[1, 2]]))
+    assert p.gather_indices.cpu().numpy().tolist() == [0, -1, -1, 9]
+    assert int(p.device_error.item()) & lmh.LMH_DEVERR_INDEX
+    # a decode segment of two tokens is a layout error
+    p = lmh.lmhead_gather_project(bf16_tensor(hid), bf16_tensor(w), i32_tensor([0, 2, 5]), 1)
+    torch.cuda.synchronize()
+    assert int(p.device_error.item()) & lmh.LMH_DEVERR_LAYOUT
+    assert np.all(np.isnan(p.logits.cpu().numpy()[0]))
+
+
+@pytest.fixture(scope="module")
+def qwen_batch():
+    return synth.selective_head_batch(4000)
+
+
+def test_selective_head_qwen_shape(qwen_batch):
+    """40 prefill segments x 2048 tokens, hidden 1024, vocab 151,936: gather the
+    40 last rows; compare sampled columns with the oracle."""
+    d = qwen_batch
+    T = d["hidden"].shape[0]
+    hid, w = bf16_tensor(d["hidden"]), bf16_tensor(d["weight"])
+    p = lmh.lmhead_gather_project(hid, w, i32_tensor(d["cu_seqlens"]), 0)
+    idx = _check_rows(p, d["cu_seqlens"], 0, T)
+    assert np.array_equal(idx, 2047 + 2048 * np.arange(40))
+    cols = np.sort(synth.rng(16).choice(w.shape[0], size=4096, replace=False))
+    z_ref = oracle.head(d["hidden"], np.ascontiguousarray(d["weight"][cols]), idx)
+    z = p.logits.cpu().numpy()[:, cols]
+    _close(z, z_ref)
+
+
+def test_selective_equals_full_projection_bitwise(qwen_batch):
+    """The selective rows equal the same rows of the full 2048-row projection
+    of segment 0, bit for bit; the row one off does not (the control)."""
+    d = qwen_batch
+    hid, w = bf16_tensor(d["hidden"]), bf16_tensor(d["weight"])
+    cu = i32_tensor(d["cu_seqlens"])
+    full = lmh.lmhead_gather_project(hid, w, cu, 0,
+                                     logits_indices=i32_tensor(np.arange(2048))).logits
+    sel = lmh.lmhead_gather_project(hid, w, cu, 0).logits
+    tiled = lmh.lmhead_gather_project(hid, w, cu, 0, variant=lmh.LMH_HEAD_TILED).logits
+    torch.cuda.synchronize()
+    assert torch.equal(full[2047].view(torch.int32), sel[0].view(torch.int32))
+    assert torch.equal(tiled.view(torch.int32), sel.view(torch.int32))
+    assert not torch.equal(full[2046], sel[0])
+    # a mid-segment row through the streaming kernel matches the full projection
+    mid = lmh.lmhead_gather_project(hid, w, cu, 0, logits_indices=i32_tensor([1000, 5, 2047]),
+                                    variant=lmh.LMH_HEAD_STREAM).logits
+    torch.cuda.synchronize()
+    assert torch.equal(mid.view(torch.int32), full[[1000, 5, 2047]].view(torch.int32))
+
+
+def test_pure_decode_identity():
+    """Pure decode: every row is sampled, in order (vllm-metal release: pure
+    decode is unchanged)."""
+    g = synth.rng(17)
+    hid = synth.normal_bf16(g, (33, 128))
+    w = synth.normal_bf16(g, (2000, 128), 128 ** -0.5)
+    cu = synth.packed_cu_seqlens(33, [])
+    p = lmh.lmhead_gather_project(bf16_tensor(hid), bf16_tensor(w), i32_tensor(cu), 33)
+    full = lmh.lmhead_gather_project(bf16_tensor(hid), bf16_tensor(w), i32_tensor(cu), 0,
+                                     logits_indices=i32_tensor(np.arange(33))).logits
+    torch.cuda.synchronize()
+    assert np.array_equal(p.gather_indices.cpu().numpy(), np.arange(33))
+    assert torch.equal(p.logits.view(torch.int32), full.view(torch.int32))

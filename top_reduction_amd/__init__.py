@@ -1,0 +1,244 @@
+"""Selective LM head and on-device logprob reduction for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``liblmhead.so`` (C ABI in ``include/lmhead.h``).
+This module only marshals arguments: tensors become device pointers and row
+pitches, outputs and workspaces are allocated with torch, and every call is
+enqueued on torch's current HIP stream. Every step of the computation runs in
+the library's HIP kernels; there is no fallback, and a missing library raises.
+
+Entry points (same names as the C ABI):
+  lmhead_gather_project  gather the sampled rows of a packed batch and project
+                         only those through the head
+  logprob_reduce         per-row logsumexp, selected logprob, exact top-K
+  lmhead_logprobs        both, fused and chunked
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblmhead.so")
+
+LMH_F32, LMH_BF16 = 0, 1
+LMH_HEAD_AUTO, LMH_HEAD_STREAM, LMH_HEAD_TILED = 0, 1, 2
+LMH_DEVERR_INDEX, LMH_DEVERR_LAYOUT = 1, 2
+STATUS = {0: "LMH_OK", 1: "LMH_ERR_NULL", 2: "LMH_ERR_SHAPE", 3: "LMH_ERR_K",
+          4: "LMH_ERR_DTYPE", 5: "LMH_ERR_ALIGN", 6: "LMH_ERR_WORKSPACE", 7: "LMH_ERR_HIP"}
+
+_lib = None
+
+
+class LmhError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+def lib():
+    """Load liblmhead.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        proj = [p, ctypes.c_int, i64, i64, i64, p, ctypes.c_int, i64, i64, p, i32, i32, p, i32]
+        L.lmhead_gather_project.argtypes = proj + [p, ctypes.c_int, i64, p, p, p, p]
+        L.lmh_debug_gather_project.argtypes = proj + [p, ctypes.c_int, i64, p, p, p, p, i32]
+        L.logprob_reduce_workspace_size.argtypes = [i64, i64, i32]
+        L.logprob_reduce_workspace_size.restype = sz
+        L.logprob_reduce.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p, p, sz, p, p]
+        L.lmh_debug_reduce_stage1.argtypes = [p, ctypes.c_int, i64, i64, i64, i32, p, sz, p]
+        L.lmhead_logprobs_workspace_size.argtypes = [i64, i64, i32, i32]
+        L.lmhead_logprobs_workspace_size.restype = sz
+        L.lmhead_logprobs.argtypes = proj + [p, i32, p, p, p, p, p, p, i32, p, p, sz, p, p]
+        L.lmh_status_string.argtypes = [ctypes.c_int]
+        L.lmh_status_string.restype = ctypes.c_char_p
+        for name in ("lmhead_gather_project", "lmh_debug_gather_project", "logprob_reduce",
+                     "lmh_debug_reduce_stage1", "lmhead_logprobs"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise LmhError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LMH_BF16
+    if t.dtype == torch.float32:
+        return LMH_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _matrix(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _i32(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    return t
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte-aligned byte buffer (torch's caching allocator aligns more)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+class Projection(NamedTuple):
+    logits: torch.Tensor
+    logits_cu_seqlens: torch.Tensor
+    gather_indices: torch.Tensor
+    device_error: torch.Tensor
+
+
+def lmhead_gather_project(hidden: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor,
+                          num_decode: int = 0, logits_indices: Optional[torch.Tensor] = None,
+                          out_dtype: torch.dtype = torch.float32,
+                          logits: Optional[torch.Tensor] = None, variant: int = LMH_HEAD_AUTO,
+                          device_error: Optional[torch.Tensor] = None) -> Projection:
+    """Gather the sampled rows of a packed batch and project them through the
+    head: logits[r] = hidden[src(r)] @ weight.T (weight is [vocab, hidden])."""
+    L = lib()
+    T, H, hld = _matrix(hidden, "hidden")
+    V, H2, wld = _matrix(weight, "weight")
+    if H2 != H:
+        raise ValueError("hidden and weight widths differ")
+    cu = _i32(cu_seqlens, "cu_seqlens")
+    ex = _i32(logits_indices, "logits_indices")
+    S = cu.shape[0] - 1
+    R = ex.shape[0] if ex is not None else S
+    dev = hidden.device
+    if logits is None:
+        logits = torch.empty((R, V), dtype=out_dtype, device=dev)
+    _, _, old = _matrix(logits, "logits") if R > 0 else (0, 0, V)
+    lcu = torch.empty(S + 1, dtype=torch.int32, device=dev)
+    gidx = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
+    err = device_error if device_error is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    args = [_ptr(hidden), _dt(hidden), T, H, hld, _ptr(weight), _dt(weight), V, wld,
+            _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
+            _ptr(logits), _dt(logits), old, _ptr(lcu), _ptr(gidx), _ptr(err), _stream()]
+    if variant == LMH_HEAD_AUTO:
+        st = L.lmhead_gather_project(*args)
+    else:
+        st = L.lmh_debug_gather_project(*args, int(variant))
+    _check(st, "lmhead_gather_project")
+    return Projection(logits, lcu, gidx[:R], err)
+
+
+class Reduction(NamedTuple):
+    lse: torch.Tensor
+    selected_logprob: Optional[torch.Tensor]
+    topk_ids: torch.Tensor
+    topk_logprobs: torch.Tensor
+    device_error: torch.Tensor
+
+
+def logprob_reduce(logits: torch.Tensor, selected_ids: Optional[torch.Tensor] = None, k: int = 0,
+                   ws: Optional[torch.Tensor] = None,
+                   out: Optional[Reduction] = None) -> Reduction:
+    """Per-row logsumexp, selected-token logprob and exact top-K (ties by
+    ascending id) of a [rows, vocab] bf16/fp32 logits matrix, on the device."""
+    L = lib()
+    R, V, ld = _matrix(logits, "logits")
+    sel = _i32(selected_ids, "selected_ids")
+    dev = logits.device
+    need = L.logprob_reduce_workspace_size(R, V, k)
+    if ws is None:
+        ws = workspace(need, dev)
+    if out is None:
+        out = Reduction(torch.empty(R, dtype=torch.float32, device=dev),
+                        torch.empty(R, dtype=torch.float32, device=dev) if sel is not None else None,
+                        torch.empty((R, k), dtype=torch.int32, device=dev),
+                        torch.empty((R, k), dtype=torch.float32, device=dev),
+                        torch.zeros(1, dtype=torch.int32, device=dev))
+    st = L.logprob_reduce(_ptr(logits), _dt(logits), R, V, ld, _ptr(sel), int(k),
+                          _ptr(out.lse), _ptr(out.selected_logprob),
+                          _ptr(out.topk_ids) if k else None, _ptr(out.topk_logprobs) if k else None,
+                          _ptr(ws), ws.numel(), _ptr(out.device_error), _stream())
+    _check(st, "logprob_reduce")
+    return out
+
+
+def reduce_stage1(logits: torch.Tensor, k: int, ws: torch.Tensor) -> None:
+    """Only the streaming pass of logprob_reduce (for timing that kernel)."""
+    L = lib()
+    R, V, ld = _matrix(logits, "logits")
+    _check(L.lmh_debug_reduce_stage1(_ptr(logits), _dt(logits), R, V, ld, int(k), _ptr(ws),
+                                     ws.numel(), _stream()), "lmh_debug_reduce_stage1")
+
+
+class Logprobs(NamedTuple):
+    lse: torch.Tensor
+    selected_logprob: Optional[torch.Tensor]
+    topk_ids: torch.Tensor
+    topk_logprobs: torch.Tensor
+    logits_cu_seqlens: torch.Tensor
+    gather_indices: torch.Tensor
+    device_error: torch.Tensor
+    logits: Optional[torch.Tensor]
+
+
+def lmhead_logprobs_workspace_size(rows: int, vocab: int, k: int, chunk_rows: int = 0) -> int:
+    return int(lib().lmhead_logprobs_workspace_size(rows, vocab, k, chunk_rows))
+
+
+def lmhead_logprobs(hidden: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor,
+                    num_decode: int = 0, selected_ids: Optional[torch.Tensor] = None, k: int = 0,
+                    logits_indices: Optional[torch.Tensor] = None, chunk_rows: int = 0,
+                    return_logits: bool = False, ws: Optional[torch.Tensor] = None) -> Logprobs:
+    """Fused gather + projection + reduction, chunked (default 256 rows)."""
+    L = lib()
+    T, H, hld = _matrix(hidden, "hidden")
+    V, H2, wld = _matrix(weight, "weight")
+    if H2 != H:
+        raise ValueError("hidden and weight widths differ")
+    cu = _i32(cu_seqlens, "cu_seqlens")
+    ex = _i32(logits_indices, "logits_indices")
+    sel = _i32(selected_ids, "selected_ids")
+    S = cu.shape[0] - 1
+    R = ex.shape[0] if ex is not None else S
+    dev = hidden.device
+    if ws is None:
+        ws = workspace(L.lmhead_logprobs_workspace_size(R, V, k, chunk_rows), dev)
+    ld = (V + 3) // 4 * 4
+    dbg = torch.empty((R, ld), dtype=torch.float32, device=dev) if return_logits else None
+    lse = torch.empty(R, dtype=torch.float32, device=dev)
+    slp = torch.empty(R, dtype=torch.float32, device=dev) if sel is not None else None
+    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
+    lps = torch.empty((R, k), dtype=torch.float32, device=dev)
+    lcu = torch.empty(S + 1, dtype=torch.int32, device=dev)
+    gidx = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = L.lmhead_logprobs(_ptr(hidden), _dt(hidden), T, H, hld, _ptr(weight), _dt(weight), V, wld,
+                           _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
+                           _ptr(sel), int(k), _ptr(lse), _ptr(slp),
+                           _ptr(ids) if k else None, _ptr(lps) if k else None,
+                           _ptr(lcu), _ptr(gidx), int(chunk_rows), _ptr(dbg),
+                           _ptr(ws), ws.numel(), _ptr(err), _stream())
+    _check(st, "lmhead_logprobs")
+    return Logprobs(lse, slp, ids, lps, lcu, gidx[:R], err,
+                    None if dbg is None else dbg[:, :V])

@@ -1,0 +1,272 @@
+// api.hip -- the C ABI of liblmhead (declared in include/lmhead.h): host-side
+// argument checks, workspace layout and kernel dispatch. Every check that can
+// be made on the host returns before the first HIP call; no entry point
+// allocates, synchronises or copies to the host.
+#include <climits>
+
+#include "lmh_internal.h"
+
+using namespace lmh;
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline bool valid_dtype(lmh_dtype d) { return d == LMH_F32 || d == LMH_BF16; }
+inline size_t esize(lmh_dtype d) { return d == LMH_BF16 ? 2 : 4; }
+inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct ProjectCheck {
+    lmh_status st;
+    int32_t rows;
+};
+
+// Checks shared by the projection entry points (everything but the output).
+ProjectCheck check_project_inputs(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                                  int64_t hidden_dim, int64_t hidden_ld, const void* weight,
+                                  lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
+                                  const int32_t* cu_seqlens, int32_t num_segments,
+                                  int32_t num_decode, const int32_t* logits_indices,
+                                  int32_t num_indices) {
+    if (!hidden || !weight || !cu_seqlens) return {LMH_ERR_NULL, 0};
+    if (num_tokens <= 0 || num_tokens > INT32_MAX || hidden_dim <= 0 || vocab <= 0 ||
+        vocab > INT32_MAX || num_segments < 0 || num_decode < 0 || num_decode > num_segments)
+        return {LMH_ERR_SHAPE, 0};
+    if (logits_indices != nullptr && num_indices < 0) return {LMH_ERR_SHAPE, 0};
+    if (hidden_ld < hidden_dim || weight_ld < hidden_dim) return {LMH_ERR_SHAPE, 0};
+    if (!valid_dtype(hidden_dt) || weight_dt != hidden_dt) return {LMH_ERR_DTYPE, 0};
+    if (hidden_dt == LMH_BF16) {
+        if (!aligned(hidden, 16) || !aligned(weight, 16) || hidden_dim % 8 || hidden_ld % 8 ||
+            weight_ld % 8)
+            return {LMH_ERR_ALIGN, 0};
+    } else {
+        if (!aligned(hidden, 4) || !aligned(weight, 4)) return {LMH_ERR_ALIGN, 0};
+    }
+    const int32_t rows = logits_indices ? num_indices : num_segments;
+    return {LMH_OK, rows};
+}
+
+// Shape, dtype, pitch and K rules of the reduction (pointer alignment is
+// checked by the callers).
+lmh_status check_reduce_shape(lmh_dtype dt, int64_t rows, int64_t vocab, int64_t ld, int32_t k) {
+    if (rows < 0 || rows > INT32_MAX || vocab <= 0 || vocab > INT32_MAX || ld < vocab)
+        return LMH_ERR_SHAPE;
+    if (!valid_dtype(dt)) return LMH_ERR_DTYPE;
+    if (((size_t)ld * esize(dt)) % 16) return LMH_ERR_ALIGN;
+    const int64_t nb = ceil_div(vocab, kBlock);
+    if (k < 0 || k > vocab) return LMH_ERR_K;
+    if ((k < nb ? k : nb) * (int64_t)kBlock > kMaxCandidates) return LMH_ERR_K;
+    if (k > 0 && nb > kMaxCandidates) return LMH_ERR_SHAPE;
+    const ReducePlan p = plan_reduce(rows, vocab, k);
+    if (rows * (int64_t)p.splits > INT32_MAX) return LMH_ERR_SHAPE;
+    return LMH_OK;
+}
+
+lmh_status from_hip(hipError_t e) { return e == hipSuccess ? LMH_OK : LMH_ERR_HIP; }
+
+lmh_status launch_head(const HeadArgs& h, bool bf16_inputs, int32_t variant, hipStream_t s) {
+    if (!bf16_inputs) return from_hip(launch_head_f32(h, s));
+    const bool stream = variant == LMH_HEAD_STREAM || (variant == LMH_HEAD_AUTO && h.rows <= kStreamMaxRows);
+    return from_hip(stream ? launch_head_stream_bf16(h, s) : launch_head_tiled_bf16(h, s));
+}
+
+lmh_status gather_project_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                               int64_t hidden_dim, int64_t hidden_ld, const void* weight,
+                               lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
+                               const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+                               const int32_t* logits_indices, int32_t num_indices, void* logits,
+                               lmh_dtype logits_dt, int64_t logits_ld, int32_t* logits_cu_seqlens,
+                               int32_t* gather_indices, int32_t* device_error, void* stream,
+                               int32_t variant) {
+    const ProjectCheck c = check_project_inputs(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                                                weight, weight_dt, vocab, weight_ld, cu_seqlens,
+                                                num_segments, num_decode, logits_indices, num_indices);
+    if (c.st != LMH_OK) return c.st;
+    if (!logits && c.rows > 0) return LMH_ERR_NULL;
+    if (logits_ld < vocab) return LMH_ERR_SHAPE;
+    if (!valid_dtype(logits_dt)) return LMH_ERR_DTYPE;
+    if (!aligned(logits, esize(logits_dt))) return LMH_ERR_ALIGN;
+    if (variant < LMH_HEAD_AUTO || variant > LMH_HEAD_TILED) return LMH_ERR_SHAPE;
+    if (variant != LMH_HEAD_AUTO && hidden_dt != LMH_BF16) return LMH_ERR_SHAPE;
+    if (variant == LMH_HEAD_STREAM && c.rows > kStreamMaxRows) return LMH_ERR_SHAPE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gather_indices || logits_cu_seqlens || device_error) {
+        RowsArgs ra{cu_seqlens, num_segments, num_decode, num_tokens, logits_indices, c.rows,
+                    gather_indices, logits_cu_seqlens, device_error};
+        const lmh_status st = from_hip(launch_rows(ra, s));
+        if (st != LMH_OK) return st;
+    }
+    if (c.rows == 0) return LMH_OK;
+    HeadArgs h{hidden, num_tokens, hidden_dim, hidden_ld, weight, vocab, weight_ld, cu_seqlens,
+               num_decode, logits_indices, 0, c.rows, logits, logits_ld, logits_dt == LMH_BF16,
+               device_error};
+    return launch_head(h, hidden_dt == LMH_BF16, variant, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lmh_status_string(lmh_status st) {
+    switch (st) {
+        case LMH_OK: return "LMH_OK";
+        case LMH_ERR_NULL: return "LMH_ERR_NULL: a required pointer is NULL";
+        case LMH_ERR_SHAPE: return "LMH_ERR_SHAPE: invalid size, pitch or size limit";
+        case LMH_ERR_K: return "LMH_ERR_K: k < 0, k > vocab or min(k, blocks) * 64 > 8192";
+        case LMH_ERR_DTYPE: return "LMH_ERR_DTYPE: unsupported dtype";
+        case LMH_ERR_ALIGN: return "LMH_ERR_ALIGN: pointer or row pitch not aligned";
+        case LMH_ERR_WORKSPACE: return "LMH_ERR_WORKSPACE: workspace missing or too small";
+        case LMH_ERR_HIP: return "LMH_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown lmh_status";
+}
+
+lmh_status lmhead_gather_project(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                                 int64_t hidden_dim, int64_t hidden_ld, const void* weight,
+                                 lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
+                                 const int32_t* cu_seqlens, int32_t num_segments,
+                                 int32_t num_decode, const int32_t* logits_indices,
+                                 int32_t num_indices, void* logits, lmh_dtype logits_dt,
+                                 int64_t logits_ld, int32_t* logits_cu_seqlens,
+                                 int32_t* gather_indices, int32_t* device_error, void* stream) {
+    return gather_project_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld, weight,
+                               weight_dt, vocab, weight_ld, cu_seqlens, num_segments, num_decode,
+                               logits_indices, num_indices, logits, logits_dt, logits_ld,
+                               logits_cu_seqlens, gather_indices, device_error, stream,
+                               LMH_HEAD_AUTO);
+}
+
+lmh_status lmh_debug_gather_project(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                                    int64_t hidden_dim, int64_t hidden_ld, const void* weight,
+                                    lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
+                                    const int32_t* cu_seqlens, int32_t num_segments,
+                                    int32_t num_decode, const int32_t* logits_indices,
+                                    int32_t num_indices, void* logits, lmh_dtype logits_dt,
+                                    int64_t logits_ld, int32_t* logits_cu_seqlens,
+                                    int32_t* gather_indices, int32_t* device_error, void* stream,
+                                    int32_t variant) {
+    return gather_project_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld, weight,
+                               weight_dt, vocab, weight_ld, cu_seqlens, num_segments, num_decode,
+                               logits_indices, num_indices, logits, logits_dt, logits_ld,
+                               logits_cu_seqlens, gather_indices, device_error, stream, variant);
+}
+
+size_t logprob_reduce_workspace_size(int64_t rows, int64_t vocab, int32_t k) {
+    if (rows < 0 || vocab <= 0) return 256;
+    return plan_reduce(rows, vocab, k < 0 ? 0 : k).bytes;
+}
+
+lmh_status logprob_reduce(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
+                          int64_t logits_ld, const int32_t* selected_ids, int32_t k, float* lse,
+                          float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+                          void* workspace, size_t workspace_bytes, int32_t* device_error,
+                          void* stream) {
+    const lmh_status st = check_reduce_shape(logits_dt, rows, vocab, logits_ld, k);
+    if (st != LMH_OK) return st;
+    if (rows == 0) return LMH_OK;   // nothing is read or written
+    if (!logits || !lse) return LMH_ERR_NULL;
+    if (selected_ids && !selected_logprob) return LMH_ERR_NULL;
+    if (k > 0 && (!topk_ids || !topk_logprobs)) return LMH_ERR_NULL;
+    if (!aligned(logits, 16)) return LMH_ERR_ALIGN;
+    const ReducePlan p = plan_reduce(rows, vocab, k);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.bytes) return LMH_ERR_WORKSPACE;
+    if (rows == 0) return LMH_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ReduceArgs a{logits, logits_dt == LMH_BF16, logits_ld, selected_ids, lse, selected_logprob,
+                 topk_ids, topk_logprobs, workspace, device_error};
+    lmh_status r = from_hip(launch_reduce_stage1(p, a, s));
+    if (r != LMH_OK) return r;
+    return from_hip(launch_reduce_stage2(p, a, s));
+}
+
+lmh_status lmh_debug_reduce_stage1(const void* logits, lmh_dtype logits_dt, int64_t rows,
+                                   int64_t vocab, int64_t logits_ld, int32_t k, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!logits) return LMH_ERR_NULL;
+    const lmh_status st = check_reduce_shape(logits_dt, rows, vocab, logits_ld, k);
+    if (st != LMH_OK) return st;
+    if (!aligned(logits, 16)) return LMH_ERR_ALIGN;
+    const ReducePlan p = plan_reduce(rows, vocab, k);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.bytes) return LMH_ERR_WORKSPACE;
+    if (rows == 0) return LMH_OK;
+    ReduceArgs a{logits, logits_dt == LMH_BF16, logits_ld, nullptr, nullptr, nullptr,
+                 nullptr, nullptr, workspace, nullptr};
+    return from_hip(launch_reduce_stage1(p, a, static_cast<hipStream_t>(stream)));
+}
+
+size_t lmhead_logprobs_workspace_size(int64_t rows, int64_t vocab, int32_t k, int32_t chunk_rows) {
+    if (rows < 0 || vocab <= 0) return 256;
+    const int64_t chunk_cfg = chunk_rows > 0 ? chunk_rows : 256;
+    const int64_t chunk = rows < chunk_cfg ? (rows > 0 ? rows : 1) : chunk_cfg;
+    const int64_t ld = ceil_div(vocab, 4) * 4;
+    return up256((size_t)chunk * (size_t)ld * sizeof(float)) + plan_reduce(chunk, vocab, k < 0 ? 0 : k).bytes;
+}
+
+lmh_status lmhead_logprobs(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                           int64_t hidden_dim, int64_t hidden_ld, const void* weight,
+                           lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
+                           const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+                           const int32_t* logits_indices, int32_t num_indices,
+                           const int32_t* selected_ids, int32_t k, float* lse,
+                           float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+                           int32_t* logits_cu_seqlens, int32_t* gather_indices, int32_t chunk_rows,
+                           float* logits_debug, void* workspace, size_t workspace_bytes,
+                           int32_t* device_error, void* stream) {
+    const ProjectCheck c = check_project_inputs(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                                                weight, weight_dt, vocab, weight_ld, cu_seqlens,
+                                                num_segments, num_decode, logits_indices, num_indices);
+    if (c.st != LMH_OK) return c.st;
+    if (c.rows > 0) {
+        if (!lse) return LMH_ERR_NULL;
+        if (selected_ids && !selected_logprob) return LMH_ERR_NULL;
+        if (k > 0 && (!topk_ids || !topk_logprobs)) return LMH_ERR_NULL;
+    }
+    if (chunk_rows < 0) return LMH_ERR_SHAPE;
+    const int64_t R = c.rows;
+    const int64_t chunk_cfg = chunk_rows > 0 ? chunk_rows : 256;
+    const int64_t chunk = R < chunk_cfg ? (R > 0 ? R : 1) : chunk_cfg;
+    const int64_t ld = ceil_div(vocab, 4) * 4;
+    {
+        // the reduction's rules, checked on the fp32 logits layout it will read
+        const lmh_status st = check_reduce_shape(LMH_F32, chunk, vocab, ld, k);
+        if (st != LMH_OK) return st;
+    }
+    const ReducePlan pc = plan_reduce(chunk, vocab, k);
+    const size_t logits_bytes = logits_debug ? 0 : up256((size_t)chunk * (size_t)ld * sizeof(float));
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < logits_bytes + pc.bytes)
+        return LMH_ERR_WORKSPACE;
+    if (logits_debug && !aligned(logits_debug, 16)) return LMH_ERR_ALIGN;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gather_indices || logits_cu_seqlens || device_error) {
+        RowsArgs ra{cu_seqlens, num_segments, num_decode, num_tokens, logits_indices, c.rows,
+                    gather_indices, logits_cu_seqlens, device_error};
+        const lmh_status st = from_hip(launch_rows(ra, s));
+        if (st != LMH_OK) return st;
+    }
+    char* ws = static_cast<char*>(workspace);
+    float* ws_logits = reinterpret_cast<float*>(ws);
+    void* ws_reduce = ws + logits_bytes;
+    for (int64_t r0 = 0; r0 < R; r0 += chunk) {
+        const int32_t n = (int32_t)((R - r0) < chunk ? (R - r0) : chunk);
+        float* out = logits_debug ? logits_debug + r0 * ld : ws_logits;
+        HeadArgs h{hidden, num_tokens, hidden_dim, hidden_ld, weight, vocab, weight_ld, cu_seqlens,
+                   num_decode, logits_indices, (int32_t)r0, n, out, ld, false, device_error};
+        lmh_status st = launch_head(h, hidden_dt == LMH_BF16, LMH_HEAD_AUTO, s);
+        if (st != LMH_OK) return st;
+        ReducePlan q = pc;
+        q.rows = n;
+        ReduceArgs a{out, false, ld, selected_ids ? selected_ids + r0 : nullptr, lse + r0,
+                     selected_ids ? selected_logprob + r0 : nullptr,
+                     k > 0 ? topk_ids + r0 * k : nullptr, k > 0 ? topk_logprobs + r0 * k : nullptr,
+                     ws_reduce, device_error};
+        st = from_hip(launch_reduce_stage1(q, a, s));
+        if (st != LMH_OK) return st;
+        st = from_hip(launch_reduce_stage2(q, a, s));
+        if (st != LMH_OK) return st;
+    }
+    return LMH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,450 @@
+// head.hip -- gathered-row LM-head projection on gfx950 (vllm-metal release
+// v0.4.0, Summary: project only the sampled rows; mlxcel PR #1969: the head
+// acts per position, so a gathered row's logits equal the full projection's).
+//
+//   logits[r][v] = sum_k hidden[src(r)][k] * W[v][k]
+//
+// bf16 operands run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Both
+// bf16 kernels feed every output element the same sequence of MFMAs: the
+// hidden dimension in ascending 32-wide steps, lane l holding k = 8*(l/16) ..
+// 8*(l/16)+7 of the step for row/column l%16, no split over k. A row's logits
+// are therefore bitwise the same whichever kernel, tile position or set of
+// companion rows produced them.
+//
+//   stream  (R <= 64): weight-streaming. Each workgroup owns a 128-row slab of
+//           W and reads it once, straight from HBM into MFMA B fragments,
+//           a full k-chunk ahead; the gathered hidden rows (small, L2
+//           resident) are staged through LDS and shared by the 4 waves.
+//   tiled   (any R): 128 x 128 output tiles, both operands staged through
+//           double-buffered LDS, 4 waves of 64 x 64; workgroups are mapped so
+//           that each XCD walks the row tiles of one W slab together.
+//   f32     fp32 operands: plain fp32 FMA in ascending k.
+#include "lmh_internal.h"
+
+namespace lmh {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr float kNaN = __builtin_nanf("");
+
+__device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+struct HeadParams {
+    const uint16_t* hidden;
+    int64_t num_tokens, H, hld;
+    const uint16_t* W;
+    int64_t V, wld;
+    const int32_t* cu;
+    int32_t num_decode;
+    const int32_t* ex;
+    int32_t row0, R;
+    void* out;
+    int64_t old;
+};
+
+template <bool OUT_BF16>
+__device__ inline void store_out(void* out, int64_t off, float v) {
+    if (OUT_BF16)
+        reinterpret_cast<uint16_t*>(out)[off] = f32_to_bf16_rne(v);
+    else
+        reinterpret_cast<float*>(out)[off] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel: MT row tiles of 16 (R <= 16*MT), 128 vocab rows
+// per workgroup (32 per wave = two 16-wide N tiles), k in chunks of 128.
+// ---------------------------------------------------------------------------
+template <int MT, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
+    constexpr int KC = 128;             // hidden elements per chunk
+    constexpr int KS = KC / 32;         // MFMA k-steps per chunk
+    constexpr int AP = KC + 8;          // LDS row pitch (elements): +16 B breaks bank aliasing
+    constexpr int ROWS = MT * 16;
+    constexpr int AV = ROWS * KC / 8 / kThreads;   // 16-B A vectors per thread per chunk
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS][AP];
+    __shared__ int32_t sIdx[ROWS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t nbase = (int64_t)blockIdx.x * 128 + wave * 32;
+    const int l16 = lane & 15;
+    const int kq = (lane >> 4) * 8;
+
+    if (tid < ROWS)
+        sIdx[tid] = (tid < p.R) ? row_source(p.row0 + tid, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
+    __syncthreads();
+
+    const int nchunks = (int)((p.H + KC - 1) / KC);
+    const int ksteps = (int)((p.H + 31) / 32);
+
+    auto load_a = [&](int c, u32x4 (&r)[AV]) {
+#pragma unroll
+        for (int j = 0; j < AV; ++j) {
+            const int idx = j * kThreads + tid;
+            const int row = idx / (KC / 8);
+            const int kv = idx % (KC / 8);
+            const int64_t k = (int64_t)c * KC + kv * 8;
+            const int32_t t = sIdx[row];
+            r[j] = u32x4{0u, 0u, 0u, 0u};
+            if (t >= 0 && k < p.H)
+                r[j] = *reinterpret_cast<const u32x4*>(p.hidden + (int64_t)t * p.hld + k);
+        }
+    };
+    auto store_a = [&](int buf, const u32x4 (&r)[AV]) {
+#pragma unroll
+        for (int j = 0; j < AV; ++j) {
+            const int idx = j * kThreads + tid;
+            const int row = idx / (KC / 8);
+            const int kv = idx % (KC / 8);
+            *reinterpret_cast<u32x4*>(&sA[buf][row][kv * 8]) = r[j];
+        }
+    };
+    auto load_w = [&](int c, u32x4 (&r)[KS][2]) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t n = nbase + j * 16 + l16;
+                const int64_t k = (int64_t)c * KC + s * 32 + kq;
+                r[s][j] = u32x4{0u, 0u, 0u, 0u};
+                if (n < p.V && k < p.H)
+                    r[s][j] = *reinterpret_cast<const u32x4*>(p.W + n * p.wld + k);
+            }
+        }
+    };
+
+    f32x4 acc[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 areg[AV];
+    u32x4 wcur[KS][2], wnext[KS][2];
+    load_a(0, areg);
+    store_a(0, areg);
+    load_w(0, wcur);
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        const bool more = (c + 1) < nchunks;
+        if (more) {
+            load_w(c + 1, wnext);
+            load_a(c + 1, areg);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (c * KS + s < ksteps) {
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(&sA[buf][i * 16 + l16][s * 32 + kq]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma16(a, wcur[s][j], acc[i][j]);
+                }
+            }
+        }
+        if (more) store_a(buf ^ 1, areg);
+        __syncthreads();
+        if (more) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) wcur[s][j] = wnext[s][j];
+        }
+    }
+
+    // D fragment: lane holds rows 4*(lane/16)+e of column lane%16
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t v = nbase + j * 16 + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = i * 16 + (lane >> 4) * 4 + e;
+                if (r < p.R && v < p.V) {
+                    const float val = sIdx[r] < 0 ? kNaN : acc[i][j][e];
+                    store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v, val);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel: 128 x 128 tile per workgroup, k in chunks of 64, both operands
+// through double-buffered LDS; waves in a 2 x 2 grid of 64 x 64.
+// ---------------------------------------------------------------------------
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
+    constexpr int BM = 128, BN = 128, BK = 64;
+    constexpr int P = BK + 8;                     // LDS pitch (elements)
+    constexpr int LV = BM * BK / 8 / kThreads;    // 16-B vectors per thread per operand
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][P];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN][P];
+    __shared__ int32_t sIdx[BM];
+
+    // XCD-aware order: hardware places workgroup i on XCD i % 8; give each
+    // XCD a contiguous run of logical tiles, row tiles fastest, so the row
+    // tiles of one W slab share that XCD's L2.
+    const int32_t total = mtiles * ntiles;
+    const int32_t per_xcd = (int32_t)((gridDim.x + 7) / 8);
+    const int32_t logical = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
+    if (logical >= total) return;
+    const int32_t mt = logical % mtiles;
+    const int32_t nt = logical / mtiles;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = (wave >> 1) * 64;
+    const int wn = (wave & 1) * 64;
+    const int l16 = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int32_t m0 = mt * BM;
+    const int64_t n0 = (int64_t)nt * BN;
+
+    if (tid < BM) {
+        const int32_t r = m0 + tid;
+        sIdx[tid] = (r < p.R) ? row_source(p.row0 + r, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
+    }
+    __syncthreads();
+
+    const int nchunks = (int)((p.H + BK - 1) / BK);
+    const int ksteps = (int)((p.H + 31) / 32);
+
+    auto load = [&](int c, u32x4 (&ra)[LV], u32x4 (&rb)[LV]) {
+#pragma unroll
+        for (int j = 0; j < LV; ++j) {
+            const int idx = j * kThreads + tid;
+            const int row = idx / (BK / 8);
+            const int kv = idx % (BK / 8);
+            const int64_t k = (int64_t)c * BK + kv * 8;
+            const int32_t t = sIdx[row];
+            ra[j] = u32x4{0u, 0u, 0u, 0u};
+            rb[j] = u32x4{0u, 0u, 0u, 0u};
+            if (t >= 0 && k < p.H)
+                ra[j] = *reinterpret_cast<const u32x4*>(p.hidden + (int64_t)t * p.hld + k);
+            const int64_t n = n0 + row;
+            if (n < p.V && k < p.H) rb[j] = *reinterpret_cast<const u32x4*>(p.W + n * p.wld + k);
+        }
+    };
+    auto store = [&](int buf, const u32x4 (&ra)[LV], const u32x4 (&rb)[LV]) {
+#pragma unroll
+        for (int j = 0; j < LV; ++j) {
+            const int idx = j * kThreads + tid;
+            const int row = idx / (BK / 8);
+            const int kv = idx % (BK / 8);
+            *reinterpret_cast<u32x4*>(&sA[buf][row][kv * 8]) = ra[j];
+            *reinterpret_cast<u32x4*>(&sB[buf][row][kv * 8]) = rb[j];
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 ra[LV], rb[LV];
+    load(0, ra, rb);
+    store(0, ra, rb);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        const bool more = (c + 1) < nchunks;
+        if (more) load(c + 1, ra, rb);
+#pragma unroll
+        for (int s = 0; s < BK / 32; ++s) {
+            if (c * (BK / 32) + s < ksteps) {
+                u32x4 a[4], b[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a[i] = *reinterpret_cast<const u32x4*>(&sA[buf][wm + i * 16 + l16][s * 32 + kq]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    b[j] = *reinterpret_cast<const u32x4*>(&sB[buf][wn + j * 16 + l16][s * 32 + kq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+            }
+        }
+        if (more) store(buf ^ 1, ra, rb);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t v = n0 + wn + j * 16 + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rl = wm + i * 16 + (lane >> 4) * 4 + e;
+                const int32_t r = m0 + rl;
+                if (r < p.R && v < p.V) {
+                    const float val = sIdx[rl] < 0 ? kNaN : acc[i][j][e];
+                    store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v, val);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: 8 rows x 256 vocab columns per workgroup; hidden rows staged in
+// LDS by k-chunks of 128; one fp32 FMA per (row, column, k), k ascending.
+// ---------------------------------------------------------------------------
+struct HeadParamsF32 {
+    const float* hidden;
+    int64_t num_tokens, H, hld;
+    const float* W;
+    int64_t V, wld;
+    const int32_t* cu;
+    int32_t num_decode;
+    const int32_t* ex;
+    int32_t row0, R;
+    void* out;
+    int64_t old;
+};
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void k_head_f32(HeadParamsF32 p) {
+    constexpr int RB = 8, KC = 128;
+    __shared__ float sA[RB][KC];
+    __shared__ int32_t sIdx[RB];
+    const int tid = threadIdx.x;
+    const int32_t m0 = blockIdx.y * RB;
+    const int64_t v = (int64_t)blockIdx.x * kThreads + tid;
+    if (tid < RB) {
+        const int32_t r = m0 + tid;
+        sIdx[tid] = (r < p.R) ? row_source(p.row0 + r, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
+    }
+    __syncthreads();
+    float acc[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) acc[i] = 0.f;
+    for (int64_t k0 = 0; k0 < p.H; k0 += KC) {
+        for (int j = tid; j < RB * KC; j += kThreads) {
+            const int r = j / KC;
+            const int64_t k = k0 + j % KC;
+            const int32_t t = sIdx[r];
+            sA[r][j % KC] = (t >= 0 && k < p.H) ? p.hidden[(int64_t)t * p.hld + k] : 0.f;
+        }
+        __syncthreads();
+        if (v < p.V) {
+            const int kn = (int)((p.H - k0) < KC ? (p.H - k0) : KC);
+            const float* wr = p.W + v * p.wld + k0;
+            for (int k = 0; k < kn; ++k) {
+                const float w = wr[k];
+#pragma unroll
+                for (int i = 0; i < RB; ++i) acc[i] = fmaf(sA[i][k], w, acc[i]);
+            }
+        }
+        __syncthreads();
+    }
+    if (v < p.V) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int32_t r = m0 + i;
+            if (r < p.R) store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v, sIdx[i] < 0 ? kNaN : acc[i]);
+        }
+    }
+}
+
+HeadParams to_params(const HeadArgs& a) {
+    HeadParams p;
+    p.hidden = static_cast<const uint16_t*>(a.hidden);
+    p.num_tokens = a.num_tokens;
+    p.H = a.hidden_dim;
+    p.hld = a.hidden_ld;
+    p.W = static_cast<const uint16_t*>(a.weight);
+    p.V = a.vocab;
+    p.wld = a.weight_ld;
+    p.cu = a.cu;
+    p.num_decode = a.num_decode;
+    p.ex = a.ex;
+    p.row0 = a.row0;
+    p.R = a.rows;
+    p.out = a.out;
+    p.old = a.out_ld;
+    return p;
+}
+
+}  // namespace
+
+hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s) {
+    if (a.rows <= 0) return hipSuccess;
+    if (a.rows > kStreamMaxRows) return hipErrorInvalidValue;
+    const HeadParams p = to_params(a);
+    const dim3 grid((unsigned)((a.vocab + 127) / 128));
+    const int mt = (a.rows + 15) / 16;
+#define LMH_STREAM_CASE(MT)                                                                   \
+    case MT:                                                                                   \
+        if (a.out_bf16)                                                                        \
+            hipLaunchKernelGGL((k_head_stream<MT, true>), grid, dim3(kThreads), 0, s, p);       \
+        else                                                                                   \
+            hipLaunchKernelGGL((k_head_stream<MT, false>), grid, dim3(kThreads), 0, s, p);      \
+        break;
+    switch (mt) {
+        LMH_STREAM_CASE(1)
+        LMH_STREAM_CASE(2)
+        LMH_STREAM_CASE(3)
+        LMH_STREAM_CASE(4)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef LMH_STREAM_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
+    if (a.rows <= 0) return hipSuccess;
+    const HeadParams p = to_params(a);
+    const int32_t mtiles = (a.rows + 127) / 128;
+    const int64_t ntiles = (a.vocab + 127) / 128;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    const dim3 grid((unsigned)(((total + 7) / 8) * 8));
+    if (a.out_bf16)
+        hipLaunchKernelGGL(k_head_tiled<true>, grid, dim3(kThreads), 0, s, p, mtiles, (int32_t)ntiles);
+    else
+        hipLaunchKernelGGL(k_head_tiled<false>, grid, dim3(kThreads), 0, s, p, mtiles, (int32_t)ntiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_head_f32(const HeadArgs& a, hipStream_t s) {
+    if (a.rows <= 0) return hipSuccess;
+    HeadParamsF32 p;
+    p.hidden = static_cast<const float*>(a.hidden);
+    p.num_tokens = a.num_tokens;
+    p.H = a.hidden_dim;
+    p.hld = a.hidden_ld;
+    p.W = static_cast<const float*>(a.weight);
+    p.V = a.vocab;
+    p.wld = a.weight_ld;
+    p.cu = a.cu;
+    p.num_decode = a.num_decode;
+    p.ex = a.ex;
+    p.row0 = a.row0;
+    p.R = a.rows;
+    p.out = a.out;
+    p.old = a.out_ld;
+    const dim3 grid((unsigned)((a.vocab + kThreads - 1) / kThreads), (unsigned)((a.rows + 7) / 8));
+    if (a.out_bf16)
+        hipLaunchKernelGGL(k_head_f32<true>, grid, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(k_head_f32<false>, grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace lmh

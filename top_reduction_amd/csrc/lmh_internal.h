@@ -1,0 +1,121 @@
+// lmh_internal.h -- launchers and small device helpers shared by the HIP
+// translation units of liblmhead (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lmhead.h"
+
+namespace lmh {
+
+constexpr int kBlock = LMH_BLOCK;                // logits per prefilter block
+constexpr int kMaxCandidates = LMH_MAX_CANDIDATES;
+constexpr int kStreamMaxRows = 64;               // weight-streaming head limit
+
+// ----------------------------------------------------------------------------
+// Row source of logits row r (vllm-metal release, Summary). Sampled mode:
+// the last row of segment r, valid only when the segment is non-empty and,
+// for a decode segment, exactly one token long. Explicit mode: ex[r].
+// Returns -1 when the row has no valid source in [0, num_tokens).
+// ----------------------------------------------------------------------------
+__device__ inline int32_t row_source(int32_t r, const int32_t* cu, int32_t num_decode,
+                                     int64_t num_tokens, const int32_t* ex) {
+    int32_t t;
+    if (ex != nullptr) {
+        t = ex[r];
+    } else {
+        const int32_t lo = cu[r], hi = cu[r + 1];
+        const int32_t len = hi - lo;
+        if (len <= 0 || (r < num_decode && len != 1)) return -1;
+        t = hi - 1;
+    }
+    return (t < 0 || (int64_t)t >= num_tokens) ? -1 : t;
+}
+
+// Monotone 32-bit key of a float: a < b  <=>  key(a) < key(b) for non-NaN
+// values, with -0 and +0 mapped to the same key.
+__device__ inline uint32_t f32_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    u = (x == 0.0f) ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float key_f32(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ----------------------------------------------------------------------------
+// Launchers (host side, enqueue only; return hipSuccess or the launch error)
+// ----------------------------------------------------------------------------
+struct RowsArgs {
+    const int32_t* cu;
+    int32_t num_segments;
+    int32_t num_decode;
+    int64_t num_tokens;
+    const int32_t* ex;   // explicit indices or nullptr
+    int32_t rows;        // R
+    int32_t* gather_out; // may be nullptr
+    int32_t* lcu_out;    // may be nullptr
+    int32_t* err;        // may be nullptr
+};
+hipError_t launch_rows(const RowsArgs& a, hipStream_t s);
+
+struct HeadArgs {
+    const void* hidden;
+    int64_t num_tokens, hidden_dim, hidden_ld;
+    const void* weight;
+    int64_t vocab, weight_ld;
+    const int32_t* cu;
+    int32_t num_decode;
+    const int32_t* ex;
+    int32_t row0;        // first logits row of this launch (chunking)
+    int32_t rows;        // rows in this launch
+    void* out;           // points at logits row `row0`
+    int64_t out_ld;
+    bool out_bf16;
+    int32_t* err;
+};
+// bf16 MFMA heads. stream: R <= kStreamMaxRows; tiled: any R.
+hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s);
+hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s);
+// fp32 FMA head.
+hipError_t launch_head_f32(const HeadArgs& a, hipStream_t s);
+
+struct ReducePlan {
+    int64_t rows, vocab;
+    int32_t k;
+    int32_t nb;          // ceil(vocab / 64)
+    int32_t splits;      // stage-1 workgroups per row
+    int32_t bps;         // blocks per split
+    size_t part_off, keys_off, bytes;  // workspace layout
+};
+ReducePlan plan_reduce(int64_t rows, int64_t vocab, int32_t k);
+
+struct ReduceArgs {
+    const void* logits;
+    bool bf16;
+    int64_t ld;
+    const int32_t* sel;  // may be nullptr
+    float* lse;
+    float* sel_lp;       // may be nullptr
+    int32_t* topk_ids;
+    float* topk_lp;
+    void* ws;
+    int32_t* err;
+};
+hipError_t launch_reduce_stage1(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
+hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
+
+}  // namespace lmh
