@@ -1,0 +1,386 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective LM head and the on-device logprob reduction on
+one MI355X.
+
+Headline (the JSON line's `value`): logprob-reduce rows/s on the
+prompt-scoring chunk -- 256 rows x 248,320 vocabulary bf16 logits, K = 20
+(MTPLX PR #532, Motivation and Evidence) -- one `logprob_reduce` call (both
+kernels) per step, inputs resident in HBM, four distinct chunks rotated so
+that no step is served from the 256 MB MALL.
+
+The same line carries:
+  roofline      the dominant kernel (the reduction's streaming pass) against
+                the 8 TB/s HBM peak, timed live with HIP events per launch;
+  cpu_baseline  the f64 CPU oracle on a bounded sample of the same chunk;
+  reduce_by_k   the chunk at K = 0, 1, 20, 128;
+  decode        32 x 151,936 decode rows, K = 5 (openinfer issue #719);
+  head          Qwen3-0.6B-shaped selective head (40 of 81,920 rows) and the
+                full 2048-row projection (vllm-metal release, Benchmarks);
+  fused         Llama-3-8B-shaped fused head + logprobs, mixed batch and a
+                1024-token prompt in 256-row chunks.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections ...]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+METRIC = "logprob-reduce rows/s & GB/s vs HBM peak; sampled-row LM-head ms"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sections", default="reduce,decode,head,fused,cpu")
+    ap.add_argument("--k", type=int, default=20)
+    return ap.parse_args()
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(kernel: str, src: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    the kernel's source has changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entries = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = entries.get(kernel)
+    if not e or e.get("source_sha256") != source_sha(src):
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP-event timing on torch's current stream (the stream every call here
+    is enqueued on). Before each timed region a spin kernel keeps the GPU busy
+    while the launches queue up, so host-side launch cost does not leak into
+    the measured intervals."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def prime(self, ms=30.0):
+        try:
+            self.torch.cuda._sleep(int(ms * 1e-3 * 2.1e9))
+        except (AttributeError, RuntimeError):
+            pass
+
+    def loop(self, fns, steps, warmup):
+        """ms per call of a back-to-back loop over `fns` (rotating)."""
+        torch = self.torch
+        for i in range(warmup):
+            fns[i % len(fns)]()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        self.prime()
+        a.record()
+        for i in range(steps):
+            fns[i % len(fns)]()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def each(self, fns, steps, warmup):
+        """Per-launch durations (ms): an event pair around every call."""
+        torch = self.torch
+        for i in range(warmup):
+            fns[i % len(fns)]()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        self.prime()
+        for i in range(steps):
+            ev[i][0].record()
+            fns[i % len(fns)]()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return np.array([x.elapsed_time(y) for x, y in ev])
+
+
+def vp(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "
+                  "the path is single-device and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import top_reduction_amd as lmh
+
+    sections = set(args.sections.split(","))
+    L = lmh.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    timer = Timer(torch)
+    steps, warmup, K = args.steps, args.warmup, args.k
+    result = {}
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------------
+    # headline: prompt-scoring chunk reduce
+    # ------------------------------------------------------------------
+    rows, V = 256, synth.VOCAB_SCORING
+    chunks = []
+    for i, dist in enumerate(["normal", "peaked", "gumbel", "normal"]):
+        bits, sel = synth.scoring_chunk(7000 + i, dist, K)
+        chunks.append((lmh_bf16(torch, bits, dev), torch.from_numpy(sel).to(dev), bits, sel))
+        log(f"chunk {i} ({dist}) ready")
+    nbytes = rows * V * 2
+    ws_size = L.logprob_reduce_workspace_size(rows, V, 128)
+    wss = [torch.empty(ws_size, dtype=torch.uint8, device=dev) for _ in chunks]
+
+    def reduce_calls(k):
+        outs = []
+        fns = []
+        for (t, s, _, _), ws in zip(chunks, wss):
+            o = (torch.empty(rows, device=dev), torch.empty(rows, device=dev),
+                 torch.empty((rows, max(k, 1)), dtype=torch.int32, device=dev),
+                 torch.empty((rows, max(k, 1)), device=dev))
+            outs.append(o)
+            a = (vp(t), lmh.LMH_BF16, rows, V, V, vp(s), k, vp(o[0]), vp(o[1]),
+                 vp(o[2]) if k else None, vp(o[3]) if k else None, vp(ws), ws.numel(), None, stream)
+            fns.append(lambda a=a: L.logprob_reduce(*a))
+        return fns, outs
+
+    fns, _ = reduce_calls(K)
+    assert all(f() == 0 for f in fns)
+    ms = timer.loop(fns, steps, warmup)
+    log(f"reduce K={K}: {ms * 1e3:.1f} us/step")
+    stage1 = []
+    for (t, _, _, _), ws in zip(chunks, wss):
+        a = (vp(t), lmh.LMH_BF16, rows, V, V, K, vp(ws), ws.numel(), stream)
+        stage1.append(lambda a=a: L.lmh_debug_reduce_stage1(*a))
+    d1 = timer.each(stage1, steps, warmup)
+    t1 = float(np.mean(d1))
+    achieved = nbytes / (t1 * 1e-3) / 1e9
+    log(f"stage1: mean {t1 * 1e3:.1f} us  median {np.median(d1) * 1e3:.1f} us  -> {achieved:.0f} GB/s")
+    stage1_src = os.path.join(ROOT, "top_reduction_amd", "csrc", "reduce.hip")
+    roofline = {"bound": "hbm", "kernel": "k_stage1<bf16> (reduce streaming pass)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic("reduce_stage1_bf16", stage1_src),
+                "bytes_per_launch": nbytes, "launch_us": round(t1 * 1e3, 2)}
+
+    if "reduce" in sections:
+        by_k = {}
+        for k in (0, 1, 20, 128):
+            f, _ = reduce_calls(k)
+            m = timer.loop(f, steps, warmup)
+            by_k[str(k)] = {"us": round(m * 1e3, 2), "rows_per_s": round(rows / (m * 1e-3)),
+                            "gbps": round(nbytes / (m * 1e-3) / 1e9, 1)}
+            log(f"reduce K={k}: {m * 1e3:.1f} us")
+        result["reduce_by_k"] = by_k
+
+    # ------------------------------------------------------------------
+    # decode rows
+    # ------------------------------------------------------------------
+    if "decode" in sections:
+        bits, sel = synth.decode_logits(7100, sel_mode="uniform")
+        base = lmh_bf16(torch, bits, dev)
+        copies = [base.clone() for _ in range(32)]
+        s = torch.from_numpy(sel).to(dev)
+        k = 5
+        wsz = L.logprob_reduce_workspace_size(32, synth.VOCAB_QWEN3, k)
+        ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+        o = (torch.empty(32, device=dev), torch.empty(32, device=dev),
+             torch.empty((32, k), dtype=torch.int32, device=dev), torch.empty((32, k), device=dev))
+        f = [lambda t=t: L.logprob_reduce(vp(t), lmh.LMH_BF16, 32, synth.VOCAB_QWEN3,
+                                          synth.VOCAB_QWEN3, vp(s), k, vp(o[0]), vp(o[1]), vp(o[2]),
+                                          vp(o[3]), vp(ws), ws.numel(), None, stream) for t in copies]
+        m = timer.loop(f, steps, warmup)
+        result["decode"] = {"workload": "32 x 151936 bf16 decode rows, K=5", "us": round(m * 1e3, 2),
+                            "rows_per_s": round(32 / (m * 1e-3)),
+                            "gbps": round(32 * synth.VOCAB_QWEN3 * 2 / (m * 1e-3) / 1e9, 1)}
+        log(f"decode: {m * 1e3:.1f} us")
+        del copies
+
+    # ------------------------------------------------------------------
+    # selective head (Qwen3-0.6B shape) and the full 2048-row projection
+    # ------------------------------------------------------------------
+    if "head" in sections:
+        d = synth.selective_head_batch(7200)
+        hid = lmh_bf16(torch, d["hidden"], dev)
+        w = lmh_bf16(torch, d["weight"], dev)
+        cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
+        T, H = d["hidden"].shape
+        Vq = w.shape[0]
+        R = 40
+        out = torch.empty((R, Vq), device=dev)
+        lcu = torch.empty(R + 1, dtype=torch.int32, device=dev)
+
+        def sel_call():
+            return L.lmhead_gather_project(vp(hid), lmh.LMH_BF16, T, H, H, vp(w), lmh.LMH_BF16, Vq, H,
+                                           vp(cu), R, 0, None, 0, vp(out), lmh.LMH_F32, Vq, vp(lcu),
+                                           None, None, stream)
+
+        def sel_kernel():
+            return L.lmhead_gather_project(vp(hid), lmh.LMH_BF16, T, H, H, vp(w), lmh.LMH_BF16, Vq, H,
+                                           vp(cu), R, 0, None, 0, vp(out), lmh.LMH_F32, Vq, None,
+                                           None, None, stream)
+        assert sel_call() == 0
+        hs = max(steps // 4, 10)
+        m_sel = timer.loop([sel_call], hs, warmup)
+        dk = timer.each([sel_kernel], hs, warmup)
+        tk = float(np.mean(dk))
+        head_bytes = Vq * H * 2 + R * H * 2 + R * Vq * 4
+        ach = head_bytes / (tk * 1e-3) / 1e9
+        log(f"selective head: call {m_sel * 1e3:.1f} us, kernel {tk * 1e3:.1f} us -> {ach:.0f} GB/s")
+
+        full_idx = torch.arange(2048, dtype=torch.int32, device=dev)
+        full = torch.empty((2048, Vq), device=dev)
+
+        def full_call():
+            return L.lmhead_gather_project(vp(hid), lmh.LMH_BF16, T, H, H, vp(w), lmh.LMH_BF16, Vq, H,
+                                           vp(cu), R, 0, vp(full_idx), 2048, vp(full), lmh.LMH_F32, Vq,
+                                           None, None, None, stream)
+        assert full_call() == 0
+        fs = max(steps // 20, 5)
+        df = timer.each([full_call], fs, 2)
+        tf = float(np.mean(df))
+        flops = 2.0 * 2048 * H * Vq
+        tfl = flops / (tf * 1e-3) / 1e12
+        log(f"full 2048-row head: {tf * 1e3:.1f} us -> {tfl:.0f} TFLOP/s")
+        result["head"] = {
+            "workload": "Qwen3-0.6B head: 40 of 81920 packed rows (40 x 2048 prefills), hidden 1024, "
+                        "vocab 151936, bf16 in, fp32 logits",
+            "selective_ms": round(m_sel, 4), "selective_kernel_us": round(tk * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                         "bytes_per_launch": head_bytes,
+                         "traffic": load_traffic("head_stream_bf16",
+                                                 os.path.join(ROOT, "top_reduction_amd", "csrc", "head.hip"))},
+            "full_2048_ms": round(tf, 4),
+            "full_roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4)},
+        }
+        del hid, w, full, out
+
+    # ------------------------------------------------------------------
+    # fused head + logprobs (Llama-3-8B shape)
+    # ------------------------------------------------------------------
+    if "fused" in sections:
+        w_np = synth.llama3_head_weight(7300)
+        w = lmh_bf16(torch, w_np, dev)
+        del w_np
+        Vl, H = w.shape
+        kk = 20
+        fused = {}
+        for mode in ("mixed", "prompt"):
+            d = synth.mixed_batch(7301) if mode == "mixed" else synth.prompt_batch(7302)
+            hid = lmh_bf16(torch, d["hidden"], dev)
+            cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
+            sel = torch.from_numpy(d["selected"]).to(dev)
+            ex = None if mode == "mixed" else torch.from_numpy(d["logits_indices"]).to(dev)
+            T = hid.shape[0]
+            S = cu.numel() - 1
+            R = S if ex is None else ex.numel()
+            wsz = L.lmhead_logprobs_workspace_size(R, Vl, kk, 256)
+            ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+            o = (torch.empty(R, device=dev), torch.empty(R, device=dev),
+                 torch.empty((R, kk), dtype=torch.int32, device=dev), torch.empty((R, kk), device=dev))
+
+            def call(hid=hid, cu=cu, sel=sel, ex=ex, T=T, S=S, R=R, ws=ws, o=o, nd=d["num_decode"]):
+                return L.lmhead_logprobs(vp(hid), lmh.LMH_BF16, T, H, H, vp(w), lmh.LMH_BF16, Vl, H,
+                                         vp(cu), S, nd, None if ex is None else vp(ex),
+                                         0 if ex is None else R, vp(sel), kk, vp(o[0]), vp(o[1]),
+                                         vp(o[2]), vp(o[3]), None, None, 256, None, vp(ws),
+                                         ws.numel(), None, stream)
+            assert call() == 0
+            n = max(steps // 10, 5)
+            m = timer.loop([call], n, 3)
+            entry = {"ms": round(m, 4), "rows": R, "rows_per_s": round(R / (m * 1e-3))}
+            if mode == "mixed":
+                entry["workload"] = ("32 decode rows + prefills 512/2048 x4 (10272 tokens), 40 sampled "
+                                     "rows, hidden 4096, vocab 128256, K=20")
+                wb = Vl * H * 2
+                entry["weight_stream_gbps"] = round(wb / (m * 1e-3) / 1e9, 1)
+            else:
+                entry["workload"] = "one 1024-token prompt, all positions, 256-row chunks, K=20"
+                entry["tflops"] = round(2.0 * R * H * Vl / (m * 1e-3) / 1e12, 1)
+            fused[mode] = entry
+            log(f"fused {mode}: {m:.3f} ms")
+            del hid, ws
+        result["fused"] = fused
+        del w
+
+    # ------------------------------------------------------------------
+    # CPU baseline: the f64 oracle on the scoring chunk
+    # ------------------------------------------------------------------
+    cpu = None
+    if "cpu" in sections:
+        import oracle
+        bits, sel = chunks[0][2], chunks[0][3]
+        nrows = rows
+        t0 = time.perf_counter()
+        oracle.reduce(bits[:nrows], sel[:nrows], K)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(nrows / dt, 2), "unit": "rows/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{nrows} rows of the 256 x 248320 bf16 chunk (normal), K={K}, f64 max + "
+                         f"exp-sum passes and a full sort per row; {dt:.2f} s"}
+        log(f"cpu oracle: {nrows / dt:.1f} rows/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(rows / (ms * 1e-3)),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prompt-scoring chunk: logprob_reduce over 256 x 248320 bf16 logits, "
+                               "K=20, selected ids uniform; 4 seeded chunks (normal, peaked, gumbel, "
+                               "normal) rotated",
+                   "rows": rows, "vocab": V, "k": K, "input_dtype": "bf16"},
+        "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    line.update(result)
+    print(json.dumps(line), flush=True)
+
+
+def lmh_bf16(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+if __name__ == "__main__":
+    main()
