@@ -58,7 +58,7 @@ lmh_status check_reduce_shape(lmh_dtype dt, int64_t rows, int64_t vocab, int64_t
     if ((k < nb ? k : nb) * (int64_t)kBlock > kMaxCandidates) return LMH_ERR_K;
     if (k > 0 && nb > kMaxCandidates) return LMH_ERR_SHAPE;
     const ReducePlan p = plan_reduce(rows, vocab, k);
-    if (rows * (int64_t)p.splits > INT32_MAX) return LMH_ERR_SHAPE;
+    if (p.wgs > INT32_MAX) return LMH_ERR_SHAPE;
     return LMH_OK;
 }
 
@@ -255,8 +255,11 @@ lmh_status lmhead_logprobs(const void* hidden, lmh_dtype hidden_dt, int64_t num_
                    num_decode, logits_indices, (int32_t)r0, n, out, ld, false, device_error};
         lmh_status st = launch_head(h, hidden_dt == LMH_BF16, LMH_HEAD_AUTO, s);
         if (st != LMH_OK) return st;
-        ReducePlan q = pc;
-        q.rows = n;
+        // this chunk's decomposition, inside the workspace layout sized for a full chunk
+        ReducePlan q = plan_reduce(n, vocab, k);
+        q.part_off = pc.part_off;
+        q.keys_off = pc.keys_off;
+        q.bytes = pc.bytes;
         ReduceArgs a{out, false, ld, selected_ids ? selected_ids + r0 : nullptr, lse + r0,
                      selected_ids ? selected_logprob + r0 : nullptr,
                      k > 0 ? topk_ids + r0 * k : nullptr, k > 0 ? topk_logprobs + r0 * k : nullptr,

@@ -23,8 +23,8 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;        // 16-byte loads in flight per lane
-constexpr int kTargetWgs = 2048;  // stage-1 workgroups to aim for (8 per CU)
+constexpr int kSeg = 4096;          // logits per stage-1 work item (one wave)
+constexpr int64_t kMaxWaves = 1 << 22; // stage-1 waves before items are doubled up
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -67,43 +67,55 @@ __device__ inline float key_value(uint32_t k) {
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1
+// Stage 1: a row is cut into fixed segments of kSeg logits (the last one
+// partial); each segment is one work item of one wave. Items are numbered
+// row-major and every wave takes `ipw` consecutive items, so a wave streams a
+// contiguous stretch of memory, prefetching the next item while it reduces
+// the current one. Lane l of a wave reads the item's 16-byte vectors l,
+// l + 64, ...; the 8 (bf16) or 16 (fp32) lanes that share a 64-logit block
+// combine its maximum with DPP. The item's (max, sum-exp) partial is merged
+// across the wave by a fixed butterfly. Neither the item boundaries nor the
+// merge order depend on how many rows a call holds, so each row's results
+// are bitwise independent of the batch around it.
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__ logits, int64_t ld,
-                                                     int64_t V, int32_t nb, int32_t bps,
-                                                     int32_t splits, float2* __restrict__ part,
-                                                     void* __restrict__ keys) {
-    constexpr int EPV = BF16 ? 8 : 4;    // elements per 16-byte vector
-    constexpr int VPB = kBlock / EPV;    // vectors (lanes) per 64-logit block
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void k_stage1(const uint8_t* __restrict__ logits, int64_t ld, int64_t V, int32_t kld, int32_t P,
+              int64_t nitems, int32_t ipw, float2* __restrict__ part, void* __restrict__ keys) {
+    constexpr int EPV = BF16 ? 8 : 4;          // elements per 16-byte vector
+    constexpr int VPB = kBlock / EPV;          // vectors (lanes) per 64-logit block
+    constexpr int VPS = 4;                     // vectors per lane per step
+    constexpr int SPI = kSeg / EPV / 64 / VPS; // steps per item (bf16 2, fp32 4)
     constexpr size_t ESZ = BF16 ? 2 : 4;
-    const int64_t wg = blockIdx.x;
-    const int64_t row = wg / splits;
-    const int32_t split = (int32_t)(wg - row * splits);
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-
-    const int32_t b0 = split * bps;
-    const int32_t b1 = min(nb, b0 + bps);
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t it0 = gw * ipw;
+    const int64_t it1 = min(nitems, it0 + ipw);
+    if (it0 >= it1) return;
+    const int64_t nsteps = (it1 - it0) * SPI;
     const int64_t nvec_row = (V + EPV - 1) / EPV;
-    const int64_t vb = (int64_t)b0 * VPB;
-    const int64_t ve = min((int64_t)b1 * VPB, nvec_row);
-    const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
-    const u32x4* vp = reinterpret_cast<const u32x4*>(rowp);
     const int64_t ragged_vec = (V % EPV) ? nvec_row - 1 : -1;
     const uint32_t ninf_word = BF16 ? 0xFF80FF80u : 0xFF800000u;
 
-    float m = kNegInf, s = 0.f;
-    const int64_t n = ve - vb;
-    for (int64_t base = 0; base < n; base += (int64_t)kThreads * kUnroll) {
-        u32x4 buf[kUnroll];
+    const int64_t nfull = V / EPV;   // vectors of the row with no element past V
+
+    // a step covers vectors [vb, vb + 64*VPS) of one segment (clipped to the row)
+    auto load_step = [&](int64_t row, int32_t seg, int32_t sub, u32x4 (&buf)[VPS]) {
+        const int64_t vb = (int64_t)seg * (kSeg / EPV) + sub * (64 * VPS);
+        const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
+        const u32x4* vp = reinterpret_cast<const u32x4*>(rowp);
+        if (vb + 64 * VPS <= nfull) {   // wave-uniform: the whole step is in the row
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t v = vb + base + u * kThreads + tid;
-            buf[u] = u32x4{ninf_word, ninf_word, ninf_word, ninf_word};
-            if (v < ve) {
+            for (int j = 0; j < VPS; ++j) buf[j] = vp[vb + j * 64 + lane];
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < VPS; ++j) {
+            const int64_t v = vb + j * 64 + lane;
+            buf[j] = u32x4{ninf_word, ninf_word, ninf_word, ninf_word};
+            if (v < nvec_row) {
                 if (v != ragged_vec) {
-                    buf[u] = vp[v];
+                    buf[j] = vp[v];
                 } else {
                     uint32_t w[4] = {ninf_word, ninf_word, ninf_word, ninf_word};
                     for (int e = 0; e < EPV; ++e) {
@@ -118,15 +130,44 @@ __global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__
                             }
                         }
                     }
-                    buf[u] = u32x4{w[0], w[1], w[2], w[3]};
+                    buf[j] = u32x4{w[0], w[1], w[2], w[3]};
                 }
             }
         }
+    };
+
+    // block keys of the current item, staged per wave and written with one
+    // coalesced store when the item is done
+    __shared__ uint32_t skeys[kThreads / 64][kSeg / kBlock];
+    uint32_t* wkeys = skeys[threadIdx.x >> 6];
+
+    u32x4 cur[VPS], nxt[VPS];
+    // (row, segment, step) of the step being loaded and of the one being reduced,
+    // advanced incrementally (no division in the loop)
+    int64_t lrow = it0 / P;
+    int32_t lseg = (int32_t)(it0 - lrow * P), lsub = 0;
+    int64_t row = lrow;
+    int32_t seg = lseg, sub = 0;
+    auto advance = [&](int64_t& r, int32_t& sg, int32_t& sb) {
+        if (++sb == SPI) {
+            sb = 0;
+            if (++sg == P) {
+                sg = 0;
+                ++r;
+            }
+        }
+    };
+    load_step(lrow, lseg, lsub, cur);
+    float m = kNegInf, s = 0.f;
+    for (int64_t q = 0; q < nsteps; ++q) {
+        advance(lrow, lseg, lsub);
+        if (q + 1 < nsteps) load_step(lrow, lseg, lsub, nxt);
+        const int64_t vb = (int64_t)seg * (kSeg / EPV) + sub * (64 * VPS);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t v = vb + base + u * kThreads + tid;
+        for (int j = 0; j < VPS; ++j) {
+            const int64_t v = vb + j * 64 + lane;
             float x[EPV];
-            const uint32_t w[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+            const uint32_t w[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
             if (BF16) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -143,13 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__
 
             // block maximum over the VPB lanes of this 64-logit block
             const float bm = BF16 ? dpp_max8(lm) : dpp_max16(lm);
-            if ((lane & (VPB - 1)) == 0 && v < ve) {
-                const int64_t blk = v / VPB;
-                if (BF16)
-                    reinterpret_cast<uint16_t*>(keys)[row * nb + blk] = (uint16_t)(f32_key(bm) >> 16);
-                else
-                    reinterpret_cast<uint32_t*>(keys)[row * nb + blk] = f32_key(bm);
-            }
+            if ((lane & (VPB - 1)) == 0) wkeys[(sub * 64 * VPS + j * 64 + lane) / VPB] = f32_key(bm);
 
             // online (max, sum-exp); a rescale by exp2(0) is exactly 1
             const float mn = fmaxf(m, lm);
@@ -160,22 +195,35 @@ __global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__
             s = acc;
             m = mn;
         }
-    }
-
-    // workgroup combine in a fixed order: butterfly in each wave, then waves 0..3
+        if (sub == SPI - 1) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(m, off);
-        const float s2 = __shfl_xor(s, off);
-        lse_merge(m, s, m2, s2);
-    }
-    __shared__ float2 wpart[kThreads / 64];
-    if (lane == 0) wpart[tid >> 6] = make_float2(m, s);
-    __syncthreads();
-    if (tid == 0) {
-        float M = wpart[0].x, S = wpart[0].y;
-        for (int w = 1; w < kThreads / 64; ++w) lse_merge(M, S, wpart[w].x, wpart[w].y);
-        part[row * splits + split] = make_float2(M, S);
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float m2 = __shfl_xor(m, off);
+                const float s2 = __shfl_xor(s, off);
+                lse_merge(m, s, m2, s2);
+            }
+            if (lane == 0) part[row * P + seg] = make_float2(m, s);
+            if (keys != nullptr) {
+                // LDS ops of one wave complete in order; keep the compiler from moving them
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                const int64_t blk = (int64_t)seg * (kSeg / kBlock) + lane;
+                if (lane < kSeg / kBlock && blk * kBlock < V) {
+                    if (BF16)
+                        reinterpret_cast<uint16_t*>(keys)[row * kld + blk] = (uint16_t)(wkeys[lane] >> 16);
+                    else
+                        reinterpret_cast<uint32_t*>(keys)[row * kld + blk] = wkeys[lane];
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+            m = kNegInf;
+            s = 0.f;
+        }
+        advance(row, seg, sub);
+        if (q + 1 < nsteps) {
+#pragma unroll
+            for (int j = 0; j < VPS; ++j) cur[j] = nxt[j];
+        }
     }
 }
 
@@ -190,6 +238,8 @@ struct SelectScratch {
 
 // k-th largest (1-based, 1 <= k <= n) of n distinct 64-bit keys held in LDS.
 // MSD radix select, 8 bits per pass. Every thread of the workgroup calls it.
+// Only used when many candidates tie (e.g. constant rows): heavily repeated
+// digits serialise its LDS atomics.
 __device__ uint64_t radix_select(const uint64_t* keys, int n, int k, SelectScratch& sc) {
     const int tid = threadIdx.x;
     uint64_t prefix = 0, mask = 0;
@@ -239,11 +289,91 @@ __device__ uint64_t radix_select(const uint64_t* keys, int n, int k, SelectScrat
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2
+// Wave and workgroup scans on DPP (row shifts, then row broadcasts of lanes
+// 15 and 31): no LDS round trips inside a wave. `OP` 0 = add, 1 = max, 2 = min.
 // ---------------------------------------------------------------------------
-template <bool BF16>
+template <int OP>
+__device__ inline uint32_t dpp_op(uint32_t a, uint32_t b) {
+    return OP == 0 ? a + b : (OP == 1 ? max(a, b) : min(a, b));
+}
+#define LMH_DPP(v, ctrl, rmask, ident) \
+    ((uint32_t)__builtin_amdgcn_update_dpp((int)(ident), (int)(v), ctrl, rmask, 0xF, false))
+
+// Inclusive scan over the 64 lanes of a wave (lane i gets op over lanes 0..i).
+template <int OP>
+__device__ inline uint32_t wave_scan(uint32_t v) {
+    constexpr uint32_t I = OP == 2 ? 0xFFFFFFFFu : 0u;
+    v = dpp_op<OP>(v, LMH_DPP(v, 0x111, 0xF, I));   // row_shr:1
+    v = dpp_op<OP>(v, LMH_DPP(v, 0x112, 0xF, I));   // row_shr:2
+    v = dpp_op<OP>(v, LMH_DPP(v, 0x114, 0xF, I));   // row_shr:4
+    v = dpp_op<OP>(v, LMH_DPP(v, 0x118, 0xF, I));   // row_shr:8
+    v = dpp_op<OP>(v, LMH_DPP(v, 0x142, 0xA, I));   // row_bcast:15 -> rows 1, 3
+    v = dpp_op<OP>(v, LMH_DPP(v, 0x143, 0xC, I));   // row_bcast:31 -> rows 2, 3
+    return v;
+}
+template <int OP>
+__device__ inline uint32_t wave_reduce(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan<OP>(v), 63);
+}
+
+// Workgroup-wide reduction of N values; every thread gets the results. `buf`
+// alternates between two halves on consecutive calls, so one barrier each.
+template <int OP, int N>
+__device__ inline void block_reduce(uint32_t (&v)[N], uint32_t (*buf)[kThreads / 64][4], int& phase) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = wave_reduce<OP>(v[i]);
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) buf[phase][wave][i] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        uint32_t t = buf[phase][0][i];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) t = dpp_op<OP>(t, buf[phase][w][i]);
+        v[i] = t;
+    }
+    phase ^= 1;
+}
+
+// Workgroup-wide exclusive prefix sum in thread order; `total` gets the sum.
+__device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wtot, uint32_t& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t inc = wave_scan<0>(v);
+    if (lane == 63) wtot[wave] = inc;
+    __syncthreads();
+    uint32_t base = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        const uint32_t sw = wtot[w];
+        base += (w < wave) ? sw : 0u;
+        total += sw;
+    }
+    __syncthreads();
+    return base + inc - v;
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2: one workgroup per row.
+//  (1) lse from the row's partials (fixed merge order);
+//  (2) the selected token's logprob;
+//  (3) T = the K-th largest block-max key counted with multiplicity: a 5-way
+//      search with exact counts over the key range [lo, max], where lo is the
+//      smallest per-thread maximum (at least K keys reach it whenever K
+//      threads hold blocks); the kept blocks are all keys above T plus the
+//      lowest-indexed keys equal to T, K in all, placed by one prefix scan;
+//  (4) one round of 16-byte loads gathers the kept blocks; entries with key
+//      >= T become candidates, compacted by a prefix scan;
+//  (5) each candidate's rank under (value desc, id asc) is counted in LDS and
+//      the first K are written.
+// Every thread holds the keys of KPT consecutive blocks in registers.
+// ---------------------------------------------------------------------------
+template <bool BF16, int KPT>
 __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__ logits, int64_t ld,
-                                                     int64_t V, int32_t nb, int32_t splits,
+                                                     int64_t V, int32_t nb, int32_t kld, int32_t splits,
                                                      const float2* __restrict__ part,
                                                      const void* __restrict__ keys,
                                                      const int32_t* __restrict__ sel, int32_t K,
@@ -251,21 +381,69 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
                                                      float* __restrict__ sel_out,
                                                      int32_t* __restrict__ topk_ids,
                                                      float* __restrict__ topk_lp,
-                                                     int32_t* __restrict__ err, int32_t region) {
-    extern __shared__ uint64_t smem[];   // [region] keys/candidates, then [K] narrowed list
+                                                     int32_t* __restrict__ err, int32_t cap) {
+    extern __shared__ uint64_t smem[];   // [cap] candidates, [K] narrowed list
+    uint64_t* cand = smem;
+    uint64_t* list2 = smem + cap;
     __shared__ SelectScratch sc;
+    __shared__ uint32_t sred[2][kThreads / 64][4];
+    __shared__ uint32_t swtot[kThreads / 64];
     __shared__ float s_lse;
     __shared__ int32_t s_blk[kMaxCandidates / kBlock];
-    __shared__ int32_t s_nblk, s_ncand, s_nlist;
+    __shared__ int32_t s_nlist;
     constexpr size_t ESZ = BF16 ? 2 : 4;
+    constexpr int EPV = BF16 ? 8 : 4;                 // elements per 16-byte vector
+    constexpr int VPB = kBlock / EPV;                 // vectors per block
+    constexpr int MAXV = kMaxCandidates / EPV / kThreads;   // vectors per thread, at most
+    constexpr int MAXBLK = kMaxCandidates / kBlock;
 
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
     const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
+    if (tid < MAXBLK) s_blk[tid] = -1;   // unfilled slots are skipped, never dereferenced
 
-    // (1) logsumexp: wave 0 merges the split partials in a fixed order
+    // this thread's block keys, blocks [b0, b0 + KPT); 0 past nb (every real
+    // key is above 0, so a 0 never counts and never ties)
+    const int b0 = tid * KPT;
+    uint32_t kr[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kr[j] = 0u;
+    if (K > 0 && K <= nb && b0 < nb) {
+        if (BF16) {
+            const uint16_t* kp = reinterpret_cast<const uint16_t*>(keys) + row * kld + b0;
+            if (KPT == 4) {
+                const uint2 q = *reinterpret_cast<const uint2*>(kp);
+                const uint32_t wq[2] = {q.x, q.y};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kr[j] = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
+            } else {
+#pragma unroll
+                for (int c = 0; c < KPT / 8; ++c) {
+                    const u32x4 q = reinterpret_cast<const u32x4*>(kp)[c];
+                    const uint32_t wq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        kr[c * 8 + j] = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
+                }
+            }
+        } else {
+            const uint32_t* kp = reinterpret_cast<const uint32_t*>(keys) + row * kld + b0;
+#pragma unroll
+            for (int c = 0; c < KPT / 4; ++c) {
+                const u32x4 q = reinterpret_cast<const u32x4*>(kp)[c];
+                kr[c * 4 + 0] = q.x;
+                kr[c * 4 + 1] = q.y;
+                kr[c * 4 + 2] = q.z;
+                kr[c * 4 + 3] = q.w;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (b0 + j >= nb) kr[j] = 0u;
+    }
+
+    // (1) logsumexp: wave 0 merges the row's partials in a fixed order
     if (tid < 64) {
         float m = kNegInf, s = 0.f;
         for (int i = tid; i < splits; i += 64) {
@@ -282,8 +460,6 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
             const float l = (m == kNegInf) ? kNegInf : m + logf(s);
             s_lse = l;
             lse_out[row] = l;
-            s_nblk = 0;
-            s_ncand = 0;
             s_nlist = 0;
         }
     }
@@ -306,72 +482,179 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     }
     if (K == 0) return;
 
-    // (3) block selection: composite key (block max key, ~block) makes ties
-    // resolve to the lower block index
-    uint64_t* comp = smem;
-    for (int b = tid; b < nb; b += kThreads) {
-        const uint32_t kb = BF16 ? ((uint32_t)reinterpret_cast<const uint16_t*>(keys)[row * nb + b] << 16)
-                                 : reinterpret_cast<const uint32_t*>(keys)[row * nb + b];
-        comp[b] = ((uint64_t)kb << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)b);
-    }
-    __syncthreads();
-    uint64_t thr = 0;
-    uint32_t tkey = 0;   // candidate threshold on the value key (0: everything)
+    // (3) threshold and kept blocks
+    int phase = 0;
+    int nblk;
+    uint32_t T = 0;                                     // key threshold (0: keep everything)
     if (K <= nb) {
-        thr = radix_select(comp, nb, K, sc);
-        tkey = (uint32_t)(thr >> 32);
-    }
-    for (int b = tid; b < nb; b += kThreads) {
-        if (comp[b] >= thr) s_blk[atomicAdd(&s_nblk, 1)] = b;
-    }
-    __syncthreads();
-    const int nblk = s_nblk;
-
-    // (4) candidates: entries of kept blocks whose key is >= tkey
-    uint64_t* cand = smem;
-    for (int j = wave; j < nblk; j += kThreads / 64) {
-        const int64_t v = (int64_t)s_blk[j] * kBlock + lane;
-        bool keep = false;
-        uint64_t c = 0;
-        if (v < V) {
-            const float x = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[v])
-                                 : reinterpret_cast<const float*>(rowp)[v];
-            const uint32_t kx = elem_key<BF16>(x);
-            keep = kx >= tkey;
-            c = ((uint64_t)kx << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+        uint32_t tmax = 0u, tmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            tmax = max(tmax, kr[j]);
+            if (b0 + j < nb) tmin = min(tmin, kr[j]);
         }
-        const uint64_t ball = __ballot(keep);
-        int basepos = 0;
-        if (lane == 0) basepos = atomicAdd(&s_ncand, (int)__popcll(ball));
-        basepos = __shfl(basepos, 0);
-        if (keep) cand[basepos + (int)__popcll(ball & ((1ull << lane) - 1ull))] = c;
+        uint32_t mx[1] = {tmax};
+        uint32_t mn[2] = {tmin, b0 < nb ? tmax : 0xFFFFFFFFu};
+        block_reduce<1, 1>(mx, sred, phase);
+        block_reduce<2, 2>(mn, sred, phase);
+        const int nth = (nb + KPT - 1) / KPT;           // threads holding blocks
+        const int sh = BF16 ? 16 : 0;
+        // Largest t with count(key >= t) >= K; count(>= lo) >= K > count(>= hi).
+        uint64_t lo = (uint64_t)((K <= nth ? mn[1] : mn[0]) >> sh);
+        uint64_t hi = (uint64_t)(mx[0] >> sh) + 1;
+        while (hi - lo > 1) {
+            const uint64_t span = hi - lo;
+            uint32_t t[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint64_t d = (span * (uint64_t)(i + 1)) / 5;
+                t[i] = (uint32_t)(lo + (d < 1 ? 1 : d));
+            }
+            uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const uint32_t kv = kr[j] >> sh;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) c[i] += (kv >= t[i]) ? 1u : 0u;
+            }
+            uint32_t pk[2] = {c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
+            block_reduce<0, 2>(pk, sred, phase);
+            const uint32_t cc[4] = {pk[0] & 0xFFFFu, pk[0] >> 16, pk[1] & 0xFFFFu, pk[1] >> 16};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (cc[i] >= (uint32_t)K) {
+                    if (t[i] > lo) lo = t[i];
+                } else if (t[i] < hi) {
+                    hi = t[i];
+                }
+            }
+        }
+        T = (uint32_t)(lo << sh);
+        // per thread (above T, equal to T); one scan places the kept blocks
+        uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            gt += (kr[j] > T) ? 1u : 0u;
+            eq += (kr[j] == T) ? 1u : 0u;
+        }
+        uint32_t tot = 0u;
+        const uint32_t ex = block_exclusive_scan(gt | (eq << 16), swtot, tot);
+        const uint32_t gt_before = ex & 0xFFFFu, eq_before = ex >> 16;
+        const int need = K - (int)(tot & 0xFFFFu);     // blocks equal to T that are kept
+        int pos = (int)gt_before + min(need, (int)eq_before);
+        int ei = (int)eq_before;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            bool keep = kr[j] > T;
+            if (kr[j] == T) {
+                keep = ei < need;
+                ++ei;
+            }
+            if (keep) {
+                if (pos < MAXBLK) s_blk[pos] = b0 + j;
+                ++pos;
+            }
+        }
+        nblk = min(K, MAXBLK);
+    } else {
+        for (int b = tid; b < nb; b += kThreads) s_blk[b] = b;
+        nblk = nb;
     }
     __syncthreads();
-    const int ncand = s_ncand;
 
-    // (5) narrow to exactly K when there are many candidates
+    // (4) gather the kept blocks in one round of loads; keep entries >= T
+    const int nvec = nblk * VPB;
+    uint32_t w[MAXV][4];
+    int64_t e0[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int j = tid + i * kThreads;
+        e0[i] = -1;
+        const int blk = j < nvec ? s_blk[j / VPB] : -1;
+        if (blk >= 0 && blk < nb) {
+            e0[i] = (int64_t)blk * kBlock + (int64_t)(j % VPB) * EPV;
+            if (e0[i] + EPV <= V) {
+                const u32x4 v4 = *reinterpret_cast<const u32x4*>(rowp + (size_t)e0[i] * ESZ);
+                w[i][0] = v4.x; w[i][1] = v4.y; w[i][2] = v4.z; w[i][3] = v4.w;
+            } else {
+                const uint32_t ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
+                w[i][0] = w[i][1] = w[i][2] = w[i][3] = ninf;
+                for (int e = 0; e < EPV; ++e) {
+                    const int64_t idx = e0[i] + e;
+                    if (idx < V) {
+                        if (BF16) {
+                            const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[idx];
+                            w[i][e >> 1] = (e & 1) ? ((w[i][e >> 1] & 0x0000FFFFu) | (h << 16))
+                                                   : ((w[i][e >> 1] & 0xFFFF0000u) | h);
+                        } else {
+                            w[i][e] = reinterpret_cast<const uint32_t*>(rowp)[idx];
+                        }
+                    }
+                }
+            }
+        }
+    }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        if (e0[i] < 0) continue;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const float x = BF16 ? ((e & 1) ? bf16_hi(w[i][e >> 1]) : bf16_lo(w[i][e >> 1]))
+                                 : __uint_as_float(w[i][e]);
+            cnt += (e0[i] + e < V && elem_key<BF16>(x) >= T) ? 1u : 0u;
+        }
+    }
+    uint32_t ncand_u = 0;
+    int cpos = (int)block_exclusive_scan(cnt, swtot, ncand_u);
+    const int ncand = min((int)ncand_u, cap);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        if (e0[i] < 0) continue;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const float x = BF16 ? ((e & 1) ? bf16_hi(w[i][e >> 1]) : bf16_lo(w[i][e >> 1]))
+                                 : __uint_as_float(w[i][e]);
+            const uint32_t kx = elem_key<BF16>(x);
+            const int64_t v = e0[i] + e;
+            if (v < V && kx >= T) {
+                if (cpos < cap) cand[cpos] = ((uint64_t)kx << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+                ++cpos;
+            }
+        }
+    }
+    __syncthreads();
+
+    // (5) exact top-K by rank under the composite (value key, ~id) order
     const uint64_t* list = cand;
     int nlist = ncand;
     if (ncand > kThreads && ncand > K) {
         const uint64_t thr2 = radix_select(cand, ncand, K, sc);
-        uint64_t* list2 = smem + region;
         for (int i = tid; i < ncand; i += kThreads) {
             const uint64_t c = cand[i];
-            if (c >= thr2) list2[atomicAdd(&s_nlist, 1)] = c;
+            if (c >= thr2) {
+                const int q = atomicAdd(&s_nlist, 1);
+                if (q < K) list2[q] = c;
+            }
         }
         __syncthreads();
         list = list2;
         nlist = K;
     }
-
-    // (6) rank by (value desc, id asc) == composite descending; write top-K
     for (int i = tid; i < nlist; i += kThreads) {
         const uint64_t c = list[i];
         int rank = 0;
-        for (int j = 0; j < nlist; ++j) rank += (list[j] > c) ? 1 : 0;
+        int j = 0;
+        for (; j + 8 <= nlist; j += 8) {
+            uint64_t q[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) q[u] = list[j + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rank += (q[u] > c) ? 1 : 0;
+        }
+        for (; j < nlist; ++j) rank += (list[j] > c) ? 1 : 0;
         if (rank < K) {
-            const int32_t id = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
-            topk_ids[row * K + rank] = id;
+            topk_ids[row * K + rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
             topk_lp[row * K + rank] = key_value<BF16>((uint32_t)(c >> 32)) - lse;
         }
     }
@@ -385,15 +668,24 @@ ReducePlan plan_reduce(int64_t rows, int64_t vocab, int32_t k) {
     p.vocab = vocab;
     p.k = k;
     p.nb = (int32_t)((vocab + kBlock - 1) / kBlock);
-    int64_t splits = rows > 0 ? (kTargetWgs + rows - 1) / rows : 1;
-    const int64_t max_splits = (p.nb + 7) / 8;   // at least 8 blocks per split
-    splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
-    p.bps = (int32_t)((p.nb + splits - 1) / splits);
-    p.splits = (int32_t)((p.nb + p.bps - 1) / p.bps);
+    p.kpt = 4;
+    while (p.kpt * kThreads < p.nb && p.kpt < kMaxCandidates / kThreads) p.kpt *= 2;
+    // stage 2 reads KPT keys per thread with 16-byte loads, so a key row spans
+    // every thread's range; beyond the stage-2 limit only stage 1 touches keys
+    p.kld = p.nb <= kMaxCandidates ? p.kpt * kThreads : (p.nb + 7) / 8 * 8;
+    p.splits = (int32_t)((vocab + kSeg - 1) / kSeg);            // partials per row
+    p.nitems = rows * (int64_t)p.splits;
+    // one item per wave: short waves dispatched in address order keep the
+    // active set on a compact stretch of memory, which streams fastest; only
+    // very large inputs give a wave several items
+    int64_t ipw = (p.nitems + kMaxWaves - 1) / kMaxWaves;
+    p.ipw = (int32_t)(ipw < 1 ? 1 : ipw);
+    const int64_t waves = (p.nitems + p.ipw - 1) / p.ipw;
+    p.wgs = (waves + 3) / 4;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     p.part_off = 0;
-    p.keys_off = up((size_t)rows * p.splits * sizeof(float2));
-    p.bytes = p.keys_off + up((size_t)rows * p.nb * sizeof(uint32_t));
+    p.keys_off = up((size_t)p.nitems * sizeof(float2));
+    p.bytes = p.keys_off + up((size_t)rows * p.kld * sizeof(uint32_t));
     if (p.bytes == 0) p.bytes = 256;
     return p;
 }
@@ -402,16 +694,41 @@ hipError_t launch_reduce_stage1(const ReducePlan& p, const ReduceArgs& a, hipStr
     if (p.rows == 0) return hipSuccess;
     char* ws = static_cast<char*>(a.ws);
     float2* part = reinterpret_cast<float2*>(ws + p.part_off);
-    void* keys = ws + p.keys_off;
-    const dim3 grid((unsigned)(p.rows * p.splits));
+    void* keys = p.k > 0 ? ws + p.keys_off : nullptr;   // block maxima only feed the top-K
+    const dim3 grid((unsigned)p.wgs);
     const uint8_t* lg = static_cast<const uint8_t*>(a.logits);
     if (a.bf16)
-        hipLaunchKernelGGL(k_stage1<true>, grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.nb, p.bps,
-                           p.splits, part, keys);
+        hipLaunchKernelGGL(k_stage1<true>, grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld, p.splits,
+                           p.nitems, p.ipw, part, keys);
     else
-        hipLaunchKernelGGL(k_stage1<false>, grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.nb, p.bps,
-                           p.splits, part, keys);
+        hipLaunchKernelGGL(k_stage1<false>, grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld, p.splits,
+                           p.nitems, p.ipw, part, keys);
     return hipGetLastError();
+}
+
+template <bool BF16, int KPT>
+hipError_t launch_stage2_kpt(const ReducePlan& p, const ReduceArgs& a, hipStream_t s, const float2* part,
+                             const void* keys, int32_t cap, size_t lds) {
+    const void* fn = (const void*)k_stage2<BF16, KPT>;
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_stage2<BF16, KPT>), dim3((unsigned)p.rows), dim3(kThreads), lds, s,
+                       static_cast<const uint8_t*>(a.logits), a.ld, p.vocab, p.nb, p.kld, p.splits, part,
+                       keys, a.sel, p.k, a.lse, a.sel_lp, a.topk_ids, a.topk_lp, a.err, cap);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_stage2_dt(const ReducePlan& p, const ReduceArgs& a, hipStream_t s, const float2* part,
+                            const void* keys, int32_t cap, size_t lds) {
+    switch (p.kpt) {
+        case 4: return launch_stage2_kpt<BF16, 4>(p, a, s, part, keys, cap, lds);
+        case 8: return launch_stage2_kpt<BF16, 8>(p, a, s, part, keys, cap, lds);
+        case 16: return launch_stage2_kpt<BF16, 16>(p, a, s, part, keys, cap, lds);
+        default: return launch_stage2_kpt<BF16, 32>(p, a, s, part, keys, cap, lds);
+    }
 }
 
 hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStream_t s) {
@@ -419,35 +736,15 @@ hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStr
     char* ws = static_cast<char*>(a.ws);
     const float2* part = reinterpret_cast<const float2*>(ws + p.part_off);
     const void* keys = ws + p.keys_off;
-    int32_t region = 0;
+    int32_t cap = 0;
     size_t lds = 0;
     if (p.k > 0) {
         const int32_t nsel = p.k < p.nb ? p.k : p.nb;
-        const int32_t cap = nsel * kBlock;
-        region = p.nb > cap ? p.nb : cap;
-        lds = ((size_t)region + (size_t)p.k) * sizeof(uint64_t);
+        cap = nsel * kBlock;
+        lds = ((size_t)cap + (size_t)p.k) * sizeof(uint64_t);
     }
-    const uint8_t* lg = static_cast<const uint8_t*>(a.logits);
-    if (a.bf16) {
-        if (lds > 65536) {
-            hipError_t e = hipFuncSetAttribute((const void*)k_stage2<true>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(k_stage2<true>, dim3((unsigned)p.rows), dim3(kThreads), lds, s, lg, a.ld,
-                           p.vocab, p.nb, p.splits, part, keys, a.sel, p.k, a.lse, a.sel_lp,
-                           a.topk_ids, a.topk_lp, a.err, region);
-    } else {
-        if (lds > 65536) {
-            hipError_t e = hipFuncSetAttribute((const void*)k_stage2<false>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(k_stage2<false>, dim3((unsigned)p.rows), dim3(kThreads), lds, s, lg, a.ld,
-                           p.vocab, p.nb, p.splits, part, keys, a.sel, p.k, a.lse, a.sel_lp,
-                           a.topk_ids, a.topk_lp, a.err, region);
-    }
-    return hipGetLastError();
+    return a.bf16 ? launch_stage2_dt<true>(p, a, s, part, keys, cap, lds)
+                  : launch_stage2_dt<false>(p, a, s, part, keys, cap, lds);
 }
 
 }  // namespace lmh
