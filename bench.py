@@ -183,10 +183,12 @@ def main():
     for (t, _, _, _), ws in zip(chunks, wss):
         a = (vp(t), lmh.LMH_BF16, rows, V, V, K, vp(ws), ws.numel(), stream)
         stage1.append(lambda a=a: L.lmh_debug_reduce_stage1(*a))
-    d1 = timer.each(stage1, steps, warmup)
-    t1 = float(np.mean(d1))
+    # back-to-back launches of the streaming kernel alone: per-launch time over
+    # the whole timed loop (an event pair around each launch would add its own
+    # overhead to every interval)
+    t1 = timer.loop(stage1, steps, warmup)
     achieved = nbytes / (t1 * 1e-3) / 1e9
-    log(f"stage1: mean {t1 * 1e3:.1f} us  median {np.median(d1) * 1e3:.1f} us  -> {achieved:.0f} GB/s")
+    log(f"stage1: {t1 * 1e3:.1f} us per launch -> {achieved:.0f} GB/s")
     stage1_src = os.path.join(ROOT, "top_reduction_amd", "csrc", "reduce.hip")
     roofline = {"bound": "hbm", "kernel": "k_stage1<bf16> (reduce streaming pass)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -253,8 +255,7 @@ def main():
         assert sel_call() == 0
         hs = max(steps // 4, 10)
         m_sel = timer.loop([sel_call], hs, warmup)
-        dk = timer.each([sel_kernel], hs, warmup)
-        tk = float(np.mean(dk))
+        tk = timer.loop([sel_kernel], hs, warmup)
         head_bytes = Vq * H * 2 + R * H * 2 + R * Vq * 4
         ach = head_bytes / (tk * 1e-3) / 1e9
         log(f"selective head: call {m_sel * 1e3:.1f} us, kernel {tk * 1e3:.1f} us -> {ach:.0f} GB/s")
@@ -268,8 +269,7 @@ def main():
                                            None, None, None, stream)
         assert full_call() == 0
         fs = max(steps // 20, 5)
-        df = timer.each([full_call], fs, 2)
-        tf = float(np.mean(df))
+        tf = timer.loop([full_call], fs, 2)
         flops = 2.0 * 2048 * H * Vq
         tfl = flops / (tf * 1e-3) / 1e12
         log(f"full 2048-row head: {tf * 1e3:.1f} us -> {tfl:.0f} TFLOP/s")

@@ -100,8 +100,7 @@ struct ReducePlan {
     int32_t kpt;         // block keys per stage-2 thread (4, 8, 16 or 32)
     int32_t kld;         // row pitch of the block-key array (elements)
     int32_t splits;      // (max, sum-exp) partials per row: one per 4096-logit segment
-    int64_t nitems;      // rows * splits stage-1 work items
-    int32_t ipw;         // items per stage-1 wave
+    int64_t nitems;      // rows * splits stage-1 work items, one per wave
     int64_t wgs;         // stage-1 workgroups
     size_t part_off, keys_off, bytes;  // workspace layout
 };

@@ -24,7 +24,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kThreads = 256;
 constexpr int kSeg = 4096;          // logits per stage-1 work item (one wave)
-constexpr int64_t kMaxWaves = 1 << 22; // stage-1 waves before items are doubled up
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -68,55 +67,68 @@ __device__ inline float key_value(uint32_t k) {
 
 // ---------------------------------------------------------------------------
 // Stage 1: a row is cut into fixed segments of kSeg logits (the last one
-// partial); each segment is one work item of one wave. Items are numbered
-// row-major and every wave takes `ipw` consecutive items, so a wave streams a
-// contiguous stretch of memory, prefetching the next item while it reduces
-// the current one. Lane l of a wave reads the item's 16-byte vectors l,
-// l + 64, ...; the 8 (bf16) or 16 (fp32) lanes that share a 64-logit block
-// combine its maximum with DPP. The item's (max, sum-exp) partial is merged
-// across the wave by a fixed butterfly. Neither the item boundaries nor the
-// merge order depend on how many rows a call holds, so each row's results
-// are bitwise independent of the batch around it.
+// partial); each segment is the work item of one wave, and items are numbered
+// row-major so that consecutively dispatched waves stream consecutive memory.
+// Lane l of a wave reads the item's 16-byte vectors l, l + 64, ...; a full
+// item's loads are all in flight before its first vector is reduced. The 8
+// (bf16) or 16 (fp32) lanes that share a 64-logit block combine its maximum
+// with DPP; the item's block maxima are staged in LDS and written with one
+// coalesced store. The item's (max, sum-exp) partial is merged across the wave
+// by a fixed DPP tree into lane 63. Neither the segments nor the merge order
+// depend on how many rows a call holds, so each row's results are bitwise
+// independent of the batch around it.
 // ---------------------------------------------------------------------------
+// One (max, sum-exp) merge step with the partner chosen by a DPP control;
+// lanes without a partner merge the identity (-inf, 0).
+#define LMH_LSE_DPP_STEP(m, s, ctrl, rmask)                                                          \
+    do {                                                                                             \
+        const float m2_ = __int_as_float(                                                            \
+            __builtin_amdgcn_update_dpp((int)0xFF800000, __float_as_int(m), ctrl, rmask, 0xF, false)); \
+        const float s2_ = __int_as_float(                                                            \
+            __builtin_amdgcn_update_dpp(0, __float_as_int(s), ctrl, rmask, 0xF, false));             \
+        lse_merge(m, s, m2_, s2_);                                                                   \
+    } while (0)
+
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void k_stage1(const uint8_t* __restrict__ logits, int64_t ld, int64_t V, int32_t kld, int32_t P,
-              int64_t nitems, int32_t ipw, float2* __restrict__ part, void* __restrict__ keys) {
+__global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__ logits, int64_t ld,
+                                                     int64_t V, int32_t kld, int32_t P, int64_t nitems,
+                                                     float2* __restrict__ part, void* __restrict__ keys) {
     constexpr int EPV = BF16 ? 8 : 4;          // elements per 16-byte vector
     constexpr int VPB = kBlock / EPV;          // vectors (lanes) per 64-logit block
-    constexpr int VPS = 4;                     // vectors per lane per step
-    constexpr int SPI = kSeg / EPV / 64 / VPS; // steps per item (bf16 2, fp32 4)
+    constexpr int VPL = kSeg / EPV / 64;       // vectors per lane per item (bf16 8, fp32 16)
+    constexpr int VPS = 8;                     // vectors per load batch
     constexpr size_t ESZ = BF16 ? 2 : 4;
+    __shared__ float smax[kThreads / 64][kSeg / kBlock];   // the item's block maxima, per wave
+
     const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    const int64_t it0 = gw * ipw;
-    const int64_t it1 = min(nitems, it0 + ipw);
-    if (it0 >= it1) return;
-    const int64_t nsteps = (it1 - it0) * SPI;
+    const int wave = threadIdx.x >> 6;
+    const int64_t it = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+    if (it >= nitems) return;
+    const int64_t row = it / P;
+    const int32_t seg = (int32_t)(it - row * P);
     const int64_t nvec_row = (V + EPV - 1) / EPV;
-    const int64_t ragged_vec = (V % EPV) ? nvec_row - 1 : -1;
+    const int64_t vb = (int64_t)seg * (kSeg / EPV);
+    const bool full = vb + kSeg / EPV <= V / EPV;   // wave-uniform: no element past V
+    const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rowp) + vb;
     const uint32_t ninf_word = BF16 ? 0xFF80FF80u : 0xFF800000u;
+    float* wmax = smax[wave];
 
-    const int64_t nfull = V / EPV;   // vectors of the row with no element past V
-
-    // a step covers vectors [vb, vb + 64*VPS) of one segment (clipped to the row)
-    auto load_step = [&](int64_t row, int32_t seg, int32_t sub, u32x4 (&buf)[VPS]) {
-        const int64_t vb = (int64_t)seg * (kSeg / EPV) + sub * (64 * VPS);
-        const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
-        const u32x4* vp = reinterpret_cast<const u32x4*>(rowp);
-        if (vb + 64 * VPS <= nfull) {   // wave-uniform: the whole step is in the row
+    float m = kNegInf, s = 0.f;
 #pragma unroll
-            for (int j = 0; j < VPS; ++j) buf[j] = vp[vb + j * 64 + lane];
-            return;
-        }
+    for (int q = 0; q < VPL / VPS; ++q) {
+        u32x4 buf[VPS];
+        if (full) {
 #pragma unroll
-        for (int j = 0; j < VPS; ++j) {
-            const int64_t v = vb + j * 64 + lane;
-            buf[j] = u32x4{ninf_word, ninf_word, ninf_word, ninf_word};
-            if (v < nvec_row) {
-                if (v != ragged_vec) {
-                    buf[j] = vp[v];
-                } else {
+            for (int j = 0; j < VPS; ++j) buf[j] = vp[(q * VPS + j) * 64 + lane];
+        } else {
+#pragma unroll
+            for (int j = 0; j < VPS; ++j) {
+                const int64_t v = vb + (q * VPS + j) * 64 + lane;
+                buf[j] = u32x4{ninf_word, ninf_word, ninf_word, ninf_word};
+                if (v + 1 <= V / EPV) {
+                    buf[j] = vp[(q * VPS + j) * 64 + lane];
+                } else if (v < nvec_row) {   // the one vector that straddles V
                     uint32_t w[4] = {ninf_word, ninf_word, ninf_word, ninf_word};
                     for (int e = 0; e < EPV; ++e) {
                         const int64_t i = v * EPV + e;
@@ -134,40 +146,10 @@ void k_stage1(const uint8_t* __restrict__ logits, int64_t ld, int64_t V, int32_t
                 }
             }
         }
-    };
-
-    // block keys of the current item, staged per wave and written with one
-    // coalesced store when the item is done
-    __shared__ uint32_t skeys[kThreads / 64][kSeg / kBlock];
-    uint32_t* wkeys = skeys[threadIdx.x >> 6];
-
-    u32x4 cur[VPS], nxt[VPS];
-    // (row, segment, step) of the step being loaded and of the one being reduced,
-    // advanced incrementally (no division in the loop)
-    int64_t lrow = it0 / P;
-    int32_t lseg = (int32_t)(it0 - lrow * P), lsub = 0;
-    int64_t row = lrow;
-    int32_t seg = lseg, sub = 0;
-    auto advance = [&](int64_t& r, int32_t& sg, int32_t& sb) {
-        if (++sb == SPI) {
-            sb = 0;
-            if (++sg == P) {
-                sg = 0;
-                ++r;
-            }
-        }
-    };
-    load_step(lrow, lseg, lsub, cur);
-    float m = kNegInf, s = 0.f;
-    for (int64_t q = 0; q < nsteps; ++q) {
-        advance(lrow, lseg, lsub);
-        if (q + 1 < nsteps) load_step(lrow, lseg, lsub, nxt);
-        const int64_t vb = (int64_t)seg * (kSeg / EPV) + sub * (64 * VPS);
 #pragma unroll
         for (int j = 0; j < VPS; ++j) {
-            const int64_t v = vb + j * 64 + lane;
             float x[EPV];
-            const uint32_t w[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+            const uint32_t w[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
             if (BF16) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -182,9 +164,11 @@ void k_stage1(const uint8_t* __restrict__ logits, int64_t ld, int64_t V, int32_t
 #pragma unroll
             for (int e = 1; e < EPV; ++e) lm = fmaxf(lm, x[e]);
 
-            // block maximum over the VPB lanes of this 64-logit block
-            const float bm = BF16 ? dpp_max8(lm) : dpp_max16(lm);
-            if ((lane & (VPB - 1)) == 0) wkeys[(sub * 64 * VPS + j * 64 + lane) / VPB] = f32_key(bm);
+            if (keys != nullptr) {
+                // block maximum over the VPB lanes of this 64-logit block
+                const float bm = BF16 ? dpp_max8(lm) : dpp_max16(lm);
+                if ((lane & (VPB - 1)) == 0) wmax[((q * VPS + j) * 64 + lane) / VPB] = bm;
+            }
 
             // online (max, sum-exp); a rescale by exp2(0) is exactly 1
             const float mn = fmaxf(m, lm);
@@ -195,34 +179,28 @@ void k_stage1(const uint8_t* __restrict__ logits, int64_t ld, int64_t V, int32_t
             s = acc;
             m = mn;
         }
-        if (sub == SPI - 1) {
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float m2 = __shfl_xor(m, off);
-                const float s2 = __shfl_xor(s, off);
-                lse_merge(m, s, m2, s2);
-            }
-            if (lane == 0) part[row * P + seg] = make_float2(m, s);
-            if (keys != nullptr) {
-                // LDS ops of one wave complete in order; keep the compiler from moving them
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                const int64_t blk = (int64_t)seg * (kSeg / kBlock) + lane;
-                if (lane < kSeg / kBlock && blk * kBlock < V) {
-                    if (BF16)
-                        reinterpret_cast<uint16_t*>(keys)[row * kld + blk] = (uint16_t)(wkeys[lane] >> 16);
-                    else
-                        reinterpret_cast<uint32_t*>(keys)[row * kld + blk] = wkeys[lane];
-                }
-                __builtin_amdgcn_wave_barrier();
-            }
-            m = kNegInf;
-            s = 0.f;
-        }
-        advance(row, seg, sub);
-        if (q + 1 < nsteps) {
-#pragma unroll
-            for (int j = 0; j < VPS; ++j) cur[j] = nxt[j];
+    }
+
+    // merge the wave's partials into lane 63 (row shifts, then row broadcasts)
+    LMH_LSE_DPP_STEP(m, s, 0x111, 0xF);
+    LMH_LSE_DPP_STEP(m, s, 0x112, 0xF);
+    LMH_LSE_DPP_STEP(m, s, 0x114, 0xF);
+    LMH_LSE_DPP_STEP(m, s, 0x118, 0xF);
+    LMH_LSE_DPP_STEP(m, s, 0x142, 0xA);
+    LMH_LSE_DPP_STEP(m, s, 0x143, 0xC);
+    if (lane == 63) part[it] = make_float2(m, s);
+
+    if (keys != nullptr) {
+        // LDS ops of one wave complete in order; keep the compiler from moving them
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const int64_t blk = (int64_t)seg * (kSeg / kBlock) + lane;
+        if (blk * kBlock < V) {
+            const uint32_t kb = f32_key(wmax[lane]);
+            if (BF16)
+                reinterpret_cast<uint16_t*>(keys)[row * kld + blk] = (uint16_t)(kb >> 16);
+            else
+                reinterpret_cast<uint32_t*>(keys)[row * kld + blk] = kb;
         }
     }
 }
@@ -676,12 +654,8 @@ ReducePlan plan_reduce(int64_t rows, int64_t vocab, int32_t k) {
     p.splits = (int32_t)((vocab + kSeg - 1) / kSeg);            // partials per row
     p.nitems = rows * (int64_t)p.splits;
     // one item per wave: short waves dispatched in address order keep the
-    // active set on a compact stretch of memory, which streams fastest; only
-    // very large inputs give a wave several items
-    int64_t ipw = (p.nitems + kMaxWaves - 1) / kMaxWaves;
-    p.ipw = (int32_t)(ipw < 1 ? 1 : ipw);
-    const int64_t waves = (p.nitems + p.ipw - 1) / p.ipw;
-    p.wgs = (waves + 3) / 4;
+    // active set on a compact stretch of memory, which streams fastest
+    p.wgs = (p.nitems + kThreads / 64 - 1) / (kThreads / 64);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     p.part_off = 0;
     p.keys_off = up((size_t)p.nitems * sizeof(float2));
@@ -699,10 +673,10 @@ hipError_t launch_reduce_stage1(const ReducePlan& p, const ReduceArgs& a, hipStr
     const uint8_t* lg = static_cast<const uint8_t*>(a.logits);
     if (a.bf16)
         hipLaunchKernelGGL(k_stage1<true>, grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld, p.splits,
-                           p.nitems, p.ipw, part, keys);
+                           p.nitems, part, keys);
     else
         hipLaunchKernelGGL(k_stage1<false>, grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld, p.splits,
-                           p.nitems, p.ipw, part, keys);
+                           p.nitems, part, keys);
     return hipGetLastError();
 }
 
