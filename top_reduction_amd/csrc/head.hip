@@ -30,6 +30,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr float kNaN = __builtin_nanf("");
+#ifndef LMH_STREAM_NT
+#define LMH_STREAM_NT 2
+#endif
+#ifndef LMH_STREAM_KC
+#define LMH_STREAM_KC 256
+#endif
+constexpr int kStreamNT = LMH_STREAM_NT;   // 16-row W tiles per wave in the streaming head
+constexpr int kStreamKC = LMH_STREAM_KC;   // hidden elements per streaming-head k-chunk
 
 __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -58,23 +66,28 @@ __device__ inline void store_out(void* out, int64_t off, float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming kernel: MT row tiles of 16 (R <= 16*MT), 128 vocab rows
-// per workgroup (32 per wave = two 16-wide N tiles), k in chunks of 128.
+// Weight-streaming kernel: MT row tiles of 16 (R <= 16*MT) against a slab of
+// 64*NT W rows per workgroup (16*NT per wave), k in chunks of 128. Each wave
+// loads its W fragments straight from HBM into MFMA B operands a whole chunk
+// ahead; the gathered hidden rows come through double-buffered LDS, shared by
+// the 4 waves. Small slabs keep the last, partly filled round of workgroups
+// short.
 // ---------------------------------------------------------------------------
-template <int MT, bool OUT_BF16>
+template <int MT, int NT, bool KFULL, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
-    constexpr int KC = 128;             // hidden elements per chunk
+    constexpr int KC = kStreamKC;       // hidden elements per chunk
     constexpr int KS = KC / 32;         // MFMA k-steps per chunk
     constexpr int AP = KC + 8;          // LDS row pitch (elements): +16 B breaks bank aliasing
     constexpr int ROWS = MT * 16;
-    constexpr int AV = ROWS * KC / 8 / kThreads;   // 16-B A vectors per thread per chunk
+    constexpr int AVN = ROWS * KC / 8;                      // 16-B A vectors per chunk
+    constexpr int AV = (AVN + kThreads - 1) / kThreads;     // ... per thread
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS][AP];
     __shared__ int32_t sIdx[ROWS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t nbase = (int64_t)blockIdx.x * 128 + wave * 32;
+    const int64_t nbase = (int64_t)blockIdx.x * (64 * NT) + wave * (16 * NT);
     const int l16 = lane & 15;
     const int kq = (lane >> 4) * 8;
 
@@ -85,88 +98,124 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
     const int nchunks = (int)((p.H + KC - 1) / KC);
     const int ksteps = (int)((p.H + 31) / 32);
 
+    // Loads are branch-free (clamped address, then a select), so the compiler
+    // can keep every prefetch in flight across the loop instead of draining
+    // the memory counters at divergent joins.
+    const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+    int64_t a_off[AV];    // element offset of this thread's A source rows
+    int a_kv[AV];         // its 8-element column group within a chunk
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+        const int idx = j * kThreads + tid;
+        const bool in = (AVN % kThreads == 0) || idx < AVN;
+        const int row = in ? idx / (KC / 8) : 0;
+        const int32_t t = sIdx[row];
+        a_off[j] = (int64_t)(t >= 0 ? t : 0) * p.hld;
+        a_kv[j] = in ? (idx % (KC / 8)) * 8 : 0;
+    }
+    int64_t w_off[NT];    // element offset of this lane's W rows
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int64_t n = nbase + j * 16 + l16;
+        w_off[j] = (n < p.V ? n : p.V - 1) * p.wld;
+    }
+
+    // A rows without a source (their outputs are written as NaN) and W rows
+    // past the vocabulary (their columns are never stored) read a clamped,
+    // valid row; only a chunk that runs past the hidden size needs zeros.
+    // KFULL (the hidden size is a multiple of KC) compiles the loads without
+    // any k guard, which keeps the memory counters exact across the loop.
     auto load_a = [&](int c, u32x4 (&r)[AV]) {
 #pragma unroll
         for (int j = 0; j < AV; ++j) {
-            const int idx = j * kThreads + tid;
-            const int row = idx / (KC / 8);
-            const int kv = idx % (KC / 8);
-            const int64_t k = (int64_t)c * KC + kv * 8;
-            const int32_t t = sIdx[row];
-            r[j] = u32x4{0u, 0u, 0u, 0u};
-            if (t >= 0 && k < p.H)
-                r[j] = *reinterpret_cast<const u32x4*>(p.hidden + (int64_t)t * p.hld + k);
+            const int64_t k = (int64_t)c * KC + a_kv[j];
+            if (KFULL) {
+                r[j] = *reinterpret_cast<const u32x4*>(p.hidden + a_off[j] + k);
+            } else {
+                const bool ok = k < p.H;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(p.hidden + a_off[j] + (ok ? k : 0));
+                r[j] = ok ? v : zero4;
+            }
         }
     };
     auto store_a = [&](int buf, const u32x4 (&r)[AV]) {
 #pragma unroll
         for (int j = 0; j < AV; ++j) {
             const int idx = j * kThreads + tid;
-            const int row = idx / (KC / 8);
-            const int kv = idx % (KC / 8);
-            *reinterpret_cast<u32x4*>(&sA[buf][row][kv * 8]) = r[j];
+            if (AVN % kThreads == 0 || idx < AVN) {
+                const int row = idx / (KC / 8);
+                const int kv = idx % (KC / 8);
+                *reinterpret_cast<u32x4*>(&sA[buf][row][kv * 8]) = r[j];
+            }
         }
     };
-    auto load_w = [&](int c, u32x4 (&r)[KS][2]) {
+    auto load_w = [&](int c, u32x4 (&r)[KS][NT]) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int64_t n = nbase + j * 16 + l16;
+            for (int j = 0; j < NT; ++j) {
                 const int64_t k = (int64_t)c * KC + s * 32 + kq;
-                r[s][j] = u32x4{0u, 0u, 0u, 0u};
-                if (n < p.V && k < p.H)
-                    r[s][j] = *reinterpret_cast<const u32x4*>(p.W + n * p.wld + k);
+                if (KFULL) {
+                    r[s][j] = *reinterpret_cast<const u32x4*>(p.W + w_off[j] + k);
+                } else {
+                    const bool ok = k < p.H;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(p.W + w_off[j] + (ok ? k : 0));
+                    r[s][j] = ok ? v : zero4;
+                }
             }
         }
     };
 
-    f32x4 acc[MT][2];
+    f32x4 acc[MT][NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x4 areg[AV];
-    u32x4 wcur[KS][2], wnext[KS][2];
+    u32x4 w0[KS][NT], w1[KS][NT];
     load_a(0, areg);
     store_a(0, areg);
-    load_w(0, wcur);
+    load_w(0, w0);
     __syncthreads();
 
-    for (int c = 0; c < nchunks; ++c) {
+    // one k-chunk: prefetch the next chunk's A and W, multiply this one
+    auto step = [&](int c, const u32x4 (&wc)[KS][NT], u32x4 (&wn)[KS][NT]) {
         const int buf = c & 1;
         const bool more = (c + 1) < nchunks;
         if (more) {
-            load_w(c + 1, wnext);
+            // A first: its loads are consumed at the end of this step, and
+            // memory counters retire in issue order, so waiting for them must
+            // not also wait for the weight prefetch issued after them
             load_a(c + 1, areg);
+            load_w(c + 1, wn);
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (c * KS + s < ksteps) {
+            if (KFULL || c * KS + s < ksteps) {
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
                     const u32x4 a = *reinterpret_cast<const u32x4*>(&sA[buf][i * 16 + l16][s * 32 + kq]);
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma16(a, wcur[s][j], acc[i][j]);
+                    for (int j = 0; j < NT; ++j) acc[i][j] = mfma16(a, wc[s][j], acc[i][j]);
                 }
             }
         }
         if (more) store_a(buf ^ 1, areg);
         __syncthreads();
-        if (more) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) wcur[s][j] = wnext[s][j];
-        }
+    };
+    // unrolled by two so the weight buffers alternate without register copies
+    // (a copy of a prefetch destination would wait for the prefetch)
+    for (int c = 0; c < nchunks; c += 2) {
+        step(c, w0, w1);
+        if (c + 1 < nchunks) step(c + 1, w1, w0);
     }
 
     // D fragment: lane holds rows 4*(lane/16)+e of column lane%16
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NT; ++j) {
             const int64_t v = nbase + j * 16 + l16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -383,29 +432,28 @@ HeadParams to_params(const HeadArgs& a) {
 
 }  // namespace
 
+template <int MT, bool OUT_BF16>
+hipError_t launch_stream_mt(const HeadParams& p, hipStream_t s) {
+    constexpr int NT = kStreamNT;
+    const dim3 grid((unsigned)((p.V + 64 * NT - 1) / (64 * NT)));
+    if (p.H % kStreamKC == 0)
+        hipLaunchKernelGGL((k_head_stream<MT, NT, true, OUT_BF16>), grid, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_head_stream<MT, NT, false, OUT_BF16>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
     if (a.rows > kStreamMaxRows) return hipErrorInvalidValue;
     const HeadParams p = to_params(a);
-    const dim3 grid((unsigned)((a.vocab + 127) / 128));
-    const int mt = (a.rows + 15) / 16;
-#define LMH_STREAM_CASE(MT)                                                                   \
-    case MT:                                                                                   \
-        if (a.out_bf16)                                                                        \
-            hipLaunchKernelGGL((k_head_stream<MT, true>), grid, dim3(kThreads), 0, s, p);       \
-        else                                                                                   \
-            hipLaunchKernelGGL((k_head_stream<MT, false>), grid, dim3(kThreads), 0, s, p);      \
-        break;
-    switch (mt) {
-        LMH_STREAM_CASE(1)
-        LMH_STREAM_CASE(2)
-        LMH_STREAM_CASE(3)
-        LMH_STREAM_CASE(4)
-        default:
-            return hipErrorInvalidValue;
+    switch ((a.rows + 15) / 16) {
+        case 1: return a.out_bf16 ? launch_stream_mt<1, true>(p, s) : launch_stream_mt<1, false>(p, s);
+        case 2: return a.out_bf16 ? launch_stream_mt<2, true>(p, s) : launch_stream_mt<2, false>(p, s);
+        case 3: return a.out_bf16 ? launch_stream_mt<3, true>(p, s) : launch_stream_mt<3, false>(p, s);
+        case 4: return a.out_bf16 ? launch_stream_mt<4, true>(p, s) : launch_stream_mt<4, false>(p, s);
+        default: return hipErrorInvalidValue;
     }
-#undef LMH_STREAM_CASE
-    return hipGetLastError();
 }
 
 hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
