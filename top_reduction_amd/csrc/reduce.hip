@@ -23,6 +23,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kThreads = 256;
+constexpr int kHistBins = 256;     // key values resolved by one stage-2 histogram
 constexpr int kSeg = 4096;          // logits per stage-1 work item (one wave)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -368,7 +369,9 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     __shared__ uint32_t swtot[kThreads / 64];
     __shared__ float s_lse;
     __shared__ int32_t s_blk[kMaxCandidates / kBlock];
-    __shared__ int32_t s_nlist;
+    __shared__ int32_t s_nlist, s_nblk;
+    __shared__ uint32_t sh_hist[kHistBins];
+    __shared__ uint32_t s_thr[3];
     constexpr size_t ESZ = BF16 ? 2 : 4;
     constexpr int EPV = BF16 ? 8 : 4;                 // elements per 16-byte vector
     constexpr int VPB = kBlock / EPV;                 // vectors per block
@@ -421,43 +424,58 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
             if (b0 + j >= nb) kr[j] = 0u;
     }
 
-    // (1) logsumexp: wave 0 merges the row's partials in a fixed order
+    // the selected token's id, issued now (thread 64: off the lse wave) and
+    // used at the end, after the loads have long landed
+    const bool sel_thread = sel != nullptr && sel_out != nullptr && tid == 64;
+    int32_t sel_id = 0;
+    if (sel_thread) sel_id = sel[row];
+
+    // (1) logsumexp: wave 0 merges the row's partials in a fixed order (a
+    // strided pass per lane, then a DPP tree into lane 63)
     if (tid < 64) {
         float m = kNegInf, s = 0.f;
         for (int i = tid; i < splits; i += 64) {
             const float2 p = part[row * splits + i];
             lse_merge(m, s, p.x, p.y);
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float m2 = __shfl_xor(m, off);
-            const float s2 = __shfl_xor(s, off);
-            lse_merge(m, s, m2, s2);
-        }
-        if (tid == 0) {
+        LMH_LSE_DPP_STEP(m, s, 0x111, 0xF);
+        LMH_LSE_DPP_STEP(m, s, 0x112, 0xF);
+        LMH_LSE_DPP_STEP(m, s, 0x114, 0xF);
+        LMH_LSE_DPP_STEP(m, s, 0x118, 0xF);
+        LMH_LSE_DPP_STEP(m, s, 0x142, 0xA);
+        LMH_LSE_DPP_STEP(m, s, 0x143, 0xC);
+        if (tid == 63) {
             const float l = (m == kNegInf) ? kNegInf : m + logf(s);
             s_lse = l;
             lse_out[row] = l;
             s_nlist = 0;
+            s_nblk = 0;
         }
     }
     __syncthreads();
     const float lse = s_lse;
 
-    // (2) selected token
-    if (sel != nullptr && sel_out != nullptr && tid == 0) {
-        const int32_t id = sel[row];
-        float lp;
-        if (id < 0 || (int64_t)id >= V) {
-            lp = __builtin_nanf("");
-            if (err) atomicOr(err, LMH_DEVERR_INDEX);
-        } else {
-            const float x = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[id])
-                                 : reinterpret_cast<const float*>(rowp)[id];
-            lp = x - lse;
+    // (2) selected token: its logit load is issued here and consumed last
+    const bool sel_ok = sel_thread && sel_id >= 0 && (int64_t)sel_id < V;
+    float xsel = 0.f;
+    if (sel_ok)
+        xsel = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[sel_id])
+                    : reinterpret_cast<const float*>(rowp)[sel_id];
+    auto write_selected = [&]() {
+        if (sel_thread) {
+            if (sel_ok) {
+                sel_out[row] = xsel - lse;
+            } else {
+                sel_out[row] = __builtin_nanf("");
+                if (err) atomicOr(err, LMH_DEVERR_INDEX);
+            }
         }
-        sel_out[row] = lp;
+    };
+    if (K == 0) {
+        write_selected();
+        return;
     }
+
     if (K == 0) return;
 
     // (3) threshold and kept blocks
@@ -471,16 +489,18 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
             tmax = max(tmax, kr[j]);
             if (b0 + j < nb) tmin = min(tmin, kr[j]);
         }
-        uint32_t mx[1] = {tmax};
-        uint32_t mn[2] = {tmin, b0 < nb ? tmax : 0xFFFFFFFFu};
-        block_reduce<1, 1>(mx, sred, phase);
-        block_reduce<2, 2>(mn, sred, phase);
+        // one max-reduction gives the maximum and (complemented) two minima:
+        // of all keys, and of the per-thread maxima of threads holding blocks
+        uint32_t mm[3] = {tmax, ~tmin, b0 < nb ? ~tmax : 0u};
+        block_reduce<1, 3>(mm, sred, phase);
         const int nth = (nb + KPT - 1) / KPT;           // threads holding blocks
         const int sh = BF16 ? 16 : 0;
         // Largest t with count(key >= t) >= K; count(>= lo) >= K > count(>= hi).
-        uint64_t lo = (uint64_t)((K <= nth ? mn[1] : mn[0]) >> sh);
-        uint64_t hi = (uint64_t)(mx[0] >> sh) + 1;
-        while (hi - lo > 1) {
+        uint64_t lo = (uint64_t)((K <= nth ? ~mm[2] : ~mm[1]) >> sh);
+        uint64_t hi = (uint64_t)(mm[0] >> sh) + 1;
+        uint32_t c_hi = 0u;                              // count(key >= hi)
+        // 5-way narrowing with exact counts until at most 256 key values remain
+        while (hi - lo > kHistBins) {
             const uint64_t span = hi - lo;
             uint32_t t[4];
 #pragma unroll
@@ -504,33 +524,78 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
                     if (t[i] > lo) lo = t[i];
                 } else if (t[i] < hi) {
                     hi = t[i];
+                    c_hi = cc[i];
                 }
             }
         }
-        T = (uint32_t)(lo << sh);
-        // per thread (above T, equal to T); one scan places the kept blocks
-        uint32_t gt = 0u, eq = 0u;
+        // histogram of the keys in [lo, hi), then a suffix scan in wave 0:
+        // T is the largest key value v with count(key >= v) >= K
+        sh_hist[tid] = 0u;
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-            gt += (kr[j] > T) ? 1u : 0u;
-            eq += (kr[j] == T) ? 1u : 0u;
+            const uint64_t kv = kr[j] >> sh;
+            if (kv >= lo && kv < hi) atomicAdd(&sh_hist[(int)(kv - lo)], 1u);
         }
-        uint32_t tot = 0u;
-        const uint32_t ex = block_exclusive_scan(gt | (eq << 16), swtot, tot);
-        const uint32_t gt_before = ex & 0xFFFFu, eq_before = ex >> 16;
-        const int need = K - (int)(tot & 0xFFFFu);     // blocks equal to T that are kept
-        int pos = (int)gt_before + min(need, (int)eq_before);
-        int ei = (int)eq_before;
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            bool keep = kr[j] > T;
-            if (kr[j] == T) {
-                keep = ei < need;
-                ++ei;
+        __syncthreads();
+        if (tid < 64) {
+            const uint32_t h0 = sh_hist[4 * tid], h1 = sh_hist[4 * tid + 1];
+            const uint32_t h2 = sh_hist[4 * tid + 2], h3 = sh_hist[4 * tid + 3];
+            const uint32_t sum4 = h0 + h1 + h2 + h3;
+            const uint32_t incl = wave_scan<0>(sum4);
+            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+            // count(key >= bin 4l + 4) and the four suffix counts inside the lane
+            const uint32_t above = c_hi + total - incl;
+            const uint32_t s3 = above + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+            const uint32_t k = (uint32_t)K;
+            int b = -1;
+            uint32_t gt = 0u, eqc = 0u;
+            if (s3 >= k && above < k) { b = 4 * tid + 3; gt = above; eqc = h3; }
+            else if (s2 >= k && s3 < k) { b = 4 * tid + 2; gt = s3; eqc = h2; }
+            else if (s1 >= k && s2 < k) { b = 4 * tid + 1; gt = s2; eqc = h1; }
+            else if (s0 >= k && s1 < k) { b = 4 * tid; gt = s1; eqc = h0; }
+            if (b >= 0) {
+                s_thr[0] = (uint32_t)((lo + (uint64_t)b) << sh);
+                s_thr[1] = gt;
+                s_thr[2] = eqc;
             }
-            if (keep) {
-                if (pos < MAXBLK) s_blk[pos] = b0 + j;
-                ++pos;
+        }
+        __syncthreads();
+        T = s_thr[0];
+        const int need = K - (int)s_thr[1];             // blocks equal to T that are kept
+        const bool all_ties = (uint32_t)need == s_thr[2];
+        if (all_ties) {
+            // every key >= T is kept: placement order does not matter
+#pragma unroll
+            for (int j = 0; j < KPT; ++j)
+                if (kr[j] >= T) {
+                    const int pos = atomicAdd(&s_nblk, 1);
+                    if (pos < MAXBLK) s_blk[pos] = b0 + j;
+                }
+        } else {
+            // the lowest-indexed keys equal to T are kept: one ordered scan
+            uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                gt += (kr[j] > T) ? 1u : 0u;
+                eq += (kr[j] == T) ? 1u : 0u;
+            }
+            uint32_t tot = 0u;
+            const uint32_t ex = block_exclusive_scan(gt | (eq << 16), swtot, tot);
+            const uint32_t gt_before = ex & 0xFFFFu, eq_before = ex >> 16;
+            int pos = (int)gt_before + min(need, (int)eq_before);
+            int ei = (int)eq_before;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                bool keep = kr[j] > T;
+                if (kr[j] == T) {
+                    keep = ei < need;
+                    ++ei;
+                }
+                if (keep) {
+                    if (pos < MAXBLK) s_blk[pos] = b0 + j;
+                    ++pos;
+                }
             }
         }
         nblk = min(K, MAXBLK);
@@ -572,15 +637,19 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
             }
         }
     }
+    // key >= T  <=>  x >= Tf for the values this row can hold (T == 0: all)
+    const bool keep_all = T == 0u;
+    const float Tf = keep_all ? kNegInf : key_value<BF16>(T);
     uint32_t cnt = 0;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
         if (e0[i] < 0) continue;
+        const bool vfull = e0[i] + EPV <= V;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const float x = BF16 ? ((e & 1) ? bf16_hi(w[i][e >> 1]) : bf16_lo(w[i][e >> 1]))
                                  : __uint_as_float(w[i][e]);
-            cnt += (e0[i] + e < V && elem_key<BF16>(x) >= T) ? 1u : 0u;
+            cnt += ((vfull || e0[i] + e < V) && (keep_all || x >= Tf)) ? 1u : 0u;
         }
     }
     uint32_t ncand_u = 0;
@@ -589,14 +658,15 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
         if (e0[i] < 0) continue;
+        const bool vfull = e0[i] + EPV <= V;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const float x = BF16 ? ((e & 1) ? bf16_hi(w[i][e >> 1]) : bf16_lo(w[i][e >> 1]))
                                  : __uint_as_float(w[i][e]);
-            const uint32_t kx = elem_key<BF16>(x);
             const int64_t v = e0[i] + e;
-            if (v < V && kx >= T) {
-                if (cpos < cap) cand[cpos] = ((uint64_t)kx << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+            if ((vfull || v < V) && (keep_all || x >= Tf)) {
+                if (cpos < cap)
+                    cand[cpos] = ((uint64_t)elem_key<BF16>(x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
                 ++cpos;
             }
         }
@@ -619,23 +689,34 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
         list = list2;
         nlist = K;
     }
-    for (int i = tid; i < nlist; i += kThreads) {
-        const uint64_t c = list[i];
-        int rank = 0;
-        int j = 0;
-        for (; j + 8 <= nlist; j += 8) {
-            uint64_t q[8];
+    // G lanes (a quad, a pair or one lane) count one candidate's predecessors
+    // over interleaved slices of the list, then sum with DPP inside the quad
+    const int G = nlist <= kThreads / 4 ? 4 : (nlist <= kThreads / 2 ? 2 : 1);
+    const int q = tid & (G - 1);
+    for (int i0 = 0; i0 < nlist * G; i0 += kThreads) {
+        const int i = (i0 + tid) / G;
+        const bool act = i0 + tid < nlist * G;
+        const uint64_t c = act ? list[i] : 0ull;
+        uint32_t rank = 0;
+        if (act) {
+            int j = q;
+            for (; j + 7 * G < nlist; j += 8 * G) {
+                uint64_t v8[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) q[u] = list[j + u];
+                for (int u = 0; u < 8; ++u) v8[u] = list[j + u * G];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) rank += (q[u] > c) ? 1 : 0;
+                for (int u = 0; u < 8; ++u) rank += (v8[u] > c) ? 1u : 0u;
+            }
+            for (; j < nlist; j += G) rank += (list[j] > c) ? 1u : 0u;
         }
-        for (; j < nlist; ++j) rank += (list[j] > c) ? 1 : 0;
-        if (rank < K) {
+        if (G >= 2) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0xB1, 0xF, 0xF, false);
+        if (G == 4) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0x4E, 0xF, 0xF, false);
+        if (act && q == 0 && rank < (uint32_t)K) {
             topk_ids[row * K + rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
             topk_lp[row * K + rank] = key_value<BF16>((uint32_t)(c >> 32)) - lse;
         }
     }
+    write_selected();
 }
 
 }  // namespace
