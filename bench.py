@@ -65,7 +65,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
     f_fetch = fetch[copy[0]] * 1024 / nbytes
     f_write = write[copy[0]] * 1024 / nbytes
     csrc = os.path.join(ROOT, "top_reduction_amd", "csrc")
-    wanted = {"reduce_stage1_bf16": ("k_stage1<true>", "reduce.hip", nbytes),
+    wanted = {"reduce_stage1_bf16": ("k_stage1<true, true>", "reduce.hip", nbytes),
               "reduce_stage2_bf16": ("k_stage2<true", "reduce.hip", None),
               "head_stream_bf16": ("k_head_stream<", "head.hip", 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
               "head_tiled_bf16": ("k_head_tiled<", "head.hip", 151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4)}

@@ -58,7 +58,7 @@ lmh_status check_reduce_shape(lmh_dtype dt, int64_t rows, int64_t vocab, int64_t
     if ((k < nb ? k : nb) * (int64_t)kBlock > kMaxCandidates) return LMH_ERR_K;
     if (k > 0 && nb > kMaxCandidates) return LMH_ERR_SHAPE;
     const ReducePlan p = plan_reduce(rows, vocab, k);
-    if (p.wgs > INT32_MAX) return LMH_ERR_SHAPE;
+    if (p.wgs >= ((int64_t)1 << 30)) return LMH_ERR_SHAPE;   // stage-1 item index fits 32 bits
     return LMH_OK;
 }
 

@@ -30,17 +30,47 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Max over lane groups of 8 (quad swap, quad pair swap, half-row mirror) and,
-// for 16, the row mirror. Every lane of a group ends with the group maximum.
-__device__ inline float dpp_max8(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-    return v;
+// Maxima written as v_max_f32 / v_max3_f32. In IEEE mode the compiler quiets
+// every fmaxf operand that is not the result of arithmetic first (here: all of
+// them, being bit-cast loads), an extra instruction per logit. NaN operands:
+// a quiet NaN loses to any number, a signalling one makes the result NaN.
+__device__ inline float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
 }
-__device__ inline float dpp_max16(float v) {
-    v = dpp_max8(v);
-    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+__device__ inline float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// max(v, v of the lane chosen by a full-row DPP pattern) as one instruction.
+// The two wait states cover a DPP read of a VGPR written by the previous VALU
+// instruction.
+#define LMH_DPP_MAX(v, PATTERN)                                                                   \
+    ([&]() {                                                                                      \
+        float r_;                                                                                 \
+        asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " PATTERN " row_mask:0xf bank_mask:0xf"         \
+            : "=v"(r_)                                                                            \
+            : "v"(v));                                                                            \
+        return r_;                                                                                \
+    }())
+// Maximum over aligned lane groups of 8 or 16; every lane of a group ends with it.
+template <int G>
+__device__ inline float group_max(float v) {
+    static_assert(G == 8 || G == 16 || G == 64, "group of 8, 16 or 64 lanes");
+    v = LMH_DPP_MAX(v, "quad_perm:[1,0,3,2]");
+    v = LMH_DPP_MAX(v, "quad_perm:[2,3,0,1]");
+    v = LMH_DPP_MAX(v, "row_half_mirror");
+    if (G >= 16) v = LMH_DPP_MAX(v, "row_mirror");
+    if (G == 64) {
+        const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+        const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+        const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+        const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+        v = fmaxf(fmaxf(a, b), fmaxf(c, d));   // wave-uniform
+    }
+    return v;
 }
 
 // Merge two (max, sum-exp) partials. A partial with max -inf has sum 0.
@@ -70,14 +100,20 @@ __device__ inline float key_value(uint32_t k) {
 // Stage 1: a row is cut into fixed segments of kSeg logits (the last one
 // partial); each segment is the work item of one wave, and items are numbered
 // row-major so that consecutively dispatched waves stream consecutive memory.
-// Lane l of a wave reads the item's 16-byte vectors l, l + 64, ...; a full
-// item's loads are all in flight before its first vector is reduced. The 8
-// (bf16) or 16 (fp32) lanes that share a 64-logit block combine its maximum
-// with DPP; the item's block maxima are staged in LDS and written with one
-// coalesced store. The item's (max, sum-exp) partial is merged across the wave
-// by a fixed DPP tree into lane 63. Neither the segments nor the merge order
-// depend on how many rows a call holds, so each row's results are bitwise
-// independent of the batch around it.
+// Lane l of a wave reads the item's 16-byte vectors l, l + 64, ...; all of an
+// item's loads are in flight before its first vector is used, and the item's
+// 64 logits per lane stay in registers for two passes:
+//   1. the maximum of each lane's slice of every 64-logit block (the 8 bf16 or
+//      16 fp32 lanes of a block then combine it with DPP), and of the lane;
+//   2. with M the wave maximum, the sum of 2^(x*log2e + c) for c = -RN(M*log2e):
+//      one fma, one exp2 and one add per logit. The rounding of c is the
+//      exactly representable e = M*log2e + c (an fma), and the sum is scaled
+//      by 2^-e once, so the partial is (M, sum of exp(x - M)) to fp32 rounding.
+// The lane sums are added by a fixed DPP tree into lane 63. The block maxima
+// are transposed across the wave (a register select, then ds_bpermute) so that
+// lane b holds block b, and stored as keys with one coalesced store. Neither
+// the segments nor the summation order depend on how many rows a call holds,
+// so each row's results are bitwise independent of the batch around it.
 // ---------------------------------------------------------------------------
 // One (max, sum-exp) merge step with the partner chosen by a DPP control;
 // lanes without a partner merge the identity (-inf, 0).
@@ -90,119 +126,164 @@ __device__ inline float key_value(uint32_t k) {
         lse_merge(m, s, m2_, s2_);                                                                   \
     } while (0)
 
+// Sum over the wave by row shifts, then row broadcasts; lane 63 ends with the
+// total (a fixed order).
+__device__ inline float wave_sum_to_63(float s) {
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x111, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x112, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x114, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x118, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x142, 0xA, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x143, 0xC, 0xF, false));
+    return s;
+}
+
+// v[r] for a lane-dependent r in [0, N), N a power of two, by a select tree.
+template <int N>
+__device__ inline float select_reg(const float (&v)[N], int r) {
+    float t[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) t[i] = v[i];
+#pragma unroll
+    for (int w = N / 2, bit = 0; w >= 1; w /= 2, ++bit) {
+        const bool hi = (r >> bit) & 1;
+#pragma unroll
+        for (int i = 0; i < w; ++i) t[i] = hi ? t[2 * i + 1] : t[2 * i];
+    }
+    return t[0];
+}
+
 template <bool BF16>
+struct Stage1Item {
+    static constexpr int EPV = BF16 ? 8 : 4;          // elements per 16-byte vector
+    static constexpr int VPB = kBlock / EPV;          // lanes per 64-logit block
+    static constexpr int VPL = kSeg / EPV / 64;       // vectors per lane (== VPB)
+    static constexpr int GPV = 64 / VPB;              // blocks per wave-wide vector
+    static_assert(VPL == VPB, "one block maximum per vector and lane group");
+};
+
+// Reduces one item held in buf (VPL vectors per lane; entries past V hold
+// -inf) and writes its partial and block keys.
+template <bool BF16, bool KEYS>
+__device__ __forceinline__ void stage1_reduce(const u32x4 (&buf)[Stage1Item<BF16>::VPL], int lane,
+                                              int64_t it, int64_t row, int32_t seg, int64_t V,
+                                              int32_t kld, float2* __restrict__ part,
+                                              void* __restrict__ keys) {
+    using I = Stage1Item<BF16>;
+    float x[I::VPL * I::EPV];
+    float bm[I::VPL];
+    float lm = kNegInf;
+#pragma unroll
+    for (int j = 0; j < I::VPL; ++j) {
+        const uint32_t w[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
+        float* xv = x + j * I::EPV;
+        float vm;
+        if (BF16) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xv[2 * e] = bf16_lo(w[e]);
+                xv[2 * e + 1] = bf16_hi(w[e]);
+            }
+            vm = vmax3(xv[6], xv[7], vmax(vmax3(xv[0], xv[1], xv[2]), vmax3(xv[3], xv[4], xv[5])));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[e] = __uint_as_float(w[e]);
+            vm = vmax(vmax(xv[0], xv[1]), vmax(xv[2], xv[3]));
+        }
+        if (KEYS) bm[j] = group_max<I::VPB>(vm);
+        lm = vmax(lm, vm);
+    }
+
+    const float M = group_max<64>(lm);
+    const float Mr = (M == kNegInf) ? 0.f : M;
+    const float c = -(Mr * kLog2e);
+    const float e = fmaf(Mr, kLog2e, c);   // exact: Mr*log2e - RN(Mr*log2e)
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < I::VPL * I::EPV; i += 4) {
+        s0 += ex2(fmaf(x[i], kLog2e, c));
+        s1 += ex2(fmaf(x[i + 1], kLog2e, c));
+        s2 += ex2(fmaf(x[i + 2], kLog2e, c));
+        s3 += ex2(fmaf(x[i + 3], kLog2e, c));
+    }
+    const float s = wave_sum_to_63((s0 + s1) + (s2 + s3));
+    if (lane == 63) part[it] = make_float2(M, s * ex2(-e));
+
+    if (KEYS) {
+        // lane g*VPB + r holds block r*GPV + g after the select; block b comes
+        // from lane (b % GPV)*VPB + b / GPV
+        const float mine = select_reg<I::VPL>(bm, lane % I::VPB);
+        const int src = (lane % I::GPV) * I::VPB + lane / I::GPV;
+        const float kbm = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(mine)));
+        const int64_t blk = (int64_t)seg * (kSeg / kBlock) + lane;
+        if (blk * kBlock < V) {
+            const uint32_t kb = f32_key(kbm);
+            if (BF16)
+                reinterpret_cast<uint16_t*>(keys)[row * kld + blk] = (uint16_t)(kb >> 16);
+            else
+                reinterpret_cast<uint32_t*>(keys)[row * kld + blk] = kb;
+        }
+    }
+}
+
+template <bool BF16, bool KEYS>
 __global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__ logits, int64_t ld,
                                                      int64_t V, int32_t kld, int32_t P, int64_t nitems,
                                                      float2* __restrict__ part, void* __restrict__ keys) {
-    constexpr int EPV = BF16 ? 8 : 4;          // elements per 16-byte vector
-    constexpr int VPB = kBlock / EPV;          // vectors (lanes) per 64-logit block
-    constexpr int VPL = kSeg / EPV / 64;       // vectors per lane per item (bf16 8, fp32 16)
-    constexpr int VPS = 8;                     // vectors per load batch
+    using I = Stage1Item<BF16>;
+    constexpr int EPV = I::EPV;
+    constexpr int VPL = I::VPL;
     constexpr size_t ESZ = BF16 ? 2 : 4;
-    __shared__ float smax[kThreads / 64][kSeg / kBlock];   // the item's block maxima, per wave
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t it = (int64_t)blockIdx.x * (kThreads / 64) + wave;
-    if (it >= nitems) return;
-    const int64_t row = it / P;
-    const int32_t seg = (int32_t)(it - row * P);
+    // wave-uniform item arithmetic in scalar registers (item count < 2^32)
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t itu = blockIdx.x * (uint32_t)(kThreads / 64) + wave;
+    if ((int64_t)itu >= nitems) return;
+    const int64_t it = itu;
+    const uint32_t rowu = itu / (uint32_t)P;
+    const int64_t row = rowu;
+    const int32_t seg = (int32_t)(itu - rowu * (uint32_t)P);
     const int64_t nvec_row = (V + EPV - 1) / EPV;
     const int64_t vb = (int64_t)seg * (kSeg / EPV);
     const bool full = vb + kSeg / EPV <= V / EPV;   // wave-uniform: no element past V
     const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp) + vb;
     const uint32_t ninf_word = BF16 ? 0xFF80FF80u : 0xFF800000u;
-    float* wmax = smax[wave];
 
-    float m = kNegInf, s = 0.f;
+    u32x4 buf[VPL];
+    if (full) {
 #pragma unroll
-    for (int q = 0; q < VPL / VPS; ++q) {
-        u32x4 buf[VPS];
-        if (full) {
+        for (int j = 0; j < VPL; ++j) buf[j] = vp[j * 64 + lane];
+        // every load issued before any result is used (the scheduler would
+        // otherwise hoist the first unpack between them and wait on it)
+        __builtin_amdgcn_sched_barrier(0);
+        stage1_reduce<BF16, KEYS>(buf, lane, it, row, seg, V, kld, part, keys);
+    } else {
 #pragma unroll
-            for (int j = 0; j < VPS; ++j) buf[j] = vp[(q * VPS + j) * 64 + lane];
-        } else {
-#pragma unroll
-            for (int j = 0; j < VPS; ++j) {
-                const int64_t v = vb + (q * VPS + j) * 64 + lane;
-                buf[j] = u32x4{ninf_word, ninf_word, ninf_word, ninf_word};
-                if (v + 1 <= V / EPV) {
-                    buf[j] = vp[(q * VPS + j) * 64 + lane];
-                } else if (v < nvec_row) {   // the one vector that straddles V
-                    uint32_t w[4] = {ninf_word, ninf_word, ninf_word, ninf_word};
-                    for (int e = 0; e < EPV; ++e) {
-                        const int64_t i = v * EPV + e;
-                        if (i < V) {
-                            if (BF16) {
-                                const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[i];
-                                w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | (h << 16))
-                                                    : ((w[e >> 1] & 0xFFFF0000u) | h);
-                            } else {
-                                w[e] = reinterpret_cast<const uint32_t*>(rowp)[i];
-                            }
+        for (int j = 0; j < VPL; ++j) {
+            const int64_t v = vb + j * 64 + lane;
+            buf[j] = u32x4{ninf_word, ninf_word, ninf_word, ninf_word};
+            if (v + 1 <= V / EPV) {
+                buf[j] = vp[j * 64 + lane];
+            } else if (v < nvec_row) {   // the one vector that straddles V
+                uint32_t w[4] = {ninf_word, ninf_word, ninf_word, ninf_word};
+                for (int e = 0; e < EPV; ++e) {
+                    const int64_t i = v * EPV + e;
+                    if (i < V) {
+                        if (BF16) {
+                            const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[i];
+                            w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | (h << 16))
+                                                : ((w[e >> 1] & 0xFFFF0000u) | h);
+                        } else {
+                            w[e] = reinterpret_cast<const uint32_t*>(rowp)[i];
                         }
                     }
-                    buf[j] = u32x4{w[0], w[1], w[2], w[3]};
                 }
+                buf[j] = u32x4{w[0], w[1], w[2], w[3]};
             }
         }
-#pragma unroll
-        for (int j = 0; j < VPS; ++j) {
-            float x[EPV];
-            const uint32_t w[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
-            if (BF16) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[2 * e] = bf16_lo(w[e]);
-                    x[2 * e + 1] = bf16_hi(w[e]);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
-            }
-            float lm = x[0];
-#pragma unroll
-            for (int e = 1; e < EPV; ++e) lm = fmaxf(lm, x[e]);
-
-            if (keys != nullptr) {
-                // block maximum over the VPB lanes of this 64-logit block
-                const float bm = BF16 ? dpp_max8(lm) : dpp_max16(lm);
-                if ((lane & (VPB - 1)) == 0) wmax[((q * VPS + j) * 64 + lane) / VPB] = bm;
-            }
-
-            // online (max, sum-exp); a rescale by exp2(0) is exactly 1
-            const float mn = fmaxf(m, lm);
-            const float mr = (mn == kNegInf) ? 0.f : mn;
-            float acc = s * ex2((m - mr) * kLog2e);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) acc += ex2((x[e] - mr) * kLog2e);
-            s = acc;
-            m = mn;
-        }
-    }
-
-    // merge the wave's partials into lane 63 (row shifts, then row broadcasts)
-    LMH_LSE_DPP_STEP(m, s, 0x111, 0xF);
-    LMH_LSE_DPP_STEP(m, s, 0x112, 0xF);
-    LMH_LSE_DPP_STEP(m, s, 0x114, 0xF);
-    LMH_LSE_DPP_STEP(m, s, 0x118, 0xF);
-    LMH_LSE_DPP_STEP(m, s, 0x142, 0xA);
-    LMH_LSE_DPP_STEP(m, s, 0x143, 0xC);
-    if (lane == 63) part[it] = make_float2(m, s);
-
-    if (keys != nullptr) {
-        // LDS ops of one wave complete in order; keep the compiler from moving them
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        const int64_t blk = (int64_t)seg * (kSeg / kBlock) + lane;
-        if (blk * kBlock < V) {
-            const uint32_t kb = f32_key(wmax[lane]);
-            if (BF16)
-                reinterpret_cast<uint16_t*>(keys)[row * kld + blk] = (uint16_t)(kb >> 16);
-            else
-                reinterpret_cast<uint32_t*>(keys)[row * kld + blk] = kb;
-        }
+        stage1_reduce<BF16, KEYS>(buf, lane, it, row, seg, V, kld, part, keys);
     }
 }
 
@@ -752,12 +833,19 @@ hipError_t launch_reduce_stage1(const ReducePlan& p, const ReduceArgs& a, hipStr
     void* keys = p.k > 0 ? ws + p.keys_off : nullptr;   // block maxima only feed the top-K
     const dim3 grid((unsigned)p.wgs);
     const uint8_t* lg = static_cast<const uint8_t*>(a.logits);
-    if (a.bf16)
-        hipLaunchKernelGGL(k_stage1<true>, grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld, p.splits,
-                           p.nitems, part, keys);
+    const bool k = keys != nullptr;
+    if (a.bf16 && k)
+        hipLaunchKernelGGL((k_stage1<true, true>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
+                           p.splits, p.nitems, part, keys);
+    else if (a.bf16)
+        hipLaunchKernelGGL((k_stage1<true, false>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
+                           p.splits, p.nitems, part, keys);
+    else if (k)
+        hipLaunchKernelGGL((k_stage1<false, true>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
+                           p.splits, p.nitems, part, keys);
     else
-        hipLaunchKernelGGL(k_stage1<false>, grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld, p.splits,
-                           p.nitems, part, keys);
+        hipLaunchKernelGGL((k_stage1<false, false>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
+                           p.splits, p.nitems, part, keys);
     return hipGetLastError();
 }
 
