@@ -15,9 +15,10 @@
 //           W and reads it once, straight from HBM into MFMA B fragments,
 //           a full k-chunk ahead; the gathered hidden rows (small, L2
 //           resident) are staged through LDS and shared by the 4 waves.
-//   tiled   (any R): 128 x 128 output tiles, both operands staged through
-//           double-buffered LDS, 4 waves of 64 x 64; workgroups are mapped so
-//           that each XCD walks the row tiles of one W slab together.
+//   tiled   (any R): 256 x 128 output tiles, 4 waves of 128 x 64; both
+//           operands pass through double-buffered LDS fed 3 k-steps ahead;
+//           workgroups are mapped so that each XCD walks the row tiles of one
+//           W slab together.
 //   f32     fp32 operands: plain fp32 FMA in ascending k.
 #include "lmh_internal.h"
 
@@ -230,17 +231,34 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: 128 x 128 tile per workgroup, k in chunks of 64, both operands
-// through double-buffered LDS; waves in a 2 x 2 grid of 64 x 64.
+// Tiled kernel: a 256 x 128 output tile per workgroup, one 128 x 64 quarter per
+// wave (8 x 4 MFMA tiles). k advances in stages of 32 (one MFMA k-step).
+// Each stage's A (gathered hidden rows, 256 x 64 B) and B (W rows, 128 x 64 B)
+// slices pass through registers into one of two LDS buffers: loads of stage
+// s+3 are issued while stage s is multiplied (three register sets in
+// flight) and stage s+1 is written to LDS at the end of stage s; the A
+// fragments are read one 16-row group ahead of their MFMAs. Two workgroups
+// share a CU. The 16-byte chunks of a
+// 64-byte LDS row are XOR-swizzled with bits 1..2 of the row, so the fragment
+// reads (16 rows, one chunk each) and the staging writes (consecutive chunks)
+// are free of bank conflicts. Loads are branch-free: rows past R or with no
+// source read row 0 (their outputs are never written or are NaN), W rows past
+// V read row V-1, and the chunks past H (the stage count is rounded up to a
+// multiple of 3) read k = 0 and are zeroed on their way into LDS.
 // ---------------------------------------------------------------------------
+constexpr int kTileM = 256, kTileN = 128, kTileK = 32;
+constexpr int kWaveN = 64;                                     // columns per wave
+constexpr int kTileLA = kTileM * 4 / kThreads;                 // A chunks per thread per stage
+constexpr int kTileLB = kTileN * 4 / kThreads;                 // B chunks per thread per stage
+constexpr int kTileStage = (kTileM + kTileN) * kTileK * 2;     // bytes per LDS stage
+constexpr int kTileLds = 2 * kTileStage + kTileM * 4;          // 2 stages + row sources
+
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
-    constexpr int BM = 128, BN = 128, BK = 64;
-    constexpr int P = BK + 8;                     // LDS pitch (elements)
-    constexpr int LV = BM * BK / 8 / kThreads;    // 16-B vectors per thread per operand
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][P];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN][P];
-    __shared__ int32_t sIdx[BM];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
+    constexpr int NF = kWaveN / 16;                 // B fragments (16-column groups) per wave
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    int32_t* sIdx = reinterpret_cast<int32_t*>(lds + 2 * kTileStage);
 
     // XCD-aware order: hardware places workgroup i on XCD i % 8; give each
     // XCD a contiguous run of logical tiles, row tiles fastest, so the row
@@ -255,98 +273,158 @@ __global__ __launch_bounds__(kThreads) void k_head_tiled(HeadParams p, int32_t m
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = (wave >> 1) * 64;
-    const int wn = (wave & 1) * 64;
-    const int l16 = lane & 15;
-    const int kq = (lane >> 4) * 8;
-    const int32_t m0 = mt * BM;
-    const int64_t n0 = (int64_t)nt * BN;
+    const int wm = (wave >> 1) * 128;
+    const int wn = (wave & 1) * kWaveN;
+    const int32_t m0 = mt * kTileM;
+    const int64_t n0 = (int64_t)nt * kTileN;
 
-    if (tid < BM) {
+    {
         const int32_t r = m0 + tid;
         sIdx[tid] = (r < p.R) ? row_source(p.row0 + r, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
     }
     __syncthreads();
 
-    const int nchunks = (int)((p.H + BK - 1) / BK);
-    const int ksteps = (int)((p.H + 31) / 32);
-
-    auto load = [&](int c, u32x4 (&ra)[LV], u32x4 (&rb)[LV]) {
+    // this thread's staging chunks: rows tid/4 + 64j, chunk tid%4
+    const int c = tid & 3;
+    int64_t ga[kTileLA], gb[kTileLB];               // element offsets of the chunks at k = 0
+    uint32_t wofs[kTileLA];                         // LDS byte offsets within a stage's A slice
 #pragma unroll
-        for (int j = 0; j < LV; ++j) {
-            const int idx = j * kThreads + tid;
-            const int row = idx / (BK / 8);
-            const int kv = idx % (BK / 8);
-            const int64_t k = (int64_t)c * BK + kv * 8;
-            const int32_t t = sIdx[row];
-            ra[j] = u32x4{0u, 0u, 0u, 0u};
-            rb[j] = u32x4{0u, 0u, 0u, 0u};
-            if (t >= 0 && k < p.H)
-                ra[j] = *reinterpret_cast<const u32x4*>(p.hidden + (int64_t)t * p.hld + k);
-            const int64_t n = n0 + row;
-            if (n < p.V && k < p.H) rb[j] = *reinterpret_cast<const u32x4*>(p.W + n * p.wld + k);
+    for (int j = 0; j < kTileLA; ++j) {
+        const int row = (tid >> 2) + 64 * j;
+        const int32_t t = sIdx[row];
+        ga[j] = (int64_t)(t < 0 ? 0 : t) * p.hld + c * 8;
+        wofs[j] = (uint32_t)(row * 64 + ((c ^ ((row >> 1) & 3)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < kTileLB; ++j) {
+        const int row = (tid >> 2) + 64 * j;
+        const int64_t n = n0 + row < p.V ? n0 + row : p.V - 1;
+        gb[j] = n * p.wld + c * 8;
+    }
+    // fragment read offset: row l%16 of a 16-row group, chunk l/16
+    const int fr = lane & 15;
+    const uint32_t rofs = (uint32_t)(fr * 64 + (((lane >> 4) ^ ((fr >> 1) & 3)) << 4));
+    const uint32_t aofs = (uint32_t)(wm * 64) + rofs;
+    const uint32_t bofs = (uint32_t)((kTileM + wn) * 64) + rofs;
+
+    // a multiple of 3 stages; the chunks past H load zeros
+    const int nst = (int)((p.H + 3 * kTileK - 1) / (3 * kTileK)) * 3;
+
+    // chunks past H (the padding stages, or the tail of a last partial one)
+    // load from k = 0 and are zeroed when written to LDS
+    auto gload = [&](int st, u32x4 (&ra)[kTileLA], u32x4 (&rb)[kTileLB]) {
+        const int64_t k0 = (int64_t)st * kTileK;
+        const int64_t k = k0 + c * 8 + 8 <= p.H ? k0 : 0;
+#pragma unroll
+        for (int j = 0; j < kTileLA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(p.hidden + ga[j] + k);
+#pragma unroll
+        for (int j = 0; j < kTileLB; ++j) rb[j] = *reinterpret_cast<const u32x4*>(p.W + gb[j] + k);
+    };
+    auto lwrite = [&](int buf, int st, const u32x4 (&ra)[kTileLA], const u32x4 (&rb)[kTileLB]) {
+        uint8_t* base = lds + buf * kTileStage;
+        const bool z = (int64_t)st * kTileK + c * 8 + 8 > p.H;
+        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < kTileLA; ++j) *reinterpret_cast<u32x4*>(base + wofs[j]) = z ? zero : ra[j];
+#pragma unroll
+        for (int j = 0; j < kTileLB; ++j)
+            *reinterpret_cast<u32x4*>(base + kTileM * 64 + wofs[j]) = z ? zero : rb[j];
+    };
+    f32x4 acc[8][NF];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // MFMAs of one stage; the A fragments are read from LDS one 16-row group
+    // ahead of their use
+    auto mma = [&](int buf) {
+        const uint8_t* base = lds + buf * kTileStage;
+        u32x4 fb[NF];
+#pragma unroll
+        for (int j = 0; j < NF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(base + bofs + j * 16 * 64);
+        u32x4 fa = *reinterpret_cast<const u32x4*>(base + aofs);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const u32x4 cur = fa;
+            if (i < 7) fa = *reinterpret_cast<const u32x4*>(base + aofs + (i + 1) * 16 * 64);
+#pragma unroll
+            for (int j = 0; j < NF; ++j) acc[i][j] = mfma16(cur, fb[j], acc[i][j]);
         }
     };
-    auto store = [&](int buf, const u32x4 (&ra)[LV], const u32x4 (&rb)[LV]) {
-#pragma unroll
-        for (int j = 0; j < LV; ++j) {
-            const int idx = j * kThreads + tid;
-            const int row = idx / (BK / 8);
-            const int kv = idx % (BK / 8);
-            *reinterpret_cast<u32x4*>(&sA[buf][row][kv * 8]) = ra[j];
-            *reinterpret_cast<u32x4*>(&sB[buf][row][kv * 8]) = rb[j];
-        }
-    };
 
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 ra[LV], rb[LV];
-    load(0, ra, rb);
-    store(0, ra, rb);
+    // stage s is multiplied from LDS buffer s%2 while stage s+1 is written to
+    // the other buffer from register set (s+1)%3 and stage s+3 is loaded into
+    // set s%3
+    u32x4 ra0[kTileLA], rb0[kTileLB], ra1[kTileLA], rb1[kTileLB], ra2[kTileLA], rb2[kTileLB];
+    gload(0, ra0, rb0);
+    gload(1, ra1, rb1);
+    gload(2, ra2, rb2);
+    lwrite(0, 0, ra0, rb0);
     __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        const bool more = (c + 1) < nchunks;
-        if (more) load(c + 1, ra, rb);
-#pragma unroll
-        for (int s = 0; s < BK / 32; ++s) {
-            if (c * (BK / 32) + s < ksteps) {
-                u32x4 a[4], b[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a[i] = *reinterpret_cast<const u32x4*>(&sA[buf][wm + i * 16 + l16][s * 32 + kq]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    b[j] = *reinterpret_cast<const u32x4*>(&sB[buf][wn + j * 16 + l16][s * 32 + kq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
-            }
-        }
-        if (more) store(buf ^ 1, ra, rb);
+    int cur = 0;                                    // LDS buffer of stage s
+    for (int s = 0; s < nst; s += 3) {
+        gload(s + 3, ra0, rb0);
+        mma(cur);
+        lwrite(cur ^ 1, s + 1, ra1, rb1);
         __syncthreads();
+        cur ^= 1;
+        gload(s + 4, ra1, rb1);
+        mma(cur);
+        lwrite(cur ^ 1, s + 2, ra2, rb2);
+        __syncthreads();
+        cur ^= 1;
+        gload(s + 5, ra2, rb2);
+        mma(cur);
+        lwrite(cur ^ 1, s + 3, ra0, rb0);
+        __syncthreads();
+        cur ^= 1;
     }
 
+    // Epilogue through LDS (free after the last barrier): per pass, each wave
+    // stages 32 rows x 64 columns of its quarter (fp32, rows padded by 16 B),
+    // then stores whole 16-byte row segments.
+    const int lq = lane >> 4;
+    float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 68);
+    const bool vec_ok = !OUT_BF16 && (p.old % 4 == 0) &&
+                        ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int h = 0; h < 4; ++h) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t v = n0 + wn + j * 16 + l16;
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = h * 2 + ii;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rl = wm + i * 16 + (lane >> 4) * 4 + e;
-                const int32_t r = m0 + rl;
-                if (r < p.R && v < p.V) {
-                    const float val = sIdx[rl] < 0 ? kNaN : acc[i][j][e];
-                    store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v, val);
+            for (int j = 0; j < NF; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) stg[(ii * 16 + lq * 4 + e) * 68 + j * 16 + fr] = acc[i][j][e];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane l stores columns 4*(l%16) .. +3 of rows l/16 + 4q, q = 0..7
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int rr = lq + 4 * q;                      // row within the pass
+            const int rl = wm + h * 32 + rr;
+            const int32_t r = m0 + rl;
+            const int cl = 4 * fr;
+            const int64_t v = n0 + wn + cl;
+            const f32x4 val = *reinterpret_cast<const f32x4*>(&stg[rr * 68 + cl]);
+            if (r < p.R) {
+                const bool valid = sIdx[rl] >= 0;
+                if (vec_ok && v + 4 <= p.V) {
+                    const f32x4 o = valid ? val : f32x4{kNaN, kNaN, kNaN, kNaN};
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v) = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (v + e < p.V) store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v + e, valid ? val[e] : kNaN);
                 }
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -456,18 +534,23 @@ hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s) {
     }
 }
 
+template <bool OUT_BF16>
+hipError_t launch_tiled(const HeadParams& p, int32_t mtiles, int32_t ntiles, hipStream_t s) {
+    const void* fn = (const void*)k_head_tiled<OUT_BF16>;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kTileLds);
+    if (e != hipSuccess) return e;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    const dim3 grid((unsigned)(((total + 7) / 8) * 8));
+    hipLaunchKernelGGL((k_head_tiled<OUT_BF16>), grid, dim3(kThreads), kTileLds, s, p, mtiles, ntiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
     const HeadParams p = to_params(a);
-    const int32_t mtiles = (a.rows + 127) / 128;
-    const int64_t ntiles = (a.vocab + 127) / 128;
-    const int64_t total = (int64_t)mtiles * ntiles;
-    const dim3 grid((unsigned)(((total + 7) / 8) * 8));
-    if (a.out_bf16)
-        hipLaunchKernelGGL(k_head_tiled<true>, grid, dim3(kThreads), 0, s, p, mtiles, (int32_t)ntiles);
-    else
-        hipLaunchKernelGGL(k_head_tiled<false>, grid, dim3(kThreads), 0, s, p, mtiles, (int32_t)ntiles);
-    return hipGetLastError();
+    const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
+    const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
+    return a.out_bf16 ? launch_tiled<true>(p, mtiles, ntiles, s) : launch_tiled<false>(p, mtiles, ntiles, s);
 }
 
 hipError_t launch_head_f32(const HeadArgs& a, hipStream_t s) {
