@@ -4,13 +4,16 @@ one MI355X.
 
 Headline (the JSON line's `value`): logprob-reduce rows/s on the
 prompt-scoring chunk -- 256 rows x 248,320 vocabulary bf16 logits, K = 20
-(MTPLX PR #532, Motivation and Evidence) -- one `logprob_reduce` call (both
-kernels) per step, inputs resident in HBM, four distinct chunks rotated so
-that no step is served from the 256 MB MALL.
+(MTPLX PR #532, Motivation and Evidence) -- one `logprob_reduce` call per
+step (on a 256-CU device: one launch, a workgroup per row), inputs resident
+in HBM, four distinct chunks rotated so that no step is served from the
+256 MB MALL.
 
 The same line carries:
-  roofline      the dominant kernel (the reduction's streaming pass) against
-                the 8 TB/s HBM peak, timed live with HIP events per launch;
+  roofline      the step's kernel (streaming pass and top-K in one launch)
+                against the 8 TB/s HBM peak, back-to-back launches timed live
+                with HIP events; split_stage1 is the streaming kernel of the
+                two-launch path (rows that do not fill the CUs) alone;
   cpu_baseline  the f64 CPU oracle on a bounded sample of the same chunk;
   reduce_by_k   the chunk at K = 0, 1, 20, 128;
   decode        32 x 151,936 decode rows, K = 5 (openinfer issue #719);
@@ -65,7 +68,8 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
     f_fetch = fetch[copy[0]] * 1024 / nbytes
     f_write = write[copy[0]] * 1024 / nbytes
     csrc = os.path.join(ROOT, "top_reduction_amd", "csrc")
-    wanted = {"reduce_stage1_bf16": ("k_stage1<true, true>", "reduce.hip", nbytes),
+    wanted = {"reduce_row_bf16": ("k_rowreduce<true, 16, true>", "reduce.hip", nbytes),
+              "reduce_stage1_bf16": ("k_stage1<true, true>", "reduce.hip", nbytes),
               "reduce_stage2_bf16": ("k_stage2<true", "reduce.hip", None),
               "head_stream_bf16": ("k_head_stream<", "head.hip", 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
               "head_tiled_bf16": ("k_head_tiled<", "head.hip", 151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4)}
@@ -235,22 +239,37 @@ def main():
     assert all(f() == 0 for f in fns)
     ms = timer.loop(fns, steps, warmup)
     log(f"reduce K={K}: {ms * 1e3:.1f} us/step")
+    red_src = os.path.join(ROOT, "top_reduction_amd", "csrc", "reduce.hip")
+    row_path = lmh.reduce_row_path(rows, V, K)
+    # back-to-back launches of the step's kernel(s): per-step time over the
+    # whole timed loop (an event pair around each launch would add its own
+    # overhead to every interval)
+    t_step = timer.loop_median(fns, steps, warmup)
+    achieved = nbytes / (t_step * 1e-3) / 1e9
+    if row_path:
+        kname = f"k_rowreduce<bf16> (the whole K={K} step in one launch: stream + in-workgroup top-K)"
+        tkey = "reduce_row_bf16"
+    else:
+        kname = f"k_stage1 + k_stage2 (split path, K={K})"
+        tkey = None
+    log(f"step kernel(s): {t_step * 1e3:.1f} us per step -> {achieved:.0f} GB/s ({kname})")
+    roofline = {"bound": "hbm", "kernel": kname,
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(tkey, red_src) if tkey else None,
+                "bytes_per_launch": nbytes, "launch_us": round(t_step * 1e3, 2)}
+    # the split path's streaming kernel alone (what rows that do not fill the
+    # CUs evenly go through)
     stage1 = []
     for (t, _, _, _), ws in zip(chunks, wss):
         a = (vp(t), lmh.LMH_BF16, rows, V, V, K, vp(ws), ws.numel(), stream)
         stage1.append(lambda a=a: L.lmh_debug_reduce_stage1(*a))
-    # back-to-back launches of the streaming kernel alone: per-launch time over
-    # the whole timed loop (an event pair around each launch would add its own
-    # overhead to every interval)
     t1 = timer.loop_median(stage1, steps, warmup)
-    achieved = nbytes / (t1 * 1e-3) / 1e9
-    log(f"stage1: {t1 * 1e3:.1f} us per launch -> {achieved:.0f} GB/s")
-    stage1_src = os.path.join(ROOT, "top_reduction_amd", "csrc", "reduce.hip")
-    roofline = {"bound": "hbm", "kernel": "k_stage1<bf16> (reduce streaming pass)",
-                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic("reduce_stage1_bf16", stage1_src),
-                "bytes_per_launch": nbytes, "launch_us": round(t1 * 1e3, 2)}
+    a1 = nbytes / (t1 * 1e-3) / 1e9
+    log(f"split-path stage1 alone: {t1 * 1e3:.1f} us per launch -> {a1:.0f} GB/s")
+    split_stage1 = {"kernel": "k_stage1<bf16> (split-path streaming pass alone)", "achieved": round(a1, 1),
+                    "frac": round(a1 / HBM_PEAK_GBS, 4), "launch_us": round(t1 * 1e3, 2),
+                    "traffic": load_traffic("reduce_stage1_bf16", red_src)}
 
     if "reduce" in sections:
         by_k = {}
@@ -412,16 +431,21 @@ def main():
     cpu = None
     if "cpu" in sections:
         import oracle
-        bits, sel = chunks[0][2], chunks[0][3]
-        nrows = rows
+        # passes over the four chunks in turn until at least 10 s of oracle work
+        # (at most 64 passes)
         t0 = time.perf_counter()
-        oracle.reduce(bits[:nrows], sel[:nrows], K)
+        nrows = passes = 0
+        while (time.perf_counter() - t0 < 10.0 and passes < 64) or passes == 0:
+            bits, sel = chunks[passes % len(chunks)][2], chunks[passes % len(chunks)][3]
+            oracle.reduce(bits, sel, K)
+            nrows += rows
+            passes += 1
         dt = time.perf_counter() - t0
         cpu = {"value": round(nrows / dt, 2), "unit": "rows/s", "cores": oracle.num_threads(),
                "kind": "oracle",
-               "sample": f"{nrows} rows of the 256 x 248320 bf16 chunk (normal), K={K}, f64 max + "
-                         f"exp-sum passes and a full sort per row; {dt:.2f} s"}
-        log(f"cpu oracle: {nrows / dt:.1f} rows/s on {cpu['cores']} threads")
+               "sample": f"{passes} passes over the 256 x 248320 bf16 chunks ({nrows} rows), K={K}, "
+                         f"f64 max + exp-sum passes and a full sort per row; {dt:.1f} s"}
+        log(f"cpu oracle: {nrows / dt:.1f} rows/s on {cpu['cores']} threads ({dt:.1f} s)")
 
     line = {
         "metric": METRIC,
@@ -443,6 +467,8 @@ def main():
         "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "split_stage1": split_stage1,
+        "reduce_path": "one workgroup per row" if row_path else "split (two launches)",
     }
     line.update(result)
     print(json.dumps(line), flush=True)

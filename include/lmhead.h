@@ -154,11 +154,17 @@ size_t logprob_reduce_workspace_size(int64_t rows, int64_t vocab, int32_t k);
  * lse [rows], selected_logprob [rows], topk_ids [rows][k] (int32),
  * topk_logprobs [rows][k] (fp32): outputs, written in full.
  * Method: one coalesced pass over each row produces online (max, sum-exp)
- * partials and the maximum of every 64-logit block; a second pass per row
- * combines the partials in a fixed order, keeps the min(k, nb) blocks with
- * the largest maxima (equal maxima by ascending block index) and takes the
- * exact top-K among the entries of those blocks that are not below the k-th
- * kept block maximum. No full-vocabulary log-softmax is formed.
+ * partials per 4096-logit segment and the maximum of every 64-logit block;
+ * the partials are combined in one fixed order, the min(k, nb) blocks with
+ * the largest maxima (equal maxima by ascending block index) are kept and the
+ * exact top-K is taken among the entries of those blocks that are not below
+ * the k-th kept block maximum. No full-vocabulary log-softmax is formed.
+ * When the rows fill the device's compute units evenly (see
+ * lmh_debug_reduce_path) one workgroup reduces each row in a single launch
+ * with the block maxima in LDS; otherwise a streaming launch over all rows
+ * writes partials and block maxima to the workspace and a second launch
+ * finishes each row. Both give bitwise-identical results, so a row's
+ * results do not depend on the rows around it.
  * An all -inf row gives lse = -inf and NaN logprobs (ids 0..k-1); a selected
  * id outside [0, vocab) gives NaN and LMH_DEVERR_INDEX. rows = 0 is a no-op
  * (pointers may then be NULL) once the shape and K rules pass.
@@ -237,6 +243,14 @@ lmh_status lmh_debug_gather_project(
 lmh_status lmh_debug_reduce_stage1(
     const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab, int64_t logits_ld,
     int32_t k, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lmh_debug_reduce_path -- 1 when logprob_reduce with these sizes runs as one
+ * workgroup per row on the current HIP device (rows fill its compute units
+ * evenly and, for k > 0, vocab <= 4096 * 64), 0 when it runs as the two-launch
+ * split path. No device work; rows, vocab and k are not validated.
+ */
+int32_t lmh_debug_reduce_path(int64_t rows, int64_t vocab, int32_t k);
 
 #ifdef __cplusplus
 }

@@ -137,3 +137,63 @@ def test_zero_rows():
     out = lmh.logprob_reduce(t, None, 5)
     torch.cuda.synchronize()
     assert out.lse.numel() == 0
+
+
+def _edge_block(V):
+    """The edge rows of test_edge_rows, for any V >= 2."""
+    rows = np.full((5, V), 0x3F80, dtype=np.uint16)
+    rows[0, :] = 0xFF80
+    rows[1, :] = 0xFF80
+    pos = synth.rng(5).choice(V, size=min(100, V), replace=False)
+    rows[1, pos] = synth.f32_to_bf16_bits(synth.normal_f32(synth.rng(6), (pos.size,)))
+    rows[3, :] = np.where(np.arange(V) % 2 == 0, 0x8000, 0x0000)
+    rows[3, V // 3] = 0x3F80
+    rows[4, :] = 0xBF80
+    rows[4, ::97] = 0x4000
+    return rows
+
+
+@pytest.mark.parametrize("V,dt,k", [(248_320, "bf16", 20), (248_320, "bf16", 128), (248_320, "bf16", 0),
+                                    (128_256, "f32", 20), (1000, "bf16", 5), (4097, "f32", 64),
+                                    (65, "bf16", 3), (1, "f32", 1)])
+def test_row_path_matches_split_path(V, dt, k):
+    """256 rows (one workgroup per row on a 256-CU device) against the same
+    rows reduced 100 at a time (split path): bitwise equal lse, selected
+    logprobs, ids and logprobs; edge rows included; oracle on sampled rows."""
+    print(f"row vs split V={V} dt={dt} k={k}", flush=True)
+    g = synth.rng(7000 + V % 1000 + k)
+    R = 256
+    ld = (V + 7) // 8 * 8            # 16-byte row pitch; the logits are a column view
+    if dt == "bf16":
+        data = synth.f32_to_bf16_bits(synth.normal_f32(g, (R, V)) * np.float32(2.0))
+        if V >= 2:
+            data[:5] = _edge_block(V)
+        full = np.zeros((R, ld), dtype=np.uint16)
+        full[:, :V] = data
+        t = bf16_tensor(full)[:, :V]
+    else:
+        data = synth.normal_f32(g, (R, V)) * np.float32(3.0)
+        data[0, :] = -np.inf
+        full = np.zeros((R, ld), dtype=np.float32)
+        full[:, :V] = data
+        t = torch.from_numpy(full).cuda()[:, :V]
+    ref_rows = data
+    sel = g.integers(0, V, size=R).astype(np.int32)
+    sel[7] = V          # out of range: NaN and the index flag, on both paths
+    if torch.cuda.get_device_properties(0).multi_processor_count <= R:
+        assert lmh.reduce_row_path(R, V, k) and not lmh.reduce_row_path(100, V, k)
+    a = lmh.logprob_reduce(t, i32_tensor(sel), k)
+    parts = [lmh.logprob_reduce(t[i:i + 100], i32_tensor(sel[i:i + 100]), k) for i in range(0, R, 100)]
+    torch.cuda.synchronize()
+    assert int(a.device_error.item()) == lmh.LMH_DEVERR_INDEX
+    cat = lambda f: torch.cat([getattr(p, f) for p in parts])
+    assert torch.equal(a.lse.view(torch.int32), cat("lse").view(torch.int32))
+    assert torch.equal(a.selected_logprob.view(torch.int32), cat("selected_logprob").view(torch.int32))
+    if k > 0:
+        assert torch.equal(a.topk_ids, cat("topk_ids"))
+        assert torch.equal(a.topk_logprobs.view(torch.int32), cat("topk_logprobs").view(torch.int32))
+    pick = np.array([0, 1, 2, 3, 4, 7, 100, 255])
+    ref = oracle.reduce(np.ascontiguousarray(ref_rows[pick]), sel[pick], k)
+    sub = lmh.Reduction(a.lse[pick], a.selected_logprob[pick], a.topk_ids[pick], a.topk_logprobs[pick],
+                        a.device_error)
+    check_reduce(sub, np.ascontiguousarray(ref_rows[pick]), sel[pick], k, *ref)

@@ -54,6 +54,8 @@ def lib():
         L.logprob_reduce_workspace_size.restype = sz
         L.logprob_reduce.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p, p, sz, p, p]
         L.lmh_debug_reduce_stage1.argtypes = [p, ctypes.c_int, i64, i64, i64, i32, p, sz, p]
+        L.lmh_debug_reduce_path.argtypes = [i64, i64, i32]
+        L.lmh_debug_reduce_path.restype = i32
         L.lmhead_logprobs_workspace_size.argtypes = [i64, i64, i32, i32]
         L.lmhead_logprobs_workspace_size.restype = sz
         L.lmhead_logprobs.argtypes = proj + [p, i32, p, p, p, p, p, p, i32, p, p, sz, p, p]
@@ -189,6 +191,12 @@ def reduce_stage1(logits: torch.Tensor, k: int, ws: torch.Tensor) -> None:
     R, V, ld = _matrix(logits, "logits")
     _check(L.lmh_debug_reduce_stage1(_ptr(logits), _dt(logits), R, V, ld, int(k), _ptr(ws),
                                      ws.numel(), _stream()), "lmh_debug_reduce_stage1")
+
+
+def reduce_row_path(rows: int, vocab: int, k: int) -> bool:
+    """True when logprob_reduce of this shape runs one workgroup per row on
+    the current device (a single launch), False for the two-launch path."""
+    return bool(lib().lmh_debug_reduce_path(int(rows), int(vocab), int(k)))
 
 
 class Logprobs(NamedTuple):

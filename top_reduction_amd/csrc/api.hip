@@ -175,9 +175,7 @@ lmh_status logprob_reduce(const void* logits, lmh_dtype logits_dt, int64_t rows,
     hipStream_t s = static_cast<hipStream_t>(stream);
     ReduceArgs a{logits, logits_dt == LMH_BF16, logits_ld, selected_ids, lse, selected_logprob,
                  topk_ids, topk_logprobs, workspace, device_error};
-    lmh_status r = from_hip(launch_reduce_stage1(p, a, s));
-    if (r != LMH_OK) return r;
-    return from_hip(launch_reduce_stage2(p, a, s));
+    return from_hip(launch_reduce(p, a, s));
 }
 
 lmh_status lmh_debug_reduce_stage1(const void* logits, lmh_dtype logits_dt, int64_t rows,
@@ -193,6 +191,11 @@ lmh_status lmh_debug_reduce_stage1(const void* logits, lmh_dtype logits_dt, int6
     ReduceArgs a{logits, logits_dt == LMH_BF16, logits_ld, nullptr, nullptr, nullptr,
                  nullptr, nullptr, workspace, nullptr};
     return from_hip(launch_reduce_stage1(p, a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmh_debug_reduce_path(int64_t rows, int64_t vocab, int32_t k) {
+    if (rows <= 0 || vocab <= 0 || k < 0) return 0;
+    return reduce_row_path(plan_reduce(rows, vocab, k)) ? 1 : 0;
 }
 
 size_t lmhead_logprobs_workspace_size(int64_t rows, int64_t vocab, int32_t k, int32_t chunk_rows) {
@@ -264,9 +267,7 @@ lmh_status lmhead_logprobs(const void* hidden, lmh_dtype hidden_dt, int64_t num_
                      selected_ids ? selected_logprob + r0 : nullptr,
                      k > 0 ? topk_ids + r0 * k : nullptr, k > 0 ? topk_logprobs + r0 * k : nullptr,
                      ws_reduce, device_error};
-        st = from_hip(launch_reduce_stage1(q, a, s));
-        if (st != LMH_OK) return st;
-        st = from_hip(launch_reduce_stage2(q, a, s));
+        st = from_hip(launch_reduce(q, a, s));
         if (st != LMH_OK) return st;
     }
     return LMH_OK;

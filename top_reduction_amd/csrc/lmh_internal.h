@@ -120,5 +120,11 @@ struct ReduceArgs {
 };
 hipError_t launch_reduce_stage1(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
+// True when the one-workgroup-per-row kernel serves this plan on the current
+// device (rows fill the CUs evenly); the split path otherwise. Both give
+// bitwise-identical results.
+bool reduce_row_path(const ReducePlan& p);
+// The whole reduction (either path).
+hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
 
 }  // namespace lmh

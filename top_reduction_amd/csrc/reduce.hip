@@ -98,22 +98,23 @@ __device__ inline float key_value(uint32_t k) {
 
 // ---------------------------------------------------------------------------
 // Stage 1: a row is cut into fixed segments of kSeg logits (the last one
-// partial); each segment is the work item of one wave, and items are numbered
-// row-major so that consecutively dispatched waves stream consecutive memory.
-// Lane l of a wave reads the item's 16-byte vectors l, l + 64, ...; all of an
-// item's loads are in flight before its first vector is used, and the item's
-// 64 logits per lane stay in registers for two passes:
+// partial), the work items. Lane l of a wave reads an item's 16-byte vectors
+// l, l + 64, ...; all of an item's loads are in flight before its first vector
+// is used, and the item's 64 logits per lane stay in registers for two passes:
 //   1. the maximum of each lane's slice of every 64-logit block (the 8 bf16 or
 //      16 fp32 lanes of a block then combine it with DPP), and of the lane;
 //   2. with M the wave maximum, the sum of 2^(x*log2e + c) for c = -RN(M*log2e):
 //      one fma, one exp2 and one add per logit. The rounding of c is the
 //      exactly representable e = M*log2e + c (an fma), and the sum is scaled
 //      by 2^-e once, so the partial is (M, sum of exp(x - M)) to fp32 rounding.
-// The lane sums are added by a fixed DPP tree into lane 63. The block maxima
-// are transposed across the wave (a register select, then ds_bpermute) so that
-// lane b holds block b, and stored as keys with one coalesced store. Neither
-// the segments nor the summation order depend on how many rows a call holds,
-// so each row's results are bitwise independent of the batch around it.
+// The lane sums are added by a fixed DPP tree. The block maxima are transposed
+// across the wave (a register select, then ds_bpermute) so that lane b holds
+// block b. The item partials of a row are merged in one canonical order:
+// item i joins merge group i mod 16, each group merges its items in
+// ascending order, and the 16 groups are merged in order. Both reduction
+// paths (the split one and the one-workgroup-per-row one) use exactly this
+// arithmetic, so each row's results are bitwise independent of the batch
+// around it and of the path that served it.
 // ---------------------------------------------------------------------------
 // One (max, sum-exp) merge step with the partner chosen by a DPP control;
 // lanes without a partner merge the identity (-inf, 0).
@@ -164,11 +165,14 @@ struct Stage1Item {
 
 // Reduces one item held in buf (VPL vectors per lane; entries past V hold
 // -inf) and writes its partial and block keys.
+constexpr int kGroups = 16;   // merge groups of a row's item partials
+
+// Reduces one item held in buf (VPL vectors per lane; entries past V hold
+// -inf): M and S (the item's max and its sum of exp(x - M)) come back
+// wave-uniform; with KEYS, kb is the monotone key of block seg*64 + lane.
 template <bool BF16, bool KEYS>
-__device__ __forceinline__ void stage1_reduce(const u32x4 (&buf)[Stage1Item<BF16>::VPL], int lane,
-                                              int64_t it, int64_t row, int32_t seg, int64_t V,
-                                              int32_t kld, float2* __restrict__ part,
-                                              void* __restrict__ keys) {
+__device__ __forceinline__ void stage1_item(const u32x4 (&buf)[Stage1Item<BF16>::VPL], int lane, float& M,
+                                            float& S, uint32_t& kb) {
     using I = Stage1Item<BF16>;
     float x[I::VPL * I::EPV];
     float bm[I::VPL];
@@ -194,7 +198,7 @@ __device__ __forceinline__ void stage1_reduce(const u32x4 (&buf)[Stage1Item<BF16
         lm = vmax(lm, vm);
     }
 
-    const float M = group_max<64>(lm);
+    M = group_max<64>(lm);
     const float Mr = (M == kNegInf) ? 0.f : M;
     const float c = -(Mr * kLog2e);
     const float e = fmaf(Mr, kLog2e, c);   // exact: Mr*log2e - RN(Mr*log2e)
@@ -206,68 +210,63 @@ __device__ __forceinline__ void stage1_reduce(const u32x4 (&buf)[Stage1Item<BF16
         s2 += ex2(fmaf(x[i + 2], kLog2e, c));
         s3 += ex2(fmaf(x[i + 3], kLog2e, c));
     }
-    const float s = wave_sum_to_63((s0 + s1) + (s2 + s3));
-    if (lane == 63) part[it] = make_float2(M, s * ex2(-e));
+    const float s63 = wave_sum_to_63((s0 + s1) + (s2 + s3));
+    S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s63), 63)) * ex2(-e);
 
     if (KEYS) {
         // lane g*VPB + r holds block r*GPV + g after the select; block b comes
         // from lane (b % GPV)*VPB + b / GPV
         const float mine = select_reg<I::VPL>(bm, lane % I::VPB);
         const int src = (lane % I::GPV) * I::VPB + lane / I::GPV;
-        const float kbm = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(mine)));
-        const int64_t blk = (int64_t)seg * (kSeg / kBlock) + lane;
-        if (blk * kBlock < V) {
-            const uint32_t kb = f32_key(kbm);
-            if (BF16)
-                reinterpret_cast<uint16_t*>(keys)[row * kld + blk] = (uint16_t)(kb >> 16);
-            else
-                reinterpret_cast<uint32_t*>(keys)[row * kld + blk] = kb;
-        }
+        kb = f32_key(__int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(mine))));
     }
 }
 
-template <bool BF16, bool KEYS>
-__global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__ logits, int64_t ld,
-                                                     int64_t V, int32_t kld, int32_t P, int64_t nitems,
-                                                     float2* __restrict__ part, void* __restrict__ keys) {
+// Loads full item `seg` of a row into buf: one 16-byte load per vector.
+template <bool BF16>
+__device__ __forceinline__ void stage1_load_full(const uint8_t* rowp, int32_t seg, int lane,
+                                                 u32x4 (&buf)[Stage1Item<BF16>::VPL]) {
+    using I = Stage1Item<BF16>;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rowp) + (int64_t)seg * (kSeg / I::EPV);
+#pragma unroll
+    for (int j = 0; j < I::VPL; ++j) buf[j] = vp[j * 64 + lane];
+}
+
+// Loads item `seg` of a row into buf. Full items: one 16-byte load per vector,
+// all issued before any is used. The partial last item fills entries past V
+// with -inf (16-byte loads up to the last whole vector, then elementwise).
+template <bool BF16>
+__device__ __forceinline__ bool stage1_load(const uint8_t* rowp, int64_t V, int32_t seg, int lane,
+                                            u32x4 (&buf)[Stage1Item<BF16>::VPL]) {
     using I = Stage1Item<BF16>;
     constexpr int EPV = I::EPV;
-    constexpr int VPL = I::VPL;
-    constexpr size_t ESZ = BF16 ? 2 : 4;
-
-    const int lane = threadIdx.x & 63;
-    // wave-uniform item arithmetic in scalar registers (item count < 2^32)
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t itu = blockIdx.x * (uint32_t)(kThreads / 64) + wave;
-    if ((int64_t)itu >= nitems) return;
-    const int64_t it = itu;
-    const uint32_t rowu = itu / (uint32_t)P;
-    const int64_t row = rowu;
-    const int32_t seg = (int32_t)(itu - rowu * (uint32_t)P);
-    const int64_t nvec_row = (V + EPV - 1) / EPV;
     const int64_t vb = (int64_t)seg * (kSeg / EPV);
     const bool full = vb + kSeg / EPV <= V / EPV;   // wave-uniform: no element past V
-    const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp) + vb;
-    const uint32_t ninf_word = BF16 ? 0xFF80FF80u : 0xFF800000u;
-
-    u32x4 buf[VPL];
     if (full) {
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) buf[j] = vp[j * 64 + lane];
-        // every load issued before any result is used (the scheduler would
-        // otherwise hoist the first unpack between them and wait on it)
-        __builtin_amdgcn_sched_barrier(0);
-        stage1_reduce<BF16, KEYS>(buf, lane, it, row, seg, V, kld, part, keys);
-    } else {
+        for (int j = 0; j < I::VPL; ++j) buf[j] = vp[j * 64 + lane];
+        return true;
+    }
+    // all whole-vector loads issued unguarded (addresses clamped to the last
+    // whole vector), then entries past V replaced by -inf; only the vector
+    // that straddles V (when V is not a multiple of EPV) is read elementwise
+    const uint32_t ninf_word = BF16 ? 0xFF80FF80u : 0xFF800000u;
+    const int64_t nwhole = V / EPV;                     // whole vectors in the row
+    const u32x4* rv = reinterpret_cast<const u32x4*>(rowp);
+    if (nwhole > 0) {
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) {
+        for (int j = 0; j < I::VPL; ++j) {
             const int64_t v = vb + j * 64 + lane;
-            buf[j] = u32x4{ninf_word, ninf_word, ninf_word, ninf_word};
-            if (v + 1 <= V / EPV) {
-                buf[j] = vp[j * 64 + lane];
-            } else if (v < nvec_row) {   // the one vector that straddles V
-                uint32_t w[4] = {ninf_word, ninf_word, ninf_word, ninf_word};
+            buf[j] = rv[v < nwhole ? v : nwhole - 1];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < I::VPL; ++j) {
+        const int64_t v = vb + j * 64 + lane;
+        if (v >= nwhole) {
+            uint32_t w[4] = {ninf_word, ninf_word, ninf_word, ninf_word};
+            if (v == nwhole) {   // the vector that straddles V, if any
                 for (int e = 0; e < EPV; ++e) {
                     const int64_t i = v * EPV + e;
                     if (i < V) {
@@ -280,10 +279,52 @@ __global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__
                         }
                     }
                 }
-                buf[j] = u32x4{w[0], w[1], w[2], w[3]};
             }
+            buf[j] = u32x4{w[0], w[1], w[2], w[3]};
         }
-        stage1_reduce<BF16, KEYS>(buf, lane, it, row, seg, V, kld, part, keys);
+    }
+    return false;
+}
+
+// Split path, first kernel: one item per wave over all rows, items numbered
+// row-major so that consecutively dispatched waves stream consecutive memory;
+// writes each item's partial and its block keys to the workspace.
+template <bool BF16, bool KEYS>
+__global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__ logits, int64_t ld,
+                                                     int64_t V, int32_t kld, int32_t P, int64_t nitems,
+                                                     float2* __restrict__ part, void* __restrict__ keys) {
+    using I = Stage1Item<BF16>;
+    constexpr size_t ESZ = BF16 ? 2 : 4;
+    const int lane = threadIdx.x & 63;
+    // wave-uniform item arithmetic in scalar registers (item count < 2^32)
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t itu = blockIdx.x * (uint32_t)(kThreads / 64) + wave;
+    if ((int64_t)itu >= nitems) return;
+    const uint32_t rowu = itu / (uint32_t)P;
+    const int64_t row = rowu;
+    const int32_t seg = (int32_t)(itu - rowu * (uint32_t)P);
+    const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
+
+    u32x4 buf[I::VPL];
+    float M, S;
+    uint32_t kb = 0;
+    if (stage1_load<BF16>(rowp, V, seg, lane, buf)) {
+        // every load issued before any result is used (the scheduler would
+        // otherwise hoist the first unpack between them and wait on it)
+        __builtin_amdgcn_sched_barrier(0);
+        stage1_item<BF16, KEYS>(buf, lane, M, S, kb);
+    } else {
+        stage1_item<BF16, KEYS>(buf, lane, M, S, kb);
+    }
+    if (lane == 0) part[itu] = make_float2(M, S);
+    if (KEYS) {
+        const int64_t blk = (int64_t)seg * (kSeg / kBlock) + lane;
+        if (blk * kBlock < V) {
+            if (BF16)
+                reinterpret_cast<uint16_t*>(keys)[row * kld + blk] = (uint16_t)(kb >> 16);
+            else
+                reinterpret_cast<uint32_t*>(keys)[row * kld + blk] = kb;
+        }
     }
 }
 
@@ -300,14 +341,15 @@ struct SelectScratch {
 // MSD radix select, 8 bits per pass. Every thread of the workgroup calls it.
 // Only used when many candidates tie (e.g. constant rows): heavily repeated
 // digits serialise its LDS atomics.
+template <int NT>
 __device__ uint64_t radix_select(const uint64_t* keys, int n, int k, SelectScratch& sc) {
     const int tid = threadIdx.x;
     uint64_t prefix = 0, mask = 0;
     int kk = k;
     for (int shift = 56; shift >= 0; shift -= 8) {
-        sc.hist[tid] = 0;
+        if (tid < 256) sc.hist[tid] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += kThreads) {
+        for (int i = tid; i < n; i += NT) {
             const uint64_t key = keys[i];
             if ((key & mask) == prefix) atomicAdd(&sc.hist[(key >> shift) & 255], 1);
         }
@@ -378,8 +420,8 @@ __device__ inline uint32_t wave_reduce(uint32_t v) {
 
 // Workgroup-wide reduction of N values; every thread gets the results. `buf`
 // alternates between two halves on consecutive calls, so one barrier each.
-template <int OP, int N>
-__device__ inline void block_reduce(uint32_t (&v)[N], uint32_t (*buf)[kThreads / 64][4], int& phase) {
+template <int OP, int N, int NT>
+__device__ inline void block_reduce(uint32_t (&v)[N], uint32_t (*buf)[NT / 64][4], int& phase) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < N; ++i) v[i] = wave_reduce<OP>(v[i]);
@@ -392,13 +434,14 @@ __device__ inline void block_reduce(uint32_t (&v)[N], uint32_t (*buf)[kThreads /
     for (int i = 0; i < N; ++i) {
         uint32_t t = buf[phase][0][i];
 #pragma unroll
-        for (int w = 1; w < kThreads / 64; ++w) t = dpp_op<OP>(t, buf[phase][w][i]);
+        for (int w = 1; w < NT / 64; ++w) t = dpp_op<OP>(t, buf[phase][w][i]);
         v[i] = t;
     }
     phase ^= 1;
 }
 
 // Workgroup-wide exclusive prefix sum in thread order; `total` gets the sum.
+template <int NT>
 __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wtot, uint32_t& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t inc = wave_scan<0>(v);
@@ -407,7 +450,7 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wtot, uint
     uint32_t base = 0;
     total = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         const uint32_t sw = wtot[w];
         base += (w < wave) ? sw : 0u;
         total += sw;
@@ -417,147 +460,42 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wtot, uint
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: one workgroup per row.
-//  (1) lse from the row's partials (fixed merge order);
-//  (2) the selected token's logprob;
-//  (3) T = the K-th largest block-max key counted with multiplicity: a 5-way
-//      search with exact counts over the key range [lo, max], where lo is the
-//      smallest per-thread maximum (at least K keys reach it whenever K
-//      threads hold blocks); the kept blocks are all keys above T plus the
-//      lowest-indexed keys equal to T, K in all, placed by one prefix scan;
-//  (4) one round of 16-byte loads gathers the kept blocks; entries with key
-//      >= T become candidates, compacted by a prefix scan;
-//  (5) each candidate's rank under (value desc, id asc) is counted in LDS and
-//      the first K are written.
-// Every thread holds the keys of KPT consecutive blocks in registers.
+// Top-K of one row by NT threads (steps a6, a7):
+//  * T = the K-th largest block-max key counted with multiplicity: a 5-way
+//    search with exact counts over the key range [lo, max], where lo is the
+//    smallest per-thread maximum (at least K keys reach it whenever K threads
+//    hold blocks), finished by a 256-bin LDS histogram; the kept blocks are
+//    all keys above T plus the lowest-indexed keys equal to T, K in all;
+//  * one round of 16-byte loads gathers the kept blocks; entries with key
+//    >= T become candidates, compacted by a prefix scan;
+//  * each candidate's rank under (value desc, id asc) is counted in LDS and
+//    the first K are written.
+// Thread t holds the keys of blocks [t*KPT, t*KPT + KPT) in kr (0 past nb: a
+// 0 never counts and never ties, every real key being above it).
 // ---------------------------------------------------------------------------
-template <bool BF16, int KPT>
-__global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__ logits, int64_t ld,
-                                                     int64_t V, int32_t nb, int32_t kld, int32_t splits,
-                                                     const float2* __restrict__ part,
-                                                     const void* __restrict__ keys,
-                                                     const int32_t* __restrict__ sel, int32_t K,
-                                                     float* __restrict__ lse_out,
-                                                     float* __restrict__ sel_out,
-                                                     int32_t* __restrict__ topk_ids,
-                                                     float* __restrict__ topk_lp,
-                                                     int32_t* __restrict__ err, int32_t cap) {
-    extern __shared__ uint64_t smem[];   // [cap] candidates, [K] narrowed list
-    uint64_t* cand = smem;
-    uint64_t* list2 = smem + cap;
-    __shared__ SelectScratch sc;
-    __shared__ uint32_t sred[2][kThreads / 64][4];
-    __shared__ uint32_t swtot[kThreads / 64];
-    __shared__ float s_lse;
-    __shared__ int32_t s_blk[kMaxCandidates / kBlock];
-    __shared__ int32_t s_nlist, s_nblk;
-    __shared__ uint32_t sh_hist[kHistBins];
-    __shared__ uint32_t s_thr[3];
+template <int NT>
+struct RowShared {
+    SelectScratch sc;
+    uint32_t sred[2][NT / 64][4];
+    uint32_t swtot[NT / 64];
+    int32_t blk[kMaxCandidates / kBlock];
+    int32_t nlist, nblk;
+    uint32_t hist[kHistBins];
+    uint32_t thr[3];
+    float lse;
+};
+
+template <bool BF16, int KPT, int NT>
+__device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t V, int32_t nb, int32_t K,
+                         const uint32_t (&kr)[KPT], float lse, uint64_t* cand, uint64_t* list2, int32_t cap,
+                         RowShared<NT>& sh, int32_t* __restrict__ topk_ids, float* __restrict__ topk_lp) {
     constexpr size_t ESZ = BF16 ? 2 : 4;
     constexpr int EPV = BF16 ? 8 : 4;                 // elements per 16-byte vector
     constexpr int VPB = kBlock / EPV;                 // vectors per block
-    constexpr int MAXV = kMaxCandidates / EPV / kThreads;   // vectors per thread, at most
+    constexpr int MAXV = (kMaxCandidates / EPV + NT - 1) / NT;   // vectors per thread, at most
     constexpr int MAXBLK = kMaxCandidates / kBlock;
-
-    const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
-    if (tid < MAXBLK) s_blk[tid] = -1;   // unfilled slots are skipped, never dereferenced
-
-    // this thread's block keys, blocks [b0, b0 + KPT); 0 past nb (every real
-    // key is above 0, so a 0 never counts and never ties)
     const int b0 = tid * KPT;
-    uint32_t kr[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) kr[j] = 0u;
-    if (K > 0 && K <= nb && b0 < nb) {
-        if (BF16) {
-            const uint16_t* kp = reinterpret_cast<const uint16_t*>(keys) + row * kld + b0;
-            if (KPT == 4) {
-                const uint2 q = *reinterpret_cast<const uint2*>(kp);
-                const uint32_t wq[2] = {q.x, q.y};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kr[j] = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
-            } else {
-#pragma unroll
-                for (int c = 0; c < KPT / 8; ++c) {
-                    const u32x4 q = reinterpret_cast<const u32x4*>(kp)[c];
-                    const uint32_t wq[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        kr[c * 8 + j] = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
-                }
-            }
-        } else {
-            const uint32_t* kp = reinterpret_cast<const uint32_t*>(keys) + row * kld + b0;
-#pragma unroll
-            for (int c = 0; c < KPT / 4; ++c) {
-                const u32x4 q = reinterpret_cast<const u32x4*>(kp)[c];
-                kr[c * 4 + 0] = q.x;
-                kr[c * 4 + 1] = q.y;
-                kr[c * 4 + 2] = q.z;
-                kr[c * 4 + 3] = q.w;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if (b0 + j >= nb) kr[j] = 0u;
-    }
-
-    // the selected token's id, issued now (thread 64: off the lse wave) and
-    // used at the end, after the loads have long landed
-    const bool sel_thread = sel != nullptr && sel_out != nullptr && tid == 64;
-    int32_t sel_id = 0;
-    if (sel_thread) sel_id = sel[row];
-
-    // (1) logsumexp: wave 0 merges the row's partials in a fixed order (a
-    // strided pass per lane, then a DPP tree into lane 63)
-    if (tid < 64) {
-        float m = kNegInf, s = 0.f;
-        for (int i = tid; i < splits; i += 64) {
-            const float2 p = part[row * splits + i];
-            lse_merge(m, s, p.x, p.y);
-        }
-        LMH_LSE_DPP_STEP(m, s, 0x111, 0xF);
-        LMH_LSE_DPP_STEP(m, s, 0x112, 0xF);
-        LMH_LSE_DPP_STEP(m, s, 0x114, 0xF);
-        LMH_LSE_DPP_STEP(m, s, 0x118, 0xF);
-        LMH_LSE_DPP_STEP(m, s, 0x142, 0xA);
-        LMH_LSE_DPP_STEP(m, s, 0x143, 0xC);
-        if (tid == 63) {
-            const float l = (m == kNegInf) ? kNegInf : m + logf(s);
-            s_lse = l;
-            lse_out[row] = l;
-            s_nlist = 0;
-            s_nblk = 0;
-        }
-    }
-    __syncthreads();
-    const float lse = s_lse;
-
-    // (2) selected token: its logit load is issued here and consumed last
-    const bool sel_ok = sel_thread && sel_id >= 0 && (int64_t)sel_id < V;
-    float xsel = 0.f;
-    if (sel_ok)
-        xsel = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[sel_id])
-                    : reinterpret_cast<const float*>(rowp)[sel_id];
-    auto write_selected = [&]() {
-        if (sel_thread) {
-            if (sel_ok) {
-                sel_out[row] = xsel - lse;
-            } else {
-                sel_out[row] = __builtin_nanf("");
-                if (err) atomicOr(err, LMH_DEVERR_INDEX);
-            }
-        }
-    };
-    if (K == 0) {
-        write_selected();
-        return;
-    }
-
-    if (K == 0) return;
 
     // (3) threshold and kept blocks
     int phase = 0;
@@ -573,12 +511,12 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
         // one max-reduction gives the maximum and (complemented) two minima:
         // of all keys, and of the per-thread maxima of threads holding blocks
         uint32_t mm[3] = {tmax, ~tmin, b0 < nb ? ~tmax : 0u};
-        block_reduce<1, 3>(mm, sred, phase);
+        block_reduce<1, 3, NT>(mm, sh.sred, phase);
         const int nth = (nb + KPT - 1) / KPT;           // threads holding blocks
-        const int sh = BF16 ? 16 : 0;
+        const int ksh = BF16 ? 16 : 0;
         // Largest t with count(key >= t) >= K; count(>= lo) >= K > count(>= hi).
-        uint64_t lo = (uint64_t)((K <= nth ? ~mm[2] : ~mm[1]) >> sh);
-        uint64_t hi = (uint64_t)(mm[0] >> sh) + 1;
+        uint64_t lo = (uint64_t)((K <= nth ? ~mm[2] : ~mm[1]) >> ksh);
+        uint64_t hi = (uint64_t)(mm[0] >> ksh) + 1;
         uint32_t c_hi = 0u;                              // count(key >= hi)
         // 5-way narrowing with exact counts until at most 256 key values remain
         while (hi - lo > kHistBins) {
@@ -592,12 +530,12 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
             uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int j = 0; j < KPT; ++j) {
-                const uint32_t kv = kr[j] >> sh;
+                const uint32_t kv = kr[j] >> ksh;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) c[i] += (kv >= t[i]) ? 1u : 0u;
             }
             uint32_t pk[2] = {c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
-            block_reduce<0, 2>(pk, sred, phase);
+            block_reduce<0, 2, NT>(pk, sh.sred, phase);
             const uint32_t cc[4] = {pk[0] & 0xFFFFu, pk[0] >> 16, pk[1] & 0xFFFFu, pk[1] >> 16};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -611,17 +549,17 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
         }
         // histogram of the keys in [lo, hi), then a suffix scan in wave 0:
         // T is the largest key value v with count(key >= v) >= K
-        sh_hist[tid] = 0u;
+        if (tid < kHistBins) sh.hist[tid] = 0u;
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-            const uint64_t kv = kr[j] >> sh;
-            if (kv >= lo && kv < hi) atomicAdd(&sh_hist[(int)(kv - lo)], 1u);
+            const uint64_t kv = kr[j] >> ksh;
+            if (kv >= lo && kv < hi) atomicAdd(&sh.hist[(int)(kv - lo)], 1u);
         }
         __syncthreads();
         if (tid < 64) {
-            const uint32_t h0 = sh_hist[4 * tid], h1 = sh_hist[4 * tid + 1];
-            const uint32_t h2 = sh_hist[4 * tid + 2], h3 = sh_hist[4 * tid + 3];
+            const uint32_t h0 = sh.hist[4 * tid], h1 = sh.hist[4 * tid + 1];
+            const uint32_t h2 = sh.hist[4 * tid + 2], h3 = sh.hist[4 * tid + 3];
             const uint32_t sum4 = h0 + h1 + h2 + h3;
             const uint32_t incl = wave_scan<0>(sum4);
             const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
@@ -636,22 +574,22 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
             else if (s1 >= k && s2 < k) { b = 4 * tid + 1; gt = s2; eqc = h1; }
             else if (s0 >= k && s1 < k) { b = 4 * tid; gt = s1; eqc = h0; }
             if (b >= 0) {
-                s_thr[0] = (uint32_t)((lo + (uint64_t)b) << sh);
-                s_thr[1] = gt;
-                s_thr[2] = eqc;
+                sh.thr[0] = (uint32_t)((lo + (uint64_t)b) << ksh);
+                sh.thr[1] = gt;
+                sh.thr[2] = eqc;
             }
         }
         __syncthreads();
-        T = s_thr[0];
-        const int need = K - (int)s_thr[1];             // blocks equal to T that are kept
-        const bool all_ties = (uint32_t)need == s_thr[2];
+        T = sh.thr[0];
+        const int need = K - (int)sh.thr[1];             // blocks equal to T that are kept
+        const bool all_ties = (uint32_t)need == sh.thr[2];
         if (all_ties) {
             // every key >= T is kept: placement order does not matter
 #pragma unroll
             for (int j = 0; j < KPT; ++j)
                 if (kr[j] >= T) {
-                    const int pos = atomicAdd(&s_nblk, 1);
-                    if (pos < MAXBLK) s_blk[pos] = b0 + j;
+                    const int pos = atomicAdd(&sh.nblk, 1);
+                    if (pos < MAXBLK) sh.blk[pos] = b0 + j;
                 }
         } else {
             // the lowest-indexed keys equal to T are kept: one ordered scan
@@ -662,7 +600,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
                 eq += (kr[j] == T) ? 1u : 0u;
             }
             uint32_t tot = 0u;
-            const uint32_t ex = block_exclusive_scan(gt | (eq << 16), swtot, tot);
+            const uint32_t ex = block_exclusive_scan<NT>(gt | (eq << 16), sh.swtot, tot);
             const uint32_t gt_before = ex & 0xFFFFu, eq_before = ex >> 16;
             int pos = (int)gt_before + min(need, (int)eq_before);
             int ei = (int)eq_before;
@@ -674,14 +612,14 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
                     ++ei;
                 }
                 if (keep) {
-                    if (pos < MAXBLK) s_blk[pos] = b0 + j;
+                    if (pos < MAXBLK) sh.blk[pos] = b0 + j;
                     ++pos;
                 }
             }
         }
         nblk = min(K, MAXBLK);
     } else {
-        for (int b = tid; b < nb; b += kThreads) s_blk[b] = b;
+        for (int b = tid; b < nb; b += NT) sh.blk[b] = b;
         nblk = nb;
     }
     __syncthreads();
@@ -692,9 +630,9 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     int64_t e0[MAXV];
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
-        const int j = tid + i * kThreads;
+        const int j = tid + i * NT;
         e0[i] = -1;
-        const int blk = j < nvec ? s_blk[j / VPB] : -1;
+        const int blk = j < nvec ? sh.blk[j / VPB] : -1;
         if (blk >= 0 && blk < nb) {
             e0[i] = (int64_t)blk * kBlock + (int64_t)(j % VPB) * EPV;
             if (e0[i] + EPV <= V) {
@@ -734,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
         }
     }
     uint32_t ncand_u = 0;
-    int cpos = (int)block_exclusive_scan(cnt, swtot, ncand_u);
+    int cpos = (int)block_exclusive_scan<NT>(cnt, sh.swtot, ncand_u);
     const int ncand = min((int)ncand_u, cap);
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
@@ -757,12 +695,12 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     // (5) exact top-K by rank under the composite (value key, ~id) order
     const uint64_t* list = cand;
     int nlist = ncand;
-    if (ncand > kThreads && ncand > K) {
-        const uint64_t thr2 = radix_select(cand, ncand, K, sc);
-        for (int i = tid; i < ncand; i += kThreads) {
+    if (ncand > NT && ncand > K) {
+        const uint64_t thr2 = radix_select<NT>(cand, ncand, K, sh.sc);
+        for (int i = tid; i < ncand; i += NT) {
             const uint64_t c = cand[i];
             if (c >= thr2) {
-                const int q = atomicAdd(&s_nlist, 1);
+                const int q = atomicAdd(&sh.nlist, 1);
                 if (q < K) list2[q] = c;
             }
         }
@@ -772,9 +710,9 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     }
     // G lanes (a quad, a pair or one lane) count one candidate's predecessors
     // over interleaved slices of the list, then sum with DPP inside the quad
-    const int G = nlist <= kThreads / 4 ? 4 : (nlist <= kThreads / 2 ? 2 : 1);
+    const int G = nlist <= NT / 4 ? 4 : (nlist <= NT / 2 ? 2 : 1);
     const int q = tid & (G - 1);
-    for (int i0 = 0; i0 < nlist * G; i0 += kThreads) {
+    for (int i0 = 0; i0 < nlist * G; i0 += NT) {
         const int i = (i0 + tid) / G;
         const bool act = i0 + tid < nlist * G;
         const uint64_t c = act ? list[i] : 0ull;
@@ -797,7 +735,280 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
             topk_lp[row * K + rank] = key_value<BF16>((uint32_t)(c >> 32)) - lse;
         }
     }
-    write_selected();
+}
+
+// Canonical merge of a row's item partials (group i mod 16, ascending items
+// within a group, then groups in order); lse = m + log(s), -inf for a row
+// whose entries are all -inf. Called by one lane.
+__device__ inline float lse_of_groups(const float2* g) {
+    float m = kNegInf, s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) lse_merge(m, s, g[i].x, g[i].y);
+    return (m == kNegInf) ? kNegInf : m + logf(s);
+}
+
+// The selected token's logit (a5), loaded long before its logprob is
+// written; an id outside [0, V) gives NaN and the index error bit.
+template <bool BF16>
+__device__ inline float load_selected(const uint8_t* rowp, int64_t V, int32_t sel_id) {
+    if (sel_id < 0 || (int64_t)sel_id >= V) return __builtin_nanf("");
+    return BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[sel_id])
+                : reinterpret_cast<const float*>(rowp)[sel_id];
+}
+__device__ inline void write_selected(int64_t V, int32_t sel_id, float xsel, float lse, float* out,
+                                      int32_t* err) {
+    if (sel_id >= 0 && (int64_t)sel_id < V) {
+        *out = xsel - lse;
+    } else {
+        *out = __builtin_nanf("");
+        if (err) atomicOr(err, LMH_DEVERR_INDEX);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split path, second kernel: one workgroup of 256 threads per row reads the
+// row's item partials and block keys from the workspace.
+// ---------------------------------------------------------------------------
+template <bool BF16, int KPT>
+__global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__ logits, int64_t ld,
+                                                     int64_t V, int32_t nb, int32_t kld, int32_t splits,
+                                                     const float2* __restrict__ part,
+                                                     const void* __restrict__ keys,
+                                                     const int32_t* __restrict__ sel, int32_t K,
+                                                     float* __restrict__ lse_out,
+                                                     float* __restrict__ sel_out,
+                                                     int32_t* __restrict__ topk_ids,
+                                                     float* __restrict__ topk_lp,
+                                                     int32_t* __restrict__ err, int32_t cap) {
+    extern __shared__ uint64_t smem[];   // [cap] candidates, [K] narrowed list
+    __shared__ RowShared<kThreads> sh;
+    __shared__ float2 sgrp[kGroups];
+    constexpr size_t ESZ = BF16 ? 2 : 4;
+    constexpr int MAXBLK = kMaxCandidates / kBlock;
+
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
+    if (tid < MAXBLK) sh.blk[tid] = -1;   // unfilled slots are skipped, never dereferenced
+    if (tid == 0) {
+        sh.nlist = 0;
+        sh.nblk = 0;
+    }
+
+    // this thread's block keys, blocks [b0, b0 + KPT); 0 past nb
+    const int b0 = tid * KPT;
+    uint32_t kr[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kr[j] = 0u;
+    if (K > 0 && K <= nb && b0 < nb) {
+        if (BF16) {
+            const uint16_t* kp = reinterpret_cast<const uint16_t*>(keys) + row * kld + b0;
+            if (KPT == 4) {
+                const uint2 q = *reinterpret_cast<const uint2*>(kp);
+                const uint32_t wq[2] = {q.x, q.y};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kr[j] = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
+            } else {
+#pragma unroll
+                for (int c = 0; c < KPT / 8; ++c) {
+                    const u32x4 q = reinterpret_cast<const u32x4*>(kp)[c];
+                    const uint32_t wq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        kr[c * 8 + j] = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
+                }
+            }
+        } else {
+            const uint32_t* kp = reinterpret_cast<const uint32_t*>(keys) + row * kld + b0;
+#pragma unroll
+            for (int c = 0; c < KPT / 4; ++c) {
+                const u32x4 q = reinterpret_cast<const u32x4*>(kp)[c];
+                kr[c * 4 + 0] = q.x;
+                kr[c * 4 + 1] = q.y;
+                kr[c * 4 + 2] = q.z;
+                kr[c * 4 + 3] = q.w;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (b0 + j >= nb) kr[j] = 0u;
+    }
+
+    // the selected token's id, issued now (thread 64: off the lse wave)
+    const bool sel_thread = sel != nullptr && sel_out != nullptr && tid == 64;
+    int32_t sel_id = 0;
+    if (sel_thread) sel_id = sel[row];
+
+    // logsumexp: lanes 0..15 of wave 0 merge their groups' partials, lane 0
+    // merges the groups
+    if (tid < kGroups) {
+        float m = kNegInf, sm = 0.f;
+        for (int i = tid; i < splits; i += kGroups) {
+            const float2 pp = part[row * splits + i];
+            lse_merge(m, sm, pp.x, pp.y);
+        }
+        sgrp[tid] = make_float2(m, sm);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (tid == 0) {
+        const float l = lse_of_groups(sgrp);
+        sh.lse = l;
+        lse_out[row] = l;
+    }
+    __syncthreads();
+    const float lse = sh.lse;
+    // the selected logit: loaded now, written after the top-K
+    const float xsel = sel_thread ? load_selected<BF16>(rowp, V, sel_id) : 0.f;
+    if (K > 0)
+        row_topk<BF16, KPT, kThreads>(rowp, row, V, nb, K, kr, lse, smem, smem + cap, cap, sh, topk_ids,
+                                      topk_lp);
+    if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
+}
+
+// ---------------------------------------------------------------------------
+// One-workgroup-per-row path (rows that fill the CUs evenly): 16 waves stream
+// the row's items (wave w: items w, w + 16, ...; the next item's loads are in
+// flight while the current one is reduced), keep the block keys in LDS and
+// their merge group's running partial in registers, then the workgroup merges
+// the 16 groups and selects the top-K from the LDS keys. One launch, and no
+// workspace round trip between the streaming pass and the selection.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = kGroups * 64;
+template <bool BF16> struct KeyType { using type = uint32_t; };
+template <> struct KeyType<true> { using type = uint16_t; };
+
+template <bool BF16, int KPT, bool KEYS>
+__global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __restrict__ logits, int64_t ld,
+                                                           int64_t V, int32_t nb, int32_t P,
+                                                           const int32_t* __restrict__ sel, int32_t K,
+                                                           float* __restrict__ lse_out,
+                                                           float* __restrict__ sel_out,
+                                                           int32_t* __restrict__ topk_ids,
+                                                           float* __restrict__ topk_lp,
+                                                           int32_t* __restrict__ err, int32_t cap) {
+    using I = Stage1Item<BF16>;
+    using key_t = typename KeyType<BF16>::type;
+    extern __shared__ uint64_t smem[];   // [KPT*256] keys, then [cap] candidates, [K] narrowed list
+    __shared__ RowShared<kThreads> sh;
+    __shared__ float2 sgrp[kGroups];
+    constexpr size_t ESZ = BF16 ? 2 : 4;
+    constexpr int MAXBLK = kMaxCandidates / kBlock;
+    key_t* skeys = reinterpret_cast<key_t*>(smem);
+    uint64_t* cand = smem + (KPT * kThreads * sizeof(key_t) + 7) / 8;
+
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
+    if (tid < MAXBLK) sh.blk[tid] = -1;
+    if (tid == 0) {
+        sh.nlist = 0;
+        sh.nblk = 0;
+    }
+    // key slots past nb read as 0
+    if (KEYS)
+        for (int b = nb + tid; b < KPT * kThreads; b += kRowThreads) skeys[b] = 0;
+
+    // the selected id and logit, issued first (thread 64)
+    const bool sel_thread = sel != nullptr && sel_out != nullptr && tid == 64;
+    int32_t sel_id = 0;
+    float xsel = 0.f;
+    if (sel_thread) {
+        sel_id = sel[row];
+        xsel = load_selected<BF16>(rowp, V, sel_id);
+    }
+
+    float gm = kNegInf, gs = 0.f;   // this wave's merge group
+    auto finish_item = [&](int32_t seg, float M, float S, uint32_t kb) {
+        if (KEYS) {
+            const int32_t blk = seg * (kSeg / kBlock) + lane;
+            if (blk < nb) skeys[blk] = BF16 ? (key_t)(kb >> 16) : (key_t)kb;
+        }
+        lse_merge(gm, gs, M, S);
+    };
+    auto reduce_item = [&](const u32x4 (&buf)[I::VPL], int32_t seg) {
+        float M, S;
+        uint32_t kb = 0;
+        stage1_item<BF16, KEYS>(buf, lane, M, S, kb);
+        finish_item(seg, M, S, kb);
+    };
+    // The partial last item (index Pf, when V is not a multiple of kSeg) is
+    // the last of its merge group but is reduced first, so that its loads are
+    // not exposed at the end; its partial is merged last.
+    const int32_t Pf = (int32_t)(V / kSeg);
+    const bool has_tail = Pf < P && wave == Pf % kGroups;   // wave-uniform
+    float tM = kNegInf, tS = 0.f;
+    auto reduce_tail = [&]() {
+        u32x4 buf[I::VPL];
+        stage1_load<BF16>(rowp, V, Pf, lane, buf);
+        uint32_t kb = 0;
+        stage1_item<BF16, KEYS>(buf, lane, tM, tS, kb);
+        if (KEYS) {
+            const int32_t blk = Pf * (kSeg / kBlock) + lane;
+            if (blk < nb) skeys[blk] = BF16 ? (key_t)(kb >> 16) : (key_t)kb;
+        }
+    };
+    // full items; bf16 items are double-buffered (the next one's loads are in
+    // flight while this one is reduced), fp32 items (twice the registers) not
+    int32_t seg = wave;
+    if (BF16) {
+        u32x4 nxt[I::VPL];
+        if (has_tail) reduce_tail();
+        if (seg < Pf) stage1_load_full<BF16>(rowp, seg, lane, nxt);
+        for (; seg < Pf; seg += kGroups) {
+            u32x4 buf[I::VPL];
+#pragma unroll
+            for (int j = 0; j < I::VPL; ++j) buf[j] = nxt[j];
+            // the next item, or this one again on the last pass (an L2 hit)
+            const int32_t nseg = seg + kGroups < Pf ? seg + kGroups : seg;
+            stage1_load_full<BF16>(rowp, nseg, lane, nxt);
+            reduce_item(buf, seg);
+        }
+    } else {
+        if (has_tail) reduce_tail();
+        for (; seg < Pf; seg += kGroups) {
+            u32x4 buf[I::VPL];
+            stage1_load_full<BF16>(rowp, seg, lane, buf);
+            __builtin_amdgcn_sched_barrier(0);
+            reduce_item(buf, seg);
+        }
+    }
+    if (has_tail) lse_merge(gm, gs, tM, tS);
+    if (lane == 0) sgrp[wave] = make_float2(gm, gs);
+    __syncthreads();
+    if (tid == 0) {
+        const float l = lse_of_groups(sgrp);
+        sh.lse = l;
+        lse_out[row] = l;
+    }
+    __syncthreads();
+    const float lse = sh.lse;
+    if (!KEYS) {
+        if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
+        return;
+    }
+
+    // the selection runs on waves 0..3 (the same 256-thread code as the split
+    // path); the other waves end here (a barrier waits on surviving waves only)
+    if (wave >= kThreads / 64) {
+        if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
+        return;
+    }
+    uint32_t kr[KPT];
+    if (K <= nb) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            kr[j] = BF16 ? ((uint32_t)skeys[tid * KPT + j] << 16) : (uint32_t)skeys[tid * KPT + j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) kr[j] = 0u;
+    }
+    row_topk<BF16, KPT, kThreads>(rowp, row, V, nb, K, kr, lse, cand, cand + cap, cap, sh, topk_ids,
+                                  topk_lp);
+    if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
 }
 
 }  // namespace
@@ -888,6 +1099,73 @@ hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStr
     }
     return a.bf16 ? launch_stage2_dt<true>(p, a, s, part, keys, cap, lds)
                   : launch_stage2_dt<false>(p, a, s, part, keys, cap, lds);
+}
+
+namespace {
+
+// Compute units of the current device (cached per device id).
+int cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <bool BF16, int KPT, bool KEYS>
+hipError_t launch_row_kpt(const ReducePlan& p, const ReduceArgs& a, hipStream_t s, int32_t cap, size_t lds) {
+    const void* fn = (const void*)k_rowreduce<BF16, KPT, KEYS>;
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_rowreduce<BF16, KPT, KEYS>), dim3((unsigned)p.rows), dim3(kRowThreads), lds, s,
+                       static_cast<const uint8_t*>(a.logits), a.ld, p.vocab, p.nb, p.splits, a.sel, p.k, a.lse,
+                       a.sel_lp, a.topk_ids, a.topk_lp, a.err, cap);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool reduce_row_path(const ReducePlan& p) {
+    const int ncu = cu_count();
+    if (ncu <= 0 || p.rows < ncu) return false;
+    if (p.k > 0 && p.kpt > 16) return false;   // more than 4096 blocks: the split path
+    // one workgroup per CU at a time: the rows must fill the CUs evenly
+    const int64_t rounds = (p.rows + ncu - 1) / ncu;
+    return p.rows * 4 >= rounds * ncu * 3;
+}
+
+hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s) {
+    if (p.rows == 0) return hipSuccess;
+    if (!reduce_row_path(p)) {
+        const hipError_t e = launch_reduce_stage1(p, a, s);
+        if (e != hipSuccess) return e;
+        return launch_reduce_stage2(p, a, s);
+    }
+    int32_t cap = 0;
+    size_t lds = 0;
+    if (p.k > 0) {
+        const int32_t nsel = p.k < p.nb ? p.k : p.nb;
+        cap = nsel * kBlock;
+        const size_t kbytes = (size_t)p.kpt * kThreads * (a.bf16 ? 2 : 4);
+        lds = kbytes + ((size_t)cap + (size_t)p.k) * sizeof(uint64_t);
+    }
+    if (p.k == 0)
+        return a.bf16 ? launch_row_kpt<true, 4, false>(p, a, s, cap, lds)
+                      : launch_row_kpt<false, 4, false>(p, a, s, cap, lds);
+    switch (p.kpt) {
+        case 4: return a.bf16 ? launch_row_kpt<true, 4, true>(p, a, s, cap, lds)
+                              : launch_row_kpt<false, 4, true>(p, a, s, cap, lds);
+        case 8: return a.bf16 ? launch_row_kpt<true, 8, true>(p, a, s, cap, lds)
+                              : launch_row_kpt<false, 8, true>(p, a, s, cap, lds);
+        default: return a.bf16 ? launch_row_kpt<true, 16, true>(p, a, s, cap, lds)
+                               : launch_row_kpt<false, 16, true>(p, a, s, cap, lds);
+    }
 }
 
 }  // namespace lmh
