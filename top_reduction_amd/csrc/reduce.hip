@@ -2,19 +2,23 @@
 // logits matrix, on gfx950 (MTPLX PR #532, Change; openinfer issue #719,
 // Suggested direction).
 //
-// Stage 1 (one coalesced read of every logit): a 1-D grid of rows x splits
-// workgroups; each streams a contiguous, block-aligned slice of one row with
-// 16-byte loads and produces
-//   * an online (max, sum of exp(x - max)) partial in fp32, and
-//   * the maximum of every 64-logit block it covers, stored as a monotone key
-//     (16-bit for bf16 rows, 32-bit for fp32 rows).
-// Stage 2 (one workgroup per row): combines the partials in a fixed order into
-// the fp32 logsumexp, writes the selected logprob, keeps the min(K, nb) blocks
-// with the largest maxima (equal maxima: lower block index first), gathers the
-// entries of those blocks that are not below the K-th kept maximum, and ranks
-// them by (value descending, id ascending) in LDS. The candidate set provably
+// Every logit is read once, with 16-byte loads, in 4096-logit items. An item
+// yields a (max, sum of exp(x - max)) partial in fp32 and the maximum of each
+// of its 64-logit blocks, as a monotone key (16-bit for bf16 rows, 32-bit for
+// fp32 rows). The partials of a row are merged in one canonical order into
+// the fp32 logsumexp; the min(K, nb) blocks with the largest maxima (equal
+// maxima: lower block index first) are kept, the entries of those blocks
+// that are not below the K-th kept maximum are gathered, and they are ranked
+// by (value descending, id ascending) in LDS. The candidate set provably
 // contains the exact top-K: a top-K entry outside the kept blocks, or below
 // the K-th kept maximum, would have K kept block maxima ahead of it.
+//
+// Two paths, with bitwise-identical results:
+//   * k_rowreduce (rows fill the CUs evenly): one workgroup per row streams
+//     the row, keeps the block keys in LDS and selects in the same launch;
+//   * k_stage1 + k_stage2 (otherwise): a streaming launch over all rows
+//     writes partials and keys to the workspace, then one workgroup per row
+//     finishes it.
 #include "lmh_internal.h"
 
 namespace lmh {
