@@ -491,7 +491,8 @@ struct RowShared {
 
 template <bool BF16, int KPT, int NT>
 __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t V, int32_t nb, int32_t K,
-                         const uint32_t (&kr)[KPT], float lse, uint64_t* cand, uint64_t* list2, int32_t cap,
+                         const uint32_t (&kr)[KPT], const float* lse_p, uint64_t* cand, uint64_t* list2,
+                         int32_t cap,
                          RowShared<NT>& sh, int32_t* __restrict__ topk_ids, float* __restrict__ topk_lp) {
     constexpr size_t ESZ = BF16 ? 2 : 4;
     constexpr int EPV = BF16 ? 8 : 4;                 // elements per 16-byte vector
@@ -714,6 +715,7 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
     }
     // G lanes (a quad, a pair or one lane) count one candidate's predecessors
     // over interleaved slices of the list, then sum with DPP inside the quad
+    const float lse = *lse_p;                           // written before the first barrier above
     const int G = nlist <= NT / 4 ? 4 : (nlist <= NT / 2 ? 2 : 1);
     const int q = tid & (G - 1);
     for (int i0 = 0; i0 < nlist * G; i0 += NT) {
@@ -866,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     // the selected logit: loaded now, written after the top-K
     const float xsel = sel_thread ? load_selected<BF16>(rowp, V, sel_id) : 0.f;
     if (K > 0)
-        row_topk<BF16, KPT, kThreads>(rowp, row, V, nb, K, kr, lse, smem, smem + cap, cap, sh, topk_ids,
+        row_topk<BF16, KPT, kThreads>(rowp, row, V, nb, K, kr, &sh.lse, smem, smem + cap, cap, sh, topk_ids,
                                       topk_lp);
     if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
 }
@@ -880,6 +882,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
 // workspace round trip between the streaming pass and the selection.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = kGroups * 64;
+constexpr int kRowMaxItems = 64;   // items per row on this path (V <= 64 * kSeg)
 template <bool BF16> struct KeyType { using type = uint32_t; };
 template <> struct KeyType<true> { using type = uint16_t; };
 
@@ -897,6 +900,9 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     extern __shared__ uint64_t smem[];   // [KPT*256] keys, then [cap] candidates, [K] narrowed list
     __shared__ RowShared<kThreads> sh;
     __shared__ float2 sgrp[kGroups];
+    __shared__ float2 sitem[kRowMaxItems];
+    __shared__ int32_t s_next, s_sel;
+    __shared__ float s_xsel;
     constexpr size_t ESZ = BF16 ? 2 : 4;
     constexpr int MAXBLK = kMaxCandidates / kBlock;
     key_t* skeys = reinterpret_cast<key_t*>(smem);
@@ -911,96 +917,105 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     if (tid == 0) {
         sh.nlist = 0;
         sh.nblk = 0;
+        s_next = kGroups;
     }
+    __syncthreads();   // s_next before the first hand-out
     // key slots past nb read as 0
     if (KEYS)
         for (int b = nb + tid; b < KPT * kThreads; b += kRowThreads) skeys[b] = 0;
 
-    // the selected id and logit, issued first (thread 64)
-    const bool sel_thread = sel != nullptr && sel_out != nullptr && tid == 64;
+    // the selected id and logit, issued first by the last wave (its item
+    // count is never above any other wave's, so its two dependent loads do
+    // not hold up the workgroup)
+    const bool sel_thread = sel != nullptr && sel_out != nullptr && tid == kRowThreads - 64;
     int32_t sel_id = 0;
     float xsel = 0.f;
     if (sel_thread) {
         sel_id = sel[row];
+        s_sel = sel_id;
         xsel = load_selected<BF16>(rowp, V, sel_id);
     }
 
-    float gm = kNegInf, gs = 0.f;   // this wave's merge group
-    auto finish_item = [&](int32_t seg, float M, float S, uint32_t kb) {
-        if (KEYS) {
-            const int32_t blk = seg * (kSeg / kBlock) + lane;
-            if (blk < nb) skeys[blk] = BF16 ? (key_t)(kb >> 16) : (key_t)kb;
-        }
-        lse_merge(gm, gs, M, S);
-    };
+    // Items are handed out dynamically (wave w starts with item w, then takes
+    // the next index from an LDS counter), so the waves finish together;
+    // each item's partial goes to LDS and the row's partials are merged in
+    // the canonical order afterwards.
     auto reduce_item = [&](const u32x4 (&buf)[I::VPL], int32_t seg) {
         float M, S;
         uint32_t kb = 0;
         stage1_item<BF16, KEYS>(buf, lane, M, S, kb);
-        finish_item(seg, M, S, kb);
-    };
-    // The partial last item (index Pf, when V is not a multiple of kSeg) is
-    // the last of its merge group but is reduced first, so that its loads are
-    // not exposed at the end; its partial is merged last.
-    const int32_t Pf = (int32_t)(V / kSeg);
-    const bool has_tail = Pf < P && wave == Pf % kGroups;   // wave-uniform
-    float tM = kNegInf, tS = 0.f;
-    auto reduce_tail = [&]() {
-        u32x4 buf[I::VPL];
-        stage1_load<BF16>(rowp, V, Pf, lane, buf);
-        uint32_t kb = 0;
-        stage1_item<BF16, KEYS>(buf, lane, tM, tS, kb);
         if (KEYS) {
-            const int32_t blk = Pf * (kSeg / kBlock) + lane;
+            const int32_t blk = seg * (kSeg / kBlock) + lane;
             if (blk < nb) skeys[blk] = BF16 ? (key_t)(kb >> 16) : (key_t)kb;
         }
+        if (lane == 0) sitem[seg] = make_float2(M, S);
     };
-    // full items; bf16 items are double-buffered (the next one's loads are in
-    // flight while this one is reduced), fp32 items (twice the registers) not
-    int32_t seg = wave;
+    auto next_item = [&]() -> int32_t {
+        int32_t v = 0;
+        if (lane == 0) v = atomicAdd(&s_next, 1);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
+    // The partial last item (index Pf, when V is not a multiple of kSeg) goes
+    // first to the last wave, so that its loads are not exposed at the end.
+    const int32_t Pf = (int32_t)(V / kSeg);
+    if (Pf < P && wave == kGroups - 1) {
+        u32x4 buf[I::VPL];
+        stage1_load<BF16>(rowp, V, Pf, lane, buf);
+        reduce_item(buf, Pf);
+    }
+    int32_t cur = wave < Pf ? wave : Pf;
     if (BF16) {
+        // double-buffered: the next item's loads are issued before the current
+        // one is reduced (on the last pass the current item is loaded again,
+        // an L2 hit, which keeps the loop free of load branches)
         u32x4 nxt[I::VPL];
-        if (has_tail) reduce_tail();
-        if (seg < Pf) stage1_load_full<BF16>(rowp, seg, lane, nxt);
-        for (; seg < Pf; seg += kGroups) {
+        if (cur < Pf) stage1_load_full<BF16>(rowp, cur, lane, nxt);
+        while (cur < Pf) {
             u32x4 buf[I::VPL];
 #pragma unroll
             for (int j = 0; j < I::VPL; ++j) buf[j] = nxt[j];
-            // the next item, or this one again on the last pass (an L2 hit)
-            const int32_t nseg = seg + kGroups < Pf ? seg + kGroups : seg;
-            stage1_load_full<BF16>(rowp, nseg, lane, nxt);
-            reduce_item(buf, seg);
+            const int32_t nx = next_item();
+            stage1_load_full<BF16>(rowp, nx < Pf ? nx : cur, lane, nxt);
+            reduce_item(buf, cur);
+            cur = nx;
         }
     } else {
-        if (has_tail) reduce_tail();
-        for (; seg < Pf; seg += kGroups) {
+        // fp32 items (twice the registers) one at a time
+        while (cur < Pf) {
             u32x4 buf[I::VPL];
-            stage1_load_full<BF16>(rowp, seg, lane, buf);
+            stage1_load_full<BF16>(rowp, cur, lane, buf);
             __builtin_amdgcn_sched_barrier(0);
-            reduce_item(buf, seg);
+            reduce_item(buf, cur);
+            cur = next_item();
         }
     }
-    if (has_tail) lse_merge(gm, gs, tM, tS);
-    if (lane == 0) sgrp[wave] = make_float2(gm, gs);
+    if (sel_thread) s_xsel = xsel;
     __syncthreads();
-    if (tid == 0) {
-        const float l = lse_of_groups(sgrp);
-        sh.lse = l;
-        lse_out[row] = l;
+
+    // lse: lanes 0..15 of wave 0 merge their groups, lane 0 the groups (the
+    // split path's arithmetic); the selection below reads it after its first
+    // barrier
+    if (wave == 0) {
+        if (lane < kGroups) {
+            float m = kNegInf, sm = 0.f;
+            for (int32_t i = lane; i < P; i += kGroups) lse_merge(m, sm, sitem[i].x, sitem[i].y);
+            sgrp[lane] = make_float2(m, sm);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane == 0) {
+            const float l = lse_of_groups(sgrp);
+            sh.lse = l;
+            lse_out[row] = l;
+            if (sel != nullptr && sel_out != nullptr) write_selected(V, s_sel, s_xsel, l, sel_out + row, err);
+        }
     }
-    __syncthreads();
-    const float lse = sh.lse;
-    if (!KEYS) {
-        if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
-        return;
-    }
+    if (!KEYS) return;
 
     // the selection runs on waves 0..3 (the same 256-thread code as the split
     // path); the other waves end here (a barrier waits on surviving waves only)
-    if (wave >= kThreads / 64) {
-        if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
-        return;
-    }
+    if (wave >= kThreads / 64) return;
     uint32_t kr[KPT];
     if (K <= nb) {
 #pragma unroll
@@ -1010,9 +1025,8 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
 #pragma unroll
         for (int j = 0; j < KPT; ++j) kr[j] = 0u;
     }
-    row_topk<BF16, KPT, kThreads>(rowp, row, V, nb, K, kr, lse, cand, cand + cap, cap, sh, topk_ids,
+    row_topk<BF16, KPT, kThreads>(rowp, row, V, nb, K, kr, &sh.lse, cand, cand + cap, cap, sh, topk_ids,
                                   topk_lp);
-    if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
 }
 
 }  // namespace
@@ -1138,6 +1152,7 @@ hipError_t launch_row_kpt(const ReducePlan& p, const ReduceArgs& a, hipStream_t 
 bool reduce_row_path(const ReducePlan& p) {
     const int ncu = cu_count();
     if (ncu <= 0 || p.rows < ncu) return false;
+    if (p.splits > kRowMaxItems) return false;   // vocab above 64 * 4096: the split path
     if (p.k > 0 && p.kpt > 16) return false;   // more than 4096 blocks: the split path
     // one workgroup per CU at a time: the rows must fill the CUs evenly
     const int64_t rounds = (p.rows + ncu - 1) / ncu;
