@@ -15,7 +15,7 @@
 //           W and reads it once, straight from HBM into MFMA B fragments,
 //           a full k-chunk ahead; the gathered hidden rows (small, L2
 //           resident) are staged through LDS and shared by the 4 waves.
-//   tiled   (any R): 256 x 128 output tiles, 4 waves of 128 x 64; both
+//   tiled   (any R): 256 x 256 output tiles, 8 waves of 128 x 64; both
 //           operands pass through double-buffered LDS fed 3 k-steps ahead;
 //           workgroups are mapped so that each XCD walks the row tiles of one
 //           W slab together.
@@ -231,14 +231,14 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: a 256 x 128 output tile per workgroup, one 128 x 64 quarter per
-// wave (8 x 4 MFMA tiles). k advances in stages of 32 (one MFMA k-step).
-// Each stage's A (gathered hidden rows, 256 x 64 B) and B (W rows, 128 x 64 B)
-// slices pass through registers into one of two LDS buffers: loads of stage
+// Tiled kernel: a 256 x 256 output tile per workgroup of 8 waves, one 128 x 64
+// eighth per wave (8 x 4 MFMA tiles). k advances in stages of 32 (one MFMA
+// k-step). Each stage's A (gathered hidden rows) and B (W rows) slices, 256 x
+// 64 B each, pass through registers into one of two LDS buffers: loads of stage
 // s+3 are issued while stage s is multiplied (three register sets in
 // flight) and stage s+1 is written to LDS at the end of stage s; the A
-// fragments are read one 16-row group ahead of their MFMAs. Two workgroups
-// share a CU. The 16-byte chunks of a
+// fragments are read one 16-row group ahead of their MFMAs. One workgroup
+// (two waves per SIMD) per CU. The 16-byte chunks of a
 // 64-byte LDS row are XOR-swizzled with bits 1..2 of the row, so the fragment
 // reads (16 rows, one chunk each) and the staging writes (consecutive chunks)
 // are free of bank conflicts. Loads are branch-free: rows past R or with no
@@ -246,19 +246,20 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
 // V read row V-1, and the chunks past H (the stage count is rounded up to a
 // multiple of 3) read k = 0 and are zeroed on their way into LDS.
 // ---------------------------------------------------------------------------
-constexpr int kTileM = 256, kTileN = 128, kTileK = 32;
+constexpr int kTileM = 256, kTileN = 256, kTileK = 32;
+constexpr int kTileThreads = 512;
 constexpr int kWaveN = 64;                                     // columns per wave
-constexpr int kTileLA = kTileM * 4 / kThreads;                 // A chunks per thread per stage
-constexpr int kTileLB = kTileN * 4 / kThreads;                 // B chunks per thread per stage
+constexpr int kTileLA = kTileM * 4 / kTileThreads;             // A chunks per thread per stage
+constexpr int kTileLB = kTileN * 4 / kTileThreads;             // B chunks per thread per stage
 constexpr int kTileStage = (kTileM + kTileN) * kTileK * 2;     // bytes per LDS stage
-constexpr int kTileLds = 2 * kTileStage + kTileM * 4;          // 2 stages + row sources
+constexpr int kTileLds = 72 * 1024 + kTileM * 4;               // 2 stages / epilogue staging + row sources
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
     constexpr int NF = kWaveN / 16;                 // B fragments (16-column groups) per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    int32_t* sIdx = reinterpret_cast<int32_t*>(lds + 2 * kTileStage);
+    int32_t* sIdx = reinterpret_cast<int32_t*>(lds + 72 * 1024);
 
     // XCD-aware order: hardware places workgroup i on XCD i % 8; give each
     // XCD a contiguous run of logical tiles, row tiles fastest, so the row
@@ -273,31 +274,31 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = (wave >> 1) * 128;
-    const int wn = (wave & 1) * kWaveN;
+    const int wm = (wave >> 2) * 128;
+    const int wn = (wave & 3) * kWaveN;
     const int32_t m0 = mt * kTileM;
     const int64_t n0 = (int64_t)nt * kTileN;
 
-    {
+    if (tid < kTileM) {
         const int32_t r = m0 + tid;
         sIdx[tid] = (r < p.R) ? row_source(p.row0 + r, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
     }
     __syncthreads();
 
-    // this thread's staging chunks: rows tid/4 + 64j, chunk tid%4
+    // this thread's staging chunks: rows tid/4 + 128j, chunk tid%4
     const int c = tid & 3;
     int64_t ga[kTileLA], gb[kTileLB];               // element offsets of the chunks at k = 0
     uint32_t wofs[kTileLA];                         // LDS byte offsets within a stage's A slice
 #pragma unroll
     for (int j = 0; j < kTileLA; ++j) {
-        const int row = (tid >> 2) + 64 * j;
+        const int row = (tid >> 2) + 128 * j;
         const int32_t t = sIdx[row];
         ga[j] = (int64_t)(t < 0 ? 0 : t) * p.hld + c * 8;
         wofs[j] = (uint32_t)(row * 64 + ((c ^ ((row >> 1) & 3)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < kTileLB; ++j) {
-        const int row = (tid >> 2) + 64 * j;
+        const int row = (tid >> 2) + 128 * j;
         const int64_t n = n0 + row < p.V ? n0 + row : p.V - 1;
         gb[j] = n * p.wld + c * 8;
     }
@@ -541,7 +542,7 @@ hipError_t launch_tiled(const HeadParams& p, int32_t mtiles, int32_t ntiles, hip
     if (e != hipSuccess) return e;
     const int64_t total = (int64_t)mtiles * ntiles;
     const dim3 grid((unsigned)(((total + 7) / 8) * 8));
-    hipLaunchKernelGGL((k_head_tiled<OUT_BF16>), grid, dim3(kThreads), kTileLds, s, p, mtiles, ntiles);
+    hipLaunchKernelGGL((k_head_tiled<OUT_BF16>), grid, dim3(kTileThreads), kTileLds, s, p, mtiles, ntiles);
     return hipGetLastError();
 }
 
