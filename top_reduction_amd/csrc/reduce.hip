@@ -28,7 +28,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kThreads = 256;
 constexpr int kHistBins = 256;     // key values resolved by one stage-2 histogram
-constexpr int kSeg = 4096;          // logits per stage-1 work item (one wave)
+constexpr int kSeg = 4096;          // logits per streaming work item (one wave)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -120,17 +120,6 @@ __device__ inline float key_value(uint32_t k) {
 // arithmetic, so each row's results are bitwise independent of the batch
 // around it and of the path that served it.
 // ---------------------------------------------------------------------------
-// One (max, sum-exp) merge step with the partner chosen by a DPP control;
-// lanes without a partner merge the identity (-inf, 0).
-#define LMH_LSE_DPP_STEP(m, s, ctrl, rmask)                                                          \
-    do {                                                                                             \
-        const float m2_ = __int_as_float(                                                            \
-            __builtin_amdgcn_update_dpp((int)0xFF800000, __float_as_int(m), ctrl, rmask, 0xF, false)); \
-        const float s2_ = __int_as_float(                                                            \
-            __builtin_amdgcn_update_dpp(0, __float_as_int(s), ctrl, rmask, 0xF, false));             \
-        lse_merge(m, s, m2_, s2_);                                                                   \
-    } while (0)
-
 // Sum over the wave by row shifts, then row broadcasts; lane 63 ends with the
 // total (a fixed order).
 __device__ inline float wave_sum_to_63(float s) {
@@ -875,11 +864,12 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
 
 // ---------------------------------------------------------------------------
 // One-workgroup-per-row path (rows that fill the CUs evenly): 16 waves stream
-// the row's items (wave w: items w, w + 16, ...; the next item's loads are in
-// flight while the current one is reduced), keep the block keys in LDS and
-// their merge group's running partial in registers, then the workgroup merges
-// the 16 groups and selects the top-K from the LDS keys. One launch, and no
-// workspace round trip between the streaming pass and the selection.
+// the row's items, handed out from an LDS counter (bf16 items double-
+// buffered: the next item's loads are in flight while the current one is
+// reduced), writing each item's partial and block keys to LDS; after one
+// barrier wave 0 merges the partials in the canonical order while waves 1-3
+// start the top-K selection on the LDS keys (waves 4-15 end there). One
+// launch, and no workspace round trip between the stream and the selection.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = kGroups * 64;
 constexpr int kRowMaxItems = 64;   // items per row on this path (V <= 64 * kSeg)
