@@ -8,15 +8,16 @@ Two independent implementations live here:
 
 * ``liboracle.so`` (``oracle.c``): the plain definition in f64 -- the row
   formula, a naive triple-loop head, a max pass plus an f64 exp-sum pass for
-  the logsumexp, and a full sort for the top-K (value descending, exact ties
-  by ascending token id). Thin numpy wrappers below.
+  the logsumexp, a full sort for the top-K (value descending, exact ties
+  by ascending token id), and the exact dequantisation of affine
+  group-quantised head weights. Thin numpy wrappers below.
 * ``ref_numpy``: the same quantities through library routines
   (``numpy`` float64 matmul, ``scipy.special.logsumexp``, ``numpy.lexsort``),
   used to cross-check the C oracle on small inputs.
 
 Parity unpinned: nothing. Every function is pinned by tests against closed
-forms, library routines, exhaustive enumeration or integer arithmetic (see
-the oracle tests).
+forms, library routines, exhaustive enumeration, integer arithmetic or
+hand-worked fixtures (see the oracle tests).
 """
 from __future__ import annotations
 
@@ -57,6 +58,8 @@ def load(path: str = _LIB_PATH):
     lib.orc_rows.restype = ctypes.c_int
     lib.orc_head.argtypes = [p, ctypes.c_int, i64, i64, i64, p, ctypes.c_int, i64, i64, p, i32, p]
     lib.orc_head.restype = None
+    lib.orc_dequant.argtypes = [p, i64, p, p, i64, ctypes.c_int, ctypes.c_int, i64, i64, p]
+    lib.orc_dequant.restype = None
     lib.orc_reduce.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p]
     lib.orc_reduce.restype = None
     lib.orc_prefilter_check.argtypes = [p, ctypes.c_int, i64, i64, i64, i32, i32, i32, p]
@@ -118,6 +121,25 @@ def head(hidden: np.ndarray, weight: np.ndarray, idx, lib=None) -> np.ndarray:
     lib.orc_head(_ptr(hidden), _dtype_code(hidden), T, H, H, _ptr(weight), _dtype_code(weight),
                  V, H, _ptr(idx), idx.shape[0], _ptr(Z))
     return Z
+
+
+def dequant(q: np.ndarray, scales: np.ndarray, biases: np.ndarray, bits: int, group: int,
+            hidden: int, lib=None) -> np.ndarray:
+    """Exact f64 weights [V][hidden] of MLX-style affine group quantisation:
+    W[v][k] = scale[v][k // group] * q(v, k) + bias[v][k // group], with q
+    unsigned `bits`-bit (4 or 8) integers packed little-endian into the uint32
+    words of q [V][words]; scales and biases are raw-bf16 uint16 [V][groups]."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    biases = np.ascontiguousarray(biases, dtype=np.uint16)
+    V, words = q.shape
+    assert words * 32 >= hidden * bits and scales.shape == biases.shape and scales.shape[0] == V
+    assert scales.shape[1] * group >= hidden
+    W = np.empty((V, hidden), dtype=np.float64)
+    lib.orc_dequant(_ptr(q), words, _ptr(scales), _ptr(biases), scales.shape[1], bits, group, V, hidden,
+                    _ptr(W))
+    return W
 
 
 def reduce(logits: np.ndarray, selected=None, k: int = 0, lib=None):

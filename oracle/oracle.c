@@ -23,6 +23,9 @@
  *     prefilter keeps the K blocks with the largest maxima.
  *   - openinfer issue #719, Description: the host routine makes a
  *     full-vocabulary max pass, an f64 exp-sum pass and a top-k pass.
+ *   - mlxcel PR #1969, description: the measured models are 4-bit; the
+ *     quantised head weights are read as MLX-style affine groups
+ *     (orc_dequant), then used by the same f64 head.
  *
  * The reduction here is the plain definition (max, f64 exp-sum, full sort),
  * not the prefilter: the prefilter is an acceleration that must reach the
@@ -133,6 +136,33 @@ void orc_head(const void* hidden, int hdt, int64_t num_tokens, int64_t H, int64_
             for (int64_t k = 0; k < H; ++k)
                 acc += widen(hidden, hdt, t * hld + k) * widen(W, wdt, v * wld + k);
             Z[r * V + v] = acc;
+        }
+    }
+}
+
+/*
+ * Quantised head weights (the pages' measured models are 4-bit MLX models:
+ * mlxcel PR #1969, description). Reading taken for the format: MLX-style
+ * affine groups -- for token v and hidden index k, with g = k / group,
+ *     W[v][k] = scale[v][g] * q(v, k) + bias[v][g],
+ * q(v, k) an unsigned `bits`-bit integer (bits 4 or 8) stored little-endian
+ * in 32-bit words: word (k * bits) / 32 of row v, starting at bit
+ * (k * bits) % 32. scale and bias are bf16, [V][groups] with row pitch
+ * s_ld; q rows have pitch q_ld words. Output W64 is [V][H] f64, exact (a bf16
+ * times a small integer plus a bf16 is exactly representable in f64).
+ */
+void orc_dequant(const uint32_t* q, int64_t q_ld, const uint16_t* scales, const uint16_t* biases,
+                 int64_t s_ld, int bits, int group, int64_t V, int64_t H, double* W64) {
+    const uint32_t mask = (bits == 32) ? 0xFFFFFFFFu : ((1u << bits) - 1u);
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < V; ++v) {
+        for (int64_t k = 0; k < H; ++k) {
+            const int64_t bit = k * bits;
+            const uint32_t word = q[v * q_ld + bit / 32];
+            const uint32_t qv = (word >> (bit % 32)) & mask;
+            const int64_t g = k / group;
+            W64[v * H + k] = widen(scales, ORC_BF16, v * s_ld + g) * (double)qv +
+                             widen(biases, ORC_BF16, v * s_ld + g);
         }
     }
 }

@@ -15,6 +15,7 @@ import synth
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rows.json")
+QUANT = os.path.join(os.path.dirname(__file__), "golden", "quant.json")
 
 
 def _rows_golden_ok(lib):
@@ -63,20 +64,36 @@ def _closed_forms_ok(lib):
             and abs(lp[0, 0] - (a - want)) <= 1e-12)
 
 
+def _dequant_golden_ok(lib):
+    with open(QUANT) as f:
+        for c in json.load(f)["cases"]:
+            W = oracle.dequant(np.array(c["q"], dtype=np.uint32), np.array(c["scales"], dtype=np.uint16),
+                               np.array(c["biases"], dtype=np.uint16), c["bits"], c["group"], c["hidden"],
+                               lib=lib)
+            if not np.array_equal(W, np.array(c["weights"], dtype=np.float64)):
+                return False
+    return True
+
+
 def _all_pins_ok(lib):
     return (_rows_golden_ok(lib) and _head_integer_ok(lib) and _head_one_hot_ok(lib)
-            and _closed_forms_ok(lib))
+            and _closed_forms_ok(lib) and _dequant_golden_ok(lib))
 
 
 MUTANTS = [
     ("sampled row off by one", "if (idx_out) idx_out[s] = cu[s + 1] - 1;", "if (idx_out) idx_out[s] = cu[s + 1];"),
     ("explicit count <= instead of <", "if (explicit_idx[r] < cu[s]) ++c;", "if (explicit_idx[r] <= cu[s]) ++c;"),
-    ("head drops the last term", "for (int64_t k = 0; k < H; ++k)", "for (int64_t k = 0; k < H - 1; ++k)"),
+    ("head drops the last term", "for (int64_t k = 0; k < H; ++k)\n                acc +=", "for (int64_t k = 0; k < H - 1; ++k)\n                acc +="),
     ("head transposed weight operand", "widen(W, wdt, v * wld + k)", "widen(W, wdt, k * wld + v)"),
     ("exp of the negated difference", "s += exp(widen(logits, dt, base + v) - m);", "s += exp(m - widen(logits, dt, base + v));"),
     ("lse drops the max", "l = m + log(s);", "l = log(s);"),
     ("ties by descending id", "return (a->id < b->id) ? -1 : (a->id > b->id ? 1 : 0);", "return (a->id > b->id) ? -1 : (a->id < b->id ? 1 : 0);"),
     ("logprob sign flipped", "topk_lp[r * K + i] = e[i].x - l;", "topk_lp[r * K + i] = l - e[i].x;"),
+    ("dequant ignores the bit offset", "const uint32_t qv = (word >> (bit % 32)) & mask;", "const uint32_t qv = word & mask;"),
+    ("dequant nibbles from the top", "const uint32_t qv = (word >> (bit % 32)) & mask;", "const uint32_t qv = (word >> (32 - bits - bit % 32)) & mask;"),
+    ("dequant drops the bias", "* (double)qv +\n                             widen(biases, ORC_BF16, v * s_ld + g);", "* (double)qv;"),
+    ("dequant scale and bias swapped", "W64[v * H + k] = widen(scales,", "W64[v * H + k] = widen(biases,"),
+    ("dequant group twice as wide", "const int64_t g = k / group;", "const int64_t g = k / (2 * group);"),
     ("selected logprob adds lse", ": widen(logits, dt, base + t) - l;", ": widen(logits, dt, base + t) + l;"),
 ]
 
