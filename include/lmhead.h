@@ -207,6 +207,56 @@ lmh_status lmhead_logprobs(
     int32_t chunk_rows, float* logits_debug,
     void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
 
+/*
+ * Quantised head weights [mlxcel: the measured models are 4-bit].
+ *
+ * The head may be given as affine group-quantised codes instead of dense
+ * weights: for token v and hidden index k, with g = k / group_size,
+ *     weight[v][k] = scales[v][g] * q(v, k) + biases[v][g],
+ * where q(v, k) is the unsigned `bits`-bit code (bits 4 or 8) stored
+ * little-endian in the 32-bit words of row v of weight_q: word
+ * (k * bits) / 32, starting at bit (k * bits) % 32.
+ *
+ * weight_q  [vocab][weight_q_ld] uint32 words, 16-B aligned, weight_q_ld a
+ *           multiple of 4 and >= hidden_dim * bits / 32.
+ * scales, biases [vocab][scales_ld] bf16 (raw uint16 bits), 2-B aligned,
+ *           scales_ld >= hidden_dim / group_size.
+ * bits 4 or 8 (else LMH_ERR_DTYPE); group_size 32, 64 or 128; hidden_dim a
+ *           multiple of 128 (else LMH_ERR_SHAPE). hidden_dt must be LMH_BF16.
+ * Each weight is formed on the device as fma(scale, q, bias) in fp32 (the
+ * product is exact) and rounded once to bf16 (nearest even), then enters the
+ * same bf16 MFMA path with fp32 accumulation as dense bf16 weights, so a
+ * row's logits do not depend on the rows projected with it (bitwise). The
+ * hidden index is summed in an order of the library's own (runs of
+ * 512 / bits elements, one run per lane and MFMA group), so results equal
+ * the dense path's on the dequantised weights up to fp32 summation order.
+ * All other arguments, outputs and rules are those of lmhead_gather_project
+ * and lmhead_logprobs (workspace: lmhead_logprobs_workspace_size).
+ */
+lmh_status lmhead_gather_project_q(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld,
+    const uint32_t* weight_q, int64_t weight_q_ld, const uint16_t* scales, const uint16_t* biases,
+    int64_t scales_ld, int32_t bits, int32_t group_size, int64_t vocab,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    void* logits, lmh_dtype logits_dt, int64_t logits_ld,
+    int32_t* logits_cu_seqlens, int32_t* gather_indices,
+    int32_t* device_error, void* stream);
+
+lmh_status lmhead_logprobs_q(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld,
+    const uint32_t* weight_q, int64_t weight_q_ld, const uint16_t* scales, const uint16_t* biases,
+    int64_t scales_ld, int32_t bits, int32_t group_size, int64_t vocab,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    const int32_t* selected_ids, int32_t k,
+    float* lse, float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+    int32_t* logits_cu_seqlens, int32_t* gather_indices,
+    int32_t chunk_rows, float* logits_debug,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
+
 /* lmh_status_string -- static, human-readable name of a status code. */
 const char* lmh_status_string(lmh_status status);
 
@@ -229,6 +279,21 @@ lmh_status lmh_debug_gather_project(
     const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
     int64_t hidden_ld,
     const void* weight, lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    void* logits, lmh_dtype logits_dt, int64_t logits_ld,
+    int32_t* logits_cu_seqlens, int32_t* gather_indices,
+    int32_t* device_error, void* stream, int32_t variant);
+
+/*
+ * lmh_debug_gather_project_q -- lmhead_gather_project_q with the head kernel
+ * forced (LMH_HEAD_STREAM with R > 64 returns LMH_ERR_SHAPE).
+ */
+lmh_status lmh_debug_gather_project_q(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld,
+    const uint32_t* weight_q, int64_t weight_q_ld, const uint16_t* scales, const uint16_t* biases,
+    int64_t scales_ld, int32_t bits, int32_t group_size, int64_t vocab,
     const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
     const int32_t* logits_indices, int32_t num_indices,
     void* logits, lmh_dtype logits_dt, int64_t logits_ld,

@@ -258,3 +258,37 @@ def small_int_bf16(seed: int, shape, lo: int = -4, hi: int = 4) -> np.ndarray:
     g = rng(seed)
     v = g.integers(lo, hi + 1, size=shape).astype(np.float32)
     return f32_to_bf16_bits(v)
+
+
+def quantized_head(seed: int, vocab: int, hidden_dim: int, bits: int = 4, group: int = 64,
+                   q_pad_words: int = 0, s_pad: int = 0, chunk_rows: int = 16384):
+    """A head in affine group-quantised form, as 4-bit MLX models ship it
+    (mlxcel PR #1969, description): ``bits``-bit codes uniform in
+    [0, 2**bits), packed little-endian into uint32 words [vocab, words +
+    q_pad_words] (code k of a row at bit k*bits of the row); bf16 scales and
+    biases [vocab, groups + s_pad]. Per group, the scale is
+    sigma * (0.28 + 0.08 U) * 15 / (2**bits - 1) and the bias is
+    -scale * (2**bits - 1) / 2 * (1 + 0.1 N), sigma = hidden_dim**-0.5: the
+    code range spans about +-2.4 sigma, like a group of N(0, sigma^2) weights.
+    Padding words are 0xFFFFFFFF and padding scales/biases NaN-free garbage
+    (bf16 1.0) so that reading them would show."""
+    assert bits in (4, 8) and hidden_dim % group == 0 and (hidden_dim * bits) % 32 == 0
+    g = rng(seed)
+    per = 32 // bits
+    words = hidden_dim // per
+    groups = hidden_dim // group
+    q = np.full((vocab, words + q_pad_words), 0xFFFFFFFF, dtype=np.uint32)
+    for r0 in range(0, vocab, chunk_rows):
+        r1 = min(vocab, r0 + chunk_rows)
+        codes = g.integers(0, 1 << bits, size=(r1 - r0, words, per), dtype=np.uint32)
+        shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))[None, None, :]
+        q[r0:r1, :words] = np.bitwise_or.reduce(codes << shifts, axis=2)
+    sigma = float(hidden_dim) ** -0.5
+    levels = float((1 << bits) - 1)
+    scale = sigma * (0.28 + 0.08 * g.random((vocab, groups), dtype=np.float32)) * 15.0 / levels
+    bias = -scale * levels / 2.0 * (1.0 + 0.1 * g.standard_normal((vocab, groups), dtype=np.float32))
+    s = np.full((vocab, groups + s_pad), 0x3F80, dtype=np.uint16)
+    b = np.full((vocab, groups + s_pad), 0x3F80, dtype=np.uint16)
+    s[:, :groups] = f32_to_bf16_bits(scale.astype(np.float32))
+    b[:, :groups] = f32_to_bf16_bits(bias.astype(np.float32))
+    return dict(q=q, scales=s, biases=b, bits=bits, group=group, hidden_dim=hidden_dim)

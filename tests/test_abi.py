@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"lmhead_gather_project", "logprob_reduce", "lmhead_logprobs",
             "logprob_reduce_workspace_size", "lmhead_logprobs_workspace_size",
-            "lmh_status_string"} <= names
+            "lmh_status_string", "lmhead_gather_project_q", "lmhead_logprobs_q"} <= names
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -85,6 +85,40 @@ def test_debug_variant_rules(L):
     f32[9] = A
     f32[10] = 5
     assert L.lmh_debug_gather_project(*f32, 2) == SHAPE       # variants are bf16-only
+
+
+def _project_q(L, debug_variant=None, **kw):
+    a = dict(hidden=A, hidden_dt=BF16, num_tokens=23, hidden_dim=128, hidden_ld=128, q=A, q_ld=16,
+             scales=A, biases=A, s_ld=2, bits=4, group=64, vocab=1000, cu=A, S=5, D=2, ex=None,
+             nex=0, logits=A, logits_dt=F32, logits_ld=1000, lcu=None, gidx=None, err=None)
+    a.update(kw)
+    args = [a["hidden"], a["hidden_dt"], a["num_tokens"], a["hidden_dim"], a["hidden_ld"], a["q"],
+            a["q_ld"], a["scales"], a["biases"], a["s_ld"], a["bits"], a["group"], a["vocab"],
+            a["cu"], a["S"], a["D"], a["ex"], a["nex"], a["logits"], a["logits_dt"],
+            a["logits_ld"], a["lcu"], a["gidx"], a["err"], None]
+    if debug_variant is None:
+        return L.lmhead_gather_project_q(*args)
+    return L.lmh_debug_gather_project_q(*args, debug_variant)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), NULL), (dict(scales=None), NULL), (dict(biases=None), NULL),
+    (dict(bits=3), DTYPE), (dict(bits=16), DTYPE), (dict(hidden_dt=F32), DTYPE),
+    (dict(group=16), SHAPE), (dict(group=256), SHAPE), (dict(group=48), SHAPE),
+    (dict(hidden_dim=64, hidden_ld=64, q_ld=8, s_ld=1), SHAPE),
+    (dict(q_ld=12), SHAPE), (dict(bits=8, q_ld=16), SHAPE), (dict(s_ld=1), SHAPE),
+    (dict(group=32, s_ld=3), SHAPE),
+    (dict(q_ld=18), ALIGN), (dict(q=A + 8), ALIGN), (dict(scales=A + 1), ALIGN),
+    (dict(biases=A + 3), ALIGN), (dict(hidden=A + 8), ALIGN),
+    (dict(num_tokens=0), SHAPE), (dict(vocab=0), SHAPE), (dict(logits_ld=999), SHAPE),
+])
+def test_gather_project_q_rejects(L, kw, want):
+    assert _project_q(L, **kw) == want
+
+
+def test_debug_variant_rules_q(L):
+    assert _project_q(L, debug_variant=1, S=100, D=0) == SHAPE   # streaming head needs R <= 64
+    assert _project_q(L, debug_variant=3) == SHAPE               # unknown variant
 
 
 def _reduce(L, **kw):

@@ -11,6 +11,10 @@ Entry points (same names as the C ABI):
                          only those through the head
   logprob_reduce         per-row logsumexp, selected logprob, exact top-K
   lmhead_logprobs        both, fused and chunked
+  lmhead_gather_project_q, lmhead_logprobs_q
+                         the same with an affine group-quantised head
+                         (QuantizedWeight: 4- or 8-bit codes, bf16 scale and
+                         bias per group)
 """
 from __future__ import annotations
 
@@ -59,10 +63,15 @@ def lib():
         L.lmhead_logprobs_workspace_size.argtypes = [i64, i64, i32, i32]
         L.lmhead_logprobs_workspace_size.restype = sz
         L.lmhead_logprobs.argtypes = proj + [p, i32, p, p, p, p, p, p, i32, p, p, sz, p, p]
+        projq = [p, ctypes.c_int, i64, i64, i64, p, i64, p, p, i64, i32, i32, i64, p, i32, i32, p, i32]
+        L.lmhead_gather_project_q.argtypes = projq + [p, ctypes.c_int, i64, p, p, p, p]
+        L.lmh_debug_gather_project_q.argtypes = projq + [p, ctypes.c_int, i64, p, p, p, p, i32]
+        L.lmhead_logprobs_q.argtypes = projq + [p, i32, p, p, p, p, p, p, i32, p, p, sz, p, p]
         L.lmh_status_string.argtypes = [ctypes.c_int]
         L.lmh_status_string.restype = ctypes.c_char_p
         for name in ("lmhead_gather_project", "lmh_debug_gather_project", "logprob_reduce",
-                     "lmh_debug_reduce_stage1", "lmhead_logprobs"):
+                     "lmh_debug_reduce_stage1", "lmhead_logprobs", "lmhead_gather_project_q",
+                     "lmh_debug_gather_project_q", "lmhead_logprobs_q"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -117,18 +126,44 @@ class Projection(NamedTuple):
     device_error: torch.Tensor
 
 
-def lmhead_gather_project(hidden: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor,
-                          num_decode: int = 0, logits_indices: Optional[torch.Tensor] = None,
-                          out_dtype: torch.dtype = torch.float32,
-                          logits: Optional[torch.Tensor] = None, variant: int = LMH_HEAD_AUTO,
-                          device_error: Optional[torch.Tensor] = None) -> Projection:
-    """Gather the sampled rows of a packed batch and project them through the
-    head: logits[r] = hidden[src(r)] @ weight.T (weight is [vocab, hidden])."""
-    L = lib()
-    T, H, hld = _matrix(hidden, "hidden")
+class QuantizedWeight(NamedTuple):
+    """An affine group-quantised head: weight[v][k] = scales[v][g] * code +
+    biases[v][g], g = k // group_size, with the `bits`-bit codes (4 or 8) of
+    row v packed little-endian in the 32-bit words q[v] (int32 storage of the
+    uint32 words). scales and biases are bfloat16 [vocab, groups] with one
+    row stride."""
+    q: torch.Tensor
+    scales: torch.Tensor
+    biases: torch.Tensor
+    bits: int
+    group_size: int
+
+
+def _dense_weight_args(weight: torch.Tensor, H: int):
     V, H2, wld = _matrix(weight, "weight")
     if H2 != H:
         raise ValueError("hidden and weight widths differ")
+    return V, [_ptr(weight), _dt(weight), V, wld]
+
+
+def _quant_weight_args(w: QuantizedWeight, H: int):
+    V, words, qld = _matrix(w.q, "q")
+    if w.q.dtype != torch.int32:
+        raise ValueError("q must hold the uint32 code words as int32")
+    Vs, G, sld = _matrix(w.scales, "scales")
+    Vb, Gb, bld = _matrix(w.biases, "biases")
+    if w.scales.dtype != torch.bfloat16 or w.biases.dtype != torch.bfloat16:
+        raise ValueError("scales and biases must be bfloat16")
+    if (Vs, G, sld) != (Vb, Gb, bld) or Vs != V:
+        raise ValueError("scales and biases must share shape and row stride, one row per token")
+    if words * 32 < H * int(w.bits) or G * int(w.group_size) < H:
+        raise ValueError("q, scales and biases do not cover the hidden width")
+    return V, [_ptr(w.q), qld, _ptr(w.scales), _ptr(w.biases), sld, int(w.bits), int(w.group_size), V]
+
+
+def _project(fn_auto, fn_debug, name, hidden, weight_args, V, cu_seqlens, num_decode,
+             logits_indices, out_dtype, logits, variant, device_error) -> Projection:
+    T, H, hld = _matrix(hidden, "hidden")
     cu = _i32(cu_seqlens, "cu_seqlens")
     ex = _i32(logits_indices, "logits_indices")
     S = cu.shape[0] - 1
@@ -140,15 +175,39 @@ def lmhead_gather_project(hidden: torch.Tensor, weight: torch.Tensor, cu_seqlens
     lcu = torch.empty(S + 1, dtype=torch.int32, device=dev)
     gidx = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
     err = device_error if device_error is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    args = [_ptr(hidden), _dt(hidden), T, H, hld, _ptr(weight), _dt(weight), V, wld,
+    args = [_ptr(hidden), _dt(hidden), T, H, hld, *weight_args,
             _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
             _ptr(logits), _dt(logits), old, _ptr(lcu), _ptr(gidx), _ptr(err), _stream()]
-    if variant == LMH_HEAD_AUTO:
-        st = L.lmhead_gather_project(*args)
-    else:
-        st = L.lmh_debug_gather_project(*args, int(variant))
-    _check(st, "lmhead_gather_project")
+    st = fn_auto(*args) if variant == LMH_HEAD_AUTO else fn_debug(*args, int(variant))
+    _check(st, name)
     return Projection(logits, lcu, gidx[:R], err)
+
+
+def lmhead_gather_project(hidden: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor,
+                          num_decode: int = 0, logits_indices: Optional[torch.Tensor] = None,
+                          out_dtype: torch.dtype = torch.float32,
+                          logits: Optional[torch.Tensor] = None, variant: int = LMH_HEAD_AUTO,
+                          device_error: Optional[torch.Tensor] = None) -> Projection:
+    """Gather the sampled rows of a packed batch and project them through the
+    head: logits[r] = hidden[src(r)] @ weight.T (weight is [vocab, hidden])."""
+    L = lib()
+    V, wargs = _dense_weight_args(weight, hidden.shape[1])
+    return _project(L.lmhead_gather_project, L.lmh_debug_gather_project, "lmhead_gather_project",
+                    hidden, wargs, V, cu_seqlens, num_decode, logits_indices, out_dtype, logits,
+                    variant, device_error)
+
+
+def lmhead_gather_project_q(hidden: torch.Tensor, weight: QuantizedWeight, cu_seqlens: torch.Tensor,
+                            num_decode: int = 0, logits_indices: Optional[torch.Tensor] = None,
+                            out_dtype: torch.dtype = torch.float32,
+                            logits: Optional[torch.Tensor] = None, variant: int = LMH_HEAD_AUTO,
+                            device_error: Optional[torch.Tensor] = None) -> Projection:
+    """lmhead_gather_project with a quantised head (bf16 hidden states)."""
+    L = lib()
+    V, wargs = _quant_weight_args(weight, hidden.shape[1])
+    return _project(L.lmhead_gather_project_q, L.lmh_debug_gather_project_q,
+                    "lmhead_gather_project_q", hidden, wargs, V, cu_seqlens, num_decode,
+                    logits_indices, out_dtype, logits, variant, device_error)
 
 
 class Reduction(NamedTuple):
@@ -214,16 +273,10 @@ def lmhead_logprobs_workspace_size(rows: int, vocab: int, k: int, chunk_rows: in
     return int(lib().lmhead_logprobs_workspace_size(rows, vocab, k, chunk_rows))
 
 
-def lmhead_logprobs(hidden: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor,
-                    num_decode: int = 0, selected_ids: Optional[torch.Tensor] = None, k: int = 0,
-                    logits_indices: Optional[torch.Tensor] = None, chunk_rows: int = 0,
-                    return_logits: bool = False, ws: Optional[torch.Tensor] = None) -> Logprobs:
-    """Fused gather + projection + reduction, chunked (default 256 rows)."""
+def _logprobs(fn, name, hidden, weight_args, V, cu_seqlens, num_decode, selected_ids, k,
+              logits_indices, chunk_rows, return_logits, ws) -> Logprobs:
     L = lib()
     T, H, hld = _matrix(hidden, "hidden")
-    V, H2, wld = _matrix(weight, "weight")
-    if H2 != H:
-        raise ValueError("hidden and weight widths differ")
     cu = _i32(cu_seqlens, "cu_seqlens")
     ex = _i32(logits_indices, "logits_indices")
     sel = _i32(selected_ids, "selected_ids")
@@ -241,12 +294,32 @@ def lmhead_logprobs(hidden: torch.Tensor, weight: torch.Tensor, cu_seqlens: torc
     lcu = torch.empty(S + 1, dtype=torch.int32, device=dev)
     gidx = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    st = L.lmhead_logprobs(_ptr(hidden), _dt(hidden), T, H, hld, _ptr(weight), _dt(weight), V, wld,
-                           _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
-                           _ptr(sel), int(k), _ptr(lse), _ptr(slp),
-                           _ptr(ids) if k else None, _ptr(lps) if k else None,
-                           _ptr(lcu), _ptr(gidx), int(chunk_rows), _ptr(dbg),
-                           _ptr(ws), ws.numel(), _ptr(err), _stream())
-    _check(st, "lmhead_logprobs")
+    st = fn(_ptr(hidden), _dt(hidden), T, H, hld, *weight_args,
+            _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
+            _ptr(sel), int(k), _ptr(lse), _ptr(slp),
+            _ptr(ids) if k else None, _ptr(lps) if k else None,
+            _ptr(lcu), _ptr(gidx), int(chunk_rows), _ptr(dbg),
+            _ptr(ws), ws.numel(), _ptr(err), _stream())
+    _check(st, name)
     return Logprobs(lse, slp, ids, lps, lcu, gidx[:R], err,
                     None if dbg is None else dbg[:, :V])
+
+
+def lmhead_logprobs(hidden: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor,
+                    num_decode: int = 0, selected_ids: Optional[torch.Tensor] = None, k: int = 0,
+                    logits_indices: Optional[torch.Tensor] = None, chunk_rows: int = 0,
+                    return_logits: bool = False, ws: Optional[torch.Tensor] = None) -> Logprobs:
+    """Fused gather + projection + reduction, chunked (default 256 rows)."""
+    V, wargs = _dense_weight_args(weight, hidden.shape[1])
+    return _logprobs(lib().lmhead_logprobs, "lmhead_logprobs", hidden, wargs, V, cu_seqlens,
+                     num_decode, selected_ids, k, logits_indices, chunk_rows, return_logits, ws)
+
+
+def lmhead_logprobs_q(hidden: torch.Tensor, weight: QuantizedWeight, cu_seqlens: torch.Tensor,
+                      num_decode: int = 0, selected_ids: Optional[torch.Tensor] = None, k: int = 0,
+                      logits_indices: Optional[torch.Tensor] = None, chunk_rows: int = 0,
+                      return_logits: bool = False, ws: Optional[torch.Tensor] = None) -> Logprobs:
+    """lmhead_logprobs with a quantised head (bf16 hidden states)."""
+    V, wargs = _quant_weight_args(weight, hidden.shape[1])
+    return _logprobs(lib().lmhead_logprobs_q, "lmhead_logprobs_q", hidden, wargs, V, cu_seqlens,
+                     num_decode, selected_ids, k, logits_indices, chunk_rows, return_logits, ws)

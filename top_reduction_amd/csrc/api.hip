@@ -21,26 +21,64 @@ struct ProjectCheck {
     int32_t rows;
 };
 
+// The head's weights: dense (fp32 or bf16, like the hidden states) or affine
+// group-quantised (bits != 0).
+struct WeightSpec {
+    const void* dense;
+    lmh_dtype dt;
+    int64_t ld;
+    const uint32_t* q;
+    int64_t q_ld;
+    const uint16_t* scales;
+    const uint16_t* biases;
+    int64_t s_ld;
+    int32_t bits;     // 0: dense
+    int32_t group;
+};
+
+WeightSpec dense_weight(const void* w, lmh_dtype dt, int64_t ld) {
+    return WeightSpec{w, dt, ld, nullptr, 0, nullptr, nullptr, 0, 0, 0};
+}
+WeightSpec quant_weight(const uint32_t* q, int64_t q_ld, const uint16_t* scales,
+                        const uint16_t* biases, int64_t s_ld, int32_t bits, int32_t group) {
+    return WeightSpec{nullptr, LMH_BF16, 0, q, q_ld, scales, biases, s_ld, bits, group};
+}
+
+int32_t log2_exact(int32_t g) {
+    int32_t s = 0;
+    while ((1 << s) < g) ++s;
+    return s;
+}
+
 // Checks shared by the projection entry points (everything but the output).
 ProjectCheck check_project_inputs(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
-                                  int64_t hidden_dim, int64_t hidden_ld, const void* weight,
-                                  lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
-                                  const int32_t* cu_seqlens, int32_t num_segments,
+                                  int64_t hidden_dim, int64_t hidden_ld, const WeightSpec& w,
+                                  int64_t vocab, const int32_t* cu_seqlens, int32_t num_segments,
                                   int32_t num_decode, const int32_t* logits_indices,
                                   int32_t num_indices) {
-    if (!hidden || !weight || !cu_seqlens) return {LMH_ERR_NULL, 0};
+    if (!hidden || !cu_seqlens) return {LMH_ERR_NULL, 0};
+    if (w.bits == 0 ? !w.dense : (!w.q || !w.scales || !w.biases)) return {LMH_ERR_NULL, 0};
     if (num_tokens <= 0 || num_tokens > INT32_MAX || hidden_dim <= 0 || vocab <= 0 ||
         vocab > INT32_MAX || num_segments < 0 || num_decode < 0 || num_decode > num_segments)
         return {LMH_ERR_SHAPE, 0};
     if (logits_indices != nullptr && num_indices < 0) return {LMH_ERR_SHAPE, 0};
-    if (hidden_ld < hidden_dim || weight_ld < hidden_dim) return {LMH_ERR_SHAPE, 0};
-    if (!valid_dtype(hidden_dt) || weight_dt != hidden_dt) return {LMH_ERR_DTYPE, 0};
-    if (hidden_dt == LMH_BF16) {
-        if (!aligned(hidden, 16) || !aligned(weight, 16) || hidden_dim % 8 || hidden_ld % 8 ||
-            weight_ld % 8)
-            return {LMH_ERR_ALIGN, 0};
+    if (hidden_ld < hidden_dim) return {LMH_ERR_SHAPE, 0};
+    if (w.bits == 0) {
+        if (w.ld < hidden_dim) return {LMH_ERR_SHAPE, 0};
+        if (!valid_dtype(hidden_dt) || w.dt != hidden_dt) return {LMH_ERR_DTYPE, 0};
     } else {
-        if (!aligned(hidden, 4) || !aligned(weight, 4)) return {LMH_ERR_ALIGN, 0};
+        if (hidden_dt != LMH_BF16 || (w.bits != 4 && w.bits != 8)) return {LMH_ERR_DTYPE, 0};
+        if (w.group != 32 && w.group != 64 && w.group != 128) return {LMH_ERR_SHAPE, 0};
+        if (hidden_dim % 128 || w.q_ld < hidden_dim * w.bits / 32 || w.s_ld < hidden_dim / w.group)
+            return {LMH_ERR_SHAPE, 0};
+        if (!aligned(w.q, 16) || w.q_ld % 4 || !aligned(w.scales, 2) || !aligned(w.biases, 2))
+            return {LMH_ERR_ALIGN, 0};
+    }
+    if (hidden_dt == LMH_BF16) {
+        if (!aligned(hidden, 16) || hidden_dim % 8 || hidden_ld % 8) return {LMH_ERR_ALIGN, 0};
+        if (w.bits == 0 && (!aligned(w.dense, 16) || w.ld % 8)) return {LMH_ERR_ALIGN, 0};
+    } else {
+        if (!aligned(hidden, 4) || !aligned(w.dense, 4)) return {LMH_ERR_ALIGN, 0};
     }
     const int32_t rows = logits_indices ? num_indices : num_segments;
     return {LMH_OK, rows};
@@ -64,23 +102,42 @@ lmh_status check_reduce_shape(lmh_dtype dt, int64_t rows, int64_t vocab, int64_t
 
 lmh_status from_hip(hipError_t e) { return e == hipSuccess ? LMH_OK : LMH_ERR_HIP; }
 
+HeadArgs head_args(const void* hidden, int64_t num_tokens, int64_t hidden_dim, int64_t hidden_ld,
+                   const WeightSpec& w, int64_t vocab, const int32_t* cu_seqlens, int32_t num_decode,
+                   const int32_t* logits_indices, int32_t row0, int32_t rows, void* out,
+                   int64_t out_ld, bool out_bf16, int32_t* device_error) {
+    HeadArgs h{hidden, num_tokens, hidden_dim, hidden_ld, w.dense, vocab, w.ld, cu_seqlens,
+               num_decode, logits_indices, row0, rows, out, out_ld, out_bf16, device_error};
+    if (w.bits != 0) {
+        h.bits = w.bits;
+        h.q = w.q;
+        h.q_ld = w.q_ld;
+        h.scales = w.scales;
+        h.biases = w.biases;
+        h.s_ld = w.s_ld;
+        h.gshift = log2_exact(w.group);
+    }
+    return h;
+}
+
 lmh_status launch_head(const HeadArgs& h, bool bf16_inputs, int32_t variant, hipStream_t s) {
     if (!bf16_inputs) return from_hip(launch_head_f32(h, s));
     const bool stream = variant == LMH_HEAD_STREAM || (variant == LMH_HEAD_AUTO && h.rows <= kStreamMaxRows);
+    if (h.bits != 16) return from_hip(stream ? launch_head_stream_q(h, s) : launch_head_tiled_q(h, s));
     return from_hip(stream ? launch_head_stream_bf16(h, s) : launch_head_tiled_bf16(h, s));
 }
 
 lmh_status gather_project_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
-                               int64_t hidden_dim, int64_t hidden_ld, const void* weight,
-                               lmh_dtype weight_dt, int64_t vocab, int64_t weight_ld,
-                               const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
-                               const int32_t* logits_indices, int32_t num_indices, void* logits,
-                               lmh_dtype logits_dt, int64_t logits_ld, int32_t* logits_cu_seqlens,
+                               int64_t hidden_dim, int64_t hidden_ld, const WeightSpec& w,
+                               int64_t vocab, const int32_t* cu_seqlens, int32_t num_segments,
+                               int32_t num_decode, const int32_t* logits_indices,
+                               int32_t num_indices, void* logits, lmh_dtype logits_dt,
+                               int64_t logits_ld, int32_t* logits_cu_seqlens,
                                int32_t* gather_indices, int32_t* device_error, void* stream,
                                int32_t variant) {
     const ProjectCheck c = check_project_inputs(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
-                                                weight, weight_dt, vocab, weight_ld, cu_seqlens,
-                                                num_segments, num_decode, logits_indices, num_indices);
+                                                w, vocab, cu_seqlens, num_segments, num_decode,
+                                                logits_indices, num_indices);
     if (c.st != LMH_OK) return c.st;
     if (!logits && c.rows > 0) return LMH_ERR_NULL;
     if (logits_ld < vocab) return LMH_ERR_SHAPE;
@@ -98,10 +155,77 @@ lmh_status gather_project_impl(const void* hidden, lmh_dtype hidden_dt, int64_t 
         if (st != LMH_OK) return st;
     }
     if (c.rows == 0) return LMH_OK;
-    HeadArgs h{hidden, num_tokens, hidden_dim, hidden_ld, weight, vocab, weight_ld, cu_seqlens,
-               num_decode, logits_indices, 0, c.rows, logits, logits_ld, logits_dt == LMH_BF16,
-               device_error};
+    const HeadArgs h = head_args(hidden, num_tokens, hidden_dim, hidden_ld, w, vocab, cu_seqlens,
+                                 num_decode, logits_indices, 0, c.rows, logits, logits_ld,
+                                 logits_dt == LMH_BF16, device_error);
     return launch_head(h, hidden_dt == LMH_BF16, variant, s);
+}
+
+lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                         int64_t hidden_dim, int64_t hidden_ld, const WeightSpec& w, int64_t vocab,
+                         const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+                         const int32_t* logits_indices, int32_t num_indices,
+                         const int32_t* selected_ids, int32_t k, float* lse,
+                         float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+                         int32_t* logits_cu_seqlens, int32_t* gather_indices, int32_t chunk_rows,
+                         float* logits_debug, void* workspace, size_t workspace_bytes,
+                         int32_t* device_error, void* stream) {
+    const ProjectCheck c = check_project_inputs(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                                                w, vocab, cu_seqlens, num_segments, num_decode,
+                                                logits_indices, num_indices);
+    if (c.st != LMH_OK) return c.st;
+    if (c.rows > 0) {
+        if (!lse) return LMH_ERR_NULL;
+        if (selected_ids && !selected_logprob) return LMH_ERR_NULL;
+        if (k > 0 && (!topk_ids || !topk_logprobs)) return LMH_ERR_NULL;
+    }
+    if (chunk_rows < 0) return LMH_ERR_SHAPE;
+    const int64_t R = c.rows;
+    const int64_t chunk_cfg = chunk_rows > 0 ? chunk_rows : 256;
+    const int64_t chunk = R < chunk_cfg ? (R > 0 ? R : 1) : chunk_cfg;
+    const int64_t ld = ceil_div(vocab, 4) * 4;
+    {
+        // the reduction's rules, checked on the fp32 logits layout it will read
+        const lmh_status st = check_reduce_shape(LMH_F32, chunk, vocab, ld, k);
+        if (st != LMH_OK) return st;
+    }
+    const ReducePlan pc = plan_reduce(chunk, vocab, k);
+    const size_t logits_bytes = logits_debug ? 0 : up256((size_t)chunk * (size_t)ld * sizeof(float));
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < logits_bytes + pc.bytes)
+        return LMH_ERR_WORKSPACE;
+    if (logits_debug && !aligned(logits_debug, 16)) return LMH_ERR_ALIGN;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gather_indices || logits_cu_seqlens || device_error) {
+        RowsArgs ra{cu_seqlens, num_segments, num_decode, num_tokens, logits_indices, c.rows,
+                    gather_indices, logits_cu_seqlens, device_error};
+        const lmh_status st = from_hip(launch_rows(ra, s));
+        if (st != LMH_OK) return st;
+    }
+    char* ws = static_cast<char*>(workspace);
+    float* ws_logits = reinterpret_cast<float*>(ws);
+    void* ws_reduce = ws + logits_bytes;
+    for (int64_t r0 = 0; r0 < R; r0 += chunk) {
+        const int32_t n = (int32_t)((R - r0) < chunk ? (R - r0) : chunk);
+        float* out = logits_debug ? logits_debug + r0 * ld : ws_logits;
+        const HeadArgs h = head_args(hidden, num_tokens, hidden_dim, hidden_ld, w, vocab, cu_seqlens,
+                                     num_decode, logits_indices, (int32_t)r0, n, out, ld, false,
+                                     device_error);
+        lmh_status st = launch_head(h, hidden_dt == LMH_BF16, LMH_HEAD_AUTO, s);
+        if (st != LMH_OK) return st;
+        // this chunk's decomposition, inside the workspace layout sized for a full chunk
+        ReducePlan q = plan_reduce(n, vocab, k);
+        q.part_off = pc.part_off;
+        q.keys_off = pc.keys_off;
+        q.bytes = pc.bytes;
+        ReduceArgs a{out, false, ld, selected_ids ? selected_ids + r0 : nullptr, lse + r0,
+                     selected_ids ? selected_logprob + r0 : nullptr,
+                     k > 0 ? topk_ids + r0 * k : nullptr, k > 0 ? topk_logprobs + r0 * k : nullptr,
+                     ws_reduce, device_error};
+        st = from_hip(launch_reduce(q, a, s));
+        if (st != LMH_OK) return st;
+    }
+    return LMH_OK;
 }
 
 }  // namespace
@@ -130,11 +254,11 @@ lmh_status lmhead_gather_project(const void* hidden, lmh_dtype hidden_dt, int64_
                                  int32_t num_indices, void* logits, lmh_dtype logits_dt,
                                  int64_t logits_ld, int32_t* logits_cu_seqlens,
                                  int32_t* gather_indices, int32_t* device_error, void* stream) {
-    return gather_project_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld, weight,
-                               weight_dt, vocab, weight_ld, cu_seqlens, num_segments, num_decode,
-                               logits_indices, num_indices, logits, logits_dt, logits_ld,
-                               logits_cu_seqlens, gather_indices, device_error, stream,
-                               LMH_HEAD_AUTO);
+    return gather_project_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                               dense_weight(weight, weight_dt, weight_ld), vocab, cu_seqlens,
+                               num_segments, num_decode, logits_indices, num_indices, logits,
+                               logits_dt, logits_ld, logits_cu_seqlens, gather_indices,
+                               device_error, stream, LMH_HEAD_AUTO);
 }
 
 lmh_status lmh_debug_gather_project(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
@@ -146,10 +270,48 @@ lmh_status lmh_debug_gather_project(const void* hidden, lmh_dtype hidden_dt, int
                                     int64_t logits_ld, int32_t* logits_cu_seqlens,
                                     int32_t* gather_indices, int32_t* device_error, void* stream,
                                     int32_t variant) {
-    return gather_project_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld, weight,
-                               weight_dt, vocab, weight_ld, cu_seqlens, num_segments, num_decode,
-                               logits_indices, num_indices, logits, logits_dt, logits_ld,
-                               logits_cu_seqlens, gather_indices, device_error, stream, variant);
+    return gather_project_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                               dense_weight(weight, weight_dt, weight_ld), vocab, cu_seqlens,
+                               num_segments, num_decode, logits_indices, num_indices, logits,
+                               logits_dt, logits_ld, logits_cu_seqlens, gather_indices,
+                               device_error, stream, variant);
+}
+
+lmh_status lmhead_gather_project_q(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                                   int64_t hidden_dim, int64_t hidden_ld, const uint32_t* weight_q,
+                                   int64_t weight_q_ld, const uint16_t* scales,
+                                   const uint16_t* biases, int64_t scales_ld, int32_t bits,
+                                   int32_t group_size, int64_t vocab, const int32_t* cu_seqlens,
+                                   int32_t num_segments, int32_t num_decode,
+                                   const int32_t* logits_indices, int32_t num_indices,
+                                   void* logits, lmh_dtype logits_dt, int64_t logits_ld,
+                                   int32_t* logits_cu_seqlens, int32_t* gather_indices,
+                                   int32_t* device_error, void* stream) {
+    return gather_project_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                               quant_weight(weight_q, weight_q_ld, scales, biases, scales_ld, bits,
+                                            group_size),
+                               vocab, cu_seqlens, num_segments, num_decode, logits_indices,
+                               num_indices, logits, logits_dt, logits_ld, logits_cu_seqlens,
+                               gather_indices, device_error, stream, LMH_HEAD_AUTO);
+}
+
+lmh_status lmh_debug_gather_project_q(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                                      int64_t hidden_dim, int64_t hidden_ld,
+                                      const uint32_t* weight_q, int64_t weight_q_ld,
+                                      const uint16_t* scales, const uint16_t* biases,
+                                      int64_t scales_ld, int32_t bits, int32_t group_size,
+                                      int64_t vocab, const int32_t* cu_seqlens,
+                                      int32_t num_segments, int32_t num_decode,
+                                      const int32_t* logits_indices, int32_t num_indices,
+                                      void* logits, lmh_dtype logits_dt, int64_t logits_ld,
+                                      int32_t* logits_cu_seqlens, int32_t* gather_indices,
+                                      int32_t* device_error, void* stream, int32_t variant) {
+    return gather_project_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                               quant_weight(weight_q, weight_q_ld, scales, biases, scales_ld, bits,
+                                            group_size),
+                               vocab, cu_seqlens, num_segments, num_decode, logits_indices,
+                               num_indices, logits, logits_dt, logits_ld, logits_cu_seqlens,
+                               gather_indices, device_error, stream, variant);
 }
 
 size_t logprob_reduce_workspace_size(int64_t rows, int64_t vocab, int32_t k) {
@@ -216,61 +378,32 @@ lmh_status lmhead_logprobs(const void* hidden, lmh_dtype hidden_dt, int64_t num_
                            int32_t* logits_cu_seqlens, int32_t* gather_indices, int32_t chunk_rows,
                            float* logits_debug, void* workspace, size_t workspace_bytes,
                            int32_t* device_error, void* stream) {
-    const ProjectCheck c = check_project_inputs(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
-                                                weight, weight_dt, vocab, weight_ld, cu_seqlens,
-                                                num_segments, num_decode, logits_indices, num_indices);
-    if (c.st != LMH_OK) return c.st;
-    if (c.rows > 0) {
-        if (!lse) return LMH_ERR_NULL;
-        if (selected_ids && !selected_logprob) return LMH_ERR_NULL;
-        if (k > 0 && (!topk_ids || !topk_logprobs)) return LMH_ERR_NULL;
-    }
-    if (chunk_rows < 0) return LMH_ERR_SHAPE;
-    const int64_t R = c.rows;
-    const int64_t chunk_cfg = chunk_rows > 0 ? chunk_rows : 256;
-    const int64_t chunk = R < chunk_cfg ? (R > 0 ? R : 1) : chunk_cfg;
-    const int64_t ld = ceil_div(vocab, 4) * 4;
-    {
-        // the reduction's rules, checked on the fp32 logits layout it will read
-        const lmh_status st = check_reduce_shape(LMH_F32, chunk, vocab, ld, k);
-        if (st != LMH_OK) return st;
-    }
-    const ReducePlan pc = plan_reduce(chunk, vocab, k);
-    const size_t logits_bytes = logits_debug ? 0 : up256((size_t)chunk * (size_t)ld * sizeof(float));
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < logits_bytes + pc.bytes)
-        return LMH_ERR_WORKSPACE;
-    if (logits_debug && !aligned(logits_debug, 16)) return LMH_ERR_ALIGN;
+    return logprobs_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                         dense_weight(weight, weight_dt, weight_ld), vocab, cu_seqlens,
+                         num_segments, num_decode, logits_indices, num_indices, selected_ids, k,
+                         lse, selected_logprob, topk_ids, topk_logprobs, logits_cu_seqlens,
+                         gather_indices, chunk_rows, logits_debug, workspace, workspace_bytes,
+                         device_error, stream);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (gather_indices || logits_cu_seqlens || device_error) {
-        RowsArgs ra{cu_seqlens, num_segments, num_decode, num_tokens, logits_indices, c.rows,
-                    gather_indices, logits_cu_seqlens, device_error};
-        const lmh_status st = from_hip(launch_rows(ra, s));
-        if (st != LMH_OK) return st;
-    }
-    char* ws = static_cast<char*>(workspace);
-    float* ws_logits = reinterpret_cast<float*>(ws);
-    void* ws_reduce = ws + logits_bytes;
-    for (int64_t r0 = 0; r0 < R; r0 += chunk) {
-        const int32_t n = (int32_t)((R - r0) < chunk ? (R - r0) : chunk);
-        float* out = logits_debug ? logits_debug + r0 * ld : ws_logits;
-        HeadArgs h{hidden, num_tokens, hidden_dim, hidden_ld, weight, vocab, weight_ld, cu_seqlens,
-                   num_decode, logits_indices, (int32_t)r0, n, out, ld, false, device_error};
-        lmh_status st = launch_head(h, hidden_dt == LMH_BF16, LMH_HEAD_AUTO, s);
-        if (st != LMH_OK) return st;
-        // this chunk's decomposition, inside the workspace layout sized for a full chunk
-        ReducePlan q = plan_reduce(n, vocab, k);
-        q.part_off = pc.part_off;
-        q.keys_off = pc.keys_off;
-        q.bytes = pc.bytes;
-        ReduceArgs a{out, false, ld, selected_ids ? selected_ids + r0 : nullptr, lse + r0,
-                     selected_ids ? selected_logprob + r0 : nullptr,
-                     k > 0 ? topk_ids + r0 * k : nullptr, k > 0 ? topk_logprobs + r0 * k : nullptr,
-                     ws_reduce, device_error};
-        st = from_hip(launch_reduce(q, a, s));
-        if (st != LMH_OK) return st;
-    }
-    return LMH_OK;
+lmh_status lmhead_logprobs_q(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                             int64_t hidden_dim, int64_t hidden_ld, const uint32_t* weight_q,
+                             int64_t weight_q_ld, const uint16_t* scales, const uint16_t* biases,
+                             int64_t scales_ld, int32_t bits, int32_t group_size, int64_t vocab,
+                             const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+                             const int32_t* logits_indices, int32_t num_indices,
+                             const int32_t* selected_ids, int32_t k, float* lse,
+                             float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+                             int32_t* logits_cu_seqlens, int32_t* gather_indices,
+                             int32_t chunk_rows, float* logits_debug, void* workspace,
+                             size_t workspace_bytes, int32_t* device_error, void* stream) {
+    return logprobs_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                         quant_weight(weight_q, weight_q_ld, scales, biases, scales_ld, bits,
+                                      group_size),
+                         vocab, cu_seqlens, num_segments, num_decode, logits_indices, num_indices,
+                         selected_ids, k, lse, selected_logprob, topk_ids, topk_logprobs,
+                         logits_cu_seqlens, gather_indices, chunk_rows, logits_debug, workspace,
+                         workspace_bytes, device_error, stream);
 }
 
 }  // extern "C"

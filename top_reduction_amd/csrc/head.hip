@@ -45,11 +45,27 @@ __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Affine group-quantised weights: token v, hidden index k, g = k >> gshift:
+//   W[v][k] = bf16( fma(scale[v][g], q(v, k), bias[v][g]) )
+// q(v, k) the unsigned BITS-bit code at bit k*BITS of row v of q (32-bit
+// words, little-endian), scale and bias bf16. The product of a bf16 and a
+// code of at most 8 bits is exact in fp32, so the only roundings are the fma's
+// and the final round to nearest even.
+struct QuantW {
+    const uint32_t* q;        // [V][qld] words
+    int64_t qld;
+    const uint16_t* scales;   // [V][sld]
+    const uint16_t* biases;   // [V][sld]
+    int64_t sld;
+    int32_t gshift;           // log2(group size)
+};
+
 struct HeadParams {
     const uint16_t* hidden;
     int64_t num_tokens, H, hld;
-    const uint16_t* W;
+    const uint16_t* W;        // bf16 weights (unused with quantised weights)
     int64_t V, wld;
+    QuantW qw;                // quantised weights (unused with bf16 weights)
     const int32_t* cu;
     int32_t num_decode;
     const int32_t* ex;
@@ -57,6 +73,61 @@ struct HeadParams {
     void* out;
     int64_t old;
 };
+
+// ---------------------------------------------------------------------------
+// Quantised-weight k order. One 16-byte run of codes (QB = 512/BITS hidden
+// elements: 128 for 4-bit, 64 for 8-bit) feeds SPB = QB/32 MFMA k-steps: in
+// step s of a run, lane quarter j (lanes 16j..16j+15) takes the 8 elements
+// starting at QB/4*j + 8*s, so each lane's codes for the whole run are one
+// contiguous 16-byte word group and every lane quarter stays inside one
+// quantisation group (group sizes 32..128). Both quantised kernels use this
+// order for the hidden operand too, so a row's logits are bitwise the same in
+// both; the sum over k is the same as the bf16 kernels' with the hidden
+// elements permuted accordingly.
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct QOrder {
+    static constexpr int QB = 512 / BITS;   // hidden elements per 16-byte code run
+    static constexpr int SPB = QB / 32;     // MFMA k-steps per run
+    static constexpr int QQ = QB / 4;       // elements per lane quarter per run
+};
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// 8 consecutive weights of a row from their codes (4-bit: the 8 nibbles of
+// w0; 8-bit: the bytes of w0 then w1), as an MFMA operand: dword j holds
+// elements 2j (low half) and 2j+1.
+template <int BITS>
+__device__ inline u32x4 dequant8(uint32_t w0, uint32_t w1, float s, float b) {
+    u32x4 r;
+    if constexpr (BITS == 4) {
+        // opaque masks keep the byte structure visible to the selector, so
+        // each code converts with one v_cvt_f32_ubyteN
+        uint32_t lo, hi;
+        asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w0));
+        asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w0 >> 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float e0 = (float)((lo >> (8 * j)) & 0xFFu);
+            const float e1 = (float)((hi >> (8 * j)) & 0xFFu);
+            r[j] = pack_bf16x2(fmaf(e0, s, b), fmaf(e1, s, b));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = j < 2 ? w0 : w1;
+            const float e0 = (float)((w >> (16 * (j & 1))) & 0xFFu);
+            const float e1 = (float)((w >> (16 * (j & 1) + 8)) & 0xFFu);
+            r[j] = pack_bf16x2(fmaf(e0, s, b), fmaf(e1, s, b));
+        }
+    }
+    return r;
+}
 
 template <bool OUT_BF16>
 __device__ inline void store_out(void* out, int64_t off, float v) {
@@ -231,6 +302,175 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Weight-streaming kernel for quantised weights: the structure of k_head_stream
+// (MT row tiles, 16*NT W rows per wave, k in chunks of KC staged through LDS
+// for the hidden rows) with the weights read as codes, one 16-byte run per
+// lane per QB hidden elements plus the lane's group scale and bias, and
+// dequantised to bf16 in registers right before their MFMAs. The hidden size
+// is a multiple of 128, so every run is whole; runs past the hidden size (in
+// the last chunk) are skipped.
+// ---------------------------------------------------------------------------
+template <int MT, int NT, int BITS, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void k_head_stream_q(HeadParams p) {
+    using O = QOrder<BITS>;
+    constexpr int KC = kStreamKC;       // hidden elements per chunk
+    constexpr int RPC = KC / O::QB;     // code runs per chunk
+    constexpr int AP = KC + 8;          // LDS row pitch (elements)
+    constexpr int ROWS = MT * 16;
+    constexpr int AVN = ROWS * KC / 8;
+    constexpr int AV = (AVN + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS][AP];
+    __shared__ int32_t sIdx[ROWS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t nbase = (int64_t)blockIdx.x * (64 * NT) + wave * (16 * NT);
+    const int l16 = lane & 15;
+    const int qd = lane >> 4;           // lane quarter
+
+    if (tid < ROWS)
+        sIdx[tid] = (tid < p.R) ? row_source(p.row0 + tid, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
+    __syncthreads();
+
+    const int nchunks = (int)((p.H + KC - 1) / KC);
+    const int nruns = (int)(p.H / O::QB);
+
+    int64_t a_off[AV];
+    int a_kv[AV];
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+        const int idx = j * kThreads + tid;
+        const bool in = (AVN % kThreads == 0) || idx < AVN;
+        const int row = in ? idx / (KC / 8) : 0;
+        const int32_t t = sIdx[row];
+        a_off[j] = (int64_t)(t >= 0 ? t : 0) * p.hld;
+        a_kv[j] = in ? (idx % (KC / 8)) * 8 : 0;
+    }
+    int64_t q_off[NT], s_off[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int64_t n = nbase + j * 16 + l16;
+        const int64_t nc = n < p.V ? n : p.V - 1;
+        q_off[j] = nc * p.qw.qld + 4 * qd;
+        s_off[j] = nc * p.qw.sld;
+    }
+
+    // hidden elements past H (last chunk) read element 0; their steps are skipped
+    auto load_a = [&](int c, u32x4 (&r)[AV]) {
+#pragma unroll
+        for (int j = 0; j < AV; ++j) {
+            const int64_t k = (int64_t)c * KC + a_kv[j];
+            r[j] = *reinterpret_cast<const u32x4*>(p.hidden + a_off[j] + (k < p.H ? k : 0));
+        }
+    };
+    auto store_a = [&](int buf, const u32x4 (&r)[AV]) {
+#pragma unroll
+        for (int j = 0; j < AV; ++j) {
+            const int idx = j * kThreads + tid;
+            if (AVN % kThreads == 0 || idx < AVN) {
+                const int row = idx / (KC / 8);
+                const int kv = idx % (KC / 8);
+                *reinterpret_cast<u32x4*>(&sA[buf][row][kv * 8]) = r[j];
+            }
+        }
+    };
+    struct WChunk {
+        u32x4 q[RPC][NT];
+        uint32_t sc[RPC][NT], bi[RPC][NT];
+    };
+    // runs past H read run 0
+    auto load_w = [&](int c, WChunk& w) {
+#pragma unroll
+        for (int u = 0; u < RPC; ++u) {
+            const int run = c * RPC + u;
+            const int rc = run < nruns ? run : 0;
+            const int g = (rc * O::QB + qd * O::QQ) >> p.qw.gshift;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                w.q[u][j] = *reinterpret_cast<const u32x4*>(p.qw.q + q_off[j] + (int64_t)rc * 16);
+                w.sc[u][j] = p.qw.scales[s_off[j] + g];
+                w.bi[u][j] = p.qw.biases[s_off[j] + g];
+            }
+        }
+    };
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 areg[AV];
+    WChunk w0, w1;
+    load_a(0, areg);
+    store_a(0, areg);
+    load_w(0, w0);
+    __syncthreads();
+
+    auto step = [&](int c, const WChunk& wc, WChunk& wn) {
+        const int buf = c & 1;
+        const bool more = (c + 1) < nchunks;
+        if (more) {
+            load_a(c + 1, areg);
+            load_w(c + 1, wn);
+        }
+#pragma unroll
+        for (int u = 0; u < RPC; ++u) {
+            if (c * RPC + u < nruns) {
+                float sf[NT], bf[NT];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    sf[j] = __uint_as_float(wc.sc[u][j] << 16);
+                    bf[j] = __uint_as_float(wc.bi[u][j] << 16);
+                }
+#pragma unroll
+                for (int st = 0; st < O::SPB; ++st) {
+                    u32x4 fb[NT];
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        const u32x4 qv = wc.q[u][j];
+                        if constexpr (BITS == 4)
+                            fb[j] = dequant8<4>(qv[st], 0u, sf[j], bf[j]);
+                        else
+                            fb[j] = dequant8<8>(qv[2 * st], qv[2 * st + 1], sf[j], bf[j]);
+                    }
+                    const int ka = u * O::QB + qd * O::QQ + 8 * st;
+#pragma unroll
+                    for (int i = 0; i < MT; ++i) {
+                        const u32x4 a = *reinterpret_cast<const u32x4*>(&sA[buf][i * 16 + l16][ka]);
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16(a, fb[j], acc[i][j]);
+                    }
+                }
+            }
+        }
+        if (more) store_a(buf ^ 1, areg);
+        __syncthreads();
+    };
+    for (int c = 0; c < nchunks; c += 2) {
+        step(c, w0, w1);
+        if (c + 1 < nchunks) step(c + 1, w1, w0);
+    }
+
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int64_t v = nbase + j * 16 + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = i * 16 + (lane >> 4) * 4 + e;
+                if (r < p.R && v < p.V) {
+                    const float val = sIdx[r] < 0 ? kNaN : acc[i][j][e];
+                    store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v, val);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Tiled kernel: a 256 x 256 output tile per workgroup of 8 waves, one 128 x 64
 // eighth per wave (8 x 4 MFMA tiles). k advances in stages of 32 (one MFMA
 // k-step). Each stage's A (gathered hidden rows) and B (W rows) slices, 256 x
@@ -254,9 +494,31 @@ constexpr int kTileLB = kTileN * 4 / kTileThreads;             // B chunks per t
 constexpr int kTileStage = (kTileM + kTileN) * kTileK * 2;     // bytes per LDS stage
 constexpr int kTileLds = 72 * 1024 + kTileM * 4;               // 2 stages / epilogue staging + row sources
 
-template <bool OUT_BF16>
+// Staging registers of one stage's B slice: bf16 chunks, or the codes of the
+// same elements with their group's scale and bias (dequantised on the way
+// into LDS).
+template <int BITS>
+struct TileB {
+    u32x4 v[kTileLB];
+};
+template <>
+struct TileB<4> {
+    uint32_t q[kTileLB], sc[kTileLB], bi[kTileLB];
+};
+template <>
+struct TileB<8> {
+    uint32_t q0[kTileLB], q1[kTileLB], sc[kTileLB], bi[kTileLB];
+};
+
+// BITS = 16: bf16 weights; 4 or 8: quantised weights (hidden size a multiple
+// of 128), whose stages follow the quantised k order: stage st is k-step
+// st % SPB of code run st / SPB, and LDS chunk c of a row holds the 8
+// elements of lane quarter c.
+template <bool OUT_BF16, int BITS>
 __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
+    constexpr bool QUANT = BITS != 16;
+    using O = QOrder<QUANT ? BITS : 4>;
     constexpr int NF = kWaveN / 16;                 // B fragments (16-column groups) per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int32_t* sIdx = reinterpret_cast<int32_t*>(lds + 72 * 1024);
@@ -287,20 +549,26 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
 
     // this thread's staging chunks: rows tid/4 + 128j, chunk tid%4
     const int c = tid & 3;
-    int64_t ga[kTileLA], gb[kTileLB];               // element offsets of the chunks at k = 0
+    int64_t ga[kTileLA], gb[kTileLB], gs[kTileLB];  // offsets of the chunks at k = 0
     uint32_t wofs[kTileLA];                         // LDS byte offsets within a stage's A slice
 #pragma unroll
     for (int j = 0; j < kTileLA; ++j) {
         const int row = (tid >> 2) + 128 * j;
         const int32_t t = sIdx[row];
-        ga[j] = (int64_t)(t < 0 ? 0 : t) * p.hld + c * 8;
+        ga[j] = (int64_t)(t < 0 ? 0 : t) * p.hld + (QUANT ? c * O::QQ : c * 8);
         wofs[j] = (uint32_t)(row * 64 + ((c ^ ((row >> 1) & 3)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < kTileLB; ++j) {
         const int row = (tid >> 2) + 128 * j;
         const int64_t n = n0 + row < p.V ? n0 + row : p.V - 1;
-        gb[j] = n * p.wld + c * 8;
+        if constexpr (QUANT) {
+            gb[j] = n * p.qw.qld + 4 * c;           // words of lane quarter c in run 0
+            gs[j] = n * p.qw.sld;
+        } else {
+            gb[j] = n * p.wld + c * 8;
+            gs[j] = 0;
+        }
     }
     // fragment read offset: row l%16 of a 16-row group, chunk l/16
     const int fr = lane & 15;
@@ -313,23 +581,58 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
 
     // chunks past H (the padding stages, or the tail of a last partial one)
     // load from k = 0 and are zeroed when written to LDS
-    auto gload = [&](int st, u32x4 (&ra)[kTileLA], u32x4 (&rb)[kTileLB]) {
-        const int64_t k0 = (int64_t)st * kTileK;
-        const int64_t k = k0 + c * 8 + 8 <= p.H ? k0 : 0;
+    auto gload = [&](int st, u32x4 (&ra)[kTileLA], TileB<BITS>& rb) {
+        if constexpr (!QUANT) {
+            const int64_t k0 = (int64_t)st * kTileK;
+            const int64_t k = k0 + c * 8 + 8 <= p.H ? k0 : 0;
 #pragma unroll
-        for (int j = 0; j < kTileLA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(p.hidden + ga[j] + k);
+            for (int j = 0; j < kTileLA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(p.hidden + ga[j] + k);
 #pragma unroll
-        for (int j = 0; j < kTileLB; ++j) rb[j] = *reinterpret_cast<const u32x4*>(p.W + gb[j] + k);
+            for (int j = 0; j < kTileLB; ++j) rb.v[j] = *reinterpret_cast<const u32x4*>(p.W + gb[j] + k);
+        } else {
+            // whole stages only (H is a multiple of 128); stages past H read run 0
+            const bool in = (int64_t)st * kTileK < p.H;
+            const int run = in ? st / O::SPB : 0;
+            const int sub = st % O::SPB;
+            const int64_t k = (int64_t)run * O::QB + 8 * sub;
+            const int g = (run * O::QB + c * O::QQ) >> p.qw.gshift;
+#pragma unroll
+            for (int j = 0; j < kTileLA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(p.hidden + ga[j] + k);
+#pragma unroll
+            for (int j = 0; j < kTileLB; ++j) {
+                const uint32_t* qp = p.qw.q + gb[j] + (int64_t)run * 16;
+                if constexpr (BITS == 4) {
+                    rb.q[j] = qp[sub];
+                } else {
+                    const uint2 w = *reinterpret_cast<const uint2*>(qp + 2 * sub);
+                    rb.q0[j] = w.x;
+                    rb.q1[j] = w.y;
+                }
+                rb.sc[j] = p.qw.scales[gs[j] + g];
+                rb.bi[j] = p.qw.biases[gs[j] + g];
+            }
+        }
     };
-    auto lwrite = [&](int buf, int st, const u32x4 (&ra)[kTileLA], const u32x4 (&rb)[kTileLB]) {
+    auto lwrite = [&](int buf, int st, const u32x4 (&ra)[kTileLA], const TileB<BITS>& rb) {
         uint8_t* base = lds + buf * kTileStage;
-        const bool z = (int64_t)st * kTileK + c * 8 + 8 > p.H;
+        const bool z = QUANT ? (int64_t)st * kTileK >= p.H : (int64_t)st * kTileK + c * 8 + 8 > p.H;
         const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < kTileLA; ++j) *reinterpret_cast<u32x4*>(base + wofs[j]) = z ? zero : ra[j];
 #pragma unroll
-        for (int j = 0; j < kTileLB; ++j)
-            *reinterpret_cast<u32x4*>(base + kTileM * 64 + wofs[j]) = z ? zero : rb[j];
+        for (int j = 0; j < kTileLB; ++j) {
+            u32x4 b;
+            if constexpr (!QUANT) {
+                b = rb.v[j];
+            } else {
+                const float sf = __uint_as_float(rb.sc[j] << 16), bf = __uint_as_float(rb.bi[j] << 16);
+                if constexpr (BITS == 4)
+                    b = dequant8<4>(rb.q[j], 0u, sf, bf);
+                else
+                    b = dequant8<8>(rb.q0[j], rb.q1[j], sf, bf);
+            }
+            *reinterpret_cast<u32x4*>(base + kTileM * 64 + wofs[j]) = z ? zero : b;
+        }
     };
     f32x4 acc[8][NF];
 #pragma unroll
@@ -357,7 +660,8 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
     // stage s is multiplied from LDS buffer s%2 while stage s+1 is written to
     // the other buffer from register set (s+1)%3 and stage s+3 is loaded into
     // set s%3
-    u32x4 ra0[kTileLA], rb0[kTileLB], ra1[kTileLA], rb1[kTileLB], ra2[kTileLA], rb2[kTileLB];
+    u32x4 ra0[kTileLA], ra1[kTileLA], ra2[kTileLA];
+    TileB<BITS> rb0, rb1, rb2;
     gload(0, ra0, rb0);
     gload(1, ra1, rb1);
     gload(2, ra2, rb2);
@@ -506,6 +810,12 @@ HeadParams to_params(const HeadArgs& a) {
     p.R = a.rows;
     p.out = a.out;
     p.old = a.out_ld;
+    p.qw.q = a.q;
+    p.qw.qld = a.q_ld;
+    p.qw.scales = a.scales;
+    p.qw.biases = a.biases;
+    p.qw.sld = a.s_ld;
+    p.qw.gshift = a.gshift;
     return p;
 }
 
@@ -535,14 +845,15 @@ hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s) {
     }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int BITS>
 hipError_t launch_tiled(const HeadParams& p, int32_t mtiles, int32_t ntiles, hipStream_t s) {
-    const void* fn = (const void*)k_head_tiled<OUT_BF16>;
+    const void* fn = (const void*)k_head_tiled<OUT_BF16, BITS>;
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kTileLds);
     if (e != hipSuccess) return e;
     const int64_t total = (int64_t)mtiles * ntiles;
     const dim3 grid((unsigned)(((total + 7) / 8) * 8));
-    hipLaunchKernelGGL((k_head_tiled<OUT_BF16>), grid, dim3(kTileThreads), kTileLds, s, p, mtiles, ntiles);
+    hipLaunchKernelGGL((k_head_tiled<OUT_BF16, BITS>), grid, dim3(kTileThreads), kTileLds, s, p, mtiles,
+                       ntiles);
     return hipGetLastError();
 }
 
@@ -551,7 +862,48 @@ hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
     const HeadParams p = to_params(a);
     const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
     const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
-    return a.out_bf16 ? launch_tiled<true>(p, mtiles, ntiles, s) : launch_tiled<false>(p, mtiles, ntiles, s);
+    return a.out_bf16 ? launch_tiled<true, 16>(p, mtiles, ntiles, s) : launch_tiled<false, 16>(p, mtiles, ntiles, s);
+}
+
+template <int MT, int BITS, bool OUT_BF16>
+hipError_t launch_stream_q_mt(const HeadParams& p, hipStream_t s) {
+    constexpr int NT = kStreamNT;
+    const dim3 grid((unsigned)((p.V + 64 * NT - 1) / (64 * NT)));
+    hipLaunchKernelGGL((k_head_stream_q<MT, NT, BITS, OUT_BF16>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_stream_q_bits(const HeadArgs& a, const HeadParams& p, hipStream_t s) {
+    switch ((a.rows + 15) / 16) {
+        case 1: return a.out_bf16 ? launch_stream_q_mt<1, BITS, true>(p, s) : launch_stream_q_mt<1, BITS, false>(p, s);
+        case 2: return a.out_bf16 ? launch_stream_q_mt<2, BITS, true>(p, s) : launch_stream_q_mt<2, BITS, false>(p, s);
+        case 3: return a.out_bf16 ? launch_stream_q_mt<3, BITS, true>(p, s) : launch_stream_q_mt<3, BITS, false>(p, s);
+        case 4: return a.out_bf16 ? launch_stream_q_mt<4, BITS, true>(p, s) : launch_stream_q_mt<4, BITS, false>(p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_head_stream_q(const HeadArgs& a, hipStream_t s) {
+    if (a.rows <= 0) return hipSuccess;
+    if (a.rows > kStreamMaxRows || a.hidden_dim % 128) return hipErrorInvalidValue;
+    const HeadParams p = to_params(a);
+    if (a.bits == 4) return launch_stream_q_bits<4>(a, p, s);
+    if (a.bits == 8) return launch_stream_q_bits<8>(a, p, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_head_tiled_q(const HeadArgs& a, hipStream_t s) {
+    if (a.rows <= 0) return hipSuccess;
+    if (a.hidden_dim % 128) return hipErrorInvalidValue;
+    const HeadParams p = to_params(a);
+    const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
+    const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
+    if (a.bits == 4)
+        return a.out_bf16 ? launch_tiled<true, 4>(p, mtiles, ntiles, s) : launch_tiled<false, 4>(p, mtiles, ntiles, s);
+    if (a.bits == 8)
+        return a.out_bf16 ? launch_tiled<true, 8>(p, mtiles, ntiles, s) : launch_tiled<false, 8>(p, mtiles, ntiles, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_head_f32(const HeadArgs& a, hipStream_t s) {

@@ -86,10 +86,24 @@ struct HeadArgs {
     int64_t out_ld;
     bool out_bf16;
     int32_t* err;
+    // affine group-quantised weights (weight is then unused): codes of `bits`
+    // bits packed in 32-bit words [vocab][q_ld], bf16 scale and bias per group
+    // [vocab][s_ld], group = 1 << gshift
+    int32_t bits = 16;
+    const uint32_t* q = nullptr;
+    int64_t q_ld = 0;
+    const uint16_t* scales = nullptr;
+    const uint16_t* biases = nullptr;
+    int64_t s_ld = 0;
+    int32_t gshift = 0;
 };
 // bf16 MFMA heads. stream: R <= kStreamMaxRows; tiled: any R.
 hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s);
 hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s);
+// The same two kernels over quantised weights (bits 4 or 8, hidden size a
+// multiple of 128, group 32, 64 or 128), dequantised to bf16 on the fly.
+hipError_t launch_head_stream_q(const HeadArgs& a, hipStream_t s);
+hipError_t launch_head_tiled_q(const HeadArgs& a, hipStream_t s);
 // fp32 FMA head.
 hipError_t launch_head_f32(const HeadArgs& a, hipStream_t s);
 
