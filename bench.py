@@ -19,6 +19,8 @@ The same line carries:
   decode        32 x 151,936 decode rows, K = 5 (openinfer issue #719);
   head          Qwen3-0.6B-shaped selective head (40 of 81,920 rows) and the
                 full 2048-row projection (vllm-metal release, Benchmarks);
+  headq         the same head with 4- and 8-bit group-quantised weights
+                (mlxcel PR #1969: the measured models are 4-bit);
   fused         Llama-3-8B-shaped fused head + logprobs, mixed batch and a
                 1024-token prompt in 256-row chunks.
 
@@ -96,7 +98,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sections", default="reduce,decode,head,fused,cpu")
+    ap.add_argument("--sections", default="reduce,decode,head,headq,fused,cpu")
     ap.add_argument("--k", type=int, default=20)
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
@@ -362,6 +364,62 @@ def main():
                               "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4)},
         }
         del hid, w, full, out
+
+    # ------------------------------------------------------------------
+    # quantised selective head (Qwen3-0.6B shape, 4- and 8-bit codes, group 64)
+    # ------------------------------------------------------------------
+    if "headq" in sections:
+        d = synth.selective_head_batch(7200, vocab=16)      # the packed hidden rows only
+        hid = lmh_bf16(torch, d["hidden"], dev)
+        cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
+        T, H = d["hidden"].shape
+        Vq, R, G = synth.VOCAB_QWEN3, 40, 64
+        out = torch.empty((R, Vq), device=dev)
+        full_idx = torch.arange(2048, dtype=torch.int32, device=dev)
+        full = torch.empty((2048, Vq), device=dev)
+        result["headq"] = {}
+        for bits in (4, 8):
+            qd = synth.quantized_head(7250 + bits, Vq, H, bits, G)
+            q = torch.from_numpy(qd["q"].view(np.int32)).to(dev)
+            sc = lmh_bf16(torch, qd["scales"], dev)
+            bi = lmh_bf16(torch, qd["biases"], dev)
+            qld, sld = q.shape[1], sc.shape[1]
+
+            def sel_q(q=q, sc=sc, bi=bi, qld=qld, sld=sld, bits=bits):
+                return L.lmhead_gather_project_q(vp(hid), lmh.LMH_BF16, T, H, H, vp(q), qld, vp(sc),
+                                                 vp(bi), sld, bits, G, Vq, vp(cu), R, 0, None, 0,
+                                                 vp(out), lmh.LMH_F32, Vq, None, None, None, stream)
+
+            def full_q(q=q, sc=sc, bi=bi, qld=qld, sld=sld, bits=bits):
+                return L.lmhead_gather_project_q(vp(hid), lmh.LMH_BF16, T, H, H, vp(q), qld, vp(sc),
+                                                 vp(bi), sld, bits, G, Vq, vp(cu), R, 0, vp(full_idx),
+                                                 2048, vp(full), lmh.LMH_F32, Vq, None, None, None,
+                                                 stream)
+            assert sel_q() == 0 and full_q() == 0
+            tk = timer.loop_median([sel_q], max(steps // 4, 10), warmup)
+            qbytes = Vq * H * bits // 8 + Vq * (H // G) * 4 + R * H * 2 + R * Vq * 4
+            ach = qbytes / (tk * 1e-3) / 1e9
+            tf = timer.loop([full_q], max(steps // 20, 5), 2)
+            tfl = 2.0 * 2048 * H * Vq / (tf * 1e-3) / 1e12
+            log(f"quantised head {bits}-bit: selective {tk * 1e3:.1f} us -> {ach:.0f} GB/s; "
+                f"full 2048 rows {tf * 1e3:.1f} us -> {tfl:.0f} TFLOP/s")
+            result["headq"][f"q{bits}"] = {
+                "workload": f"Qwen3-0.6B head, {bits}-bit codes, group {G}, bf16 scale+bias: 40 of "
+                            "81920 packed rows, fp32 logits",
+                "selective_kernel_us": round(tk * 1e3, 2),
+                "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                             "bytes_per_launch": qbytes,
+                             "traffic": load_traffic(f"head_stream_q{bits}",
+                                                     os.path.join(ROOT, "top_reduction_amd", "csrc",
+                                                                  "head.hip"))},
+                "full_2048_ms": round(tf, 4),
+                "full_roofline": {"bound": "mfma", "achieved": round(tfl, 1),
+                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tfl / BF16_PEAK_TFLOPS, 4)},
+            }
+            del q, sc, bi
+        del hid, out, full
 
     # ------------------------------------------------------------------
     # fused head + logprobs (Llama-3-8B shape)

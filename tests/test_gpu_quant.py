@@ -82,20 +82,26 @@ def _check_vs_oracle(z, hid_bits, idx, W_exact):
 
 CASES = [  # (bits, group, H, V)
     (4, 64, 256, 1000), (4, 32, 384, 1001), (4, 128, 128, 4096), (4, 64, 1024, 2053),
-    (8, 64, 256, 1000), (8, 32, 128, 777), (8, 128, 640, 3000),
+    (4, 32, 512, 999), (4, 128, 768, 1500),
+    (8, 64, 256, 1000), (8, 32, 128, 777), (8, 128, 640, 3000), (8, 32, 512, 2001),
+    (8, 128, 1024, 1024),
 ]
 
 
+@pytest.mark.parametrize("s_pad", [2, 3])
 @pytest.mark.parametrize("variant", [lmh.LMH_HEAD_STREAM, lmh.LMH_HEAD_TILED])
 @pytest.mark.parametrize("bits,group,H,V", CASES)
-def test_quant_head_vs_oracle(bits, group, H, V, variant):
+def test_quant_head_vs_oracle(bits, group, H, V, variant, s_pad):
     """Sampled mode over decode and prefill segments, ragged vocab tails,
-    hidden sizes with a partial last chunk (384, 640), both kernels."""
+    hidden sizes with a partial last chunk (384, 640), both kernels; an even
+    and an odd scale row pitch (the streaming kernel reads a chunk's scales
+    with one vector load when the pitch is even and the hidden size a
+    multiple of 256, one value at a time otherwise)."""
     g = synth.rng(bits * 1000 + group + H + V)
     cu = synth.packed_cu_seqlens(5, [3, 40, 1, 17, 9])
     T = int(cu[-1])
     hid = synth.normal_bf16(g, (T, H))
-    d = synth.quantized_head(bits * 7 + H, V, H, bits, group, q_pad_words=4, s_pad=3)
+    d = synth.quantized_head(bits * 7 + H, V, H, bits, group, q_pad_words=4, s_pad=s_pad)
     p = lmh.lmhead_gather_project_q(bf16_tensor(hid), _qweight(d), i32_tensor(cu), 5, variant=variant)
     st, idx, lcu = oracle.rows(cu, 5, T)
     torch.cuda.synchronize()

@@ -20,6 +20,8 @@
 //           workgroups are mapped so that each XCD walks the row tiles of one
 //           W slab together.
 //   f32     fp32 operands: plain fp32 FMA in ascending k.
+#include <type_traits>
+
 #include "lmh_internal.h"
 
 namespace lmh {
@@ -32,13 +34,29 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr float kNaN = __builtin_nanf("");
 #ifndef LMH_STREAM_NT
-#define LMH_STREAM_NT 2
+#define LMH_STREAM_NT 1
 #endif
 #ifndef LMH_STREAM_KC
 #define LMH_STREAM_KC 256
 #endif
+#ifndef LMH_STREAM_WAVES
+#define LMH_STREAM_WAVES 4
+#endif
+#ifndef LMH_STREAMQ_NT
+#define LMH_STREAMQ_NT 1
+#endif
+#ifndef LMH_STREAMQ_KC
+#define LMH_STREAMQ_KC 256
+#endif
 constexpr int kStreamNT = LMH_STREAM_NT;   // 16-row W tiles per wave in the streaming head
 constexpr int kStreamKC = LMH_STREAM_KC;   // hidden elements per streaming-head k-chunk
+constexpr int kStreamThreads = 64 * LMH_STREAM_WAVES;    // threads per streaming-head workgroup
+#ifndef LMH_STREAMQ_WAVES
+#define LMH_STREAMQ_WAVES 8
+#endif
+constexpr int kStreamQNT = LMH_STREAMQ_NT; // the same for quantised weights
+constexpr int kStreamQKC = LMH_STREAMQ_KC;
+constexpr int kStreamQThreads = 64 * LMH_STREAMQ_WAVES;   // threads per quantised-stream workgroup
 
 __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -137,6 +155,29 @@ __device__ inline void store_out(void* out, int64_t off, float v) {
         reinterpret_cast<float*>(out)[off] = v;
 }
 
+// Drives step(PF, c, current, next) over chunks 0..n-1 with two weight
+// register sets that alternate without copies (a copy of a prefetch
+// destination would wait for the prefetch). Inside the loop every step
+// prefetches, so the loop header is reached with the same loads in flight on
+// every path and the wait counts stay exact; the last one or two steps, the
+// last of which prefetches nothing, are peeled after it.
+template <typename Step, typename W>
+__device__ inline void chunk_loop(int n, Step& step, W& w0, W& w1) {
+    using Y = std::integral_constant<bool, true>;
+    using N = std::integral_constant<bool, false>;
+    int c = 0;
+    for (; c + 2 < n; c += 2) {
+        step(Y{}, c, w0, w1);
+        step(Y{}, c + 1, w1, w0);
+    }
+    if (c + 1 < n) {
+        step(Y{}, c, w0, w1);
+        step(N{}, c + 1, w1, w0);
+    } else {
+        step(N{}, c, w0, w1);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel: MT row tiles of 16 (R <= 16*MT) against a slab of
 // 64*NT W rows per workgroup (16*NT per wave), k in chunks of 128. Each wave
@@ -146,20 +187,21 @@ __device__ inline void store_out(void* out, int64_t off, float v) {
 // short.
 // ---------------------------------------------------------------------------
 template <int MT, int NT, bool KFULL, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
+__global__ __launch_bounds__(kStreamThreads) void k_head_stream(HeadParams p) {
     constexpr int KC = kStreamKC;       // hidden elements per chunk
     constexpr int KS = KC / 32;         // MFMA k-steps per chunk
     constexpr int AP = KC + 8;          // LDS row pitch (elements): +16 B breaks bank aliasing
     constexpr int ROWS = MT * 16;
     constexpr int AVN = ROWS * KC / 8;                      // 16-B A vectors per chunk
-    constexpr int AV = (AVN + kThreads - 1) / kThreads;     // ... per thread
+    constexpr int TPB = kStreamThreads;
+    constexpr int AV = (AVN + TPB - 1) / TPB;               // ... per thread
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS][AP];
     __shared__ int32_t sIdx[ROWS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t nbase = (int64_t)blockIdx.x * (64 * NT) + wave * (16 * NT);
+    const int64_t nbase = (int64_t)blockIdx.x * (TPB / 4 * NT) + wave * (16 * NT);
     const int l16 = lane & 15;
     const int kq = (lane >> 4) * 8;
 
@@ -178,8 +220,8 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
     int a_kv[AV];         // its 8-element column group within a chunk
 #pragma unroll
     for (int j = 0; j < AV; ++j) {
-        const int idx = j * kThreads + tid;
-        const bool in = (AVN % kThreads == 0) || idx < AVN;
+        const int idx = j * TPB + tid;
+        const bool in = (AVN % TPB == 0) || idx < AVN;
         const int row = in ? idx / (KC / 8) : 0;
         const int32_t t = sIdx[row];
         a_off[j] = (int64_t)(t >= 0 ? t : 0) * p.hld;
@@ -213,8 +255,8 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
     auto store_a = [&](int buf, const u32x4 (&r)[AV]) {
 #pragma unroll
         for (int j = 0; j < AV; ++j) {
-            const int idx = j * kThreads + tid;
-            if (AVN % kThreads == 0 || idx < AVN) {
+            const int idx = j * TPB + tid;
+            if (AVN % TPB == 0 || idx < AVN) {
                 const int row = idx / (KC / 8);
                 const int kv = idx % (KC / 8);
                 *reinterpret_cast<u32x4*>(&sA[buf][row][kv * 8]) = r[j];
@@ -251,16 +293,19 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
     load_w(0, w0);
     __syncthreads();
 
-    // one k-chunk: prefetch the next chunk's A and W, multiply this one
-    auto step = [&](int c, const u32x4 (&wc)[KS][NT], u32x4 (&wn)[KS][NT]) {
+    // one k-chunk: prefetch the next chunk's A and W (PF: every step but the
+    // last), multiply this one
+    auto step = [&](auto PF, int c, const u32x4 (&wc)[KS][NT], u32x4 (&wn)[KS][NT]) {
         const int buf = c & 1;
-        const bool more = (c + 1) < nchunks;
-        if (more) {
+        if constexpr (decltype(PF)::value) {
             // A first: its loads are consumed at the end of this step, and
             // memory counters retire in issue order, so waiting for them must
             // not also wait for the weight prefetch issued after them
             load_a(c + 1, areg);
+            __builtin_amdgcn_sched_barrier(0);
             load_w(c + 1, wn);
+            // keep the whole prefetch at the top of the step, A first
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -273,15 +318,10 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
                 }
             }
         }
-        if (more) store_a(buf ^ 1, areg);
+        if constexpr (decltype(PF)::value) store_a(buf ^ 1, areg);
         __syncthreads();
     };
-    // unrolled by two so the weight buffers alternate without register copies
-    // (a copy of a prefetch destination would wait for the prefetch)
-    for (int c = 0; c < nchunks; c += 2) {
-        step(c, w0, w1);
-        if (c + 1 < nchunks) step(c + 1, w1, w0);
-    }
+    chunk_loop(nchunks, step, w0, w1);
 
     // D fragment: lane holds rows 4*(lane/16)+e of column lane%16
 #pragma unroll
@@ -310,22 +350,27 @@ __global__ __launch_bounds__(kThreads) void k_head_stream(HeadParams p) {
 // is a multiple of 128, so every run is whole; runs past the hidden size (in
 // the last chunk) are skipped.
 // ---------------------------------------------------------------------------
-template <int MT, int NT, int BITS, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void k_head_stream_q(HeadParams p) {
+// NG > 0: the chunk's NG group scales (and biases) of a W row are read with
+// one vector load per lane (the hidden size is a multiple of KC = NG * group
+// and the scale row pitch is even); NG = 0: one 2-byte load per run and lane.
+template <int MT, int NT, int BITS, int NG, bool OUT_BF16>
+__global__ __launch_bounds__(kStreamQThreads) void k_head_stream_q(HeadParams p) {
     using O = QOrder<BITS>;
-    constexpr int KC = kStreamKC;       // hidden elements per chunk
+    constexpr int KC = kStreamQKC;      // hidden elements per chunk
     constexpr int RPC = KC / O::QB;     // code runs per chunk
+    constexpr int ND = NG > 0 ? NG / 2 : 1;   // scale dwords per chunk and row
     constexpr int AP = KC + 8;          // LDS row pitch (elements)
     constexpr int ROWS = MT * 16;
     constexpr int AVN = ROWS * KC / 8;
-    constexpr int AV = (AVN + kThreads - 1) / kThreads;
+    constexpr int TPB = kStreamQThreads;
+    constexpr int AV = (AVN + TPB - 1) / TPB;
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS][AP];
     __shared__ int32_t sIdx[ROWS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t nbase = (int64_t)blockIdx.x * (64 * NT) + wave * (16 * NT);
+    const int64_t nbase = (int64_t)blockIdx.x * (TPB / 4 * NT) + wave * (16 * NT);
     const int l16 = lane & 15;
     const int qd = lane >> 4;           // lane quarter
 
@@ -340,8 +385,8 @@ __global__ __launch_bounds__(kThreads) void k_head_stream_q(HeadParams p) {
     int a_kv[AV];
 #pragma unroll
     for (int j = 0; j < AV; ++j) {
-        const int idx = j * kThreads + tid;
-        const bool in = (AVN % kThreads == 0) || idx < AVN;
+        const int idx = j * TPB + tid;
+        const bool in = (AVN % TPB == 0) || idx < AVN;
         const int row = in ? idx / (KC / 8) : 0;
         const int32_t t = sIdx[row];
         a_off[j] = (int64_t)(t >= 0 ? t : 0) * p.hld;
@@ -367,32 +412,56 @@ __global__ __launch_bounds__(kThreads) void k_head_stream_q(HeadParams p) {
     auto store_a = [&](int buf, const u32x4 (&r)[AV]) {
 #pragma unroll
         for (int j = 0; j < AV; ++j) {
-            const int idx = j * kThreads + tid;
-            if (AVN % kThreads == 0 || idx < AVN) {
+            const int idx = j * TPB + tid;
+            if (AVN % TPB == 0 || idx < AVN) {
                 const int row = idx / (KC / 8);
                 const int kv = idx % (KC / 8);
                 *reinterpret_cast<u32x4*>(&sA[buf][row][kv * 8]) = r[j];
             }
         }
     };
+    // scale and bias stay 16-bit (or packed pairs) until used: a widening at
+    // the loop back-edge would wait for the prefetch
+    typedef uint32_t u32v __attribute__((ext_vector_type(ND), aligned(4)));
     struct WChunk {
         u32x4 q[RPC][NT];
-        uint32_t sc[RPC][NT], bi[RPC][NT];
+        uint16_t sc[RPC][NT], bi[RPC][NT];      // NG == 0
+        u32v sv[NT], bv[NT];                    // NG > 0: groups c*NG .. c*NG+NG-1
     };
-    // runs past H read run 0
+    // runs past H read run 0 (NG == 0 only; with NG > 0 every chunk is whole)
     auto load_w = [&](int c, WChunk& w) {
 #pragma unroll
         for (int u = 0; u < RPC; ++u) {
             const int run = c * RPC + u;
-            const int rc = run < nruns ? run : 0;
-            const int g = (rc * O::QB + qd * O::QQ) >> p.qw.gshift;
+            const int rc = NG > 0 ? run : (run < nruns ? run : 0);
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
+            for (int j = 0; j < NT; ++j)
                 w.q[u][j] = *reinterpret_cast<const u32x4*>(p.qw.q + q_off[j] + (int64_t)rc * 16);
-                w.sc[u][j] = p.qw.scales[s_off[j] + g];
-                w.bi[u][j] = p.qw.biases[s_off[j] + g];
+            if constexpr (NG == 0) {
+                const int g = (rc * O::QB + qd * O::QQ) >> p.qw.gshift;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    w.sc[u][j] = p.qw.scales[s_off[j] + g];
+                    w.bi[u][j] = p.qw.biases[s_off[j] + g];
+                }
             }
         }
+        if constexpr (NG > 0) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                w.sv[j] = *reinterpret_cast<const u32v*>(p.qw.scales + s_off[j] + c * NG);
+                w.bv[j] = *reinterpret_cast<const u32v*>(p.qw.biases + s_off[j] + c * NG);
+            }
+        }
+    };
+    // fp32 value of the group scale (or bias) of run u for this lane
+    auto pick = [&](const u32v& v, int u) -> float {
+        constexpr int G = NG > 0 ? KC / NG : 1;
+        const int e = (u * O::QB + qd * O::QQ) / G;     // group within the chunk
+        uint32_t d = v[0];
+#pragma unroll
+        for (int i = 1; i < ND; ++i) d = (e >> 1) == i ? v[i] : d;
+        return __uint_as_float((e & 1) ? (d & 0xFFFF0000u) : (d << 16));
     };
 
     f32x4 acc[MT][NT];
@@ -408,12 +477,15 @@ __global__ __launch_bounds__(kThreads) void k_head_stream_q(HeadParams p) {
     load_w(0, w0);
     __syncthreads();
 
-    auto step = [&](int c, const WChunk& wc, WChunk& wn) {
+    // PF: this step prefetches the next chunk (every step but the last)
+    auto step = [&](auto PF, int c, const WChunk& wc, WChunk& wn) {
         const int buf = c & 1;
-        const bool more = (c + 1) < nchunks;
-        if (more) {
+        if constexpr (decltype(PF)::value) {
             load_a(c + 1, areg);
+            __builtin_amdgcn_sched_barrier(0);
             load_w(c + 1, wn);
+            // keep the whole prefetch at the top of the step, A first
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int u = 0; u < RPC; ++u) {
@@ -421,8 +493,13 @@ __global__ __launch_bounds__(kThreads) void k_head_stream_q(HeadParams p) {
                 float sf[NT], bf[NT];
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
-                    sf[j] = __uint_as_float(wc.sc[u][j] << 16);
-                    bf[j] = __uint_as_float(wc.bi[u][j] << 16);
+                    if constexpr (NG > 0) {
+                        sf[j] = pick(wc.sv[j], u);
+                        bf[j] = pick(wc.bv[j], u);
+                    } else {
+                        sf[j] = __uint_as_float((uint32_t)wc.sc[u][j] << 16);
+                        bf[j] = __uint_as_float((uint32_t)wc.bi[u][j] << 16);
+                    }
                 }
 #pragma unroll
                 for (int st = 0; st < O::SPB; ++st) {
@@ -445,13 +522,10 @@ __global__ __launch_bounds__(kThreads) void k_head_stream_q(HeadParams p) {
                 }
             }
         }
-        if (more) store_a(buf ^ 1, areg);
+        if constexpr (decltype(PF)::value) store_a(buf ^ 1, areg);
         __syncthreads();
     };
-    for (int c = 0; c < nchunks; c += 2) {
-        step(c, w0, w1);
-        if (c + 1 < nchunks) step(c + 1, w1, w0);
-    }
+    chunk_loop(nchunks, step, w0, w1);
 
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -503,11 +577,13 @@ struct TileB {
 };
 template <>
 struct TileB<4> {
-    uint32_t q[kTileLB], sc[kTileLB], bi[kTileLB];
+    uint32_t q[kTileLB];
+    uint16_t sc[kTileLB], bi[kTileLB];
 };
 template <>
 struct TileB<8> {
-    uint32_t q0[kTileLB], q1[kTileLB], sc[kTileLB], bi[kTileLB];
+    uint32_t q0[kTileLB], q1[kTileLB];
+    uint16_t sc[kTileLB], bi[kTileLB];
 };
 
 // BITS = 16: bf16 weights; 4 or 8: quantised weights (hidden size a multiple
@@ -625,7 +701,8 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
             if constexpr (!QUANT) {
                 b = rb.v[j];
             } else {
-                const float sf = __uint_as_float(rb.sc[j] << 16), bf = __uint_as_float(rb.bi[j] << 16);
+                const float sf = __uint_as_float((uint32_t)rb.sc[j] << 16);
+                const float bf = __uint_as_float((uint32_t)rb.bi[j] << 16);
                 if constexpr (BITS == 4)
                     b = dequant8<4>(rb.q[j], 0u, sf, bf);
                 else
@@ -824,11 +901,12 @@ HeadParams to_params(const HeadArgs& a) {
 template <int MT, bool OUT_BF16>
 hipError_t launch_stream_mt(const HeadParams& p, hipStream_t s) {
     constexpr int NT = kStreamNT;
-    const dim3 grid((unsigned)((p.V + 64 * NT - 1) / (64 * NT)));
+    constexpr int SLAB = kStreamThreads / 4 * NT;    // W rows per workgroup
+    const dim3 grid((unsigned)((p.V + SLAB - 1) / SLAB));
     if (p.H % kStreamKC == 0)
-        hipLaunchKernelGGL((k_head_stream<MT, NT, true, OUT_BF16>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((k_head_stream<MT, NT, true, OUT_BF16>), grid, dim3(kStreamThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((k_head_stream<MT, NT, false, OUT_BF16>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((k_head_stream<MT, NT, false, OUT_BF16>), grid, dim3(kStreamThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -867,9 +945,22 @@ hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
 
 template <int MT, int BITS, bool OUT_BF16>
 hipError_t launch_stream_q_mt(const HeadParams& p, hipStream_t s) {
-    constexpr int NT = kStreamNT;
-    const dim3 grid((unsigned)((p.V + 64 * NT - 1) / (64 * NT)));
-    hipLaunchKernelGGL((k_head_stream_q<MT, NT, BITS, OUT_BF16>), grid, dim3(kThreads), 0, s, p);
+    constexpr int NT = kStreamQNT;
+    constexpr int SLAB = kStreamQThreads / 4 * NT;   // W rows per workgroup
+    const dim3 grid((unsigned)((p.V + SLAB - 1) / SLAB));
+    // vector scale loads: whole chunks, even scale pitch, 4-byte aligned rows
+    const int group = 1 << p.qw.gshift;
+    const bool vec = p.H % kStreamQKC == 0 && p.qw.sld % 2 == 0 &&
+                     (reinterpret_cast<uintptr_t>(p.qw.scales) & 3) == 0 &&
+                     (reinterpret_cast<uintptr_t>(p.qw.biases) & 3) == 0;
+    if (vec && group == kStreamQKC / 8)
+        hipLaunchKernelGGL((k_head_stream_q<MT, NT, BITS, 8, OUT_BF16>), grid, dim3(kStreamQThreads), 0, s, p);
+    else if (vec && group == kStreamQKC / 4)
+        hipLaunchKernelGGL((k_head_stream_q<MT, NT, BITS, 4, OUT_BF16>), grid, dim3(kStreamQThreads), 0, s, p);
+    else if (vec && group == kStreamQKC / 2)
+        hipLaunchKernelGGL((k_head_stream_q<MT, NT, BITS, 2, OUT_BF16>), grid, dim3(kStreamQThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_head_stream_q<MT, NT, BITS, 0, OUT_BF16>), grid, dim3(kStreamQThreads), 0, s, p);
     return hipGetLastError();
 }
 
