@@ -85,6 +85,8 @@ CASES = [  # (bits, group, H, V)
     (4, 32, 512, 999), (4, 128, 768, 1500),
     (8, 64, 256, 1000), (8, 32, 128, 777), (8, 128, 640, 3000), (8, 32, 512, 2001),
     (8, 128, 1024, 1024),
+    # more than 86 groups per row: the tiled kernel loads scales per stage
+    (4, 32, 3072, 700), (8, 32, 2816, 500),
 ]
 
 

@@ -579,18 +579,27 @@ template <>
 struct TileB<4> {
     uint32_t q[kTileLB];
     uint16_t sc[kTileLB], bi[kTileLB];
+    uint32_t sb[kTileLB];          // (scale, bias) from the LDS table
 };
 template <>
 struct TileB<8> {
     uint32_t q0[kTileLB], q1[kTileLB];
     uint16_t sc[kTileLB], bi[kTileLB];
+    uint32_t sb[kTileLB];
 };
+
+// Largest group count per row for which the quantised tiled kernel keeps its
+// tile's scale/bias table in LDS (256 rows x (groups + 1) dwords after the
+// stage buffers, within the 160 KB of a CU).
+constexpr int kTileMaxTableGroups = (160 * 1024 - kTileLds) / (kTileN * 4) - 1;
 
 // BITS = 16: bf16 weights; 4 or 8: quantised weights (hidden size a multiple
 // of 128), whose stages follow the quantised k order: stage st is k-step
 // st % SPB of code run st / SPB, and LDS chunk c of a row holds the 8
-// elements of lane quarter c.
-template <bool OUT_BF16, int BITS>
+// elements of lane quarter c. STAB (quantised only): the scale and bias of
+// every group of the tile's 256 W rows are loaded once into an LDS table of
+// (scale, bias) dwords; otherwise each stage loads the two values it needs.
+template <bool OUT_BF16, int BITS, bool STAB>
 __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
     constexpr bool QUANT = BITS != 16;
@@ -620,6 +629,19 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
     if (tid < kTileM) {
         const int32_t r = m0 + tid;
         sIdx[tid] = (r < p.R) ? row_source(p.row0 + r, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
+    }
+    uint32_t* tab = reinterpret_cast<uint32_t*>(lds + kTileLds);
+    const int tsp = STAB ? (int)(p.H >> p.qw.gshift) + 1 : 0;   // table row pitch (dwords)
+    if constexpr (STAB) {
+        const int ng = tsp - 1;
+        for (int e = tid; e < kTileN * ng; e += kTileThreads) {
+            const int row = e / ng;
+            const int g = e - row * ng;
+            const int64_t n = n0 + row < p.V ? n0 + row : p.V - 1;
+            const uint32_t sv = p.qw.scales[n * p.qw.sld + g];
+            const uint32_t bv = p.qw.biases[n * p.qw.sld + g];
+            tab[row * tsp + g] = sv | (bv << 16);
+        }
     }
     __syncthreads();
 
@@ -684,8 +706,12 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
                     rb.q0[j] = w.x;
                     rb.q1[j] = w.y;
                 }
-                rb.sc[j] = p.qw.scales[gs[j] + g];
-                rb.bi[j] = p.qw.biases[gs[j] + g];
+                if constexpr (STAB) {
+                    rb.sb[j] = tab[((tid >> 2) + 128 * j) * tsp + g];
+                } else {
+                    rb.sc[j] = p.qw.scales[gs[j] + g];
+                    rb.bi[j] = p.qw.biases[gs[j] + g];
+                }
             }
         }
     };
@@ -701,8 +727,14 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
             if constexpr (!QUANT) {
                 b = rb.v[j];
             } else {
-                const float sf = __uint_as_float((uint32_t)rb.sc[j] << 16);
-                const float bf = __uint_as_float((uint32_t)rb.bi[j] << 16);
+                float sf, bf;
+                if constexpr (STAB) {
+                    sf = __uint_as_float(rb.sb[j] << 16);
+                    bf = __uint_as_float(rb.sb[j] & 0xFFFF0000u);
+                } else {
+                    sf = __uint_as_float((uint32_t)rb.sc[j] << 16);
+                    bf = __uint_as_float((uint32_t)rb.bi[j] << 16);
+                }
                 if constexpr (BITS == 4)
                     b = dequant8<4>(rb.q[j], 0u, sf, bf);
                 else
@@ -923,16 +955,24 @@ hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s) {
     }
 }
 
-template <bool OUT_BF16, int BITS>
+template <bool OUT_BF16, int BITS, bool STAB>
 hipError_t launch_tiled(const HeadParams& p, int32_t mtiles, int32_t ntiles, hipStream_t s) {
-    const void* fn = (const void*)k_head_tiled<OUT_BF16, BITS>;
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kTileLds);
+    const void* fn = (const void*)k_head_tiled<OUT_BF16, BITS, STAB>;
+    const int ng = STAB ? (int)(p.H >> p.qw.gshift) : 0;
+    const size_t lds = kTileLds + (STAB ? (size_t)kTileN * (ng + 1) * 4 : 0);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t total = (int64_t)mtiles * ntiles;
     const dim3 grid((unsigned)(((total + 7) / 8) * 8));
-    hipLaunchKernelGGL((k_head_tiled<OUT_BF16, BITS>), grid, dim3(kTileThreads), kTileLds, s, p, mtiles,
-                       ntiles);
+    hipLaunchKernelGGL((k_head_tiled<OUT_BF16, BITS, STAB>), grid, dim3(kTileThreads), lds, s, p,
+                       mtiles, ntiles);
     return hipGetLastError();
+}
+
+template <bool OUT_BF16, int BITS>
+hipError_t launch_tiled_q(const HeadParams& p, int32_t mtiles, int32_t ntiles, hipStream_t s) {
+    if ((p.H >> p.qw.gshift) <= kTileMaxTableGroups) return launch_tiled<OUT_BF16, BITS, true>(p, mtiles, ntiles, s);
+    return launch_tiled<OUT_BF16, BITS, false>(p, mtiles, ntiles, s);
 }
 
 hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
@@ -940,7 +980,8 @@ hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
     const HeadParams p = to_params(a);
     const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
     const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
-    return a.out_bf16 ? launch_tiled<true, 16>(p, mtiles, ntiles, s) : launch_tiled<false, 16>(p, mtiles, ntiles, s);
+    return a.out_bf16 ? launch_tiled<true, 16, false>(p, mtiles, ntiles, s)
+                      : launch_tiled<false, 16, false>(p, mtiles, ntiles, s);
 }
 
 template <int MT, int BITS, bool OUT_BF16>
@@ -991,9 +1032,9 @@ hipError_t launch_head_tiled_q(const HeadArgs& a, hipStream_t s) {
     const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
     const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
     if (a.bits == 4)
-        return a.out_bf16 ? launch_tiled<true, 4>(p, mtiles, ntiles, s) : launch_tiled<false, 4>(p, mtiles, ntiles, s);
+        return a.out_bf16 ? launch_tiled_q<true, 4>(p, mtiles, ntiles, s) : launch_tiled_q<false, 4>(p, mtiles, ntiles, s);
     if (a.bits == 8)
-        return a.out_bf16 ? launch_tiled<true, 8>(p, mtiles, ntiles, s) : launch_tiled<false, 8>(p, mtiles, ntiles, s);
+        return a.out_bf16 ? launch_tiled_q<true, 8>(p, mtiles, ntiles, s) : launch_tiled_q<false, 8>(p, mtiles, ntiles, s);
     return hipErrorInvalidValue;
 }
 
