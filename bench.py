@@ -49,7 +49,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-    WRITE_SIZE, both with --sections copycal,head) into HBM bytes per launch.
+    WRITE_SIZE, both with --sections copycal,head,headq) into HBM bytes per
+    launch.
     Each counter is scaled by what it reads for the plain elementwise copy of
     known size that the copycal section runs."""
     import csv
@@ -74,7 +75,14 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
               "reduce_stage1_bf16": ("k_stage1<true, true>", "reduce.hip", nbytes),
               "reduce_stage2_bf16": ("k_stage2<true", "reduce.hip", None),
               "head_stream_bf16": ("k_head_stream<", "head.hip", 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
-              "head_tiled_bf16": ("k_head_tiled<", "head.hip", 151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4)}
+              "head_tiled_bf16": ("k_head_tiled<false, 16", "head.hip",
+                                  151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4)}
+    for bits in (4, 8):
+        qbytes = 151936 * 1024 * bits // 8 + 151936 * 16 * 4
+        wanted[f"head_stream_q{bits}"] = (f"k_head_stream_q<3, 1, {bits}, ", "head.hip",
+                                          qbytes + 40 * 1024 * 2 + 40 * 151936 * 4)
+        wanted[f"head_tiled_q{bits}"] = (f"k_head_tiled<false, {bits}, ", "head.hip",
+                                         qbytes + 2048 * 1024 * 2 + 2048 * 151936 * 4)
     res = {"calibration": {"kernel": copy[0][:80], "bytes_read": nbytes, "bytes_written": nbytes,
                            "fetch_kib": fetch[copy[0]], "write_kib": write[copy[0]],
                            "fetch_factor": round(f_fetch, 5), "write_factor": round(f_write, 5)}}
