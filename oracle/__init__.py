@@ -60,6 +60,8 @@ def load(path: str = _LIB_PATH):
     lib.orc_head.restype = None
     lib.orc_dequant.argtypes = [p, i64, p, p, i64, ctypes.c_int, ctypes.c_int, i64, i64, p]
     lib.orc_dequant.restype = None
+    lib.orc_scale_logits.argtypes = [p, i64, ctypes.c_int, ctypes.c_double]
+    lib.orc_scale_logits.restype = None
     lib.orc_reduce.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p]
     lib.orc_reduce.restype = None
     lib.orc_prefilter_check.argtypes = [p, ctypes.c_int, i64, i64, i64, i32, i32, i32, p]
@@ -106,8 +108,13 @@ def rows(cu_seqlens, num_decode: int, num_tokens: int, logits_indices=None, lib=
     return st, idx, lcu
 
 
-def head(hidden: np.ndarray, weight: np.ndarray, idx, lib=None) -> np.ndarray:
-    """f64 logits Z[r][v] = sum_k hidden[idx[r]][k] * weight[v][k] (k ascending).
+SCALE_NONE, SCALE_MUL, SCALE_DIV = 0, 1, 2
+
+
+def head(hidden: np.ndarray, weight: np.ndarray, idx, lib=None, scale_mode: int = SCALE_NONE,
+         scale: float = 1.0) -> np.ndarray:
+    """f64 logits Z[r][v] = sum_k hidden[idx[r]][k] * weight[v][k] (k ascending),
+    then multiplied by `scale` (SCALE_MUL) or divided by it (SCALE_DIV).
     hidden [T][H] and weight [V][H] are float32 or raw-bf16 uint16 (2-D, any
     row pitch through numpy strides is flattened to a contiguous copy)."""
     lib = lib or load()
@@ -120,6 +127,7 @@ def head(hidden: np.ndarray, weight: np.ndarray, idx, lib=None) -> np.ndarray:
     Z = np.empty((idx.shape[0], V), dtype=np.float64)
     lib.orc_head(_ptr(hidden), _dtype_code(hidden), T, H, H, _ptr(weight), _dtype_code(weight),
                  V, H, _ptr(idx), idx.shape[0], _ptr(Z))
+    lib.orc_scale_logits(_ptr(Z), Z.size, int(scale_mode), float(scale))
     return Z
 
 

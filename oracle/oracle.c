@@ -141,6 +141,21 @@ void orc_head(const void* hidden, int hdt, int64_t num_tokens, int64_t H, int64_
 }
 
 /*
+ * Head output scaling (vllm-metal release, Summary: some heads scale their
+ * logits outside the projection, Cohere's logit_scale and Granite's
+ * logits_scaling). Reading taken: mode 1 multiplies every logit by `value`,
+ * mode 2 divides it by `value`, mode 0 leaves it; applied to the exact f64
+ * logits in place.
+ */
+void orc_scale_logits(double* Z, int64_t n, int mode, double value) {
+    if (mode == 1) {
+        for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] * value;
+    } else if (mode == 2) {
+        for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] / value;
+    }
+}
+
+/*
  * Quantised head weights (the pages' measured models are 4-bit MLX models:
  * mlxcel PR #1969, description). Reading taken for the format: MLX-style
  * affine groups -- for token v and hidden index k, with g = k / group,

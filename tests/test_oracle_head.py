@@ -77,3 +77,46 @@ def test_invalid_row_gives_nan():
     Z = oracle.head(hid, w, np.array([0, 4, -1, 3], dtype=np.int32))
     assert np.all(Z[0] == 8.0) and np.all(Z[3] == 8.0)
     assert np.all(np.isnan(Z[1])) and np.all(np.isnan(Z[2]))
+
+
+def _int_head(scale_mode=oracle.SCALE_NONE, scale=1.0, lib=None):
+    hid = synth.small_int_bf16(31, (9, 80))
+    w = synth.small_int_bf16(32, (50, 80))
+    idx = np.array([8, 0, 5], dtype=np.int32)
+    exact = (synth.bf16_bits_to_f32(hid).astype(np.int64)[idx]
+             @ synth.bf16_bits_to_f32(w).astype(np.int64).T)
+    return oracle.head(hid, w, idx, lib=lib, scale_mode=scale_mode, scale=scale), exact
+
+
+def test_scale_modes_closed_forms():
+    """Output scaling (vllm-metal release, Summary: Cohere's logit_scale,
+    Granite's logits_scaling): none leaves the integer head; multiply by
+    0.5 halves it exactly; divide by 4 quarters it exactly."""
+    z, exact = _int_head()
+    assert np.array_equal(z, exact.astype(np.float64))
+    z, _ = _int_head(oracle.SCALE_MUL, 0.5)
+    assert np.array_equal(z, exact / 2.0)
+    z, _ = _int_head(oracle.SCALE_DIV, 4.0)
+    assert np.array_equal(z, exact / 4.0)
+
+
+def _div49_case(lib=None):
+    """Integer head times 49 (the weights are 49 x small integers, exact in
+    fp32), divided by 49."""
+    hid = synth.small_int_bf16(33, (6, 64))
+    wi = synth.bf16_bits_to_f32(synth.small_int_bf16(34, (40, 64)))
+    w = (wi * np.float32(49.0)).astype(np.float32)
+    idx = np.arange(6, dtype=np.int32)
+    z = oracle.head(hid, w, idx, lib=lib, scale_mode=oracle.SCALE_DIV, scale=49.0)
+    ints = synth.bf16_bits_to_f32(hid).astype(np.int64) @ wi.astype(np.int64).T
+    return z, ints
+
+
+def test_divide_is_a_true_division():
+    """Dividing logits that are multiples of 49 by 49 returns the integers
+    exactly; a multiply by the rounded reciprocal would miss some of them on
+    this data (checked below), so the pin tells the two apart."""
+    z, ints = _div49_case()
+    assert np.array_equal(z, ints.astype(np.float64))
+    recip = (ints * 49.0) * (1.0 / 49.0)
+    assert not np.array_equal(recip, ints.astype(np.float64))

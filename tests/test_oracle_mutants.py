@@ -75,9 +75,26 @@ def _dequant_golden_ok(lib):
     return True
 
 
+def _scale_ok(lib):
+    hid = synth.small_int_bf16(31, (5, 48))
+    w = synth.small_int_bf16(32, (30, 48))
+    idx = np.array([4, 0, 2], dtype=np.int32)
+    exact = (synth.bf16_bits_to_f32(hid).astype(np.int64)[idx]
+             @ synth.bf16_bits_to_f32(w).astype(np.int64).T).astype(np.float64)
+    if not np.array_equal(oracle.head(hid, w, idx, lib=lib, scale_mode=oracle.SCALE_MUL, scale=0.5),
+                          exact / 2.0):
+        return False
+    wi = synth.bf16_bits_to_f32(synth.small_int_bf16(34, (40, 64)))
+    hid2 = synth.small_int_bf16(33, (6, 64))
+    z = oracle.head(hid2, (wi * np.float32(49.0)).astype(np.float32), np.arange(6, dtype=np.int32),
+                    lib=lib, scale_mode=oracle.SCALE_DIV, scale=49.0)
+    ints = synth.bf16_bits_to_f32(hid2).astype(np.int64) @ wi.astype(np.int64).T
+    return np.array_equal(z, ints.astype(np.float64))
+
+
 def _all_pins_ok(lib):
     return (_rows_golden_ok(lib) and _head_integer_ok(lib) and _head_one_hot_ok(lib)
-            and _closed_forms_ok(lib) and _dequant_golden_ok(lib))
+            and _closed_forms_ok(lib) and _dequant_golden_ok(lib) and _scale_ok(lib))
 
 
 MUTANTS = [
@@ -94,6 +111,8 @@ MUTANTS = [
     ("dequant drops the bias", "* (double)qv +\n                             widen(biases, ORC_BF16, v * s_ld + g);", "* (double)qv;"),
     ("dequant scale and bias swapped", "W64[v * H + k] = widen(scales,", "W64[v * H + k] = widen(biases,"),
     ("dequant group twice as wide", "const int64_t g = k / group;", "const int64_t g = k / (2 * group);"),
+    ("multiply mode divides", "for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] * value;", "for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] / value;"),
+    ("divide mode by the reciprocal", "for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] / value;", "for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] * (1.0 / value);"),
     ("selected logprob adds lse", ": widen(logits, dt, base + t) - l;", ": widen(logits, dt, base + t) + l;"),
 ]
 
