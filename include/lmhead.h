@@ -257,6 +257,102 @@ lmh_status lmhead_logprobs_q(
     int32_t chunk_rows, float* logits_debug,
     void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Head descriptor and extended entry points.
+ *
+ * Head output scaling [vllm-metal, Summary: some heads scale their logits
+ * outside the projection -- Cohere's logit_scale, Granite's logits_scaling --
+ * and a selective path that leaves the scaling out gives wrong logits without
+ * failing]. scale_mode LMH_SCALE_MUL multiplies every fp32 logit by `scale`,
+ * LMH_SCALE_DIV divides it by `scale` (IEEE fp32 division, correctly
+ * rounded); the scaling is applied to the fp32 accumulator before any bf16
+ * rounding of the output, on every head kernel alike.
+ * ------------------------------------------------------------------------- */
+#define LMH_SCALE_NONE 0
+#define LMH_SCALE_MUL 1
+#define LMH_SCALE_DIV 2
+
+typedef struct lmh_head {
+    /* dense weights (bits == 0): [vocab][weight_ld], weight_dt == hidden_dt */
+    const void* weight;
+    lmh_dtype weight_dt;
+    int64_t weight_ld;
+    /* affine group-quantised weights (bits 4 or 8), as for lmhead_gather_project_q */
+    int32_t bits;
+    int32_t group_size;
+    const uint32_t* weight_q;
+    int64_t weight_q_ld;
+    const uint16_t* scales;
+    const uint16_t* biases;
+    int64_t scales_ld;
+    /* output scaling */
+    int32_t scale_mode;   /* LMH_SCALE_NONE, LMH_SCALE_MUL or LMH_SCALE_DIV */
+    float scale;          /* finite and nonzero when scale_mode != LMH_SCALE_NONE */
+} lmh_head;
+
+/*
+ * lmhead_gather_project_ex -- lmhead_gather_project / lmhead_gather_project_q
+ * with the head given by `head` (NULL is LMH_ERR_NULL) and output scaling.
+ * `variant` is LMH_HEAD_AUTO or forces a kernel as in
+ * lmh_debug_gather_project. An unknown scale_mode, or a zero or non-finite
+ * scale with a mode set, returns LMH_ERR_SHAPE.
+ */
+lmh_status lmhead_gather_project_ex(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld, const lmh_head* head, int64_t vocab,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    void* logits, lmh_dtype logits_dt, int64_t logits_ld,
+    int32_t* logits_cu_seqlens, int32_t* gather_indices,
+    int32_t* device_error, void* stream, int32_t variant);
+
+/*
+ * lmhead_logprobs_ex -- lmhead_logprobs with the head given by `head` (dense
+ * or quantised, with output scaling: the reduction sees the scaled logits).
+ * vocab_mask must be NULL (reserved).
+ */
+lmh_status lmhead_logprobs_ex(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld, const lmh_head* head, int64_t vocab,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    const int32_t* selected_ids, int32_t k,
+    float* lse, float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+    int32_t* logits_cu_seqlens, int32_t* gather_indices,
+    int32_t chunk_rows, float* logits_debug,
+    const uint32_t* vocab_mask, int64_t vocab_mask_ld,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
+
+/*
+ * lmhead_selfcheck_workspace_size -- bytes of device workspace
+ * lmhead_selfcheck needs: rows x roundup(vocab, 4) fp32.
+ */
+size_t lmhead_selfcheck_workspace_size(int64_t rows, int64_t vocab);
+
+/*
+ * lmhead_selfcheck -- bit-exact check of the selective path against a head's
+ * own full output [vllm-metal, Summary: selective logits are used only where
+ * the selected rows equal the model's own output bit for bit; Testing: a
+ * scaled head the selective path does not reproduce is rejected].
+ *
+ * Projects the R selected rows (sampled or explicit mode, as in
+ * lmhead_gather_project) through `head` into the workspace as fp32 and
+ * compares each with row src(r) of full_logits [num_tokens][full_ld] fp32 --
+ * the logits the model's own forward produced for every position -- as bit
+ * patterns. result is a DEVICE int64[2]: result[0] = number of differing
+ * logits, result[1] = the smallest r * vocab + v that differs (INT64_MAX when
+ * none). Rows without a valid source are skipped (and flagged in
+ * device_error). result is written by the call (no need to clear it).
+ */
+lmh_status lmhead_selfcheck(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld, const lmh_head* head, int64_t vocab,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    const float* full_logits, int64_t full_ld,
+    void* workspace, size_t workspace_bytes, int64_t* result,
+    int32_t* device_error, void* stream);
+
 /* lmh_status_string -- static, human-readable name of a status code. */
 const char* lmh_status_string(lmh_status status);
 

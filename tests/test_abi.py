@@ -184,3 +184,85 @@ def test_fused_rejects(L):
     bad = list(base)
     bad[22] = -1                        # chunk_rows
     assert L.lmhead_logprobs(*bad) == SHAPE
+
+
+def _head(**kw):
+    import top_reduction_amd as lmh
+    h = lmh.LmhHead()
+    h.weight, h.weight_dt, h.weight_ld, h.bits, h.group_size = A, BF16, 64, 0, 0
+    h.weight_q, h.weight_q_ld, h.scales, h.biases, h.scales_ld = None, 0, None, None, 0
+    h.scale_mode, h.scale = 0, 1.0
+    for k, v in kw.items():
+        setattr(h, k, v)
+    return h
+
+
+def _project_ex(L, head, **kw):
+    a = dict(hidden=A, hidden_dt=BF16, num_tokens=23, hidden_dim=64, hidden_ld=64, vocab=1000, cu=A,
+             S=5, D=2, ex=None, nex=0, logits=A, logits_dt=F32, logits_ld=1000, variant=0)
+    a.update(kw)
+    return L.lmhead_gather_project_ex(a["hidden"], a["hidden_dt"], a["num_tokens"], a["hidden_dim"],
+                                      a["hidden_ld"], None if head is None else ctypes.byref(head),
+                                      a["vocab"], a["cu"], a["S"], a["D"], a["ex"], a["nex"],
+                                      a["logits"], a["logits_dt"], a["logits_ld"], None, None, None,
+                                      None, a["variant"])
+
+
+@pytest.mark.parametrize("hkw,want", [
+    (dict(scale_mode=3), SHAPE), (dict(scale_mode=-1), SHAPE),
+    (dict(scale_mode=1, scale=0.0), SHAPE), (dict(scale_mode=2, scale=0.0), SHAPE),
+    (dict(scale_mode=1, scale=float("nan")), SHAPE), (dict(scale_mode=2, scale=float("inf")), SHAPE),
+    (dict(weight=None), NULL), (dict(weight_dt=F32), DTYPE),
+    (dict(bits=4, group_size=64), NULL),                        # quantised without codes
+    (dict(weight=A + 2), ALIGN),
+])
+def test_gather_project_ex_rejects(L, hkw, want):
+    assert _project_ex(L, _head(**hkw)) == want
+
+
+def test_gather_project_ex_null_head_and_variant(L):
+    assert _project_ex(L, None) == NULL
+    assert _project_ex(L, _head(), variant=3) == SHAPE
+    assert _project_ex(L, _head(), S=100, D=0, variant=1) == SHAPE
+
+
+def test_logprobs_ex_mask_reserved(L):
+    h = _head()
+    args = [A, BF16, 23, 64, 64, ctypes.byref(h), 1000, A, 5, 2, None, 0, A, 5, A, A, A, A, None,
+            None, 0, None]
+    assert L.lmhead_logprobs_ex(*args, A, 32, A, 1 << 30, None, None) == SHAPE
+    assert L.lmhead_logprobs_ex(None, BF16, 23, 64, 64, ctypes.byref(h), 1000, A, 5, 2, None, 0,
+                                A, 5, A, A, A, A, None, None, 0, None, None, 0, A, 1 << 30, None,
+                                None) == NULL
+
+
+def test_selfcheck_rejects(L):
+    h = _head()
+    base = [A, BF16, 23, 64, 64, ctypes.byref(h), 1000, A, 5, 2, None, 0]
+    need = L.lmhead_selfcheck_workspace_size(5, 1000)
+    assert need == 5 * 1000 * 4 + (256 - 5 * 1000 * 4 % 256) % 256
+    assert L.lmhead_selfcheck(*base, None, 1000, A, need, A, None, None) == NULL       # no full logits
+    assert L.lmhead_selfcheck(*base, A, 1000, A, need, None, None, None) == NULL       # no result
+    assert L.lmhead_selfcheck(*base, A, 999, A, need, A, None, None) == SHAPE          # full_ld < vocab
+    assert L.lmhead_selfcheck(*base, A, 1000, A, need - 1, A, None, None) == WS
+    assert L.lmhead_selfcheck(*base, A, 1000, None, need, A, None, None) == WS
+    assert L.lmhead_selfcheck(*base, A + 2, 1000, A, need, A, None, None) == ALIGN
+    assert L.lmhead_selfcheck(*base, A, 1000, A, need, A + 4, None, None) == ALIGN
+
+
+def test_head_struct_layout_matches_c(tmp_path):
+    """The ctypes mirror of lmh_head has C's size and field offsets (compiled
+    against include/lmhead.h with the host C compiler)."""
+    import subprocess
+    import top_reduction_amd as lmh
+    fields = [f for f, _ in lmh.LmhHead._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lmhead.h"\nint main(void){\n'
+                   + 'printf("%zu\\n", sizeof(lmh_head));\n'
+                   + "".join(f'printf("%zu\\n", offsetof(lmh_head, {f}));\n' for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(lmh.LmhHead)
+    assert out[1:] == [getattr(lmh.LmhHead, f).offset for f in fields]

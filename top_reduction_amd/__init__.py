@@ -15,6 +15,11 @@ Entry points (same names as the C ABI):
                          the same with an affine group-quantised head
                          (QuantizedWeight: 4- or 8-bit codes, bf16 scale and
                          bias per group)
+  lmhead_gather_project_ex, lmhead_logprobs_ex
+                         the same with a HeadSpec (dense or quantised weights
+                         plus output scaling)
+  lmhead_selfcheck       bit-exact check of the selective rows against a
+                         head's own full output
 """
 from __future__ import annotations
 
@@ -29,11 +34,21 @@ LIB_PATH = os.path.join(_HERE, "liblmhead.so")
 
 LMH_F32, LMH_BF16 = 0, 1
 LMH_HEAD_AUTO, LMH_HEAD_STREAM, LMH_HEAD_TILED = 0, 1, 2
+LMH_SCALE_NONE, LMH_SCALE_MUL, LMH_SCALE_DIV = 0, 1, 2
 LMH_DEVERR_INDEX, LMH_DEVERR_LAYOUT = 1, 2
 STATUS = {0: "LMH_OK", 1: "LMH_ERR_NULL", 2: "LMH_ERR_SHAPE", 3: "LMH_ERR_K",
           4: "LMH_ERR_DTYPE", 5: "LMH_ERR_ALIGN", 6: "LMH_ERR_WORKSPACE", 7: "LMH_ERR_HIP"}
 
 _lib = None
+
+
+class LmhHead(ctypes.Structure):
+    """ctypes mirror of the C `lmh_head` descriptor (include/lmhead.h)."""
+    _fields_ = [("weight", ctypes.c_void_p), ("weight_dt", ctypes.c_int), ("weight_ld", ctypes.c_int64),
+                ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("weight_q", ctypes.c_void_p), ("weight_q_ld", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p), ("scales_ld", ctypes.c_int64),
+                ("scale_mode", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 class LmhError(RuntimeError):
@@ -67,11 +82,19 @@ def lib():
         L.lmhead_gather_project_q.argtypes = projq + [p, ctypes.c_int, i64, p, p, p, p]
         L.lmh_debug_gather_project_q.argtypes = projq + [p, ctypes.c_int, i64, p, p, p, p, i32]
         L.lmhead_logprobs_q.argtypes = projq + [p, i32, p, p, p, p, p, p, i32, p, p, sz, p, p]
+        hp = ctypes.POINTER(LmhHead)
+        projx = [p, ctypes.c_int, i64, i64, i64, hp, i64, p, i32, i32, p, i32]
+        L.lmhead_gather_project_ex.argtypes = projx + [p, ctypes.c_int, i64, p, p, p, p, i32]
+        L.lmhead_logprobs_ex.argtypes = projx + [p, i32, p, p, p, p, p, p, i32, p, p, i64, p, sz, p, p]
+        L.lmhead_selfcheck_workspace_size.argtypes = [i64, i64]
+        L.lmhead_selfcheck_workspace_size.restype = sz
+        L.lmhead_selfcheck.argtypes = projx + [p, i64, p, sz, p, p, p]
         L.lmh_status_string.argtypes = [ctypes.c_int]
         L.lmh_status_string.restype = ctypes.c_char_p
         for name in ("lmhead_gather_project", "lmh_debug_gather_project", "logprob_reduce",
                      "lmh_debug_reduce_stage1", "lmhead_logprobs", "lmhead_gather_project_q",
-                     "lmh_debug_gather_project_q", "lmhead_logprobs_q"):
+                     "lmh_debug_gather_project_q", "lmhead_logprobs_q", "lmhead_gather_project_ex",
+                     "lmhead_logprobs_ex", "lmhead_selfcheck"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -323,3 +346,125 @@ def lmhead_logprobs_q(hidden: torch.Tensor, weight: QuantizedWeight, cu_seqlens:
     V, wargs = _quant_weight_args(weight, hidden.shape[1])
     return _logprobs(lib().lmhead_logprobs_q, "lmhead_logprobs_q", hidden, wargs, V, cu_seqlens,
                      num_decode, selected_ids, k, logits_indices, chunk_rows, return_logits, ws)
+
+
+class HeadSpec(NamedTuple):
+    """A head for the *_ex entry points: dense weights ([vocab, hidden]
+    tensor) or a QuantizedWeight, and output scaling (LMH_SCALE_MUL multiplies
+    the fp32 logits by `scale`, LMH_SCALE_DIV divides them by it)."""
+    weight: object
+    scale_mode: int = LMH_SCALE_NONE
+    scale: float = 1.0
+
+
+def _head_struct(head: HeadSpec, H: int):
+    h = LmhHead()
+    if isinstance(head.weight, QuantizedWeight):
+        V, a = _quant_weight_args(head.weight, H)
+        h.weight, h.weight_dt, h.weight_ld = None, LMH_BF16, 0
+        h.weight_q, h.weight_q_ld, h.scales, h.biases, h.scales_ld = a[0], a[1], a[2], a[3], a[4]
+        h.bits, h.group_size = a[5], a[6]
+    else:
+        V, a = _dense_weight_args(head.weight, H)
+        h.weight, h.weight_dt, h.weight_ld = a[0], a[1], a[3]
+        h.bits, h.group_size = 0, 0
+    h.scale_mode, h.scale = int(head.scale_mode), float(head.scale)
+    return V, h
+
+
+def lmhead_gather_project_ex(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: torch.Tensor,
+                             num_decode: int = 0, logits_indices: Optional[torch.Tensor] = None,
+                             out_dtype: torch.dtype = torch.float32,
+                             logits: Optional[torch.Tensor] = None, variant: int = LMH_HEAD_AUTO,
+                             device_error: Optional[torch.Tensor] = None) -> Projection:
+    """lmhead_gather_project with a HeadSpec (weights and output scaling)."""
+    L = lib()
+    V, h = _head_struct(head, hidden.shape[1])
+    T, H, hld = _matrix(hidden, "hidden")
+    cu = _i32(cu_seqlens, "cu_seqlens")
+    ex = _i32(logits_indices, "logits_indices")
+    S = cu.shape[0] - 1
+    R = ex.shape[0] if ex is not None else S
+    dev = hidden.device
+    if logits is None:
+        logits = torch.empty((R, V), dtype=out_dtype, device=dev)
+    _, _, old = _matrix(logits, "logits") if R > 0 else (0, 0, V)
+    lcu = torch.empty(S + 1, dtype=torch.int32, device=dev)
+    gidx = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
+    err = device_error if device_error is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    st = L.lmhead_gather_project_ex(_ptr(hidden), _dt(hidden), T, H, hld, ctypes.byref(h), V,
+                                    _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
+                                    _ptr(logits), _dt(logits), old, _ptr(lcu), _ptr(gidx), _ptr(err),
+                                    _stream(), int(variant))
+    _check(st, "lmhead_gather_project_ex")
+    return Projection(logits, lcu, gidx[:R], err)
+
+
+def lmhead_logprobs_ex(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: torch.Tensor,
+                       num_decode: int = 0, selected_ids: Optional[torch.Tensor] = None, k: int = 0,
+                       logits_indices: Optional[torch.Tensor] = None, chunk_rows: int = 0,
+                       return_logits: bool = False, ws: Optional[torch.Tensor] = None) -> Logprobs:
+    """lmhead_logprobs with a HeadSpec (the reduction sees the scaled logits)."""
+    L = lib()
+    V, h = _head_struct(head, hidden.shape[1])
+    T, H, hld = _matrix(hidden, "hidden")
+    cu = _i32(cu_seqlens, "cu_seqlens")
+    ex = _i32(logits_indices, "logits_indices")
+    sel = _i32(selected_ids, "selected_ids")
+    S = cu.shape[0] - 1
+    R = ex.shape[0] if ex is not None else S
+    dev = hidden.device
+    if ws is None:
+        ws = workspace(L.lmhead_logprobs_workspace_size(R, V, k, chunk_rows), dev)
+    ld = (V + 3) // 4 * 4
+    dbg = torch.empty((R, ld), dtype=torch.float32, device=dev) if return_logits else None
+    lse = torch.empty(R, dtype=torch.float32, device=dev)
+    slp = torch.empty(R, dtype=torch.float32, device=dev) if sel is not None else None
+    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
+    lps = torch.empty((R, k), dtype=torch.float32, device=dev)
+    lcu = torch.empty(S + 1, dtype=torch.int32, device=dev)
+    gidx = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = L.lmhead_logprobs_ex(_ptr(hidden), _dt(hidden), T, H, hld, ctypes.byref(h), V,
+                              _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
+                              _ptr(sel), int(k), _ptr(lse), _ptr(slp),
+                              _ptr(ids) if k else None, _ptr(lps) if k else None,
+                              _ptr(lcu), _ptr(gidx), int(chunk_rows), _ptr(dbg), None, 0,
+                              _ptr(ws), ws.numel(), _ptr(err), _stream())
+    _check(st, "lmhead_logprobs_ex")
+    return Logprobs(lse, slp, ids, lps, lcu, gidx[:R], err, None if dbg is None else dbg[:, :V])
+
+
+class SelfCheck(NamedTuple):
+    result: torch.Tensor          # int64[2]: differing logits, first r * vocab + v (INT64_MAX: none)
+    device_error: torch.Tensor
+
+
+def lmhead_selfcheck(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: torch.Tensor,
+                     full_logits: torch.Tensor, num_decode: int = 0,
+                     logits_indices: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> SelfCheck:
+    """Project the selected rows through `head` and compare them bit for bit
+    with the rows of `full_logits` ([num_tokens, vocab] fp32, the head's own
+    output at every position) they come from."""
+    L = lib()
+    V, h = _head_struct(head, hidden.shape[1])
+    T, H, hld = _matrix(hidden, "hidden")
+    Tf, Vf, fld = _matrix(full_logits, "full_logits")
+    if full_logits.dtype != torch.float32 or Vf != V or Tf != T:
+        raise ValueError("full_logits must be fp32 [num_tokens, vocab]")
+    cu = _i32(cu_seqlens, "cu_seqlens")
+    ex = _i32(logits_indices, "logits_indices")
+    S = cu.shape[0] - 1
+    R = ex.shape[0] if ex is not None else S
+    dev = hidden.device
+    if ws is None:
+        ws = workspace(L.lmhead_selfcheck_workspace_size(R, V), dev)
+    res = torch.empty(2, dtype=torch.int64, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = L.lmhead_selfcheck(_ptr(hidden), _dt(hidden), T, H, hld, ctypes.byref(h), V,
+                            _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
+                            _ptr(full_logits), fld, _ptr(ws), ws.numel(), _ptr(res), _ptr(err),
+                            _stream())
+    _check(st, "lmhead_selfcheck")
+    return SelfCheck(res, err)

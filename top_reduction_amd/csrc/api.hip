@@ -3,6 +3,7 @@
 // be made on the host returns before the first HIP call; no entry point
 // allocates, synchronises or copies to the host.
 #include <climits>
+#include <cmath>
 
 #include "lmh_internal.h"
 
@@ -34,14 +35,21 @@ struct WeightSpec {
     int64_t s_ld;
     int32_t bits;     // 0: dense
     int32_t group;
+    int32_t scale_mode;
+    float scale;
 };
 
 WeightSpec dense_weight(const void* w, lmh_dtype dt, int64_t ld) {
-    return WeightSpec{w, dt, ld, nullptr, 0, nullptr, nullptr, 0, 0, 0};
+    return WeightSpec{w, dt, ld, nullptr, 0, nullptr, nullptr, 0, 0, 0, LMH_SCALE_NONE, 1.0f};
 }
 WeightSpec quant_weight(const uint32_t* q, int64_t q_ld, const uint16_t* scales,
                         const uint16_t* biases, int64_t s_ld, int32_t bits, int32_t group) {
-    return WeightSpec{nullptr, LMH_BF16, 0, q, q_ld, scales, biases, s_ld, bits, group};
+    return WeightSpec{nullptr, LMH_BF16, 0, q, q_ld, scales, biases, s_ld, bits, group,
+                      LMH_SCALE_NONE, 1.0f};
+}
+WeightSpec head_weight(const lmh_head& h) {
+    return WeightSpec{h.weight, h.weight_dt, h.weight_ld, h.weight_q, h.weight_q_ld, h.scales,
+                      h.biases, h.scales_ld, h.bits, h.group_size, h.scale_mode, h.scale};
 }
 
 int32_t log2_exact(int32_t g) {
@@ -63,6 +71,10 @@ ProjectCheck check_project_inputs(const void* hidden, lmh_dtype hidden_dt, int64
         return {LMH_ERR_SHAPE, 0};
     if (logits_indices != nullptr && num_indices < 0) return {LMH_ERR_SHAPE, 0};
     if (hidden_ld < hidden_dim) return {LMH_ERR_SHAPE, 0};
+    if (w.scale_mode != LMH_SCALE_NONE &&
+        ((w.scale_mode != LMH_SCALE_MUL && w.scale_mode != LMH_SCALE_DIV) || !std::isfinite(w.scale) ||
+         w.scale == 0.0f))
+        return {LMH_ERR_SHAPE, 0};
     if (w.bits == 0) {
         if (w.ld < hidden_dim) return {LMH_ERR_SHAPE, 0};
         if (!valid_dtype(hidden_dt) || w.dt != hidden_dt) return {LMH_ERR_DTYPE, 0};
@@ -108,6 +120,8 @@ HeadArgs head_args(const void* hidden, int64_t num_tokens, int64_t hidden_dim, i
                    int64_t out_ld, bool out_bf16, int32_t* device_error) {
     HeadArgs h{hidden, num_tokens, hidden_dim, hidden_ld, w.dense, vocab, w.ld, cu_seqlens,
                num_decode, logits_indices, row0, rows, out, out_ld, out_bf16, device_error};
+    h.scale_mode = w.scale_mode;
+    h.scale = w.scale;
     if (w.bits != 0) {
         h.bits = w.bits;
         h.q = w.q;
@@ -404,6 +418,83 @@ lmh_status lmhead_logprobs_q(const void* hidden, lmh_dtype hidden_dt, int64_t nu
                          selected_ids, k, lse, selected_logprob, topk_ids, topk_logprobs,
                          logits_cu_seqlens, gather_indices, chunk_rows, logits_debug, workspace,
                          workspace_bytes, device_error, stream);
+}
+
+lmh_status lmhead_gather_project_ex(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                                    int64_t hidden_dim, int64_t hidden_ld, const lmh_head* head,
+                                    int64_t vocab, const int32_t* cu_seqlens, int32_t num_segments,
+                                    int32_t num_decode, const int32_t* logits_indices,
+                                    int32_t num_indices, void* logits, lmh_dtype logits_dt,
+                                    int64_t logits_ld, int32_t* logits_cu_seqlens,
+                                    int32_t* gather_indices, int32_t* device_error, void* stream,
+                                    int32_t variant) {
+    if (!head) return LMH_ERR_NULL;
+    return gather_project_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                               head_weight(*head), vocab, cu_seqlens, num_segments, num_decode,
+                               logits_indices, num_indices, logits, logits_dt, logits_ld,
+                               logits_cu_seqlens, gather_indices, device_error, stream, variant);
+}
+
+lmh_status lmhead_logprobs_ex(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                              int64_t hidden_dim, int64_t hidden_ld, const lmh_head* head,
+                              int64_t vocab, const int32_t* cu_seqlens, int32_t num_segments,
+                              int32_t num_decode, const int32_t* logits_indices,
+                              int32_t num_indices, const int32_t* selected_ids, int32_t k,
+                              float* lse, float* selected_logprob, int32_t* topk_ids,
+                              float* topk_logprobs, int32_t* logits_cu_seqlens,
+                              int32_t* gather_indices, int32_t chunk_rows, float* logits_debug,
+                              const uint32_t* vocab_mask, int64_t vocab_mask_ld, void* workspace,
+                              size_t workspace_bytes, int32_t* device_error, void* stream) {
+    if (!head) return LMH_ERR_NULL;
+    if (vocab_mask != nullptr || vocab_mask_ld != 0) return LMH_ERR_SHAPE;
+    return logprobs_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld, head_weight(*head),
+                         vocab, cu_seqlens, num_segments, num_decode, logits_indices, num_indices,
+                         selected_ids, k, lse, selected_logprob, topk_ids, topk_logprobs,
+                         logits_cu_seqlens, gather_indices, chunk_rows, logits_debug, workspace,
+                         workspace_bytes, device_error, stream);
+}
+
+size_t lmhead_selfcheck_workspace_size(int64_t rows, int64_t vocab) {
+    if (rows <= 0 || vocab <= 0) return 256;
+    return up256((size_t)rows * (size_t)(ceil_div(vocab, 4) * 4) * sizeof(float));
+}
+
+lmh_status lmhead_selfcheck(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                            int64_t hidden_dim, int64_t hidden_ld, const lmh_head* head,
+                            int64_t vocab, const int32_t* cu_seqlens, int32_t num_segments,
+                            int32_t num_decode, const int32_t* logits_indices, int32_t num_indices,
+                            const float* full_logits, int64_t full_ld, void* workspace,
+                            size_t workspace_bytes, int64_t* result, int32_t* device_error,
+                            void* stream) {
+    if (!head || !full_logits || !result) return LMH_ERR_NULL;
+    const WeightSpec w = head_weight(*head);
+    const ProjectCheck c = check_project_inputs(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
+                                                w, vocab, cu_seqlens, num_segments, num_decode,
+                                                logits_indices, num_indices);
+    if (c.st != LMH_OK) return c.st;
+    if (full_ld < vocab) return LMH_ERR_SHAPE;
+    if (!aligned(full_logits, 4) || !aligned(result, 8)) return LMH_ERR_ALIGN;
+    const int64_t ld = ceil_div(vocab, 4) * 4;
+    if (!workspace || !aligned(workspace, 256) ||
+        workspace_bytes < lmhead_selfcheck_workspace_size(c.rows, vocab))
+        return LMH_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (device_error) {
+        RowsArgs ra{cu_seqlens, num_segments, num_decode, num_tokens, logits_indices, c.rows,
+                    nullptr, nullptr, device_error};
+        const lmh_status st = from_hip(launch_rows(ra, s));
+        if (st != LMH_OK) return st;
+    }
+    float* sel = static_cast<float*>(workspace);
+    if (c.rows > 0) {
+        const HeadArgs h = head_args(hidden, num_tokens, hidden_dim, hidden_ld, w, vocab, cu_seqlens,
+                                     num_decode, logits_indices, 0, c.rows, sel, ld, false,
+                                     device_error);
+        const lmh_status st = launch_head(h, hidden_dt == LMH_BF16, LMH_HEAD_AUTO, s);
+        if (st != LMH_OK) return st;
+    }
+    return from_hip(launch_selfcheck(sel, ld, full_logits, full_ld, c.rows, vocab, cu_seqlens,
+                                     num_decode, num_tokens, logits_indices, result, s));
 }
 
 }  // extern "C"

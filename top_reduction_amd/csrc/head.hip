@@ -90,7 +90,16 @@ struct HeadParams {
     int32_t row0, R;
     void* out;
     int64_t old;
+    int32_t scale_mode;       // 0 none, 1 multiply by scale, 2 divide by scale
+    float scale;
 };
+
+// Head output scaling on the fp32 accumulator, before any output rounding
+// (vllm-metal release, Summary: heads that scale their logits outside the
+// projection). The division is IEEE fp32 division, correctly rounded.
+__device__ inline float scale_logit(float v, int32_t mode, float s) {
+    return mode == 1 ? v * s : (mode == 2 ? v / s : v);
+}
 
 // ---------------------------------------------------------------------------
 // Quantised-weight k order. One 16-byte run of codes (QB = 512/BITS hidden
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_head_stream(HeadParams p) {
             for (int e = 0; e < 4; ++e) {
                 const int r = i * 16 + (lane >> 4) * 4 + e;
                 if (r < p.R && v < p.V) {
-                    const float val = sIdx[r] < 0 ? kNaN : acc[i][j][e];
+                    const float val = sIdx[r] < 0 ? kNaN : scale_logit(acc[i][j][e], p.scale_mode, p.scale);
                     store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v, val);
                 }
             }
@@ -536,7 +545,7 @@ __global__ __launch_bounds__(kStreamQThreads) void k_head_stream_q(HeadParams p)
             for (int e = 0; e < 4; ++e) {
                 const int r = i * 16 + (lane >> 4) * 4 + e;
                 if (r < p.R && v < p.V) {
-                    const float val = sIdx[r] < 0 ? kNaN : acc[i][j][e];
+                    const float val = sIdx[r] < 0 ? kNaN : scale_logit(acc[i][j][e], p.scale_mode, p.scale);
                     store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v, val);
                 }
             }
@@ -823,7 +832,9 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
             const int32_t r = m0 + rl;
             const int cl = 4 * fr;
             const int64_t v = n0 + wn + cl;
-            const f32x4 val = *reinterpret_cast<const f32x4*>(&stg[rr * 68 + cl]);
+            f32x4 val = *reinterpret_cast<const f32x4*>(&stg[rr * 68 + cl]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[e] = scale_logit(val[e], p.scale_mode, p.scale);
             if (r < p.R) {
                 const bool valid = sIdx[rl] >= 0;
                 if (vec_ok && v + 4 <= p.V) {
@@ -847,6 +858,8 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
 // LDS by k-chunks of 128; one fp32 FMA per (row, column, k), k ascending.
 // ---------------------------------------------------------------------------
 struct HeadParamsF32 {
+    int32_t scale_mode;
+    float scale;
     const float* hidden;
     int64_t num_tokens, H, hld;
     const float* W;
@@ -898,7 +911,9 @@ __global__ __launch_bounds__(kThreads) void k_head_f32(HeadParamsF32 p) {
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             const int32_t r = m0 + i;
-            if (r < p.R) store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v, sIdx[i] < 0 ? kNaN : acc[i]);
+            if (r < p.R)
+                store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v,
+                                    sIdx[i] < 0 ? kNaN : scale_logit(acc[i], p.scale_mode, p.scale));
         }
     }
 }
@@ -919,6 +934,8 @@ HeadParams to_params(const HeadArgs& a) {
     p.R = a.rows;
     p.out = a.out;
     p.old = a.out_ld;
+    p.scale_mode = a.scale_mode;
+    p.scale = a.scale;
     p.qw.q = a.q;
     p.qw.qld = a.q_ld;
     p.qw.scales = a.scales;
@@ -1041,6 +1058,8 @@ hipError_t launch_head_tiled_q(const HeadArgs& a, hipStream_t s) {
 hipError_t launch_head_f32(const HeadArgs& a, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
     HeadParamsF32 p;
+    p.scale_mode = a.scale_mode;
+    p.scale = a.scale;
     p.hidden = static_cast<const float*>(a.hidden);
     p.num_tokens = a.num_tokens;
     p.H = a.hidden_dim;

@@ -96,6 +96,9 @@ struct HeadArgs {
     const uint16_t* biases = nullptr;
     int64_t s_ld = 0;
     int32_t gshift = 0;
+    // output scaling on the fp32 accumulator: 0 none, 1 multiply, 2 divide
+    int32_t scale_mode = 0;
+    float scale = 1.0f;
 };
 // bf16 MFMA heads. stream: R <= kStreamMaxRows; tiled: any R.
 hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s);
@@ -106,6 +109,15 @@ hipError_t launch_head_stream_q(const HeadArgs& a, hipStream_t s);
 hipError_t launch_head_tiled_q(const HeadArgs& a, hipStream_t s);
 // fp32 FMA head.
 hipError_t launch_head_f32(const HeadArgs& a, hipStream_t s);
+
+// Bitwise comparison of R selective logits rows `sel` [R][sel_ld] (fp32)
+// with the rows of `full` [num_tokens][full_ld] they were projected from
+// (row r against full row src(r); rows with no valid source are skipped):
+// res[0] = number of differing logits, res[1] = smallest r * vocab + v that
+// differs (INT64_MAX if none). `res` is initialised by the launch.
+hipError_t launch_selfcheck(const float* sel, int64_t sel_ld, const float* full, int64_t full_ld,
+                            int32_t rows, int64_t vocab, const int32_t* cu, int32_t num_decode,
+                            int64_t num_tokens, const int32_t* ex, int64_t* res, hipStream_t s);
 
 struct ReducePlan {
     int64_t rows, vocab;
