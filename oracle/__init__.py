@@ -31,7 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
 
-F32, BF16, F64 = 0, 1, 2
+F32, BF16, F64, F16 = 0, 1, 2, 3
 OK, ERR_LAYOUT, ERR_INDEX = 0, 1, 2
 BLOCK = 64
 
@@ -62,6 +62,8 @@ def load(path: str = _LIB_PATH):
     lib.orc_dequant.restype = None
     lib.orc_scale_logits.argtypes = [p, i64, ctypes.c_int, ctypes.c_double]
     lib.orc_scale_logits.restype = None
+    lib.orc_widen.argtypes = [p, ctypes.c_int, i64, p]
+    lib.orc_widen.restype = None
     lib.orc_reduce.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p]
     lib.orc_reduce.restype = None
     lib.orc_prefilter_check.argtypes = [p, ctypes.c_int, i64, i64, i64, i32, i32, i32, p]
@@ -84,7 +86,19 @@ def _dtype_code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float64:
         return F64
+    if a.dtype == np.float16:
+        return F16
     raise TypeError(f"unsupported oracle dtype {a.dtype}")
+
+
+def widen(a: np.ndarray, lib=None) -> np.ndarray:
+    """The oracle's exact f64 value of every element of a float32, raw-bf16
+    (uint16), float16 or float64 array."""
+    lib = lib or load()
+    a = np.ascontiguousarray(a)
+    out = np.empty(a.size, dtype=np.float64)
+    lib.orc_widen(_ptr(a), _dtype_code(a), a.size, _ptr(out))
+    return out.reshape(a.shape)
 
 
 def num_threads(lib=None) -> int:

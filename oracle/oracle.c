@@ -43,6 +43,7 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 #define ORC_F64 2
+#define ORC_F16 3
 
 /* status codes */
 #define ORC_OK 0
@@ -52,11 +53,30 @@
 static double widen(const void* base, int dt, int64_t i) {
     if (dt == ORC_F32) return (double)((const float*)base)[i];
     if (dt == ORC_F64) return ((const double*)base)[i];
+    if (dt == ORC_F16) {
+        /* IEEE binary16: sign, 5-bit exponent (bias 15), 10-bit fraction */
+        const uint16_t h = ((const uint16_t*)base)[i];
+        const int e = (h >> 10) & 0x1F;
+        const int m = h & 0x3FF;
+        double v;
+        if (e == 0)
+            v = ldexp((double)m, -24);                 /* subnormal: m * 2^-14 * 2^-10 */
+        else if (e == 31)
+            v = m ? NAN : INFINITY;
+        else
+            v = ldexp((double)(m | 0x400), e - 25);    /* (1 + m/1024) * 2^(e-15) */
+        return (h & 0x8000) ? -v : v;
+    }
     /* bf16: the top 16 bits of an IEEE binary32 */
     uint32_t u = (uint32_t)((const uint16_t*)base)[i] << 16;
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* f64 values of n elements of dtype dt (exposed for the pins of widen). */
+void orc_widen(const void* base, int dt, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = widen(base, dt, i);
 }
 
 /*

@@ -92,9 +92,17 @@ def _scale_ok(lib):
     return np.array_equal(z, ints.astype(np.float64))
 
 
+def _f16_ok(lib):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    got, want = oracle.widen(h, lib=lib), h.astype(np.float64)
+    nan = np.isnan(want)
+    return np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], want[~nan])
+
+
 def _all_pins_ok(lib):
     return (_rows_golden_ok(lib) and _head_integer_ok(lib) and _head_one_hot_ok(lib)
-            and _closed_forms_ok(lib) and _dequant_golden_ok(lib) and _scale_ok(lib))
+            and _closed_forms_ok(lib) and _dequant_golden_ok(lib) and _scale_ok(lib)
+            and _f16_ok(lib))
 
 
 MUTANTS = [
@@ -113,6 +121,9 @@ MUTANTS = [
     ("dequant group twice as wide", "const int64_t g = k / group;", "const int64_t g = k / (2 * group);"),
     ("multiply mode divides", "for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] * value;", "for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] / value;"),
     ("divide mode by the reciprocal", "for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] / value;", "for (int64_t i = 0; i < n; ++i) Z[i] = Z[i] * (1.0 / value);"),
+    ("f16 exponent bias off by one", "v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)(m | 0x400), e - 26);"),
+    ("f16 subnormal scale", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    ("f16 drops the implicit bit", "v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)m, e - 25);"),
     ("selected logprob adds lse", ": widen(logits, dt, base + t) - l;", ": widen(logits, dt, base + t) + l;"),
 ]
 
