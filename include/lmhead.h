@@ -361,15 +361,20 @@ const char* lmh_status_string(lmh_status status);
  * ------------------------------------------------------------------------- */
 
 /* Head kernel choices for lmh_debug_gather_project's `variant`. */
-#define LMH_HEAD_AUTO 0   /* weight streaming for R <= 64, tiled otherwise   */
+#define LMH_HEAD_AUTO 0   /* k-pipelined streaming where it applies and R >  */
+                          /* 16, weight streaming for other R <= 64, tiled    */
+                          /* otherwise                                        */
 #define LMH_HEAD_STREAM 1 /* weight-streaming kernel (requires R <= 64)      */
 #define LMH_HEAD_TILED 2  /* LDS-tiled kernel                                */
+#define LMH_HEAD_PIPE 3   /* k-pipelined weight streaming: bf16 weights,      */
+                          /* R <= 64, hidden 512, 1024, 1536 or 2048, and     */
+                          /* R * logits_ld * element size below 2^31 bytes    */
 
 /*
  * lmh_debug_gather_project -- lmhead_gather_project with the bf16 head kernel
- * forced (tests use it to show both kernels give bitwise-identical rows).
- * LMH_HEAD_STREAM with R > 64, or any non-auto variant with fp32 inputs,
- * returns LMH_ERR_SHAPE.
+ * forced (tests use it to show the kernels give bitwise-identical rows).
+ * LMH_HEAD_STREAM with R > 64, LMH_HEAD_PIPE outside its shapes, or any
+ * non-auto variant with fp32 inputs, returns LMH_ERR_SHAPE.
  */
 lmh_status lmh_debug_gather_project(
     const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,

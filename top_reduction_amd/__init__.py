@@ -33,7 +33,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblmhead.so")
 
 LMH_F32, LMH_BF16 = 0, 1
-LMH_HEAD_AUTO, LMH_HEAD_STREAM, LMH_HEAD_TILED = 0, 1, 2
+LMH_HEAD_AUTO, LMH_HEAD_STREAM, LMH_HEAD_TILED, LMH_HEAD_PIPE = 0, 1, 2, 3
 LMH_SCALE_NONE, LMH_SCALE_MUL, LMH_SCALE_DIV = 0, 1, 2
 LMH_DEVERR_INDEX, LMH_DEVERR_LAYOUT = 1, 2
 STATUS = {0: "LMH_OK", 1: "LMH_ERR_NULL", 2: "LMH_ERR_SHAPE", 3: "LMH_ERR_K",

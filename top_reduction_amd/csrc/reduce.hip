@@ -1109,8 +1109,6 @@ hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStr
                   : launch_stage2_dt<false>(p, a, s, part, keys, cap, lds);
 }
 
-namespace {
-
 // Compute units of the current device (cached per device id).
 int cu_count() {
     static int cache[64] = {0};
@@ -1123,6 +1121,8 @@ int cu_count() {
     }
     return cache[dev];
 }
+
+namespace {
 
 template <bool BF16, int KPT, bool KEYS>
 hipError_t launch_row_kpt(const ReducePlan& p, const ReduceArgs& a, hipStream_t s, int32_t cap, size_t lds) {
