@@ -79,7 +79,10 @@ typedef enum {
     LMH_ERR_HIP = 7        /* a HIP launch failed                               */
 } lmh_status;
 
-typedef enum { LMH_F32 = 0, LMH_BF16 = 1 } lmh_dtype;
+/* LMH_F16 (IEEE binary16) is accepted for the logits of logprob_reduce only
+ * [MTPLX PR #532, Tests: bf16/f16 logits]; every other dtype argument takes
+ * LMH_F32 or LMH_BF16. */
+typedef enum { LMH_F32 = 0, LMH_BF16 = 1, LMH_F16 = 2 } lmh_dtype;
 
 /* device_error bits */
 #define LMH_DEVERR_INDEX 1  /* a row index or selected id outside its range            */
@@ -145,8 +148,8 @@ size_t logprob_reduce_workspace_size(int64_t rows, int64_t vocab, int32_t k);
  * logprob_reduce -- per-row logsumexp, selected logprob and exact top-K
  * [MTPLX, openinfer].
  *
- * logits  [rows][vocab], pitch logits_ld, fp32 or bf16; 16-B aligned base
- *         and pitch.
+ * logits  [rows][vocab], pitch logits_ld, fp32, bf16 or f16; 16-B aligned
+ *         base and pitch. f16 and bf16 values are widened to fp32 exactly.
  * selected_ids [rows] int32 or NULL (then selected_logprob is not written).
  * k       0 <= k <= vocab and min(k, ceil(vocab/64)) * 64 <= 8192 (so k <= 128
  *         at vocabularies above 8192). k = 0 computes lse and the selected

@@ -133,10 +133,11 @@ def _scoring_rows_f32(g, dist: str, rows: int, vocab: int) -> np.ndarray:
 
 def scoring_chunk(seed: int, dist: str, k: int, rows: int = 256,
                   vocab: int = VOCAB_SCORING, neg_inf_frac: float = 1e-3,
-                  plant_ties: bool = True):
-    """Prompt-scoring chunk of bf16 logits (raw bits) plus uniform selected ids.
+                  plant_ties: bool = True, dtype: str = "bf16"):
+    """Prompt-scoring chunk of bf16 logits (raw bits; ``dtype='f16'``: an IEEE
+    binary16 array instead) plus uniform selected ids.
 
-    Per row: the distribution's draw, rounded to bf16; about ``neg_inf_frac``
+    Per row: the distribution's draw, rounded to bf16 (or f16, nearest even); about ``neg_inf_frac``
     of the entries (uniform positions, drawn with replacement) and one whole
     64-logit block set to -inf; then, when 0 < ``k`` < vocab, exact ties
     planted at the K-th value v_K (K-th under value-desc/id-asc): v_K is
@@ -145,14 +146,17 @@ def scoring_chunk(seed: int, dist: str, k: int, rows: int = 256,
     maximum is below v_K (that block's maximum becomes v_K, so equal block
     maxima meet at the selection boundary), and one anywhere.
     """
+    if dtype not in ("bf16", "f16"):
+        raise ValueError(dtype)
     g = rng(seed)
     nb = (vocab + BLOCK - 1) // BLOCK
     bits = np.empty((rows, vocab), dtype=np.uint16)
-    neg_inf_bits = np.uint16(0xFF80)
+    neg_inf_bits = np.uint16(0xFF80 if dtype == "bf16" else 0xFC00)
     step = 32
     for r0 in range(0, rows, step):
         r1 = min(rows, r0 + step)
-        bits[r0:r1] = f32_to_bf16_bits(_scoring_rows_f32(g, dist, r1 - r0, vocab))
+        x = _scoring_rows_f32(g, dist, r1 - r0, vocab)
+        bits[r0:r1] = f32_to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float16).view(np.uint16)
     n_inf = int(round(neg_inf_frac * vocab))
     if n_inf:
         pos = g.integers(0, vocab, size=(rows, n_inf))
@@ -163,14 +167,14 @@ def scoring_chunk(seed: int, dist: str, k: int, rows: int = 256,
         bits[r, b0:min(vocab, b0 + BLOCK)] = neg_inf_bits
     if plant_ties and 0 < k < vocab:
         for r in range(rows):
-            _plant_ties(g, bits[r], k)
+            _plant_ties(g, bits[r], k, dtype)
     sel = g.integers(0, vocab, size=rows).astype(np.int32)
-    return bits, sel
+    return (bits if dtype == "bf16" else bits.view(np.float16)), sel
 
 
-def _plant_ties(g, b: np.ndarray, k: int) -> None:
+def _plant_ties(g, b: np.ndarray, k: int, dtype: str = "bf16") -> None:
     vocab = b.shape[0]
-    xf = bf16_bits_to_f32(b).astype(np.float64)
+    xf = (bf16_bits_to_f32(b) if dtype == "bf16" else b.view(np.float16)).astype(np.float64)
     v_k = -np.partition(-xf, k - 1)[k - 1]      # K-th largest value
     if not np.isfinite(v_k):
         return

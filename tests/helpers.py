@@ -40,7 +40,8 @@ def check_reduce(out, logits_np, sel, k, lse_ref, sel_ref, ids_ref, lp_ref, atol
     assert np.array_equal(np.isnan(lse), np.isnan(lse_ref))
     assert np.array_equal(np.isneginf(lse), np.isneginf(lse_ref))
     fin = np.isfinite(lse_ref)
-    assert np.all(np.abs(lse[fin] - lse_ref[fin]) <= atol), np.max(np.abs(lse[fin] - lse_ref[fin]))
+    lse_tol = np.maximum(atol, np.abs(lse_ref[fin]) * 2.0 ** -23)   # see _close_or_same_special
+    assert np.all(np.abs(lse[fin] - lse_ref[fin]) <= lse_tol), np.max(np.abs(lse[fin] - lse_ref[fin]))
     x = as_f32(logits_np)
     if sel is not None:
         s = out.selected_logprob.cpu().numpy()
@@ -56,6 +57,10 @@ def check_reduce(out, logits_np, sel, k, lse_ref, sel_ref, ids_ref, lp_ref, atol
 
 
 def _close_or_same_special(a, ref, atol):
+    """|a - ref| <= atol, or one fp32 ulp of ref (2^-23 |ref|) where that is
+    larger: above |ref| = 84 an fp32 result cannot be within 1e-5 of every
+    exact value (half an ulp exceeds it), and the GPU's lse and logprobs are
+    fp32 by definition (MTPLX PR #532, Change)."""
     a = np.asarray(a, dtype=np.float64)
     nan_ref = np.isnan(ref)
     assert np.array_equal(np.isnan(a), nan_ref)
@@ -63,8 +68,9 @@ def _close_or_same_special(a, ref, atol):
     assert np.array_equal(a[inf_ref], ref[inf_ref])
     m = ~nan_ref & ~inf_ref
     if m.any():
-        d = np.max(np.abs(a[m] - ref[m]))
-        assert d <= atol, d
+        d = np.abs(a[m] - ref[m])
+        tol = np.maximum(atol, np.abs(ref[m]) * 2.0 ** -23)
+        assert np.all(d <= tol), float(np.max(d - tol))
 
 
 def _first_diff(a, b):

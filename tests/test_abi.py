@@ -12,7 +12,7 @@ HEADER = os.path.join(ROOT, "include", "lmhead.h")
 LIB = os.path.join(ROOT, "top_reduction_amd", "liblmhead.so")
 
 OK, NULL, SHAPE, K, DTYPE, ALIGN, WS, HIP = range(8)
-F32, BF16, BAD_DT = 0, 1, 7
+F32, BF16, F16, BAD_DT = 0, 1, 2, 7
 A = 0x10000  # a 256-aligned stand-in address; never dereferenced on these paths
 
 
@@ -68,6 +68,7 @@ def _project(L, **kw):
     (dict(hidden_ld=32), SHAPE), (dict(weight_ld=63), SHAPE), (dict(logits_ld=999), SHAPE),
     (dict(ex=A, nex=-1), SHAPE),
     (dict(hidden_dt=BAD_DT, weight_dt=BAD_DT), DTYPE), (dict(weight_dt=F32), DTYPE),
+    (dict(hidden_dt=F16, weight_dt=F16), DTYPE), (dict(logits_dt=F16), DTYPE),   # f16: reduction only
     (dict(logits_dt=BAD_DT), DTYPE),
     (dict(hidden=A + 8), ALIGN), (dict(weight=A + 2), ALIGN), (dict(hidden_dim=60, hidden_ld=64), ALIGN),
     (dict(hidden_ld=68), ALIGN), (dict(logits=A + 2), ALIGN),
@@ -135,6 +136,7 @@ def _reduce(L, **kw):
     (dict(rows=-1), SHAPE), (dict(vocab=0), SHAPE), (dict(ld=248319), SHAPE),
     (dict(dt=BAD_DT), DTYPE),
     (dict(logits=A + 8), ALIGN), (dict(ld=248324), ALIGN),
+    (dict(dt=F16, wsb=1024), WS), (dict(dt=F16, ld=248324), ALIGN),   # f16 logits are accepted
     (dict(k=-1), K), (dict(k=129), K), (dict(vocab=100, ld=104, k=101), K),
     (dict(vocab=9 * 8192 * 64, ld=9 * 8192 * 64, k=1), SHAPE),
     (dict(ws=None), WS), (dict(wsb=1024), WS), (dict(ws=A + 16), WS),

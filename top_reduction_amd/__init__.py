@@ -32,7 +32,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblmhead.so")
 
-LMH_F32, LMH_BF16 = 0, 1
+LMH_F32, LMH_BF16, LMH_F16 = 0, 1, 2
 LMH_HEAD_AUTO, LMH_HEAD_STREAM, LMH_HEAD_TILED, LMH_HEAD_PIPE = 0, 1, 2, 3
 LMH_SCALE_NONE, LMH_SCALE_MUL, LMH_SCALE_DIV = 0, 1, 2
 LMH_DEVERR_INDEX, LMH_DEVERR_LAYOUT = 1, 2
@@ -114,11 +114,15 @@ def _stream():
 
 
 def _dt(t: torch.Tensor) -> int:
+    """lmh_dtype of a tensor (the library rejects f16 everywhere but in the
+    reduction's logits)."""
     if t.dtype == torch.bfloat16:
         return LMH_BF16
     if t.dtype == torch.float32:
         return LMH_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+    if t.dtype == torch.float16:
+        return LMH_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16, f16 or fp32)")
 
 
 def _matrix(t: torch.Tensor, name: str):

@@ -13,7 +13,8 @@ namespace {
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline bool valid_dtype(lmh_dtype d) { return d == LMH_F32 || d == LMH_BF16; }
-inline size_t esize(lmh_dtype d) { return d == LMH_BF16 ? 2 : 4; }
+inline bool valid_logits_dtype(lmh_dtype d) { return valid_dtype(d) || d == LMH_F16; }   // reduction input
+inline size_t esize(lmh_dtype d) { return d == LMH_F32 ? 4 : 2; }
 inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -101,7 +102,7 @@ ProjectCheck check_project_inputs(const void* hidden, lmh_dtype hidden_dt, int64
 lmh_status check_reduce_shape(lmh_dtype dt, int64_t rows, int64_t vocab, int64_t ld, int32_t k) {
     if (rows < 0 || rows > INT32_MAX || vocab <= 0 || vocab > INT32_MAX || ld < vocab)
         return LMH_ERR_SHAPE;
-    if (!valid_dtype(dt)) return LMH_ERR_DTYPE;
+    if (!valid_logits_dtype(dt)) return LMH_ERR_DTYPE;
     if (((size_t)ld * esize(dt)) % 16) return LMH_ERR_ALIGN;
     const int64_t nb = ceil_div(vocab, kBlock);
     if (k < 0 || k > vocab) return LMH_ERR_K;
@@ -236,7 +237,7 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
         q.part_off = pc.part_off;
         q.keys_off = pc.keys_off;
         q.bytes = pc.bytes;
-        ReduceArgs a{out, false, ld, selected_ids ? selected_ids + r0 : nullptr, lse + r0,
+        ReduceArgs a{out, LMH_F32, ld, selected_ids ? selected_ids + r0 : nullptr, lse + r0,
                      selected_ids ? selected_logprob + r0 : nullptr,
                      k > 0 ? topk_ids + r0 * k : nullptr, k > 0 ? topk_logprobs + r0 * k : nullptr,
                      ws_reduce, device_error};
@@ -353,7 +354,7 @@ lmh_status logprob_reduce(const void* logits, lmh_dtype logits_dt, int64_t rows,
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.bytes) return LMH_ERR_WORKSPACE;
     if (rows == 0) return LMH_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    ReduceArgs a{logits, logits_dt == LMH_BF16, logits_ld, selected_ids, lse, selected_logprob,
+    ReduceArgs a{logits, (int32_t)logits_dt, logits_ld, selected_ids, lse, selected_logprob,
                  topk_ids, topk_logprobs, workspace, device_error};
     return from_hip(launch_reduce(p, a, s));
 }
@@ -368,7 +369,7 @@ lmh_status lmh_debug_reduce_stage1(const void* logits, lmh_dtype logits_dt, int6
     const ReducePlan p = plan_reduce(rows, vocab, k);
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.bytes) return LMH_ERR_WORKSPACE;
     if (rows == 0) return LMH_OK;
-    ReduceArgs a{logits, logits_dt == LMH_BF16, logits_ld, nullptr, nullptr, nullptr,
+    ReduceArgs a{logits, (int32_t)logits_dt, logits_ld, nullptr, nullptr, nullptr,
                  nullptr, nullptr, workspace, nullptr};
     return from_hip(launch_reduce_stage1(p, a, static_cast<hipStream_t>(stream)));
 }

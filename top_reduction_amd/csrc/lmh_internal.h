@@ -140,7 +140,7 @@ ReducePlan plan_reduce(int64_t rows, int64_t vocab, int32_t k);
 
 struct ReduceArgs {
     const void* logits;
-    bool bf16;
+    int32_t dt;          // LMH_F32, LMH_BF16 or LMH_F16
     int64_t ld;
     const int32_t* sel;  // may be nullptr
     float* lse;

@@ -19,6 +19,8 @@
 //   * k_stage1 + k_stage2 (otherwise): a streaming launch over all rows
 //     writes partials and keys to the workspace, then one workgroup per row
 //     finishes it.
+#include <type_traits>
+
 #include "lmh_internal.h"
 
 namespace lmh {
@@ -85,19 +87,63 @@ __device__ inline void lse_merge(float& m, float& s, float m2, float s2) {
     m = M;
 }
 
-template <bool BF16>
-__device__ inline uint32_t elem_key(float x) {
-    return BF16 ? (f32_key(x) & 0xFFFF0000u) : f32_key(x);
+// Logits element types. Both 16-bit types stream 8 elements per 16-byte vector
+// and keep 16-bit block keys (in the top half of a 32-bit key).
+constexpr int kDtF32 = LMH_F32, kDtBf16 = LMH_BF16, kDtF16 = LMH_F16;
+constexpr bool w16(int dt) { return dt != kDtF32; }
+
+__device__ inline float f16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+// The low and high 16-bit elements of a word as fp32 (exact).
+template <int DT>
+__device__ inline float lo16(uint32_t w) {
+    return DT == kDtBf16 ? bf16_lo(w) : f16_bits_to_f32(w & 0xFFFFu);
+}
+template <int DT>
+__device__ inline float hi16(uint32_t w) {
+    return DT == kDtBf16 ? bf16_hi(w) : f16_bits_to_f32(w >> 16);
+}
+// One element of a 16-bit row.
+template <int DT>
+__device__ inline float elem16(const uint8_t* rowp, int64_t i) {
+    const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[i];
+    return DT == kDtBf16 ? bf16_to_f32((uint16_t)h) : f16_bits_to_f32(h);
+}
+// -inf in both halves of a word (16-bit types) or the word (fp32)
+template <int DT>
+constexpr uint32_t ninf_word() {
+    return DT == kDtBf16 ? 0xFF80FF80u : (DT == kDtF16 ? 0xFC00FC00u : 0xFF800000u);
 }
 
-template <bool BF16>
-__device__ inline float key_value(uint32_t k) {
-    if (BF16) {
-        const uint32_t k16 = k >> 16;
-        const uint32_t b = (k16 & 0x8000u) ? (k16 & 0x7FFFu) : (~k16 & 0xFFFFu);
-        return __uint_as_float(b << 16);
+// Block keys: a monotone map of the block maximum, -0 folded into +0. fp32:
+// the 32-bit key; bf16: its top 16 bits (exact for a bf16 value); f16: the
+// 16-bit key of the f16 bits, in the top half.
+template <int DT>
+__device__ inline uint32_t block_key(float x) {
+    if (DT == kDtF16) {
+        uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)x);   // exact: x is an f16 value
+        h = (x == 0.0f) ? 0u : h;
+        return ((h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u)) << 16;
     }
-    return key_f32(k);
+    return DT == kDtBf16 ? (f32_key(x) & 0xFFFF0000u) : f32_key(x);
+}
+template <int DT>
+__device__ inline float block_value(uint32_t k) {
+    if (DT == kDtF32) return key_f32(k);
+    const uint32_t k16 = k >> 16;
+    const uint32_t b = (k16 & 0x8000u) ? (k16 & 0x7FFFu) : (~k16 & 0xFFFFu);
+    return DT == kDtBf16 ? __uint_as_float(b << 16) : f16_bits_to_f32(b);
+}
+// Candidate keys (ranking among a row's candidates): the block key for bf16,
+// the full 32-bit key otherwise.
+template <int DT>
+__device__ inline uint32_t elem_key(float x) {
+    return DT == kDtBf16 ? (f32_key(x) & 0xFFFF0000u) : f32_key(x);
+}
+template <int DT>
+__device__ inline float elem_value(uint32_t k) {
+    return DT == kDtBf16 ? block_value<kDtBf16>(k) : key_f32(k);
 }
 
 // ---------------------------------------------------------------------------
@@ -147,9 +193,9 @@ __device__ inline float select_reg(const float (&v)[N], int r) {
     return t[0];
 }
 
-template <bool BF16>
+template <int DT>
 struct Stage1Item {
-    static constexpr int EPV = BF16 ? 8 : 4;          // elements per 16-byte vector
+    static constexpr int EPV = w16(DT) ? 8 : 4;          // elements per 16-byte vector
     static constexpr int VPB = kBlock / EPV;          // lanes per 64-logit block
     static constexpr int VPL = kSeg / EPV / 64;       // vectors per lane (== VPB)
     static constexpr int GPV = 64 / VPB;              // blocks per wave-wide vector
@@ -163,10 +209,10 @@ constexpr int kGroups = 16;   // merge groups of a row's item partials
 // Reduces one item held in buf (VPL vectors per lane; entries past V hold
 // -inf): M and S (the item's max and its sum of exp(x - M)) come back
 // wave-uniform; with KEYS, kb is the monotone key of block seg*64 + lane.
-template <bool BF16, bool KEYS>
-__device__ __forceinline__ void stage1_item(const u32x4 (&buf)[Stage1Item<BF16>::VPL], int lane, float& M,
+template <int DT, bool KEYS>
+__device__ __forceinline__ void stage1_item(const u32x4 (&buf)[Stage1Item<DT>::VPL], int lane, float& M,
                                             float& S, uint32_t& kb) {
-    using I = Stage1Item<BF16>;
+    using I = Stage1Item<DT>;
     float x[I::VPL * I::EPV];
     float bm[I::VPL];
     float lm = kNegInf;
@@ -175,11 +221,11 @@ __device__ __forceinline__ void stage1_item(const u32x4 (&buf)[Stage1Item<BF16>:
         const uint32_t w[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
         float* xv = x + j * I::EPV;
         float vm;
-        if (BF16) {
+        if (w16(DT)) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                xv[2 * e] = bf16_lo(w[e]);
-                xv[2 * e + 1] = bf16_hi(w[e]);
+                xv[2 * e] = lo16<DT>(w[e]);
+                xv[2 * e + 1] = hi16<DT>(w[e]);
             }
             vm = vmax3(xv[6], xv[7], vmax(vmax3(xv[0], xv[1], xv[2]), vmax3(xv[3], xv[4], xv[5])));
         } else {
@@ -211,15 +257,15 @@ __device__ __forceinline__ void stage1_item(const u32x4 (&buf)[Stage1Item<BF16>:
         // from lane (b % GPV)*VPB + b / GPV
         const float mine = select_reg<I::VPL>(bm, lane % I::VPB);
         const int src = (lane % I::GPV) * I::VPB + lane / I::GPV;
-        kb = f32_key(__int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(mine))));
+        kb = block_key<DT>(__int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(mine))));
     }
 }
 
 // Loads full item `seg` of a row into buf: one 16-byte load per vector.
-template <bool BF16>
+template <int DT>
 __device__ __forceinline__ void stage1_load_full(const uint8_t* rowp, int32_t seg, int lane,
-                                                 u32x4 (&buf)[Stage1Item<BF16>::VPL]) {
-    using I = Stage1Item<BF16>;
+                                                 u32x4 (&buf)[Stage1Item<DT>::VPL]) {
+    using I = Stage1Item<DT>;
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp) + (int64_t)seg * (kSeg / I::EPV);
 #pragma unroll
     for (int j = 0; j < I::VPL; ++j) buf[j] = vp[j * 64 + lane];
@@ -228,10 +274,10 @@ __device__ __forceinline__ void stage1_load_full(const uint8_t* rowp, int32_t se
 // Loads item `seg` of a row into buf. Full items: one 16-byte load per vector,
 // all issued before any is used. The partial last item fills entries past V
 // with -inf (16-byte loads up to the last whole vector, then elementwise).
-template <bool BF16>
+template <int DT>
 __device__ __forceinline__ bool stage1_load(const uint8_t* rowp, int64_t V, int32_t seg, int lane,
-                                            u32x4 (&buf)[Stage1Item<BF16>::VPL]) {
-    using I = Stage1Item<BF16>;
+                                            u32x4 (&buf)[Stage1Item<DT>::VPL]) {
+    using I = Stage1Item<DT>;
     constexpr int EPV = I::EPV;
     const int64_t vb = (int64_t)seg * (kSeg / EPV);
     const bool full = vb + kSeg / EPV <= V / EPV;   // wave-uniform: no element past V
@@ -244,7 +290,7 @@ __device__ __forceinline__ bool stage1_load(const uint8_t* rowp, int64_t V, int3
     // all whole-vector loads issued unguarded (addresses clamped to the last
     // whole vector), then entries past V replaced by -inf; only the vector
     // that straddles V (when V is not a multiple of EPV) is read elementwise
-    const uint32_t ninf_word = BF16 ? 0xFF80FF80u : 0xFF800000u;
+    constexpr uint32_t ninf_w = ninf_word<DT>();
     const int64_t nwhole = V / EPV;                     // whole vectors in the row
     const u32x4* rv = reinterpret_cast<const u32x4*>(rowp);
     if (nwhole > 0) {
@@ -258,12 +304,12 @@ __device__ __forceinline__ bool stage1_load(const uint8_t* rowp, int64_t V, int3
     for (int j = 0; j < I::VPL; ++j) {
         const int64_t v = vb + j * 64 + lane;
         if (v >= nwhole) {
-            uint32_t w[4] = {ninf_word, ninf_word, ninf_word, ninf_word};
+            uint32_t w[4] = {ninf_w, ninf_w, ninf_w, ninf_w};
             if (v == nwhole) {   // the vector that straddles V, if any
                 for (int e = 0; e < EPV; ++e) {
                     const int64_t i = v * EPV + e;
                     if (i < V) {
-                        if (BF16) {
+                        if (w16(DT)) {
                             const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[i];
                             w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | (h << 16))
                                                 : ((w[e >> 1] & 0xFFFF0000u) | h);
@@ -282,12 +328,12 @@ __device__ __forceinline__ bool stage1_load(const uint8_t* rowp, int64_t V, int3
 // Split path, first kernel: one item per wave over all rows, items numbered
 // row-major so that consecutively dispatched waves stream consecutive memory;
 // writes each item's partial and its block keys to the workspace.
-template <bool BF16, bool KEYS>
+template <int DT, bool KEYS>
 __global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__ logits, int64_t ld,
                                                      int64_t V, int32_t kld, int32_t P, int64_t nitems,
                                                      float2* __restrict__ part, void* __restrict__ keys) {
-    using I = Stage1Item<BF16>;
-    constexpr size_t ESZ = BF16 ? 2 : 4;
+    using I = Stage1Item<DT>;
+    constexpr size_t ESZ = w16(DT) ? 2 : 4;
     const int lane = threadIdx.x & 63;
     // wave-uniform item arithmetic in scalar registers (item count < 2^32)
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -301,19 +347,19 @@ __global__ __launch_bounds__(kThreads) void k_stage1(const uint8_t* __restrict__
     u32x4 buf[I::VPL];
     float M, S;
     uint32_t kb = 0;
-    if (stage1_load<BF16>(rowp, V, seg, lane, buf)) {
+    if (stage1_load<DT>(rowp, V, seg, lane, buf)) {
         // every load issued before any result is used (the scheduler would
         // otherwise hoist the first unpack between them and wait on it)
         __builtin_amdgcn_sched_barrier(0);
-        stage1_item<BF16, KEYS>(buf, lane, M, S, kb);
+        stage1_item<DT, KEYS>(buf, lane, M, S, kb);
     } else {
-        stage1_item<BF16, KEYS>(buf, lane, M, S, kb);
+        stage1_item<DT, KEYS>(buf, lane, M, S, kb);
     }
     if (lane == 0) part[itu] = make_float2(M, S);
     if (KEYS) {
         const int64_t blk = (int64_t)seg * (kSeg / kBlock) + lane;
         if (blk * kBlock < V) {
-            if (BF16)
+            if (w16(DT))
                 reinterpret_cast<uint16_t*>(keys)[row * kld + blk] = (uint16_t)(kb >> 16);
             else
                 reinterpret_cast<uint32_t*>(keys)[row * kld + blk] = kb;
@@ -478,13 +524,13 @@ struct RowShared {
     float lse;
 };
 
-template <bool BF16, int KPT, int NT>
+template <int DT, int KPT, int NT>
 __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t V, int32_t nb, int32_t K,
                          const uint32_t (&kr)[KPT], const float* lse_p, uint64_t* cand, uint64_t* list2,
                          int32_t cap,
                          RowShared<NT>& sh, int32_t* __restrict__ topk_ids, float* __restrict__ topk_lp) {
-    constexpr size_t ESZ = BF16 ? 2 : 4;
-    constexpr int EPV = BF16 ? 8 : 4;                 // elements per 16-byte vector
+    constexpr size_t ESZ = w16(DT) ? 2 : 4;
+    constexpr int EPV = w16(DT) ? 8 : 4;                 // elements per 16-byte vector
     constexpr int VPB = kBlock / EPV;                 // vectors per block
     constexpr int MAXV = (kMaxCandidates / EPV + NT - 1) / NT;   // vectors per thread, at most
     constexpr int MAXBLK = kMaxCandidates / kBlock;
@@ -507,7 +553,7 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
         uint32_t mm[3] = {tmax, ~tmin, b0 < nb ? ~tmax : 0u};
         block_reduce<1, 3, NT>(mm, sh.sred, phase);
         const int nth = (nb + KPT - 1) / KPT;           // threads holding blocks
-        const int ksh = BF16 ? 16 : 0;
+        const int ksh = w16(DT) ? 16 : 0;
         // Largest t with count(key >= t) >= K; count(>= lo) >= K > count(>= hi).
         uint64_t lo = (uint64_t)((K <= nth ? ~mm[2] : ~mm[1]) >> ksh);
         uint64_t hi = (uint64_t)(mm[0] >> ksh) + 1;
@@ -633,12 +679,12 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
                 const u32x4 v4 = *reinterpret_cast<const u32x4*>(rowp + (size_t)e0[i] * ESZ);
                 w[i][0] = v4.x; w[i][1] = v4.y; w[i][2] = v4.z; w[i][3] = v4.w;
             } else {
-                const uint32_t ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
+                const uint32_t ninf = ninf_word<DT>();
                 w[i][0] = w[i][1] = w[i][2] = w[i][3] = ninf;
                 for (int e = 0; e < EPV; ++e) {
                     const int64_t idx = e0[i] + e;
                     if (idx < V) {
-                        if (BF16) {
+                        if (w16(DT)) {
                             const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[idx];
                             w[i][e >> 1] = (e & 1) ? ((w[i][e >> 1] & 0x0000FFFFu) | (h << 16))
                                                    : ((w[i][e >> 1] & 0xFFFF0000u) | h);
@@ -652,7 +698,7 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
     }
     // key >= T  <=>  x >= Tf for the values this row can hold (T == 0: all)
     const bool keep_all = T == 0u;
-    const float Tf = keep_all ? kNegInf : key_value<BF16>(T);
+    const float Tf = keep_all ? kNegInf : block_value<DT>(T);
     uint32_t cnt = 0;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
@@ -660,7 +706,7 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
         const bool vfull = e0[i] + EPV <= V;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-            const float x = BF16 ? ((e & 1) ? bf16_hi(w[i][e >> 1]) : bf16_lo(w[i][e >> 1]))
+            const float x = w16(DT) ? ((e & 1) ? hi16<DT>(w[i][e >> 1]) : lo16<DT>(w[i][e >> 1]))
                                  : __uint_as_float(w[i][e]);
             cnt += ((vfull || e0[i] + e < V) && (keep_all || x >= Tf)) ? 1u : 0u;
         }
@@ -674,12 +720,12 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
         const bool vfull = e0[i] + EPV <= V;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-            const float x = BF16 ? ((e & 1) ? bf16_hi(w[i][e >> 1]) : bf16_lo(w[i][e >> 1]))
+            const float x = w16(DT) ? ((e & 1) ? hi16<DT>(w[i][e >> 1]) : lo16<DT>(w[i][e >> 1]))
                                  : __uint_as_float(w[i][e]);
             const int64_t v = e0[i] + e;
             if ((vfull || v < V) && (keep_all || x >= Tf)) {
                 if (cpos < cap)
-                    cand[cpos] = ((uint64_t)elem_key<BF16>(x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+                    cand[cpos] = ((uint64_t)elem_key<DT>(x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
                 ++cpos;
             }
         }
@@ -727,7 +773,7 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
         if (G == 4) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0x4E, 0xF, 0xF, false);
         if (act && q == 0 && rank < (uint32_t)K) {
             topk_ids[row * K + rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
-            topk_lp[row * K + rank] = key_value<BF16>((uint32_t)(c >> 32)) - lse;
+            topk_lp[row * K + rank] = elem_value<DT>((uint32_t)(c >> 32)) - lse;
         }
     }
 }
@@ -744,10 +790,10 @@ __device__ inline float lse_of_groups(const float2* g) {
 
 // The selected token's logit (a5), loaded long before its logprob is
 // written; an id outside [0, V) gives NaN and the index error bit.
-template <bool BF16>
+template <int DT>
 __device__ inline float load_selected(const uint8_t* rowp, int64_t V, int32_t sel_id) {
     if (sel_id < 0 || (int64_t)sel_id >= V) return __builtin_nanf("");
-    return BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[sel_id])
+    return w16(DT) ? elem16<DT>(rowp, sel_id)
                 : reinterpret_cast<const float*>(rowp)[sel_id];
 }
 __device__ inline void write_selected(int64_t V, int32_t sel_id, float xsel, float lse, float* out,
@@ -764,7 +810,7 @@ __device__ inline void write_selected(int64_t V, int32_t sel_id, float xsel, flo
 // Split path, second kernel: one workgroup of 256 threads per row reads the
 // row's item partials and block keys from the workspace.
 // ---------------------------------------------------------------------------
-template <bool BF16, int KPT>
+template <int DT, int KPT>
 __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__ logits, int64_t ld,
                                                      int64_t V, int32_t nb, int32_t kld, int32_t splits,
                                                      const float2* __restrict__ part,
@@ -778,7 +824,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     extern __shared__ uint64_t smem[];   // [cap] candidates, [K] narrowed list
     __shared__ RowShared<kThreads> sh;
     __shared__ float2 sgrp[kGroups];
-    constexpr size_t ESZ = BF16 ? 2 : 4;
+    constexpr size_t ESZ = w16(DT) ? 2 : 4;
     constexpr int MAXBLK = kMaxCandidates / kBlock;
 
     const int64_t row = blockIdx.x;
@@ -796,7 +842,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
 #pragma unroll
     for (int j = 0; j < KPT; ++j) kr[j] = 0u;
     if (K > 0 && K <= nb && b0 < nb) {
-        if (BF16) {
+        if (w16(DT)) {
             const uint16_t* kp = reinterpret_cast<const uint16_t*>(keys) + row * kld + b0;
             if (KPT == 4) {
                 const uint2 q = *reinterpret_cast<const uint2*>(kp);
@@ -855,9 +901,9 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     __syncthreads();
     const float lse = sh.lse;
     // the selected logit: loaded now, written after the top-K
-    const float xsel = sel_thread ? load_selected<BF16>(rowp, V, sel_id) : 0.f;
+    const float xsel = sel_thread ? load_selected<DT>(rowp, V, sel_id) : 0.f;
     if (K > 0)
-        row_topk<BF16, KPT, kThreads>(rowp, row, V, nb, K, kr, &sh.lse, smem, smem + cap, cap, sh, topk_ids,
+        row_topk<DT, KPT, kThreads>(rowp, row, V, nb, K, kr, &sh.lse, smem, smem + cap, cap, sh, topk_ids,
                                       topk_lp);
     if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
 }
@@ -873,10 +919,10 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = kGroups * 64;
 constexpr int kRowMaxItems = 64;   // items per row on this path (V <= 64 * kSeg)
-template <bool BF16> struct KeyType { using type = uint32_t; };
+template <bool W16> struct KeyType { using type = uint32_t; };
 template <> struct KeyType<true> { using type = uint16_t; };
 
-template <bool BF16, int KPT, bool KEYS>
+template <int DT, int KPT, bool KEYS>
 __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __restrict__ logits, int64_t ld,
                                                            int64_t V, int32_t nb, int32_t P,
                                                            const int32_t* __restrict__ sel, int32_t K,
@@ -885,15 +931,15 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
                                                            int32_t* __restrict__ topk_ids,
                                                            float* __restrict__ topk_lp,
                                                            int32_t* __restrict__ err, int32_t cap) {
-    using I = Stage1Item<BF16>;
-    using key_t = typename KeyType<BF16>::type;
+    using I = Stage1Item<DT>;
+    using key_t = typename KeyType<w16(DT)>::type;
     extern __shared__ uint64_t smem[];   // [KPT*256] keys, then [cap] candidates, [K] narrowed list
     __shared__ RowShared<kThreads> sh;
     __shared__ float2 sgrp[kGroups];
     __shared__ float2 sitem[kRowMaxItems];
     __shared__ int32_t s_next, s_sel;
     __shared__ float s_xsel;
-    constexpr size_t ESZ = BF16 ? 2 : 4;
+    constexpr size_t ESZ = w16(DT) ? 2 : 4;
     constexpr int MAXBLK = kMaxCandidates / kBlock;
     key_t* skeys = reinterpret_cast<key_t*>(smem);
     uint64_t* cand = smem + (KPT * kThreads * sizeof(key_t) + 7) / 8;
@@ -923,7 +969,7 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     if (sel_thread) {
         sel_id = sel[row];
         s_sel = sel_id;
-        xsel = load_selected<BF16>(rowp, V, sel_id);
+        xsel = load_selected<DT>(rowp, V, sel_id);
     }
 
     // Items are handed out dynamically (wave w starts with item w, then takes
@@ -933,10 +979,10 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     auto reduce_item = [&](const u32x4 (&buf)[I::VPL], int32_t seg) {
         float M, S;
         uint32_t kb = 0;
-        stage1_item<BF16, KEYS>(buf, lane, M, S, kb);
+        stage1_item<DT, KEYS>(buf, lane, M, S, kb);
         if (KEYS) {
             const int32_t blk = seg * (kSeg / kBlock) + lane;
-            if (blk < nb) skeys[blk] = BF16 ? (key_t)(kb >> 16) : (key_t)kb;
+            if (blk < nb) skeys[blk] = w16(DT) ? (key_t)(kb >> 16) : (key_t)kb;
         }
         if (lane == 0) sitem[seg] = make_float2(M, S);
     };
@@ -950,22 +996,22 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     const int32_t Pf = (int32_t)(V / kSeg);
     if (Pf < P && wave == kGroups - 1) {
         u32x4 buf[I::VPL];
-        stage1_load<BF16>(rowp, V, Pf, lane, buf);
+        stage1_load<DT>(rowp, V, Pf, lane, buf);
         reduce_item(buf, Pf);
     }
     int32_t cur = wave < Pf ? wave : Pf;
-    if (BF16) {
+    if (w16(DT)) {
         // double-buffered: the next item's loads are issued before the current
         // one is reduced (on the last pass the current item is loaded again,
         // an L2 hit, which keeps the loop free of load branches)
         u32x4 nxt[I::VPL];
-        if (cur < Pf) stage1_load_full<BF16>(rowp, cur, lane, nxt);
+        if (cur < Pf) stage1_load_full<DT>(rowp, cur, lane, nxt);
         while (cur < Pf) {
             u32x4 buf[I::VPL];
 #pragma unroll
             for (int j = 0; j < I::VPL; ++j) buf[j] = nxt[j];
             const int32_t nx = next_item();
-            stage1_load_full<BF16>(rowp, nx < Pf ? nx : cur, lane, nxt);
+            stage1_load_full<DT>(rowp, nx < Pf ? nx : cur, lane, nxt);
             reduce_item(buf, cur);
             cur = nx;
         }
@@ -973,7 +1019,7 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
         // fp32 items (twice the registers) one at a time
         while (cur < Pf) {
             u32x4 buf[I::VPL];
-            stage1_load_full<BF16>(rowp, cur, lane, buf);
+            stage1_load_full<DT>(rowp, cur, lane, buf);
             __builtin_amdgcn_sched_barrier(0);
             reduce_item(buf, cur);
             cur = next_item();
@@ -1010,12 +1056,12 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     if (K <= nb) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j)
-            kr[j] = BF16 ? ((uint32_t)skeys[tid * KPT + j] << 16) : (uint32_t)skeys[tid * KPT + j];
+            kr[j] = w16(DT) ? ((uint32_t)skeys[tid * KPT + j] << 16) : (uint32_t)skeys[tid * KPT + j];
     } else {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) kr[j] = 0u;
     }
-    row_topk<BF16, KPT, kThreads>(rowp, row, V, nb, K, kr, &sh.lse, cand, cand + cap, cap, sh, topk_ids,
+    row_topk<DT, KPT, kThreads>(rowp, row, V, nb, K, kr, &sh.lse, cand, cand + cap, cap, sh, topk_ids,
                                   topk_lp);
 }
 
@@ -1053,43 +1099,46 @@ hipError_t launch_reduce_stage1(const ReducePlan& p, const ReduceArgs& a, hipStr
     const dim3 grid((unsigned)p.wgs);
     const uint8_t* lg = static_cast<const uint8_t*>(a.logits);
     const bool k = keys != nullptr;
-    if (a.bf16 && k)
-        hipLaunchKernelGGL((k_stage1<true, true>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
-                           p.splits, p.nitems, part, keys);
-    else if (a.bf16)
-        hipLaunchKernelGGL((k_stage1<true, false>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
-                           p.splits, p.nitems, part, keys);
-    else if (k)
-        hipLaunchKernelGGL((k_stage1<false, true>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
-                           p.splits, p.nitems, part, keys);
+    auto go = [&](auto dt) {
+        constexpr int DT = decltype(dt)::value;
+        if (k)
+            hipLaunchKernelGGL((k_stage1<DT, true>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
+                               p.splits, p.nitems, part, keys);
+        else
+            hipLaunchKernelGGL((k_stage1<DT, false>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
+                               p.splits, p.nitems, part, keys);
+    };
+    if (a.dt == kDtBf16)
+        go(std::integral_constant<int, kDtBf16>{});
+    else if (a.dt == kDtF16)
+        go(std::integral_constant<int, kDtF16>{});
     else
-        hipLaunchKernelGGL((k_stage1<false, false>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.kld,
-                           p.splits, p.nitems, part, keys);
+        go(std::integral_constant<int, kDtF32>{});
     return hipGetLastError();
 }
 
-template <bool BF16, int KPT>
+template <int DT, int KPT>
 hipError_t launch_stage2_kpt(const ReducePlan& p, const ReduceArgs& a, hipStream_t s, const float2* part,
                              const void* keys, int32_t cap, size_t lds) {
-    const void* fn = (const void*)k_stage2<BF16, KPT>;
+    const void* fn = (const void*)k_stage2<DT, KPT>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_stage2<BF16, KPT>), dim3((unsigned)p.rows), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((k_stage2<DT, KPT>), dim3((unsigned)p.rows), dim3(kThreads), lds, s,
                        static_cast<const uint8_t*>(a.logits), a.ld, p.vocab, p.nb, p.kld, p.splits, part,
                        keys, a.sel, p.k, a.lse, a.sel_lp, a.topk_ids, a.topk_lp, a.err, cap);
     return hipGetLastError();
 }
 
-template <bool BF16>
+template <int DT>
 hipError_t launch_stage2_dt(const ReducePlan& p, const ReduceArgs& a, hipStream_t s, const float2* part,
                             const void* keys, int32_t cap, size_t lds) {
     switch (p.kpt) {
-        case 4: return launch_stage2_kpt<BF16, 4>(p, a, s, part, keys, cap, lds);
-        case 8: return launch_stage2_kpt<BF16, 8>(p, a, s, part, keys, cap, lds);
-        case 16: return launch_stage2_kpt<BF16, 16>(p, a, s, part, keys, cap, lds);
-        default: return launch_stage2_kpt<BF16, 32>(p, a, s, part, keys, cap, lds);
+        case 4: return launch_stage2_kpt<DT, 4>(p, a, s, part, keys, cap, lds);
+        case 8: return launch_stage2_kpt<DT, 8>(p, a, s, part, keys, cap, lds);
+        case 16: return launch_stage2_kpt<DT, 16>(p, a, s, part, keys, cap, lds);
+        default: return launch_stage2_kpt<DT, 32>(p, a, s, part, keys, cap, lds);
     }
 }
 
@@ -1105,8 +1154,9 @@ hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStr
         cap = nsel * kBlock;
         lds = ((size_t)cap + (size_t)p.k) * sizeof(uint64_t);
     }
-    return a.bf16 ? launch_stage2_dt<true>(p, a, s, part, keys, cap, lds)
-                  : launch_stage2_dt<false>(p, a, s, part, keys, cap, lds);
+    if (a.dt == kDtBf16) return launch_stage2_dt<kDtBf16>(p, a, s, part, keys, cap, lds);
+    if (a.dt == kDtF16) return launch_stage2_dt<kDtF16>(p, a, s, part, keys, cap, lds);
+    return launch_stage2_dt<kDtF32>(p, a, s, part, keys, cap, lds);
 }
 
 // Compute units of the current device (cached per device id).
@@ -1124,14 +1174,14 @@ int cu_count() {
 
 namespace {
 
-template <bool BF16, int KPT, bool KEYS>
+template <int DT, int KPT, bool KEYS>
 hipError_t launch_row_kpt(const ReducePlan& p, const ReduceArgs& a, hipStream_t s, int32_t cap, size_t lds) {
-    const void* fn = (const void*)k_rowreduce<BF16, KPT, KEYS>;
+    const void* fn = (const void*)k_rowreduce<DT, KPT, KEYS>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_rowreduce<BF16, KPT, KEYS>), dim3((unsigned)p.rows), dim3(kRowThreads), lds, s,
+    hipLaunchKernelGGL((k_rowreduce<DT, KPT, KEYS>), dim3((unsigned)p.rows), dim3(kRowThreads), lds, s,
                        static_cast<const uint8_t*>(a.logits), a.ld, p.vocab, p.nb, p.splits, a.sel, p.k, a.lse,
                        a.sel_lp, a.topk_ids, a.topk_lp, a.err, cap);
     return hipGetLastError();
@@ -1161,20 +1211,21 @@ hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s
     if (p.k > 0) {
         const int32_t nsel = p.k < p.nb ? p.k : p.nb;
         cap = nsel * kBlock;
-        const size_t kbytes = (size_t)p.kpt * kThreads * (a.bf16 ? 2 : 4);
+        const size_t kbytes = (size_t)p.kpt * kThreads * (w16(a.dt) ? 2 : 4);
         lds = kbytes + ((size_t)cap + (size_t)p.k) * sizeof(uint64_t);
     }
-    if (p.k == 0)
-        return a.bf16 ? launch_row_kpt<true, 4, false>(p, a, s, cap, lds)
-                      : launch_row_kpt<false, 4, false>(p, a, s, cap, lds);
-    switch (p.kpt) {
-        case 4: return a.bf16 ? launch_row_kpt<true, 4, true>(p, a, s, cap, lds)
-                              : launch_row_kpt<false, 4, true>(p, a, s, cap, lds);
-        case 8: return a.bf16 ? launch_row_kpt<true, 8, true>(p, a, s, cap, lds)
-                              : launch_row_kpt<false, 8, true>(p, a, s, cap, lds);
-        default: return a.bf16 ? launch_row_kpt<true, 16, true>(p, a, s, cap, lds)
-                               : launch_row_kpt<false, 16, true>(p, a, s, cap, lds);
-    }
+    auto go = [&](auto dt) -> hipError_t {
+        constexpr int DT = decltype(dt)::value;
+        if (p.k == 0) return launch_row_kpt<DT, 4, false>(p, a, s, cap, lds);
+        switch (p.kpt) {
+            case 4: return launch_row_kpt<DT, 4, true>(p, a, s, cap, lds);
+            case 8: return launch_row_kpt<DT, 8, true>(p, a, s, cap, lds);
+            default: return launch_row_kpt<DT, 16, true>(p, a, s, cap, lds);
+        }
+    };
+    if (a.dt == kDtBf16) return go(std::integral_constant<int, kDtBf16>{});
+    if (a.dt == kDtF16) return go(std::integral_constant<int, kDtF16>{});
+    return go(std::integral_constant<int, kDtF32>{});
 }
 
 }  // namespace lmh
