@@ -9,8 +9,9 @@ Two independent implementations live here:
 * ``liboracle.so`` (``oracle.c``): the plain definition in f64 -- the row
   formula, a naive triple-loop head, a max pass plus an f64 exp-sum pass for
   the logsumexp, a full sort for the top-K (value descending, exact ties
-  by ascending token id), and the exact dequantisation of affine
-  group-quantised head weights. Thin numpy wrappers below.
+  by ascending token id), the exact dequantisation of affine
+  group-quantised head weights, and a token bitmask applied to the
+  compacted logits rows of each segment. Thin numpy wrappers below.
 * ``ref_numpy``: the same quantities through library routines
   (``numpy`` float64 matmul, ``scipy.special.logsumexp``, ``numpy.lexsort``),
   used to cross-check the C oracle on small inputs.
@@ -68,6 +69,8 @@ def load(path: str = _LIB_PATH):
     lib.orc_reduce.restype = None
     lib.orc_prefilter_check.argtypes = [p, ctypes.c_int, i64, i64, i64, i32, i32, i32, p]
     lib.orc_prefilter_check.restype = ctypes.c_int64
+    lib.orc_apply_bitmask.argtypes = [p, i64, i64, i64, p, i64, p, i32]
+    lib.orc_apply_bitmask.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
     if path == _LIB_PATH:
@@ -178,6 +181,25 @@ def reduce(logits: np.ndarray, selected=None, k: int = 0, lib=None):
     lib.orc_reduce(_ptr(logits), _dtype_code(logits), R, V, V, _ptr(sel), k,
                    _ptr(lse), _ptr(sel_lp), _ptr(ids) if k else None, _ptr(lp) if k else None)
     return lse, sel_lp, ids, lp
+
+
+def apply_bitmask(logits: np.ndarray, mask: np.ndarray, logits_cu_seqlens=None, lib=None):
+    """f64 copy of ``logits`` [rows][V] with segment s's token bitmask (uint32
+    words [S][ceil(V/32)], bit set = token kept) applied to its rows
+    logits_cu_seqlens[s] .. [s+1]-1 (None: segment s is row s): (status,
+    masked f64 logits)."""
+    lib = lib or load()
+    Z = np.ascontiguousarray(widen(logits, lib))
+    R, V = Z.shape
+    mask = np.ascontiguousarray(mask, dtype=np.uint32)
+    S = mask.shape[0]
+    lcu = None if logits_cu_seqlens is None else np.ascontiguousarray(logits_cu_seqlens, dtype=np.int32)
+    if lcu is not None:
+        assert lcu.shape[0] == S + 1
+    else:
+        assert S == R
+    st = lib.orc_apply_bitmask(_ptr(Z), R, V, V, _ptr(mask), mask.shape[1], _ptr(lcu), S)
+    return int(st), Z
 
 
 def prefilter_check(logits: np.ndarray, k: int, block: int = BLOCK, lib=None,

@@ -135,6 +135,36 @@ int orc_rows(const int32_t* cu, int32_t S, int32_t num_decode, int64_t num_token
 }
 
 /*
+ * Token bitmask on the compacted logits (vllm-metal release, Testing:
+ * bitmask application under the compacted layout). Segment s owns the logits
+ * rows lcu[s] .. lcu[s+1]-1 (the logits_cu_seqlens of orc_rows; lcu NULL:
+ * S == rows and segment s owns row s alone). Token v of those rows keeps its
+ * value when bit v % 32 of word v / 32 of mask row s is set and becomes -inf
+ * otherwise (bits past V are ignored). Z is f64 [rows][ld], changed in
+ * place. A segment whose bounds decrease or leave [0, rows] is left alone
+ * and the call returns ORC_ERR_LAYOUT.
+ */
+int orc_apply_bitmask(double* Z, int64_t rows, int64_t V, int64_t ld, const uint32_t* mask,
+                      int64_t mask_ld, const int32_t* lcu, int32_t S) {
+    int st = ORC_OK;
+    for (int32_t s = 0; s < S; ++s) {
+        const int64_t r0 = lcu ? lcu[s] : s;
+        const int64_t r1 = lcu ? lcu[s + 1] : s + 1;
+        if (r0 < 0 || r1 < r0 || r1 > rows) {
+            st = ORC_ERR_LAYOUT;
+            continue;
+        }
+        for (int64_t r = r0; r < r1; ++r) {
+            for (int64_t v = 0; v < V; ++v) {
+                const uint32_t word = mask[s * mask_ld + v / 32];
+                if (((word >> (v % 32)) & 1u) == 0) Z[r * ld + v] = -INFINITY;
+            }
+        }
+    }
+    return st;
+}
+
+/*
  * Head projection on gathered rows (vllm-metal release, Summary; mlxcel
  * PR #1969): Z[r][v] = sum_{k=0}^{H-1} hidden[idx[r]][k] * W[v][k], summed in
  * ascending k, in f64. hidden is [num_tokens][H] with row pitch hld; W is

@@ -16,6 +16,7 @@ import synth
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rows.json")
 QUANT = os.path.join(os.path.dirname(__file__), "golden", "quant.json")
+BITMASK = os.path.join(os.path.dirname(__file__), "golden", "bitmask.json")
 
 
 def _rows_golden_ok(lib):
@@ -99,10 +100,21 @@ def _f16_ok(lib):
     return np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], want[~nan])
 
 
+def _bitmask_golden_ok(lib):
+    with open(BITMASK) as f:
+        for c in json.load(f)["cases"]:
+            x = synth.normal_f32(synth.rng(81), (c["rows"], c["vocab"]))
+            st, Z = oracle.apply_bitmask(x, np.array(c["mask"], dtype=np.uint32), c["logits_cu_seqlens"],
+                                         lib=lib)
+            if st != 0 or [np.flatnonzero(np.isfinite(z)).tolist() for z in Z] != c["kept"]:
+                return False
+    return True
+
+
 def _all_pins_ok(lib):
     return (_rows_golden_ok(lib) and _head_integer_ok(lib) and _head_one_hot_ok(lib)
             and _closed_forms_ok(lib) and _dequant_golden_ok(lib) and _scale_ok(lib)
-            and _f16_ok(lib))
+            and _f16_ok(lib) and _bitmask_golden_ok(lib))
 
 
 MUTANTS = [
@@ -125,6 +137,10 @@ MUTANTS = [
     ("f16 subnormal scale", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     ("f16 drops the implicit bit", "v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)m, e - 25);"),
     ("selected logprob adds lse", ": widen(logits, dt, base + t) - l;", ": widen(logits, dt, base + t) + l;"),
+    ("bitmask bits read from the top", "if (((word >> (v % 32)) & 1u) == 0)", "if (((word >> (31 - v % 32)) & 1u) == 0)"),
+    ("bitmask row of the logits row, not the segment", "mask[s * mask_ld + v / 32]", "mask[r * mask_ld + v / 32]"),
+    ("bitmask set bit masks", "if (((word >> (v % 32)) & 1u) == 0)", "if (((word >> (v % 32)) & 1u) != 0)"),
+    ("bitmask word index off by one", "mask[s * mask_ld + v / 32]", "mask[s * mask_ld + (v + 1) / 32]"),
 ]
 
 
