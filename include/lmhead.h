@@ -179,6 +179,31 @@ lmh_status logprob_reduce(
     void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
 
 /*
+ * lmhead_apply_bitmask -- token bitmask on the compacted logits, in place
+ * [vllm-metal, Testing: bitmask application under the compacted layout].
+ *
+ * logits  [rows][vocab], pitch logits_ld, fp32, bf16 or f16; 16-B aligned
+ *         base and pitch (the layout logprob_reduce takes).
+ * bitmask [num_segments][bitmask_ld] 32-bit words, bitmask_ld >=
+ *         ceil(vocab/32), 4-B aligned: bit v % 32 of word v / 32 of row s set
+ *         keeps token v in segment s's rows; clear sets it to -inf. Bits past
+ *         vocab are ignored.
+ * logits_cu_seqlens [num_segments + 1] or NULL: segment s owns the logits
+ *         rows logits_cu_seqlens[s] .. logits_cu_seqlens[s+1]-1 (the array
+ *         lmhead_gather_project writes); NULL requires num_segments == rows
+ *         and gives segment s the row s.
+ * Only masked entries are written (no logits are read); padding between
+ * vocab and logits_ld is never touched. A segment whose bounds decrease or
+ * leave [0, rows] is skipped and sets LMH_DEVERR_LAYOUT in *device_error.
+ * num_segments = 0 is a no-op (pointers may then be NULL).
+ */
+lmh_status lmhead_apply_bitmask(
+    void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab, int64_t logits_ld,
+    const int32_t* bitmask, int64_t bitmask_ld,
+    const int32_t* logits_cu_seqlens, int32_t num_segments,
+    int32_t* device_error, void* stream);
+
+/*
  * lmhead_logprobs_workspace_size -- bytes of device workspace lmhead_logprobs
  * needs: room for one chunk of fp32 logits (chunk_rows x vocab, chunk_rows = 0
  * meaning 256) plus the reduction's workspace for that chunk.

@@ -268,3 +268,24 @@ def test_head_struct_layout_matches_c(tmp_path):
     out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert out[0] == ctypes.sizeof(lmh.LmhHead)
     assert out[1:] == [getattr(lmh.LmhHead, f).offset for f in fields]
+
+
+def _bitmask(L, **kw):
+    a = dict(logits=A, dt=BF16, rows=4, vocab=1000, ld=1000, mask=A, mld=32, lcu=A, S=3, err=None)
+    a.update(kw)
+    return L.lmhead_apply_bitmask(a["logits"], a["dt"], a["rows"], a["vocab"], a["ld"], a["mask"],
+                                  a["mld"], a["lcu"], a["S"], a["err"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-1), SHAPE), (dict(vocab=0), SHAPE), (dict(ld=999), SHAPE), (dict(mld=31), SHAPE),
+    (dict(S=-1), SHAPE), (dict(lcu=None), SHAPE), (dict(dt=BAD_DT), DTYPE),
+    (dict(logits=None), NULL), (dict(mask=None), NULL),
+    (dict(logits=A + 8), ALIGN), (dict(ld=1004), ALIGN), (dict(mask=A + 2), ALIGN),
+])
+def test_bitmask_rejects(L, kw, want):
+    assert _bitmask(L, **kw) == want
+
+
+def test_bitmask_no_segments_is_a_no_op(L):
+    assert _bitmask(L, logits=None, mask=None, lcu=None, S=0, rows=0) == OK

@@ -20,6 +20,8 @@ Entry points (same names as the C ABI):
                          plus output scaling)
   lmhead_selfcheck       bit-exact check of the selective rows against a
                          head's own full output
+  lmhead_apply_bitmask   token bitmask on the compacted logits rows of each
+                         segment, in place
 """
 from __future__ import annotations
 
@@ -89,12 +91,13 @@ def lib():
         L.lmhead_selfcheck_workspace_size.argtypes = [i64, i64]
         L.lmhead_selfcheck_workspace_size.restype = sz
         L.lmhead_selfcheck.argtypes = projx + [p, i64, p, sz, p, p, p]
+        L.lmhead_apply_bitmask.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i64, p, i32, p, p]
         L.lmh_status_string.argtypes = [ctypes.c_int]
         L.lmh_status_string.restype = ctypes.c_char_p
         for name in ("lmhead_gather_project", "lmh_debug_gather_project", "logprob_reduce",
                      "lmh_debug_reduce_stage1", "lmhead_logprobs", "lmhead_gather_project_q",
                      "lmh_debug_gather_project_q", "lmhead_logprobs_q", "lmhead_gather_project_ex",
-                     "lmhead_logprobs_ex", "lmhead_selfcheck"):
+                     "lmhead_logprobs_ex", "lmhead_selfcheck", "lmhead_apply_bitmask"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -442,6 +445,28 @@ def lmhead_logprobs_ex(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: torch.T
 class SelfCheck(NamedTuple):
     result: torch.Tensor          # int64[2]: differing logits, first r * vocab + v (INT64_MAX: none)
     device_error: torch.Tensor
+
+
+def lmhead_apply_bitmask(logits: torch.Tensor, bitmask: torch.Tensor,
+                         logits_cu_seqlens: Optional[torch.Tensor] = None,
+                         device_error: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Token bitmask on compacted logits, in place: segment s (bitmask row s,
+    int32 words, bit v % 32 of word v // 32 set = token v kept) covers the
+    logits rows logits_cu_seqlens[s] .. [s+1]-1 (None: row s); masked tokens
+    become -inf. Returns the device error word."""
+    L = lib()
+    R, V, ld = _matrix(logits, "logits")
+    S, words, mld = _matrix(bitmask, "bitmask")
+    if bitmask.dtype != torch.int32:
+        raise ValueError("bitmask must be int32 words")
+    lcu = _i32(logits_cu_seqlens, "logits_cu_seqlens")
+    if lcu is not None and lcu.shape[0] != S + 1:
+        raise ValueError("logits_cu_seqlens needs one entry more than bitmask has rows")
+    err = device_error if device_error is not None else torch.zeros(1, dtype=torch.int32,
+                                                                    device=logits.device)
+    _check(L.lmhead_apply_bitmask(_ptr(logits), _dt(logits), R, V, ld, _ptr(bitmask), mld, _ptr(lcu), S,
+                                  _ptr(err), _stream()), "lmhead_apply_bitmask")
+    return err
 
 
 def lmhead_selfcheck(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: torch.Tensor,

@@ -374,6 +374,27 @@ lmh_status lmh_debug_reduce_stage1(const void* logits, lmh_dtype logits_dt, int6
     return from_hip(launch_reduce_stage1(p, a, static_cast<hipStream_t>(stream)));
 }
 
+lmh_status lmhead_apply_bitmask(void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
+                                int64_t logits_ld, const int32_t* bitmask, int64_t bitmask_ld,
+                                const int32_t* logits_cu_seqlens, int32_t num_segments,
+                                int32_t* device_error, void* stream) {
+    if (rows < 0 || rows > INT32_MAX || vocab <= 0 || vocab > INT32_MAX || logits_ld < vocab ||
+        num_segments < 0)
+        return LMH_ERR_SHAPE;
+    const int64_t words = ceil_div(vocab, 32);
+    if (bitmask_ld < words) return LMH_ERR_SHAPE;
+    if (logits_cu_seqlens == nullptr && num_segments != rows) return LMH_ERR_SHAPE;
+    if (ceil_div(words, 256) * (int64_t)num_segments >= ((int64_t)1 << 31)) return LMH_ERR_SHAPE;
+    if (!valid_logits_dtype(logits_dt)) return LMH_ERR_DTYPE;
+    if (num_segments == 0) return LMH_OK;   // nothing is read or written
+    if (!logits || !bitmask) return LMH_ERR_NULL;
+    if (!aligned(logits, 16) || ((size_t)logits_ld * esize(logits_dt)) % 16 || !aligned(bitmask, 4))
+        return LMH_ERR_ALIGN;
+    MaskArgs a{logits, (int32_t)logits_dt, rows, vocab, logits_ld, bitmask, bitmask_ld,
+               logits_cu_seqlens, num_segments, device_error};
+    return from_hip(launch_apply_bitmask(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t lmh_debug_reduce_path(int64_t rows, int64_t vocab, int32_t k) {
     if (rows <= 0 || vocab <= 0 || k < 0) return 0;
     return reduce_row_path(plan_reduce(rows, vocab, k)) ? 1 : 0;

@@ -125,6 +125,19 @@ hipError_t launch_selfcheck(const float* sel, int64_t sel_ld, const float* full,
                             int32_t rows, int64_t vocab, const int32_t* cu, int32_t num_decode,
                             int64_t num_tokens, const int32_t* ex, int64_t* res, hipStream_t s);
 
+// Token bitmask on compacted logits rows (see mask.hip).
+struct MaskArgs {
+    void* logits;
+    int32_t dt;           // LMH_F32, LMH_BF16 or LMH_F16
+    int64_t rows, vocab, ld;
+    const int32_t* mask;  // [segments][mask_ld] 32-bit words
+    int64_t mask_ld;
+    const int32_t* lcu;   // [segments + 1] or nullptr (segment s is row s)
+    int32_t segments;
+    int32_t* err;         // may be nullptr
+};
+hipError_t launch_apply_bitmask(const MaskArgs& a, hipStream_t s);
+
 struct ReducePlan {
     int64_t rows, vocab;
     int32_t k;

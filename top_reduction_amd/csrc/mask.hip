@@ -1,0 +1,89 @@
+// mask.hip -- token bitmask on the compacted logits (vllm-metal release
+// v0.4.0, Testing: bitmask application under the compacted layout).
+//
+//   Segment s owns the logits rows lcu[s] .. lcu[s+1]-1 (the head's
+//   logits_cu_seqlens; without them segment s is row s). Token v of those
+//   rows keeps its value when bit v % 32 of word v / 32 of mask row s is
+//   set, and becomes -inf otherwise.
+//
+// The logits are written, never read. Each thread owns one mask word (32
+// tokens) of one segment: a full word writes nothing, an empty word writes
+// its 32 tokens as -inf with 16-byte stores, a partly set word writes its
+// masked tokens one element at a time. Rows past the vocabulary's end (the
+// row pitch's padding) are never touched.
+#include "lmh_internal.h"
+
+namespace lmh {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaskThreads = 256;
+
+template <int ES>   // element size: 2 (bf16, f16) or 4 (fp32)
+__global__ __launch_bounds__(kMaskThreads) void k_apply_bitmask(uint8_t* __restrict__ logits, int64_t ld,
+                                                                int64_t rows, int64_t V,
+                                                                const uint32_t* __restrict__ mask,
+                                                                int64_t mask_ld, const int32_t* __restrict__ lcu,
+                                                                int32_t chunks, uint32_t ninf,
+                                                                int32_t* __restrict__ err) {
+    const int32_t s = (int32_t)(blockIdx.x / (uint32_t)chunks);
+    const int64_t w = (int64_t)(blockIdx.x - (uint32_t)s * (uint32_t)chunks) * kMaskThreads + threadIdx.x;
+    int64_t r0 = s, r1 = (int64_t)s + 1;
+    if (lcu != nullptr) {
+        r0 = lcu[s];
+        r1 = lcu[s + 1];
+    }
+    if (r0 < 0 || r1 < r0 || r1 > rows) {   // malformed bounds: the segment is left alone
+        if (err != nullptr && w == 0) atomicOr(err, LMH_DEVERR_LAYOUT);
+        return;
+    }
+    const int64_t nw = (V + 31) / 32;
+    if (w >= nw || r0 == r1) return;
+    const uint32_t word = mask[(int64_t)s * mask_ld + w];
+    if (word == 0xFFFFFFFFu) return;
+    const int64_t v0 = w * 32;
+    const bool whole = v0 + 32 <= V;
+    for (int64_t r = r0; r < r1; ++r) {
+        uint8_t* row = logits + r * ld * ES;
+        if (word == 0u && whole) {
+            // 64 (16-bit) or 128 (fp32) bytes at a multiple of 64 bytes into a
+            // 16-byte aligned row
+            u32x4* p = reinterpret_cast<u32x4*>(row + v0 * ES);
+            const u32x4 fill = {ninf, ninf, ninf, ninf};
+#pragma unroll
+            for (int i = 0; i < 2 * ES; ++i) p[i] = fill;
+        } else {
+            for (int b = 0; b < 32; ++b) {
+                const int64_t v = v0 + b;
+                if (v < V && ((word >> b) & 1u) == 0u) {
+                    if (ES == 2)
+                        reinterpret_cast<uint16_t*>(row)[v] = (uint16_t)ninf;
+                    else
+                        reinterpret_cast<uint32_t*>(row)[v] = ninf;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_apply_bitmask(const MaskArgs& a, hipStream_t s) {
+    if (a.segments == 0) return hipSuccess;
+    const int64_t nw = (a.vocab + 31) / 32;
+    const int64_t chunks = (nw + kMaskThreads - 1) / kMaskThreads;
+    const dim3 grid((unsigned)(chunks * a.segments));
+    uint8_t* lg = static_cast<uint8_t*>(a.logits);
+    const uint32_t* m = reinterpret_cast<const uint32_t*>(a.mask);
+    if (a.dt == LMH_F32)
+        hipLaunchKernelGGL((k_apply_bitmask<4>), grid, dim3(kMaskThreads), 0, s, lg, a.ld, a.rows, a.vocab, m,
+                           a.mask_ld, a.lcu, (int32_t)chunks, 0xFF800000u, a.err);
+    else
+        hipLaunchKernelGGL((k_apply_bitmask<2>), grid, dim3(kMaskThreads), 0, s, lg, a.ld, a.rows, a.vocab, m,
+                           a.mask_ld, a.lcu, (int32_t)chunks, a.dt == LMH_BF16 ? 0xFF80FF80u : 0xFC00FC00u,
+                           a.err);
+    return hipGetLastError();
+}
+
+}  // namespace lmh
