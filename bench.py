@@ -71,10 +71,12 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
     f_fetch = fetch[copy[0]] * 1024 / nbytes
     f_write = write[copy[0]] * 1024 / nbytes
     csrc = os.path.join(ROOT, "top_reduction_amd", "csrc")
-    wanted = {"reduce_row_bf16": ("k_rowreduce<true, 16, true>", "reduce.hip", nbytes),
-              "reduce_stage1_bf16": ("k_stage1<true, true>", "reduce.hip", nbytes),
-              "reduce_stage2_bf16": ("k_stage2<true", "reduce.hip", None),
+    wanted = {"reduce_row_bf16": ("k_rowreduce<1, 16, true>", "reduce.hip", nbytes),
+              "reduce_stage1_bf16": ("k_stage1<1, true>", "reduce.hip", nbytes),
+              "reduce_stage2_bf16": ("k_stage2<1", "reduce.hip", None),
               "head_stream_bf16": ("k_head_stream<", "head.hip", 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
+              "head_pipe_bf16": ("k_head_pipe<3, 2, 16, 4, false, false, true>", "head.hip",
+                                 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
               "head_tiled_bf16": ("k_head_tiled<false, 16", "head.hip",
                                   151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4)}
     for bits in (4, 8):
@@ -290,6 +292,21 @@ def main():
                             "gbps": round(nbytes / (m * 1e-3) / 1e9, 1)}
             log(f"reduce K={k}: {m * 1e3:.1f} us")
         result["reduce_by_k"] = by_k
+        # the same chunks as f16 logits (MTPLX PR #532, Tests: bf16/f16), K = 20
+        f16 = [(t.to(torch.float16), s_) for (t, s_, _, _) in chunks]
+        fns16 = []
+        for (t, s_), ws in zip(f16, wss):
+            o = (torch.empty(rows, device=dev), torch.empty(rows, device=dev),
+                 torch.empty((rows, K), dtype=torch.int32, device=dev), torch.empty((rows, K), device=dev))
+            a = (vp(t), lmh.LMH_F16, rows, V, V, vp(s_), K, vp(o[0]), vp(o[1]), vp(o[2]), vp(o[3]), vp(ws),
+                 ws.numel(), None, stream)
+            fns16.append(lambda a=a, o=o: L.logprob_reduce(*a))
+        assert all(f() == 0 for f in fns16)
+        m = timer.loop(fns16, steps, warmup)
+        result["reduce_f16"] = {"k": K, "us": round(m * 1e3, 2), "rows_per_s": round(rows / (m * 1e-3)),
+                                "gbps": round(nbytes / (m * 1e-3) / 1e9, 1)}
+        log(f"reduce f16 K={K}: {m * 1e3:.1f} us")
+        del f16, fns16
 
     # ------------------------------------------------------------------
     # decode rows
@@ -365,13 +382,31 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                          "bytes_per_launch": head_bytes,
-                         "traffic": load_traffic("head_stream_bf16",
+                         "kernel": "k_head_pipe (k-pipelined weight stream, 16-wave chain per CU)",
+                         "traffic": load_traffic("head_pipe_bf16",
                                                  os.path.join(ROOT, "top_reduction_amd", "csrc", "head.hip"))},
             "full_2048_ms": round(tf, 4),
             "full_roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4)},
         }
-        del hid, w, full, out
+        # token bitmask on the 40 selective rows (one segment per row): mask
+        # words read once, masked logits written as -inf, nothing else touched
+        g = synth.rng(7300)
+        words = (Vq + 31) // 32
+        masks = [torch.from_numpy(g.integers(0, 2 ** 32, size=(R, words), dtype=np.uint64)
+                                  .astype(np.uint32).view(np.int32)).to(dev) for _ in range(4)]
+        for m in masks:
+            m[:, : words // 2] = 0                           # half the vocabulary fully masked
+        outs = [torch.empty((R, Vq), device=dev) for _ in range(4)]
+
+        def mask_call(i):
+            return L.lmhead_apply_bitmask(vp(outs[i]), lmh.LMH_F32, R, Vq, Vq, vp(masks[i]), words, None, R,
+                                          None, stream)
+        assert mask_call(0) == 0
+        tm = timer.loop([lambda i=i: mask_call(i) for i in range(4)], hs, warmup)
+        result["head"]["bitmask_us"] = round(tm * 1e3, 2)
+        log(f"bitmask on 40 x {Vq} fp32 logits: {tm * 1e3:.1f} us")
+        del hid, w, full, out, outs, masks
 
     # ------------------------------------------------------------------
     # quantised selective head (Qwen3-0.6B shape, 4- and 8-bit codes, group 64)

@@ -384,7 +384,7 @@ lmh_status lmhead_apply_bitmask(void* logits, lmh_dtype logits_dt, int64_t rows,
     const int64_t words = ceil_div(vocab, 32);
     if (bitmask_ld < words) return LMH_ERR_SHAPE;
     if (logits_cu_seqlens == nullptr && num_segments != rows) return LMH_ERR_SHAPE;
-    if (ceil_div(words, 256) * (int64_t)num_segments >= ((int64_t)1 << 31)) return LMH_ERR_SHAPE;
+    if (ceil_div(ceil_div(vocab, 4), 256) * (int64_t)num_segments >= ((int64_t)1 << 31)) return LMH_ERR_SHAPE;
     if (!valid_logits_dtype(logits_dt)) return LMH_ERR_DTYPE;
     if (num_segments == 0) return LMH_OK;   // nothing is read or written
     if (!logits || !bitmask) return LMH_ERR_NULL;

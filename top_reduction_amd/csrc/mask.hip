@@ -6,11 +6,12 @@
 //   rows keeps its value when bit v % 32 of word v / 32 of mask row s is
 //   set, and becomes -inf otherwise.
 //
-// The logits are written, never read. Each thread owns one mask word (32
-// tokens) of one segment: a full word writes nothing, an empty word writes
-// its 32 tokens as -inf with 16-byte stores, a partly set word writes its
-// masked tokens one element at a time. Rows past the vocabulary's end (the
-// row pitch's padding) are never touched.
+// The logits are written, never read. Each thread owns one 16-byte group of
+// a row (8 bf16/f16 or 4 fp32 tokens, inside one mask word), so a wave's
+// stores cover consecutive memory: a fully masked group is one 16-byte store
+// of -inf, a fully kept one writes nothing, a mixed one writes its masked
+// tokens one element at a time. The row pitch's padding past the vocabulary
+// is never touched.
 #include "lmh_internal.h"
 
 namespace lmh {
@@ -27,40 +28,36 @@ __global__ __launch_bounds__(kMaskThreads) void k_apply_bitmask(uint8_t* __restr
                                                                 int64_t mask_ld, const int32_t* __restrict__ lcu,
                                                                 int32_t chunks, uint32_t ninf,
                                                                 int32_t* __restrict__ err) {
+    constexpr int EPG = 16 / ES;                     // tokens per 16-byte group (divides 32)
     const int32_t s = (int32_t)(blockIdx.x / (uint32_t)chunks);
-    const int64_t w = (int64_t)(blockIdx.x - (uint32_t)s * (uint32_t)chunks) * kMaskThreads + threadIdx.x;
+    const int64_t g = (int64_t)(blockIdx.x - (uint32_t)s * (uint32_t)chunks) * kMaskThreads + threadIdx.x;
     int64_t r0 = s, r1 = (int64_t)s + 1;
     if (lcu != nullptr) {
         r0 = lcu[s];
         r1 = lcu[s + 1];
     }
     if (r0 < 0 || r1 < r0 || r1 > rows) {   // malformed bounds: the segment is left alone
-        if (err != nullptr && w == 0) atomicOr(err, LMH_DEVERR_LAYOUT);
+        if (err != nullptr && g == 0) atomicOr(err, LMH_DEVERR_LAYOUT);
         return;
     }
-    const int64_t nw = (V + 31) / 32;
-    if (w >= nw || r0 == r1) return;
-    const uint32_t word = mask[(int64_t)s * mask_ld + w];
-    if (word == 0xFFFFFFFFu) return;
-    const int64_t v0 = w * 32;
-    const bool whole = v0 + 32 <= V;
+    const int64_t v0 = g * EPG;
+    if (v0 >= V || r0 == r1) return;
+    const int nv = V - v0 < EPG ? (int)(V - v0) : EPG;              // tokens of this group in the row
+    const uint32_t keep = (mask[(int64_t)s * mask_ld + v0 / 32] >> (v0 % 32)) & ((1u << EPG) - 1u);
+    const uint32_t live = (1u << nv) - 1u;
+    if ((keep & live) == live) return;                                // nothing masked
     for (int64_t r = r0; r < r1; ++r) {
         uint8_t* row = logits + r * ld * ES;
-        if (word == 0u && whole) {
-            // 64 (16-bit) or 128 (fp32) bytes at a multiple of 64 bytes into a
-            // 16-byte aligned row
-            u32x4* p = reinterpret_cast<u32x4*>(row + v0 * ES);
+        if (keep == 0u && nv == EPG) {
             const u32x4 fill = {ninf, ninf, ninf, ninf};
-#pragma unroll
-            for (int i = 0; i < 2 * ES; ++i) p[i] = fill;
+            *reinterpret_cast<u32x4*>(row + v0 * ES) = fill;   // base and pitch 16-byte aligned, v0 * ES too
         } else {
-            for (int b = 0; b < 32; ++b) {
-                const int64_t v = v0 + b;
-                if (v < V && ((word >> b) & 1u) == 0u) {
+            for (int e = 0; e < nv; ++e) {
+                if (((keep >> e) & 1u) == 0u) {
                     if (ES == 2)
-                        reinterpret_cast<uint16_t*>(row)[v] = (uint16_t)ninf;
+                        reinterpret_cast<uint16_t*>(row)[v0 + e] = (uint16_t)ninf;
                     else
-                        reinterpret_cast<uint32_t*>(row)[v] = ninf;
+                        reinterpret_cast<uint32_t*>(row)[v0 + e] = ninf;
                 }
             }
         }
@@ -71,8 +68,8 @@ __global__ __launch_bounds__(kMaskThreads) void k_apply_bitmask(uint8_t* __restr
 
 hipError_t launch_apply_bitmask(const MaskArgs& a, hipStream_t s) {
     if (a.segments == 0) return hipSuccess;
-    const int64_t nw = (a.vocab + 31) / 32;
-    const int64_t chunks = (nw + kMaskThreads - 1) / kMaskThreads;
+    const int64_t groups = (a.vocab + (a.dt == LMH_F32 ? 3 : 7)) / (a.dt == LMH_F32 ? 4 : 8);   // 16-byte groups
+    const int64_t chunks = (groups + kMaskThreads - 1) / kMaskThreads;
     const dim3 grid((unsigned)(chunks * a.segments));
     uint8_t* lg = static_cast<uint8_t*>(a.logits);
     const uint32_t* m = reinterpret_cast<const uint32_t*>(a.mask);
