@@ -137,10 +137,10 @@ HeadArgs head_args(const void* hidden, int64_t num_tokens, int64_t hidden_dim, i
 
 lmh_status launch_head(const HeadArgs& h, bool bf16_inputs, int32_t variant, hipStream_t s) {
     if (!bf16_inputs) return from_hip(launch_head_f32(h, s));
-    if (variant == LMH_HEAD_PIPE) return head_pipe_ok(h) ? from_hip(launch_head_pipe_bf16(h, s)) : LMH_ERR_SHAPE;
+    if (variant == LMH_HEAD_PIPE) return head_pipe_ok(h) ? from_hip(launch_head_pipe(h, s)) : LMH_ERR_SHAPE;
     // the pipelined stream pays off once there are two or more 16-row tiles
     // of hidden rows (measured: equal or slightly behind the plain stream for one)
-    if (variant == LMH_HEAD_AUTO && h.rows > 16 && head_pipe_ok(h)) return from_hip(launch_head_pipe_bf16(h, s));
+    if (variant == LMH_HEAD_AUTO && h.rows > 16 && head_pipe_ok(h)) return from_hip(launch_head_pipe(h, s));
     const bool stream = variant == LMH_HEAD_STREAM || (variant == LMH_HEAD_AUTO && h.rows <= kStreamMaxRows);
     if (h.bits != 16) return from_hip(stream ? launch_head_stream_q(h, s) : launch_head_tiled_q(h, s));
     return from_hip(stream ? launch_head_stream_bf16(h, s) : launch_head_tiled_bf16(h, s));

@@ -103,11 +103,12 @@ struct HeadArgs {
 // Compute units of the current device (0 if it cannot be queried).
 int cu_count();
 
-// bf16 MFMA heads. stream: R <= kStreamMaxRows; tiled: any R; pipe: the
-// k-pipelined weight stream, for the shapes head_pipe_ok accepts.
+// bf16 MFMA heads. stream: R <= kStreamMaxRows; tiled: any R.
 hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s);
+// The k-pipelined weight stream (bf16 or quantised weights), for the shapes
+// head_pipe_ok accepts.
 bool head_pipe_ok(const HeadArgs& a);
-hipError_t launch_head_pipe_bf16(const HeadArgs& a, hipStream_t s);
+hipError_t launch_head_pipe(const HeadArgs& a, hipStream_t s);
 hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s);
 // The same two kernels over quantised weights (bits 4 or 8, hidden size a
 // multiple of 128, group 32, 64 or 128), dequantised to bf16 on the fly.
