@@ -75,7 +75,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
               "reduce_stage1_bf16": ("k_stage1<1, true>", "reduce.hip", nbytes),
               "reduce_stage2_bf16": ("k_stage2<1", "reduce.hip", None),
               "head_stream_bf16": ("k_head_stream<", "head.hip", 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
-              "head_pipe_bf16": ("k_head_pipe<3, 2, 16, 4, false, false, true>", "head.hip",
+              "head_pipe_bf16": ("k_head_pipe<3, 2, 4, false, false, true>", "pipe.hip",
                                  151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
               "head_tiled_bf16": ("k_head_tiled<false, 16", "head.hip",
                                   151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4)}
@@ -384,7 +384,7 @@ def main():
                          "bytes_per_launch": head_bytes,
                          "kernel": "k_head_pipe (k-pipelined weight stream, 16-wave chain per CU)",
                          "traffic": load_traffic("head_pipe_bf16",
-                                                 os.path.join(ROOT, "top_reduction_amd", "csrc", "head.hip"))},
+                                                 os.path.join(ROOT, "top_reduction_amd", "csrc", "pipe.hip"))},
             "full_2048_ms": round(tf, 4),
             "full_roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4)},

@@ -32,6 +32,10 @@ namespace {
 #endif
 constexpr int kPipeWaves = 16;                   // waves per chain (one workgroup per CU)
 constexpr int kPipeInflight = LMH_PIPE_INFLIGHT; // k-steps of weight fragments in flight per wave
+// Cache policy of the logits stores: non-temporal (the logits are not read
+// again by this launch; measured 2-5 % faster than default stores at 40 and
+// 64 rows of the Qwen3-0.6B head)
+constexpr int kNT = 2;
 
 // Logits output: the last wave stores each tile's logits right away, with
 // 16-byte stores through a small LDS staging tile (VEC: fp32 logits,
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(64 * kPipeWaves) void k_head_pipe(HeadParams p, int
                 const int r = i * 16 + (lane >> 2);
                 const f32x4 v = *reinterpret_cast<const f32x4*>(&stage_out[r * 16 + cq]);
                 const uint32_t off = (cok && r < p.R) ? (uint32_t)r * rowbytes + coff : 0x80000000u;
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), orsrc, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), orsrc, off, 0, kNT);
             }
         } else {
             const bool vok = c0 + l16 < p.V;
@@ -140,9 +144,9 @@ __global__ __launch_bounds__(64 * kPipeWaves) void k_head_pipe(HeadParams p, int
                     const bool ok = vok && i * 16 + rl + e < p.R;
                     const uint32_t off = ok ? toff + (uint32_t)(i * 16 + e) * rowbytes : 0x80000000u;
                     if (OUT_BF16)
-                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(val), orsrc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(val), orsrc, off, 0, kNT);
                     else
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), orsrc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), orsrc, off, 0, kNT);
                 }
         }
     };
