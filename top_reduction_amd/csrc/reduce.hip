@@ -528,7 +528,8 @@ template <int DT, int KPT, int NT>
 __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t V, int32_t nb, int32_t K,
                          const uint32_t (&kr)[KPT], const float* lse_p, uint64_t* cand, uint64_t* list2,
                          int32_t cap,
-                         RowShared<NT>& sh, int32_t* __restrict__ topk_ids, float* __restrict__ topk_lp) {
+                         RowShared<NT>& sh, int32_t* __restrict__ topk_ids, float* __restrict__ topk_lp,
+                         const int32_t* lse_ready = nullptr) {
     constexpr size_t ESZ = w16(DT) ? 2 : 4;
     constexpr int EPV = w16(DT) ? 8 : 4;                 // elements per 16-byte vector
     constexpr int VPB = kBlock / EPV;                 // vectors per block
@@ -542,6 +543,8 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
     int nblk;
     uint32_t T = 0;                                     // key threshold (0: keep everything)
     if (K <= nb) {
+        const int ksh = w16(DT) ? 16 : 0;
+        // Largest t with count(key >= t) >= K; count(>= lo) >= K > count(>= hi).
         uint32_t tmax = 0u, tmin = 0xFFFFFFFFu;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
@@ -553,8 +556,6 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
         uint32_t mm[3] = {tmax, ~tmin, b0 < nb ? ~tmax : 0u};
         block_reduce<1, 3, NT>(mm, sh.sred, phase);
         const int nth = (nb + KPT - 1) / KPT;           // threads holding blocks
-        const int ksh = w16(DT) ? 16 : 0;
-        // Largest t with count(key >= t) >= K; count(>= lo) >= K > count(>= hi).
         uint64_t lo = (uint64_t)((K <= nth ? ~mm[2] : ~mm[1]) >> ksh);
         uint64_t hi = (uint64_t)(mm[0] >> ksh) + 1;
         uint32_t c_hi = 0u;                              // count(key >= hi)
@@ -750,7 +751,13 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
     }
     // G lanes (a quad, a pair or one lane) count one candidate's predecessors
     // over interleaved slices of the list, then sum with DPP inside the quad
-    const float lse = *lse_p;                           // written before the first barrier above
+    // the row's lse: written before the first barrier above, or (lse_ready)
+    // by another wave of the workgroup that raises the flag after it
+    if (lse_ready != nullptr)
+        while (__hip_atomic_load(lse_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+        }
+    const float lse = lse_ready != nullptr ? __hip_atomic_load(lse_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                                           : *lse_p;
     const int G = nlist <= NT / 4 ? 4 : (nlist <= NT / 2 ? 2 : 1);
     const int q = tid & (G - 1);
     for (int i0 = 0; i0 < nlist * G; i0 += NT) {
@@ -937,7 +944,7 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     __shared__ RowShared<kThreads> sh;
     __shared__ float2 sgrp[kGroups];
     __shared__ float2 sitem[kRowMaxItems];
-    __shared__ int32_t s_next, s_sel;
+    __shared__ int32_t s_next, s_sel, s_lse_ready;
     __shared__ float s_xsel;
     constexpr size_t ESZ = w16(DT) ? 2 : 4;
     constexpr int MAXBLK = kMaxCandidates / kBlock;
@@ -954,6 +961,7 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
         sh.nlist = 0;
         sh.nblk = 0;
         s_next = kGroups;
+        s_lse_ready = 0;
     }
     __syncthreads();   // s_next before the first hand-out
     // key slots past nb read as 0
@@ -1028,10 +1036,11 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     if (sel_thread) s_xsel = xsel;
     __syncthreads();
 
-    // lse: lanes 0..15 of wave 0 merge their groups, lane 0 the groups (the
-    // split path's arithmetic); the selection below reads it after its first
-    // barrier
-    if (wave == 0) {
+    // lse: lanes 0..15 of wave 4 merge their groups, lane 0 the groups (the
+    // split path's arithmetic), then raise s_lse_ready; the selection on
+    // waves 0..3 starts at once and reads the lse only for its last step
+    constexpr int kLseWave = kThreads / 64;
+    if (wave == kLseWave) {
         if (lane < kGroups) {
             float m = kNegInf, sm = 0.f;
             for (int32_t i = lane; i < P; i += kGroups) lse_merge(m, sm, sitem[i].x, sitem[i].y);
@@ -1042,10 +1051,12 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if (lane == 0) {
             const float l = lse_of_groups(sgrp);
-            sh.lse = l;
+            __hip_atomic_store(&sh.lse, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(&s_lse_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             lse_out[row] = l;
             if (sel != nullptr && sel_out != nullptr) write_selected(V, s_sel, s_xsel, l, sel_out + row, err);
         }
+        return;
     }
     if (!KEYS) return;
 
@@ -1062,7 +1073,7 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
         for (int j = 0; j < KPT; ++j) kr[j] = 0u;
     }
     row_topk<DT, KPT, kThreads>(rowp, row, V, nb, K, kr, &sh.lse, cand, cand + cap, cap, sh, topk_ids,
-                                  topk_lp);
+                                  topk_lp, &s_lse_ready);
 }
 
 }  // namespace
