@@ -507,6 +507,12 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wtot, uint
 //    all keys above T plus the lowest-indexed keys equal to T, K in all;
 //  * one round of 16-byte loads gathers the kept blocks; entries with key
 //    >= T become candidates, compacted by a prefix scan;
+//  * with PF (16-bit logits), each thread loads the block holding its own
+//    largest key as soon as the keys are known, so those loads land while
+//    T is searched; when at most capb blocks reach T, every block >= T is a
+//    candidate block, copied from those registers to an LDS staging area
+//    (a second block >= T of the same thread is loaded then) and filtered
+//    there by all threads, instead of the placement and gather above;
 //  * each candidate's rank under (value desc, id asc) is counted in LDS and
 //    the first K are written.
 // Thread t holds the keys of blocks [t*KPT, t*KPT + KPT) in kr (0 past nb: a
@@ -521,15 +527,117 @@ struct RowShared {
     int32_t nlist, nblk;
     uint32_t hist[kHistBins];
     uint32_t thr[3];
+    int32_t ncand;
     float lse;
 };
 
-template <int DT, int KPT, int NT>
-__device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t V, int32_t nb, int32_t K,
+// (5) exact top-K of the ncand candidates by rank under the composite
+// (value key, ~id) order; logprobs against the row's lse.
+template <int DT, int NT>
+__device__ __forceinline__ void rank_topk(int64_t row, int32_t K, uint64_t* cand, int ncand, uint64_t* list2,
+                          RowShared<NT>& sh, int32_t* __restrict__ topk_ids, float* __restrict__ topk_lp,
+                          const float* lse_p, const int32_t* lse_ready) {
+    const int tid = threadIdx.x;
+    const uint64_t* list = cand;
+    int nlist = ncand;
+    if (ncand > NT && ncand > K) {
+        const uint64_t thr2 = radix_select<NT>(cand, ncand, K, sh.sc);
+        for (int i = tid; i < ncand; i += NT) {
+            const uint64_t c = cand[i];
+            if (c >= thr2) {
+                const int q = atomicAdd(&sh.nlist, 1);
+                if (q < K) list2[q] = c;
+            }
+        }
+        __syncthreads();
+        list = list2;
+        nlist = K;
+    }
+    // G lanes (a quad, a pair or one lane) count one candidate's predecessors
+    // over interleaved slices of the list, then sum with DPP inside the quad
+    // the row's lse: written before the first barrier above, or (lse_ready)
+    // by another wave of the workgroup that raises the flag after it
+    if (lse_ready != nullptr)
+        while (__hip_atomic_load(lse_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+        }
+    const float lse = lse_ready != nullptr ? __hip_atomic_load(lse_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                                           : *lse_p;
+    const int G = nlist <= NT / 4 ? 4 : (nlist <= NT / 2 ? 2 : 1);
+    const int q = tid & (G - 1);
+    for (int i0 = 0; i0 < nlist * G; i0 += NT) {
+        const int i = (i0 + tid) / G;
+        const bool act = i0 + tid < nlist * G;
+        const uint64_t c = act ? list[i] : 0ull;
+        uint32_t rank = 0;
+        if (act) {
+            int j = q;
+            for (; j + 7 * G < nlist; j += 8 * G) {
+                uint64_t v8[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v8[u] = list[j + u * G];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) rank += (v8[u] > c) ? 1u : 0u;
+            }
+            for (; j < nlist; j += G) rank += (list[j] > c) ? 1u : 0u;
+        }
+        if (G >= 2) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0xB1, 0xF, 0xF, false);
+        if (G == 4) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0x4E, 0xF, 0xF, false);
+        if (act && q == 0 && rank < (uint32_t)K) {
+            topk_ids[row * K + rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
+            topk_lp[row * K + rank] = elem_value<DT>((uint32_t)(c >> 32)) - lse;
+        }
+    }
+}
+
+// The 64 entries of block blk as 16-byte words; entries at or past V read
+// as -inf.
+template <int DT>
+__device__ __forceinline__ void load_block(const uint8_t* __restrict__ rowp, int64_t V, int32_t blk,
+                                  u32x4 (&v)[kBlock / (w16(DT) ? 8 : 4)]) {
+    constexpr int EPV = w16(DT) ? 8 : 4;
+    constexpr int VPB = kBlock / EPV;
+    const int64_t e0 = (int64_t)blk * kBlock;
+    if (e0 + kBlock <= V) {
+        const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + (size_t)e0 * (w16(DT) ? 2 : 4));
+#pragma unroll
+        for (int i = 0; i < VPB; ++i) v[i] = vp[i];
+        return;
+    }
+    const uint32_t ninf = ninf_word<DT>();
+#pragma unroll
+    for (int i = 0; i < VPB; ++i) v[i] = u32x4{ninf, ninf, ninf, ninf};
+#pragma unroll
+    for (int e = 0; e < kBlock; ++e) {
+        if (e0 + e >= V) continue;
+        const int q = (e % EPV) / (w16(DT) ? 2 : 1);
+        if (w16(DT)) {
+            const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[e0 + e];
+            v[e / EPV][q] = (e & 1) ? ((v[e / EPV][q] & 0x0000FFFFu) | (h << 16))
+                                    : ((v[e / EPV][q] & 0xFFFF0000u) | h);
+        } else {
+            v[e / EPV][q] = reinterpret_cast<const uint32_t*>(rowp)[e0 + e];
+        }
+    }
+}
+
+// Copies one candidate block to the next free LDS staging slot and records
+// its index there.
+template <int DT, int NT>
+__device__ __forceinline__ void stage_block(const u32x4 (&v)[kBlock / (w16(DT) ? 8 : 4)], int32_t blk,
+                                            u32x4* stage, RowShared<NT>& sh) {
+    constexpr int VPB = kBlock / (w16(DT) ? 8 : 4);
+    const int slot = atomicAdd(&sh.nblk, 1);
+    sh.blk[slot] = blk;
+#pragma unroll
+    for (int i = 0; i < VPB; ++i) stage[slot * VPB + i] = v[i];
+}
+
+template <int DT, int KPT, int NT, bool PF = false>
+__device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t V, int32_t nb, int32_t K,
                          const uint32_t (&kr)[KPT], const float* lse_p, uint64_t* cand, uint64_t* list2,
                          int32_t cap,
                          RowShared<NT>& sh, int32_t* __restrict__ topk_ids, float* __restrict__ topk_lp,
-                         const int32_t* lse_ready = nullptr) {
+                         const int32_t* lse_ready = nullptr, int32_t capb = 0, u32x4* stage = nullptr) {
     constexpr size_t ESZ = w16(DT) ? 2 : 4;
     constexpr int EPV = w16(DT) ? 8 : 4;                 // elements per 16-byte vector
     constexpr int VPB = kBlock / EPV;                 // vectors per block
@@ -537,6 +645,28 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
     constexpr int MAXBLK = kMaxCandidates / kBlock;
     const int tid = threadIdx.x;
     const int b0 = tid * KPT;
+
+    // PF: the block of this thread's largest key (lowest index among equal
+    // keys), loaded now and used after T is known
+    int32_t pf_blk = -1, pf_j = -1;
+    uint32_t pf_key = 0u;
+    u32x4 pf[PF ? VPB : 1];
+    if (PF && K <= nb) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (kr[j] > pf_key) {                        // slots past nb hold 0
+                pf_key = kr[j];
+                pf_j = j;
+            }
+        pf_blk = pf_j >= 0 ? b0 + pf_j : -1;
+        if (pf_blk >= 0 && (int64_t)pf_blk * kBlock + kBlock <= V) {
+            const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + (size_t)pf_blk * kBlock * ESZ);
+#pragma unroll
+            for (int i = 0; i < VPB; ++i) pf[i] = vp[i];
+        } else {
+            pf_blk = pf_j = -1;                          // the partial last block: loaded when needed
+        }
+    }
 
     // (3) threshold and kept blocks
     int phase = 0;
@@ -546,10 +676,11 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
         const int ksh = w16(DT) ? 16 : 0;
         // Largest t with count(key >= t) >= K; count(>= lo) >= K > count(>= hi).
         uint32_t tmax = 0u, tmin = 0xFFFFFFFFu;
+        const int nbt = nb - b0;                         // blocks of this thread
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             tmax = max(tmax, kr[j]);
-            if (b0 + j < nb) tmin = min(tmin, kr[j]);
+            if (j < nbt) tmin = min(tmin, kr[j]);
         }
         // one max-reduction gives the maximum and (complemented) two minima:
         // of all keys, and of the per-thread maxima of threads holding blocks
@@ -622,6 +753,53 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
         }
         __syncthreads();
         T = sh.thr[0];
+        if constexpr (PF) if (sh.thr[1] + sh.thr[2] <= (uint32_t)capb) {
+            // every block with key >= T is a candidate block: staged in LDS
+            // (sh.nblk counts the slots), then filtered by all threads
+            if (tid == 0) sh.ncand = 0;
+            uint32_t more = 0u;                          // bit j: block b0 + j >= T, not prefetched
+#pragma unroll
+            for (int j = 0; j < KPT; ++j)
+                if (kr[j] >= T && j != pf_j) more |= 1u << j;   // slots past nb hold 0 < T
+            if (pf_blk >= 0 && pf_key >= T) stage_block<DT, NT>(pf, pf_blk, stage, sh);
+            while (more != 0u) {
+                const int j = __builtin_ctz(more);
+                more &= more - 1u;
+                u32x4 v[VPB];
+                load_block<DT>(rowp, V, b0 + j, v);
+                stage_block<DT, NT>(v, b0 + j, stage, sh);
+            }
+            __syncthreads();
+            const bool keep_all = T == 0u;
+            const float Tf = keep_all ? kNegInf : block_value<DT>(T);
+            const int nvec = sh.nblk * VPB;
+            for (int i = tid; i < nvec; i += NT) {
+                const u32x4 w = stage[i];
+                const int64_t e0 = (int64_t)sh.blk[i / VPB] * kBlock + (int64_t)(i % VPB) * EPV;
+                uint32_t m = 0u;                         // bit e: entry e0 + e is a candidate
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const uint32_t wd = w[e / (w16(DT) ? 2 : 1)];
+                    const float x = w16(DT) ? ((e & 1) ? hi16<DT>(wd) : lo16<DT>(wd)) : __uint_as_float(wd);
+                    if (e0 + e < V && (keep_all || x >= Tf)) m |= 1u << e;
+                }
+                if (m != 0u) {
+                    int pos = atomicAdd(&sh.ncand, __builtin_popcount(m));
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        if ((m >> e) & 1u) {
+                            const uint32_t wd = w[e / (w16(DT) ? 2 : 1)];
+                            const float x = w16(DT) ? ((e & 1) ? hi16<DT>(wd) : lo16<DT>(wd)) : __uint_as_float(wd);
+                            cand[pos++] = ((uint64_t)elem_key<DT>(x) << 32) |
+                                          (uint64_t)(0xFFFFFFFFu - (uint32_t)(e0 + e));
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            rank_topk<DT, NT>(row, K, cand, sh.ncand, list2, sh, topk_ids, topk_lp, lse_p, lse_ready);
+            return;
+        }
         const int need = K - (int)sh.thr[1];             // blocks equal to T that are kept
         const bool all_ties = (uint32_t)need == sh.thr[2];
         if (all_ties) {
@@ -733,56 +911,7 @@ __device__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t 
     }
     __syncthreads();
 
-    // (5) exact top-K by rank under the composite (value key, ~id) order
-    const uint64_t* list = cand;
-    int nlist = ncand;
-    if (ncand > NT && ncand > K) {
-        const uint64_t thr2 = radix_select<NT>(cand, ncand, K, sh.sc);
-        for (int i = tid; i < ncand; i += NT) {
-            const uint64_t c = cand[i];
-            if (c >= thr2) {
-                const int q = atomicAdd(&sh.nlist, 1);
-                if (q < K) list2[q] = c;
-            }
-        }
-        __syncthreads();
-        list = list2;
-        nlist = K;
-    }
-    // G lanes (a quad, a pair or one lane) count one candidate's predecessors
-    // over interleaved slices of the list, then sum with DPP inside the quad
-    // the row's lse: written before the first barrier above, or (lse_ready)
-    // by another wave of the workgroup that raises the flag after it
-    if (lse_ready != nullptr)
-        while (__hip_atomic_load(lse_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-        }
-    const float lse = lse_ready != nullptr ? __hip_atomic_load(lse_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
-                                           : *lse_p;
-    const int G = nlist <= NT / 4 ? 4 : (nlist <= NT / 2 ? 2 : 1);
-    const int q = tid & (G - 1);
-    for (int i0 = 0; i0 < nlist * G; i0 += NT) {
-        const int i = (i0 + tid) / G;
-        const bool act = i0 + tid < nlist * G;
-        const uint64_t c = act ? list[i] : 0ull;
-        uint32_t rank = 0;
-        if (act) {
-            int j = q;
-            for (; j + 7 * G < nlist; j += 8 * G) {
-                uint64_t v8[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) v8[u] = list[j + u * G];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) rank += (v8[u] > c) ? 1u : 0u;
-            }
-            for (; j < nlist; j += G) rank += (list[j] > c) ? 1u : 0u;
-        }
-        if (G >= 2) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0xB1, 0xF, 0xF, false);
-        if (G == 4) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0x4E, 0xF, 0xF, false);
-        if (act && q == 0 && rank < (uint32_t)K) {
-            topk_ids[row * K + rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
-            topk_lp[row * K + rank] = elem_value<DT>((uint32_t)(c >> 32)) - lse;
-        }
-    }
+    rank_topk<DT, NT>(row, K, cand, ncand, list2, sh, topk_ids, topk_lp, lse_p, lse_ready);
 }
 
 // Canonical merge of a row's item partials (group i mod 16, ascending items
@@ -916,15 +1045,19 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// One-workgroup-per-row path (rows that fill the CUs evenly): 16 waves stream
+// One-workgroup-per-row path (rows that fill the CUs evenly): 8 waves stream
 // the row's items, handed out from an LDS counter (bf16 items double-
 // buffered: the next item's loads are in flight while the current one is
 // reduced), writing each item's partial and block keys to LDS; after one
-// barrier wave 0 merges the partials in the canonical order while waves 1-3
-// start the top-K selection on the LDS keys (waves 4-15 end there). One
-// launch, and no workspace round trip between the stream and the selection.
+// barrier wave 4 merges the partials in the canonical order while waves 0-3
+// run the top-K selection on the LDS keys (waves 5-7 end there). One launch,
+// and no workspace round trip between the stream and the selection. Eight
+// waves keep two 8 KiB items per wave in flight, which holds the CU's share
+// of HBM bandwidth; sixteen waves streamed no faster and took longer to
+// dispatch (28.6 against 30.3 us on 256 rows of 248,320 bf16 logits).
 // ---------------------------------------------------------------------------
-constexpr int kRowThreads = kGroups * 64;
+constexpr int kRowWaves = 8;
+constexpr int kRowThreads = kRowWaves * 64;
 constexpr int kRowMaxItems = 64;   // items per row on this path (V <= 64 * kSeg)
 template <bool W16> struct KeyType { using type = uint32_t; };
 template <> struct KeyType<true> { using type = uint16_t; };
@@ -940,7 +1073,8 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
                                                            int32_t* __restrict__ err, int32_t cap) {
     using I = Stage1Item<DT>;
     using key_t = typename KeyType<w16(DT)>::type;
-    extern __shared__ uint64_t smem[];   // [KPT*256] keys, then [cap] candidates, [K] narrowed list
+    // [KPT*256] keys, [cap] candidates, [K] narrowed list (even count), staged blocks
+    extern __shared__ __attribute__((aligned(16))) uint64_t smem[];
     __shared__ RowShared<kThreads> sh;
     __shared__ float2 sgrp[kGroups];
     __shared__ float2 sitem[kRowMaxItems];
@@ -960,7 +1094,7 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     if (tid == 0) {
         sh.nlist = 0;
         sh.nblk = 0;
-        s_next = kGroups;
+        s_next = kRowWaves;
         s_lse_ready = 0;
     }
     __syncthreads();   // s_next before the first hand-out
@@ -1002,7 +1136,7 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     // The partial last item (index Pf, when V is not a multiple of kSeg) goes
     // first to the last wave, so that its loads are not exposed at the end.
     const int32_t Pf = (int32_t)(V / kSeg);
-    if (Pf < P && wave == kGroups - 1) {
+    if (Pf < P && wave == kRowWaves - 1) {
         u32x4 buf[I::VPL];
         stage1_load<DT>(rowp, V, Pf, lane, buf);
         reduce_item(buf, Pf);
@@ -1072,8 +1206,9 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
 #pragma unroll
         for (int j = 0; j < KPT; ++j) kr[j] = 0u;
     }
-    row_topk<DT, KPT, kThreads>(rowp, row, V, nb, K, kr, &sh.lse, cand, cand + cap, cap, sh, topk_ids,
-                                  topk_lp, &s_lse_ready);
+    row_topk<DT, KPT, kThreads, w16(DT)>(rowp, row, V, nb, K, kr, &sh.lse, cand, cand + cap, cap, sh,
+                                          topk_ids, topk_lp, &s_lse_ready, cap / kBlock,
+                                          reinterpret_cast<u32x4*>(cand + cap + ((K + 1) & ~1)));
 }
 
 }  // namespace
@@ -1220,10 +1355,14 @@ hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s
     int32_t cap = 0;
     size_t lds = 0;
     if (p.k > 0) {
-        const int32_t nsel = p.k < p.nb ? p.k : p.nb;
-        cap = nsel * kBlock;
+        // 16-bit logits: room for up to 2K candidate blocks (at most 128), so
+        // that the prefetched-candidate path also takes blocks tied at T
+        const int32_t kb2 = w16(a.dt) ? std::min(std::max(p.k, std::min(2 * p.k, kMaxCandidates / kBlock)), p.nb)
+                                      : std::min(p.k, p.nb);
+        cap = kb2 * kBlock;
         const size_t kbytes = (size_t)p.kpt * kThreads * (w16(a.dt) ? 2 : 4);
-        lds = kbytes + ((size_t)cap + (size_t)p.k) * sizeof(uint64_t);
+        const size_t stage = w16(a.dt) ? (size_t)cap * 2 : 0;   // staged candidate blocks
+        lds = kbytes + ((size_t)cap + (size_t)((p.k + 1) & ~1)) * sizeof(uint64_t) + stage;
     }
     auto go = [&](auto dt) -> hipError_t {
         constexpr int DT = decltype(dt)::value;
