@@ -161,7 +161,8 @@ __device__ inline float elem_value(uint32_t k) {
 // across the wave (a register select, then ds_bpermute) so that lane b holds
 // block b. The item partials of a row are merged in one canonical order:
 // item i joins merge group i mod 16, each group merges its items in
-// ascending order, and the 16 groups are merged in order. Both reduction
+// ascending order, and the 16 groups are merged as a pairwise tree (one lane
+// per group, lower groups on the left). Both reduction
 // paths (the split one and the one-workgroup-per-row one) use exactly this
 // arithmetic, so each row's results are bitwise independent of the batch
 // around it and of the path that served it.
@@ -509,10 +510,12 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wtot, uint
 //    >= T become candidates, compacted by a prefix scan;
 //  * with PF (16-bit logits), each thread loads the block holding its own
 //    largest key as soon as the keys are known, so those loads land while
-//    T is searched; when at most capb blocks reach T, every block >= T is a
-//    candidate block, copied from those registers to an LDS staging area
-//    (a second block >= T of the same thread is loaded then) and filtered
-//    there by all threads, instead of the placement and gather above;
+//    T is searched (eight lanes load the eight 16-byte parts of a block, so
+//    a wave instruction reads eight whole blocks); when at most capb blocks
+//    reach T, every block >= T is a candidate block, copied from those
+//    registers to an LDS staging area (a second block >= T of the same
+//    thread is loaded then) and filtered there by all threads, instead of
+//    the placement and gather above;
 //  * each candidate's rank under (value desc, id asc) is counted in LDS and
 //    the first K are written.
 // Thread t holds the keys of blocks [t*KPT, t*KPT + KPT) in kr (0 past nb: a
@@ -524,6 +527,7 @@ struct RowShared {
     uint32_t sred[2][NT / 64][4];
     uint32_t swtot[NT / 64];
     int32_t blk[kMaxCandidates / kBlock];
+    int32_t cslot[kMaxCandidates / kBlock];   // staging slot of each candidate block (PF path)
     int32_t nlist, nblk;
     uint32_t hist[kHistBins];
     uint32_t thr[3];
@@ -620,18 +624,6 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ rowp, int
     }
 }
 
-// Copies one candidate block to the next free LDS staging slot and records
-// its index there.
-template <int DT, int NT>
-__device__ __forceinline__ void stage_block(const u32x4 (&v)[kBlock / (w16(DT) ? 8 : 4)], int32_t blk,
-                                            u32x4* stage, RowShared<NT>& sh) {
-    constexpr int VPB = kBlock / (w16(DT) ? 8 : 4);
-    const int slot = atomicAdd(&sh.nblk, 1);
-    sh.blk[slot] = blk;
-#pragma unroll
-    for (int i = 0; i < VPB; ++i) stage[slot * VPB + i] = v[i];
-}
-
 template <int DT, int KPT, int NT, bool PF = false>
 __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t V, int32_t nb, int32_t K,
                          const uint32_t (&kr)[KPT], const float* lse_p, uint64_t* cand, uint64_t* list2,
@@ -659,12 +651,16 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
                 pf_j = j;
             }
         pf_blk = pf_j >= 0 ? b0 + pf_j : -1;
-        if (pf_blk >= 0 && (int64_t)pf_blk * kBlock + kBlock <= V) {
-            const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + (size_t)pf_blk * kBlock * ESZ);
-#pragma unroll
-            for (int i = 0; i < VPB; ++i) pf[i] = vp[i];
-        } else {
+        if (pf_blk >= 0 && (int64_t)pf_blk * kBlock + kBlock > V)
             pf_blk = pf_j = -1;                          // the partial last block: loaded when needed
+        // coalesced: load i of lane l brings the 16-byte part l % 8 of the
+        // block of lane 8i + l / 8 (eight whole blocks per wave instruction)
+        static_assert(!PF || VPB == 8, "the prefetch spreads a block over eight lanes");
+#pragma unroll
+        for (int i = 0; i < VPB; ++i) {
+            const int blk = __shfl(pf_blk, i * 8 + ((tid & 63) >> 3));
+            if (blk >= 0)
+                pf[i] = *reinterpret_cast<const u32x4*>(rowp + ((size_t)blk * kBlock + (size_t)(tid & 7) * EPV) * ESZ);
         }
     }
 
@@ -761,20 +757,33 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
 #pragma unroll
             for (int j = 0; j < KPT; ++j)
                 if (kr[j] >= T && j != pf_j) more |= 1u << j;   // slots past nb hold 0 < T
-            if (pf_blk >= 0 && pf_key >= T) stage_block<DT, NT>(pf, pf_blk, stage, sh);
+            // staging slot t holds thread t's prefetched block (every part
+            // is written; only the slots of candidate blocks are read), slots
+            // NT + c the blocks loaded now
+#pragma unroll
+            for (int i = 0; i < VPB; ++i) stage[((tid & ~63) + i * 8 + ((tid & 63) >> 3)) * VPB + (tid & 7)] = pf[i];
+            if (pf_blk >= 0 && pf_key >= T) {
+                const int c = atomicAdd(&sh.nblk, 1);
+                sh.blk[c] = pf_blk;
+                sh.cslot[c] = tid;
+            }
             while (more != 0u) {
                 const int j = __builtin_ctz(more);
                 more &= more - 1u;
                 u32x4 v[VPB];
                 load_block<DT>(rowp, V, b0 + j, v);
-                stage_block<DT, NT>(v, b0 + j, stage, sh);
+                const int c = atomicAdd(&sh.nblk, 1);
+                sh.blk[c] = b0 + j;
+                sh.cslot[c] = NT + c;
+#pragma unroll
+                for (int i = 0; i < VPB; ++i) stage[(NT + c) * VPB + i] = v[i];
             }
             __syncthreads();
             const bool keep_all = T == 0u;
             const float Tf = keep_all ? kNegInf : block_value<DT>(T);
             const int nvec = sh.nblk * VPB;
             for (int i = tid; i < nvec; i += NT) {
-                const u32x4 w = stage[i];
+                const u32x4 w = stage[sh.cslot[i / VPB] * VPB + i % VPB];
                 const int64_t e0 = (int64_t)sh.blk[i / VPB] * kBlock + (int64_t)(i % VPB) * EPV;
                 uint32_t m = 0u;                         // bit e: entry e0 + e is a candidate
 #pragma unroll
@@ -914,13 +923,33 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
     rank_topk<DT, NT>(row, K, cand, ncand, list2, sh, topk_ids, topk_lp, lse_p, lse_ready);
 }
 
-// Canonical merge of a row's item partials (group i mod 16, ascending items
-// within a group, then groups in order); lse = m + log(s), -inf for a row
-// whose entries are all -inf. Called by one lane.
-__device__ inline float lse_of_groups(const float2* g) {
-    float m = kNegInf, s = 0.f;
-#pragma unroll
-    for (int i = 0; i < kGroups; ++i) lse_merge(m, s, g[i].x, g[i].y);
+// Canonical merge of a row's item partials: lane g < 16 holds the partial
+// of group g (items i with i mod 16 == g, merged in ascending order); the 16
+// groups are merged as a pairwise tree (2j with 2j+1, then the pairs, ...;
+// the lower groups always the left operand), so every lane takes the same
+// rounding steps. lse = m + log(s), -inf for a row whose entries are all
+// -inf. Called by a whole wave (lanes 16-63 hold copies of no use); lanes
+// 0-15 return the row's lse.
+__device__ inline float lse_tree16(float m, float s) {
+    const int lane = threadIdx.x & 63;
+    // partner lane at each level: lane ^ 1, lane ^ 2 (quad permutes), then
+    // the mirror lane in the half row and in the row; after each level the
+    // lanes of a merged subgroup hold identical values, so any lane of the
+    // partner subgroup serves
+    auto level = [&](auto ctl, int d) {
+        constexpr int C = decltype(ctl)::value;
+        const float m2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), C, 0xF, 0xF, false));
+        const float s2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), C, 0xF, 0xF, false));
+        const bool left = (lane & d) == 0;
+        float mL = left ? m : m2, sL = left ? s : s2;
+        lse_merge(mL, sL, left ? m2 : m, left ? s2 : s);
+        m = mL;
+        s = sL;
+    };
+    level(std::integral_constant<int, 0xB1>{}, 1);
+    level(std::integral_constant<int, 0x4E>{}, 2);
+    level(std::integral_constant<int, 0x141>{}, 4);
+    level(std::integral_constant<int, 0x140>{}, 8);
     return (m == kNegInf) ? kNegInf : m + logf(s);
 }
 
@@ -959,7 +988,6 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
                                                      int32_t* __restrict__ err, int32_t cap) {
     extern __shared__ uint64_t smem[];   // [cap] candidates, [K] narrowed list
     __shared__ RowShared<kThreads> sh;
-    __shared__ float2 sgrp[kGroups];
     constexpr size_t ESZ = w16(DT) ? 2 : 4;
     constexpr int MAXBLK = kMaxCandidates / kBlock;
 
@@ -1016,23 +1044,20 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     int32_t sel_id = 0;
     if (sel_thread) sel_id = sel[row];
 
-    // logsumexp: lanes 0..15 of wave 0 merge their groups' partials, lane 0
-    // merges the groups
-    if (tid < kGroups) {
+    // logsumexp: lanes 0..15 of wave 0 merge their groups' partials, then
+    // the wave merges the groups
+    if (tid < 64) {
         float m = kNegInf, sm = 0.f;
-        for (int i = tid; i < splits; i += kGroups) {
-            const float2 pp = part[row * splits + i];
-            lse_merge(m, sm, pp.x, pp.y);
+        if (tid < kGroups)
+            for (int i = tid; i < splits; i += kGroups) {
+                const float2 pp = part[row * splits + i];
+                lse_merge(m, sm, pp.x, pp.y);
+            }
+        const float l = lse_tree16(m, sm);
+        if (tid == 0) {
+            sh.lse = l;
+            lse_out[row] = l;
         }
-        sgrp[tid] = make_float2(m, sm);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (tid == 0) {
-        const float l = lse_of_groups(sgrp);
-        sh.lse = l;
-        lse_out[row] = l;
     }
     __syncthreads();
     const float lse = sh.lse;
@@ -1076,7 +1101,6 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     // [KPT*256] keys, [cap] candidates, [K] narrowed list (even count), staged blocks
     extern __shared__ __attribute__((aligned(16))) uint64_t smem[];
     __shared__ RowShared<kThreads> sh;
-    __shared__ float2 sgrp[kGroups];
     __shared__ float2 sitem[kRowMaxItems];
     __shared__ int32_t s_next, s_sel, s_lse_ready;
     __shared__ float s_xsel;
@@ -1170,21 +1194,16 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     if (sel_thread) s_xsel = xsel;
     __syncthreads();
 
-    // lse: lanes 0..15 of wave 4 merge their groups, lane 0 the groups (the
-    // split path's arithmetic), then raise s_lse_ready; the selection on
-    // waves 0..3 starts at once and reads the lse only for its last step
+    // lse: lanes 0..15 of wave 4 merge their groups, the wave the groups
+    // (the split path's arithmetic), then lane 0 raises s_lse_ready; the
+    // selection on waves 0..3 reads the lse only for its last step
     constexpr int kLseWave = kThreads / 64;
     if (wave == kLseWave) {
-        if (lane < kGroups) {
-            float m = kNegInf, sm = 0.f;
+        float m = kNegInf, sm = 0.f;
+        if (lane < kGroups)
             for (int32_t i = lane; i < P; i += kGroups) lse_merge(m, sm, sitem[i].x, sitem[i].y);
-            sgrp[lane] = make_float2(m, sm);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float l = lse_tree16(m, sm);
         if (lane == 0) {
-            const float l = lse_of_groups(sgrp);
             __hip_atomic_store(&sh.lse, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_store(&s_lse_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             lse_out[row] = l;
@@ -1361,7 +1380,8 @@ hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s
                                       : std::min(p.k, p.nb);
         cap = kb2 * kBlock;
         const size_t kbytes = (size_t)p.kpt * kThreads * (w16(a.dt) ? 2 : 4);
-        const size_t stage = w16(a.dt) ? (size_t)cap * 2 : 0;   // staged candidate blocks
+        // staged blocks: one per selection thread, then the candidate blocks
+        const size_t stage = w16(a.dt) ? ((size_t)kThreads * kBlock + (size_t)cap) * 2 : 0;
         lds = kbytes + ((size_t)cap + (size_t)((p.k + 1) & ~1)) * sizeof(uint64_t) + stage;
     }
     auto go = [&](auto dt) -> hipError_t {
