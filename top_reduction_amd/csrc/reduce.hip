@@ -624,12 +624,16 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ rowp, int
     }
 }
 
-template <int DT, int KPT, int NT, bool PF = false>
+// PRE: the caller already holds, per selection thread t, the maximum and
+// minimum of its keys (tkey[0][t], tkey[1][t]; 0 and ~0 for a thread without
+// blocks) and has zeroed sh.hist, which saves two workgroup barriers.
+template <int DT, int KPT, int NT, bool PF = false, bool PRE = false>
 __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64_t row, int64_t V, int32_t nb, int32_t K,
                          const uint32_t (&kr)[KPT], const float* lse_p, uint64_t* cand, uint64_t* list2,
                          int32_t cap,
                          RowShared<NT>& sh, int32_t* __restrict__ topk_ids, float* __restrict__ topk_lp,
-                         const int32_t* lse_ready = nullptr, int32_t capb = 0, u32x4* stage = nullptr) {
+                         const int32_t* lse_ready = nullptr, int32_t capb = 0, u32x4* stage = nullptr,
+                         const uint32_t (*tkey)[NT] = nullptr) {
     constexpr size_t ESZ = w16(DT) ? 2 : 4;
     constexpr int EPV = w16(DT) ? 8 : 4;                 // elements per 16-byte vector
     constexpr int VPB = kBlock / EPV;                 // vectors per block
@@ -656,12 +660,15 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
         // coalesced: load i of lane l brings the 16-byte part l % 8 of the
         // block of lane 8i + l / 8 (eight whole blocks per wave instruction)
         static_assert(!PF || VPB == 8, "the prefetch spreads a block over eight lanes");
+        // (all lane exchanges first, then branch-free loads: a lane whose
+        // owner has no block reads block 0, never used)
+        int blk[VPB];
 #pragma unroll
-        for (int i = 0; i < VPB; ++i) {
-            const int blk = __shfl(pf_blk, i * 8 + ((tid & 63) >> 3));
-            if (blk >= 0)
-                pf[i] = *reinterpret_cast<const u32x4*>(rowp + ((size_t)blk * kBlock + (size_t)(tid & 7) * EPV) * ESZ);
-        }
+        for (int i = 0; i < VPB; ++i) blk[i] = __shfl(pf_blk, i * 8 + ((tid & 63) >> 3));
+#pragma unroll
+        for (int i = 0; i < VPB; ++i)
+            pf[i] = *reinterpret_cast<const u32x4*>(
+                rowp + ((size_t)(blk[i] < 0 ? 0 : blk[i]) * kBlock + (size_t)(tid & 7) * EPV) * ESZ);
     }
 
     // (3) threshold and kept blocks
@@ -671,17 +678,36 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
     if (K <= nb) {
         const int ksh = w16(DT) ? 16 : 0;
         // Largest t with count(key >= t) >= K; count(>= lo) >= K > count(>= hi).
-        uint32_t tmax = 0u, tmin = 0xFFFFFFFFu;
-        const int nbt = nb - b0;                         // blocks of this thread
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            tmax = max(tmax, kr[j]);
-            if (j < nbt) tmin = min(tmin, kr[j]);
-        }
         // one max-reduction gives the maximum and (complemented) two minima:
         // of all keys, and of the per-thread maxima of threads holding blocks
-        uint32_t mm[3] = {tmax, ~tmin, b0 < nb ? ~tmax : 0u};
-        block_reduce<1, 3, NT>(mm, sh.sred, phase);
+        uint32_t mm[3];
+        if constexpr (PRE) {
+            // every wave reduces the per-thread extremes itself (no barrier)
+            const int lane = tid & 63;
+            mm[0] = mm[1] = mm[2] = 0u;
+#pragma unroll
+            for (int i = 0; i < NT / 64; ++i) {
+                const int t = lane + 64 * i;
+                const uint32_t hi_t = tkey[0][t], lo_t = tkey[1][t];
+                mm[0] = max(mm[0], hi_t);
+                mm[1] = max(mm[1], ~lo_t);
+                mm[2] = max(mm[2], t * KPT < nb ? ~hi_t : 0u);
+            }
+#pragma unroll
+            for (int i = 0; i < 3; ++i) mm[i] = wave_reduce<1>(mm[i]);
+        } else {
+            uint32_t tmax = 0u, tmin = 0xFFFFFFFFu;
+            const int nbt = nb - b0;                     // blocks of this thread
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                tmax = max(tmax, kr[j]);
+                if (j < nbt) tmin = min(tmin, kr[j]);
+            }
+            mm[0] = tmax;
+            mm[1] = ~tmin;
+            mm[2] = b0 < nb ? ~tmax : 0u;
+            block_reduce<1, 3, NT>(mm, sh.sred, phase);
+        }
         const int nth = (nb + KPT - 1) / KPT;           // threads holding blocks
         uint64_t lo = (uint64_t)((K <= nth ? ~mm[2] : ~mm[1]) >> ksh);
         uint64_t hi = (uint64_t)(mm[0] >> ksh) + 1;
@@ -717,8 +743,10 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
         }
         // histogram of the keys in [lo, hi), then a suffix scan in wave 0:
         // T is the largest key value v with count(key >= v) >= K
-        if (tid < kHistBins) sh.hist[tid] = 0u;
-        __syncthreads();
+        if constexpr (!PRE) {
+            if (tid < kHistBins) sh.hist[tid] = 0u;
+            __syncthreads();
+        }
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const uint64_t kv = kr[j] >> ksh;
@@ -1104,6 +1132,9 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
     __shared__ float2 sitem[kRowMaxItems];
     __shared__ int32_t s_next, s_sel, s_lse_ready;
     __shared__ float s_xsel;
+    // per selection thread t (blocks t*KPT .. t*KPT + KPT - 1): the maximum
+    // and minimum of its keys, gathered while the items are reduced
+    __shared__ uint32_t s_tkey[2][kThreads];
     constexpr size_t ESZ = w16(DT) ? 2 : 4;
     constexpr int MAXBLK = kMaxCandidates / kBlock;
     key_t* skeys = reinterpret_cast<key_t*>(smem);
@@ -1120,6 +1151,13 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
         sh.nblk = 0;
         s_next = kRowWaves;
         s_lse_ready = 0;
+    }
+    if (KEYS) {
+        for (int t = tid; t < kThreads; t += kRowThreads) {
+            s_tkey[0][t] = 0u;
+            s_tkey[1][t] = 0xFFFFFFFFu;
+        }
+        for (int i = tid; i < kHistBins; i += kRowThreads) sh.hist[i] = 0u;
     }
     __syncthreads();   // s_next before the first hand-out
     // key slots past nb read as 0
@@ -1149,6 +1187,25 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
         if (KEYS) {
             const int32_t blk = seg * (kSeg / kBlock) + lane;
             if (blk < nb) skeys[blk] = w16(DT) ? (key_t)(kb >> 16) : (key_t)kb;
+            // the key as the selection holds it; extremes over the KPT lanes
+            // of one selection thread (partners: lane ^ 1, ^ 2, then the
+            // mirror lane in the half row and in the row)
+            const uint32_t kv = w16(DT) ? (kb & 0xFFFF0000u) : kb;
+            uint32_t hi = blk < nb ? kv : 0u, lo = blk < nb ? kv : 0xFFFFFFFFu;
+            auto fold = [&](auto ctl) {
+                constexpr int C = decltype(ctl)::value;
+                hi = max(hi, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, C, 0xF, 0xF, false));
+                lo = min(lo, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, C, 0xF, 0xF, false));
+            };
+            fold(std::integral_constant<int, 0xB1>{});
+            fold(std::integral_constant<int, 0x4E>{});
+            if (KPT >= 8) fold(std::integral_constant<int, 0x141>{});
+            if (KPT >= 16) fold(std::integral_constant<int, 0x140>{});
+            const int t = blk / KPT;
+            if (lane % KPT == 0 && t < kThreads) {
+                s_tkey[0][t] = hi;
+                s_tkey[1][t] = lo;
+            }
         }
         if (lane == 0) sitem[seg] = make_float2(M, S);
     };
@@ -1225,9 +1282,9 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
 #pragma unroll
         for (int j = 0; j < KPT; ++j) kr[j] = 0u;
     }
-    row_topk<DT, KPT, kThreads, w16(DT)>(rowp, row, V, nb, K, kr, &sh.lse, cand, cand + cap, cap, sh,
-                                          topk_ids, topk_lp, &s_lse_ready, cap / kBlock,
-                                          reinterpret_cast<u32x4*>(cand + cap + ((K + 1) & ~1)));
+    row_topk<DT, KPT, kThreads, w16(DT), true>(rowp, row, V, nb, K, kr, &sh.lse, cand, cand + cap, cap, sh,
+                                                topk_ids, topk_lp, &s_lse_ready, cap / kBlock,
+                                                reinterpret_cast<u32x4*>(cand + cap + ((K + 1) & ~1)), s_tkey);
 }
 
 }  // namespace
