@@ -197,3 +197,62 @@ def test_row_path_matches_split_path(V, dt, k):
     sub = lmh.Reduction(a.lse[pick], a.selected_logprob[pick], a.topk_ids[pick], a.topk_logprobs[pick],
                         a.device_error)
     check_reduce(sub, np.ascontiguousarray(ref_rows[pick]), sel[pick], k, *ref)
+
+
+def _prefetch_rows(V, dt, seed):
+    """256 rows that steer the one-workgroup-per-row selection of 16-bit
+    logits through each of its branches: the row maximum in the partial last
+    block (never prefetched: loaded after the threshold); the top values in
+    eight consecutive blocks, all held by one selection thread (its extra
+    blocks are loaded after the threshold); 300 blocks tied at the top, more
+    than the prefetched path takes (the placement path runs); plain rows."""
+    g = synth.rng(seed)
+    x = synth.normal_f32(g, (256, V), 2.0)
+    nb = -(-V // 64)
+    for r in range(256):
+        kind = r % 4
+        if kind == 0:
+            x[r, V - 1] = 24.0
+            x[r, V - 2] = 23.0
+        elif kind == 1:
+            b0 = 64 * (16 * (r % (nb // 16)))                   # the first block of a selection thread
+            x[r, b0:b0 + 8 * 64:64] = np.arange(8, dtype=np.float32) + 16.0
+        elif kind == 2:
+            blocks = g.choice(nb - 1, size=300, replace=False)
+            x[r, blocks * 64 + 7] = 12.0
+    if dt == "bf16":
+        return synth.f32_to_bf16_bits(x)
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("k", [1, 20, 128])
+def test_prefetched_candidate_paths(dt, k):
+    """Oracle parity on every row, and bitwise equality with the split path
+    (which never prefetches), for rows built to take each branch."""
+    V = 248_280                                              # last block holds 24 entries
+    print(f"prefetch paths dt={dt} k={k}", flush=True)
+    data = _prefetch_rows(V, dt, 7700 + k)
+    g = synth.rng(7800 + k)
+    sel = g.integers(0, V, size=256).astype(np.int32)
+    ld = (V + 7) // 8 * 8
+    if dt == "bf16":
+        full = np.zeros((256, ld), dtype=np.uint16)
+        full[:, :V] = data
+        t = bf16_tensor(full)[:, :V]
+    else:
+        full = np.zeros((256, ld), dtype=np.float16)
+        full[:, :V] = data
+        t = torch.from_numpy(full).cuda()[:, :V]
+    if torch.cuda.get_device_properties(0).multi_processor_count <= 256:
+        assert lmh.reduce_row_path(256, V, k)
+    a = lmh.logprob_reduce(t, i32_tensor(sel), k)
+    check_reduce(a, data, sel, k, *oracle.reduce(data, sel, k))
+    parts = [lmh.logprob_reduce(t[i:i + 100], i32_tensor(sel[i:i + 100]), k) for i in range(0, 256, 100)]
+    torch.cuda.synchronize()
+    cat = lambda f: torch.cat([getattr(p, f) for p in parts])
+    assert torch.equal(a.lse.view(torch.int32), cat("lse").view(torch.int32))
+    assert torch.equal(a.topk_ids, cat("topk_ids"))
+    assert torch.equal(a.topk_logprobs.view(torch.int32), cat("topk_logprobs").view(torch.int32))
+    ids = a.topk_ids.cpu().numpy()
+    assert np.all(ids[0::4, 0] == V - 1)                     # the partial block's entry leads
