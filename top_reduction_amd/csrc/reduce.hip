@@ -1014,7 +1014,8 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
                                                      int32_t* __restrict__ topk_ids,
                                                      float* __restrict__ topk_lp,
                                                      int32_t* __restrict__ err, int32_t cap) {
-    extern __shared__ uint64_t smem[];   // [cap] candidates, [K] narrowed list
+    // [cap] candidates, [K] narrowed list (even count), staged blocks (16-bit logits)
+    extern __shared__ __attribute__((aligned(16))) uint64_t smem[];
     __shared__ RowShared<kThreads> sh;
     constexpr size_t ESZ = w16(DT) ? 2 : 4;
     constexpr int MAXBLK = kMaxCandidates / kBlock;
@@ -1092,8 +1093,9 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     // the selected logit: loaded now, written after the top-K
     const float xsel = sel_thread ? load_selected<DT>(rowp, V, sel_id) : 0.f;
     if (K > 0)
-        row_topk<DT, KPT, kThreads>(rowp, row, V, nb, K, kr, &sh.lse, smem, smem + cap, cap, sh, topk_ids,
-                                      topk_lp);
+        row_topk<DT, KPT, kThreads, w16(DT)>(rowp, row, V, nb, K, kr, &sh.lse, smem, smem + cap, cap, sh,
+                                              topk_ids, topk_lp, nullptr, cap / kBlock,
+                                              reinterpret_cast<u32x4*>(smem + cap + ((K + 1) & ~1)));
     if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
 }
 
@@ -1372,9 +1374,15 @@ hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStr
     int32_t cap = 0;
     size_t lds = 0;
     if (p.k > 0) {
-        const int32_t nsel = p.k < p.nb ? p.k : p.nb;
-        cap = nsel * kBlock;
-        lds = ((size_t)cap + (size_t)p.k) * sizeof(uint64_t);
+        // 16-bit logits: room for up to 2K candidate blocks (at most 128) and
+        // their staging slots, so that the prefetched-candidate path also
+        // takes blocks tied at T
+        const int32_t kb2 = w16(a.dt) ? std::min(std::max(p.k, std::min(2 * p.k, kMaxCandidates / kBlock)), p.nb)
+                                      : std::min(p.k, p.nb);
+        cap = kb2 * kBlock;
+        // (the staging path exists only when K <= nb)
+        const size_t stage = w16(a.dt) && p.k <= p.nb ? ((size_t)kThreads * kBlock + (size_t)cap) * 2 : 0;
+        lds = ((size_t)cap + (size_t)((p.k + 1) & ~1)) * sizeof(uint64_t) + stage;
     }
     if (a.dt == kDtBf16) return launch_stage2_dt<kDtBf16>(p, a, s, part, keys, cap, lds);
     if (a.dt == kDtF16) return launch_stage2_dt<kDtF16>(p, a, s, part, keys, cap, lds);
@@ -1438,7 +1446,8 @@ hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s
         cap = kb2 * kBlock;
         const size_t kbytes = (size_t)p.kpt * kThreads * (w16(a.dt) ? 2 : 4);
         // staged blocks: one per selection thread, then the candidate blocks
-        const size_t stage = w16(a.dt) ? ((size_t)kThreads * kBlock + (size_t)cap) * 2 : 0;
+        // (the staging path exists only when K <= nb)
+        const size_t stage = w16(a.dt) && p.k <= p.nb ? ((size_t)kThreads * kBlock + (size_t)cap) * 2 : 0;
         lds = kbytes + ((size_t)cap + (size_t)((p.k + 1) & ~1)) * sizeof(uint64_t) + stage;
     }
     auto go = [&](auto dt) -> hipError_t {
