@@ -11,7 +11,10 @@
 // that are not below the K-th kept maximum are gathered, and they are ranked
 // by (value descending, id ascending) in LDS. The candidate set provably
 // contains the exact top-K: a top-K entry outside the kept blocks, or below
-// the K-th kept maximum, would have K kept block maxima ahead of it.
+// the K-th kept maximum, would have K kept block maxima ahead of it. With
+// 16-bit logits, when few blocks reach the K-th largest maximum, all of them
+// are kept (a superset; ties at that maximum need no ordering then), taken
+// from blocks each thread prefetched while the threshold was searched.
 //
 // Two paths, with bitwise-identical results:
 //   * k_rowreduce (rows fill the CUs evenly): one workgroup per row streams
