@@ -752,6 +752,178 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 tiled kernel with 64-wide k stages (hidden size a multiple of 128):
+// the same 256 x 256 tile, waves, MFMA sequence and epilogue as k_head_tiled,
+// but each stage carries two MFMA k-steps (a whole 128-byte row of A and of
+// W per stage), so a tile takes half the barriers and every row load is a
+// full cache line. Two register sets keep the loads two stages ahead of
+// double-buffered LDS (2 x 64 KB). The 16-byte chunks of a 128-byte LDS row
+// are XOR-swizzled with bits 0..2 of the row.
+// ---------------------------------------------------------------------------
+constexpr int kT64K = 64;
+constexpr int kT64L = kTileM * (kT64K / 8) / kTileThreads;       // chunks per thread per stage (A and B each)
+constexpr int kT64Stage = (kTileM + kTileN) * kT64K * 2;         // 64 KB
+constexpr int kT64Lds = 2 * kT64Stage + kTileM * 4;
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
+    constexpr int NF = kWaveN / 16;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    int32_t* sIdx = reinterpret_cast<int32_t*>(lds + 2 * kT64Stage);
+
+    const int32_t total = mtiles * ntiles;
+    const int32_t per_xcd = (int32_t)((gridDim.x + 7) / 8);
+    const int32_t logical = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
+    if (logical >= total) return;
+    const int32_t mt = logical % mtiles;
+    const int32_t nt = logical / mtiles;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = (wave >> 2) * 128;
+    const int wn = (wave & 3) * kWaveN;
+    const int32_t m0 = mt * kTileM;
+    const int64_t n0 = (int64_t)nt * kTileN;
+
+    if (tid < kTileM) {
+        const int32_t r = m0 + tid;
+        sIdx[tid] = (r < p.R) ? row_source(p.row0 + r, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
+    }
+    __syncthreads();
+
+    // this thread's staging chunks: rows tid/8 + 64j, chunk tid%8
+    const int c = tid & 7;
+    int64_t ga[kT64L], gb[kT64L];
+    uint32_t wofs[kT64L];
+#pragma unroll
+    for (int j = 0; j < kT64L; ++j) {
+        const int row = (tid >> 3) + 64 * j;
+        const int32_t t = sIdx[row];
+        ga[j] = (int64_t)(t < 0 ? 0 : t) * p.hld + c * 8;
+        const int64_t n = n0 + row < p.V ? n0 + row : p.V - 1;
+        gb[j] = n * p.wld + c * 8;
+        wofs[j] = (uint32_t)(row * 128 + ((c ^ (row & 7)) << 4));
+    }
+    // fragment reads of k-step h of a stage: row l%16 of a 16-row group,
+    // chunk l/16 + 4h
+    const int fr = lane & 15;
+    const uint32_t rofs0 = (uint32_t)(fr * 128 + ((((lane >> 4) + 0) ^ (fr & 7)) << 4));
+    const uint32_t rofs1 = (uint32_t)(fr * 128 + ((((lane >> 4) + 4) ^ (fr & 7)) << 4));
+    const int nst = (int)(p.H / kT64K);                  // even: H is a multiple of 128
+
+    // loads of stages past the last read k = 0 (never written to LDS)
+    auto gload = [&](int st, u32x4 (&ra)[kT64L], u32x4 (&rb)[kT64L]) {
+        const int64_t k = st < nst ? (int64_t)st * kT64K : 0;
+#pragma unroll
+        for (int j = 0; j < kT64L; ++j) ra[j] = *reinterpret_cast<const u32x4*>(p.hidden + ga[j] + k);
+#pragma unroll
+        for (int j = 0; j < kT64L; ++j) rb[j] = *reinterpret_cast<const u32x4*>(p.W + gb[j] + k);
+    };
+    auto lwrite = [&](int buf, const u32x4 (&ra)[kT64L], const u32x4 (&rb)[kT64L]) {
+        uint8_t* base = lds + buf * kT64Stage;
+#pragma unroll
+        for (int j = 0; j < kT64L; ++j) *reinterpret_cast<u32x4*>(base + wofs[j]) = ra[j];
+#pragma unroll
+        for (int j = 0; j < kT64L; ++j) *reinterpret_cast<u32x4*>(base + kTileM * 128 + wofs[j]) = rb[j];
+    };
+    f32x4 acc[8][NF];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto mma = [&](int buf) {
+        const uint8_t* base = lds + buf * kT64Stage;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t rofs = h == 0 ? rofs0 : rofs1;
+            const uint32_t aofs = (uint32_t)(wm * 128) + rofs;
+            const uint32_t bofs = (uint32_t)((kTileM + wn) * 128) + rofs;
+            u32x4 fb[NF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(base + bofs + j * 16 * 128);
+            u32x4 fa = *reinterpret_cast<const u32x4*>(base + aofs);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 cur = fa;
+                if (i < 7) fa = *reinterpret_cast<const u32x4*>(base + aofs + (i + 1) * 16 * 128);
+#pragma unroll
+                for (int j = 0; j < NF; ++j) acc[i][j] = mfma16(cur, fb[j], acc[i][j]);
+            }
+        }
+    };
+
+    // stage s is multiplied from LDS buffer s%2 while stage s+1 is written to
+    // the other buffer and stage s+2 is loaded into the register set that
+    // stage s came from
+    u32x4 ra0[kT64L], ra1[kT64L], rb0[kT64L], rb1[kT64L];
+    gload(0, ra0, rb0);
+    gload(1, ra1, rb1);
+    lwrite(0, ra0, rb0);
+    __syncthreads();
+    for (int s = 0; s < nst; s += 2) {
+        gload(s + 2, ra0, rb0);
+        mma(0);
+        lwrite(1, ra1, rb1);
+        __syncthreads();
+        gload(s + 3, ra1, rb1);
+        mma(1);
+        lwrite(0, ra0, rb0);
+        __syncthreads();
+    }
+
+    // Epilogue through LDS (free after the last barrier): per pass, each wave
+    // stages 32 rows x 64 columns of its quarter (fp32, rows padded by 16 B),
+    // then stores whole 16-byte row segments.
+    const int lq = lane >> 4;
+    float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 68);
+    const bool vec_ok = !OUT_BF16 && (p.old % 4 == 0) &&
+                        ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = h * 2 + ii;
+#pragma unroll
+            for (int j = 0; j < NF; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) stg[(ii * 16 + lq * 4 + e) * 68 + j * 16 + fr] = acc[i][j][e];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane l stores columns 4*(l%16) .. +3 of rows l/16 + 4q, q = 0..7
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int rr = lq + 4 * q;                      // row within the pass
+            const int rl = wm + h * 32 + rr;
+            const int32_t r = m0 + rl;
+            const int cl = 4 * fr;
+            const int64_t v = n0 + wn + cl;
+            f32x4 val = *reinterpret_cast<const f32x4*>(&stg[rr * 68 + cl]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[e] = scale_logit(val[e], p.scale_mode, p.scale);
+            if (r < p.R) {
+                const bool valid = sIdx[rl] >= 0;
+                if (vec_ok && v + 4 <= p.V) {
+                    const f32x4 o = valid ? val : f32x4{kNaN, kNaN, kNaN, kNaN};
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v) = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (v + e < p.V) store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v + e, valid ? val[e] : kNaN);
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel: 8 rows x 256 vocab columns per workgroup; hidden rows staged in
 // LDS by k-chunks of 128; one fp32 FMA per (row, column, k), k ascending.
 // ---------------------------------------------------------------------------
@@ -864,11 +1036,24 @@ hipError_t launch_tiled_q(const HeadParams& p, int32_t mtiles, int32_t ntiles, h
     return launch_tiled<OUT_BF16, BITS, false>(p, mtiles, ntiles, s);
 }
 
+template <bool OUT_BF16>
+hipError_t launch_tiled64(const HeadParams& p, int32_t mtiles, int32_t ntiles, hipStream_t s) {
+    const void* fn = (const void*)k_head_tiled64<OUT_BF16>;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kT64Lds);
+    if (e != hipSuccess) return e;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    const dim3 grid((unsigned)(((total + 7) / 8) * 8));
+    hipLaunchKernelGGL((k_head_tiled64<OUT_BF16>), grid, dim3(kTileThreads), kT64Lds, s, p, mtiles, ntiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
     const HeadParams p = to_params(a);
     const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
     const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
+    if (p.H % 128 == 0)
+        return a.out_bf16 ? launch_tiled64<true>(p, mtiles, ntiles, s) : launch_tiled64<false>(p, mtiles, ntiles, s);
     return a.out_bf16 ? launch_tiled<true, 16, false>(p, mtiles, ntiles, s)
                       : launch_tiled<false, 16, false>(p, mtiles, ntiles, s);
 }
