@@ -77,7 +77,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
               "head_stream_bf16": ("k_head_stream<", "head.hip", 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
               "head_pipe_bf16": ("k_head_pipe<3, 2, 4, false, false, true>", "pipe.hip",
                                  151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
-              "head_tiled_bf16": ("k_head_tiled<false, 16", "head.hip",
+              "head_tiled_bf16": ("k_head_tiled64<false, 8>", "head.hip",
                                   151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4)}
     for bits in (4, 8):
         qbytes = 151936 * 1024 * bits // 8 + 151936 * 16 * 4
