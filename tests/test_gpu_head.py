@@ -103,6 +103,24 @@ def test_bf16_output_is_rne_of_fp32():
     assert np.array_equal(bf16_bits(b), synth.f32_to_bf16_bits(f.cpu().numpy()))
 
 
+@pytest.mark.parametrize("H", [96, 512])
+def test_bf16_output_is_rne_of_fp32_tiled(H):
+    """The same for row counts the tiled kernels take (64-wide k stages when
+    the hidden size is a multiple of 128, 32-wide otherwise), with a partial
+    last row tile and a partial vocabulary tile."""
+    g = synth.rng(15 + H)
+    T, V, R = 400, 3000, 300
+    hid = synth.normal_bf16(g, (T, H))
+    w = synth.normal_bf16(g, (V, H), H ** -0.5)
+    cu = np.array([0, T], dtype=np.int32)
+    ex = g.integers(0, T, size=R).astype(np.int32)
+    args = (bf16_tensor(hid), bf16_tensor(w), i32_tensor(cu), 0)
+    f = lmh.lmhead_gather_project(*args, logits_indices=i32_tensor(ex)).logits
+    b = lmh.lmhead_gather_project(*args, logits_indices=i32_tensor(ex), out_dtype=torch.bfloat16).logits
+    assert np.array_equal(bf16_bits(b), synth.f32_to_bf16_bits(f.cpu().numpy()))
+    _close(f.cpu().numpy(), oracle.head(hid, w, ex))
+
+
 def test_invalid_rows_are_nan_and_flagged():
     g = synth.rng(15)
     hid = synth.normal_bf16(g, (10, 64))
