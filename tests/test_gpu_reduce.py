@@ -155,7 +155,7 @@ def _edge_block(V):
 
 @pytest.mark.parametrize("V,dt,k", [(248_320, "bf16", 20), (248_320, "bf16", 128), (248_320, "bf16", 0),
                                     (128_256, "f32", 20), (1000, "bf16", 5), (4097, "f32", 64),
-                                    (65, "bf16", 3), (1, "f32", 1), (8192, "bf16", 8192)])
+                                    (65, "bf16", 3), (1, "f32", 1), (8192, "bf16", 8192), (40, "bf16", 1)])
 def test_row_path_matches_split_path(V, dt, k):
     """256 rows (one workgroup per row on a 256-CU device) against the same
     rows reduced 100 at a time (split path): bitwise equal lse, selected

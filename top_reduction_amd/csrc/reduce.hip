@@ -664,14 +664,17 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
         // block of lane 8i + l / 8 (eight whole blocks per wave instruction)
         static_assert(!PF || VPB == 8, "the prefetch spreads a block over eight lanes");
         // (all lane exchanges first, then branch-free loads: a lane whose
-        // owner has no block reads block 0, never used)
+        // owner has no block reads block 0, never used; a row shorter than
+        // one block has no whole block and loads nothing)
         int blk[VPB];
 #pragma unroll
         for (int i = 0; i < VPB; ++i) blk[i] = __shfl(pf_blk, i * 8 + ((tid & 63) >> 3));
+        if (V >= kBlock) {
 #pragma unroll
-        for (int i = 0; i < VPB; ++i)
-            pf[i] = *reinterpret_cast<const u32x4*>(
-                rowp + ((size_t)(blk[i] < 0 ? 0 : blk[i]) * kBlock + (size_t)(tid & 7) * EPV) * ESZ);
+            for (int i = 0; i < VPB; ++i)
+                pf[i] = *reinterpret_cast<const u32x4*>(
+                    rowp + ((size_t)(blk[i] < 0 ? 0 : blk[i]) * kBlock + (size_t)(tid & 7) * EPV) * ESZ);
+        }
     }
 
     // (3) threshold and kept blocks
@@ -1115,6 +1118,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
 // dispatch (28.6 against 30.3 us on 256 rows of 248,320 bf16 logits).
 // ---------------------------------------------------------------------------
 constexpr int kRowWaves = 8;
+static_assert(kRowWaves > kThreads / 64, "the lse wave follows the selection waves");
 constexpr int kRowThreads = kRowWaves * 64;
 constexpr int kRowMaxItems = 64;   // items per row on this path (V <= 64 * kSeg)
 template <bool W16> struct KeyType { using type = uint32_t; };
