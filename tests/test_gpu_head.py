@@ -140,6 +140,30 @@ def test_invalid_rows_are_nan_and_flagged():
     assert np.all(np.isnan(p.logits.cpu().numpy()[0]))
 
 
+@pytest.mark.parametrize("H", [64, 128])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_invalid_rows_are_nan_tiled(H, out):
+    """Row counts the tiled kernels take (64-wide k stages at H = 128): rows
+    with an out-of-range index come out NaN and flagged, the others match
+    the oracle."""
+    g = synth.rng(16 + H)
+    T, V, R = 50, 700, 100
+    hid = synth.normal_bf16(g, (T, H))
+    w = synth.normal_bf16(g, (V, H), H ** -0.5)
+    ex = g.integers(0, T, size=R).astype(np.int32)
+    bad = np.array([3, 50, 99])
+    ex[bad] = [T, -1, T + 7]
+    p = lmh.lmhead_gather_project(bf16_tensor(hid), bf16_tensor(w), i32_tensor([0, T]), 0,
+                                  logits_indices=i32_tensor(ex), out_dtype=out)
+    torch.cuda.synchronize()
+    z = p.logits.float().cpu().numpy()
+    good = np.setdiff1d(np.arange(R), bad)
+    assert np.all(np.isnan(z[bad])) and np.all(np.isfinite(z[good]))
+    assert int(p.device_error.item()) & lmh.LMH_DEVERR_INDEX
+    if out == torch.float32:
+        _close(z[good], oracle.head(hid, w, ex[good]))
+
+
 @pytest.fixture(scope="module")
 def qwen_batch():
     return synth.selective_head_batch(4000)
