@@ -204,8 +204,11 @@ def _prefetch_rows(V, dt, seed):
     logits through each of its branches: the row maximum in the partial last
     block (never prefetched: loaded after the threshold); the top values in
     eight consecutive blocks, all held by one selection thread (its extra
-    blocks are loaded after the threshold); 300 blocks tied at the top, more
-    than the prefetched path takes (the placement path runs); plain rows."""
+    blocks are loaded after the threshold); 300 scattered blocks tied at the
+    top, or four runs of 50 consecutive tied blocks (some with two tied
+    entries) under five larger blocks: more tied blocks than the path stages
+    whole, so only the lowest-indexed ones needed for K are kept, the cut
+    falling inside one selection thread's blocks for the runs; plain rows."""
     g = synth.rng(seed)
     x = synth.normal_f32(g, (256, V), 2.0)
     nb = -(-V // 64)
@@ -217,9 +220,16 @@ def _prefetch_rows(V, dt, seed):
         elif kind == 1:
             b0 = 64 * (16 * (r % (nb // 16)))                   # the first block of a selection thread
             x[r, b0:b0 + 8 * 64:64] = np.arange(8, dtype=np.float32) + 16.0
-        elif kind == 2:
+        elif kind == 2 and r % 8 == 2:
             blocks = g.choice(nb - 1, size=300, replace=False)
             x[r, blocks * 64 + 7] = 12.0
+        elif kind == 2:
+            runs = 50 * g.choice((nb - 1) // 50, size=4, replace=False)
+            blocks = (runs[:, None] + np.arange(50)).ravel()
+            x[r, blocks * 64 + 7] = 12.0
+            x[r, blocks[::3] * 64 + 40] = 12.0
+            above = g.choice(nb - 1, size=5, replace=False)
+            x[r, above * 64 + 9] = 30.0
     if dt == "bf16":
         return synth.f32_to_bf16_bits(x)
     return x.astype(np.float16)

@@ -514,11 +514,13 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wtot, uint
 //  * with PF (16-bit logits), each thread loads the block holding its own
 //    largest key as soon as the keys are known, so those loads land while
 //    T is searched (eight lanes load the eight 16-byte parts of a block, so
-//    a wave instruction reads eight whole blocks); when at most capb blocks
-//    reach T, every block >= T is a candidate block, copied from those
-//    registers to an LDS staging area (a second block >= T of the same
-//    thread is loaded then) and filtered there by all threads, instead of
-//    the placement and gather above;
+//    a wave instruction reads eight whole blocks); every block >= T is a
+//    candidate block when at most capb blocks reach T, else the K kept
+//    blocks above (one prefix count orders the blocks tied at T); the
+//    candidate blocks are copied from those registers to an LDS staging
+//    area (the other candidate blocks are loaded then, by all threads in
+//    one round) and filtered there by all threads, instead of the
+//    placement and gather above;
 //  * each candidate's rank under (value desc, id asc) is counted in LDS and
 //    the first K are written.
 // Thread t holds the keys of blocks [t*KPT, t*KPT + KPT) in kr (0 past nb: a
@@ -596,35 +598,26 @@ __device__ __forceinline__ void rank_topk(int64_t row, int32_t K, uint64_t* cand
     }
 }
 
-// The 64 entries of block blk as 16-byte words; entries at or past V read
-// as -inf.
+// The 16-byte part of a row starting at entry e0 (a multiple of the entries
+// per part); entries at or past V read as -inf and are not loaded.
 template <int DT>
-__device__ __forceinline__ void load_block(const uint8_t* __restrict__ rowp, int64_t V, int32_t blk,
-                                  u32x4 (&v)[kBlock / (w16(DT) ? 8 : 4)]) {
+__device__ __forceinline__ u32x4 load_part(const uint8_t* __restrict__ rowp, int64_t V, int64_t e0) {
     constexpr int EPV = w16(DT) ? 8 : 4;
-    constexpr int VPB = kBlock / EPV;
-    const int64_t e0 = (int64_t)blk * kBlock;
-    if (e0 + kBlock <= V) {
-        const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + (size_t)e0 * (w16(DT) ? 2 : 4));
-#pragma unroll
-        for (int i = 0; i < VPB; ++i) v[i] = vp[i];
-        return;
-    }
+    if (e0 + EPV <= V) return *reinterpret_cast<const u32x4*>(rowp + (size_t)e0 * (w16(DT) ? 2 : 4));
     const uint32_t ninf = ninf_word<DT>();
+    u32x4 v = u32x4{ninf, ninf, ninf, ninf};
 #pragma unroll
-    for (int i = 0; i < VPB; ++i) v[i] = u32x4{ninf, ninf, ninf, ninf};
-#pragma unroll
-    for (int e = 0; e < kBlock; ++e) {
+    for (int e = 0; e < EPV; ++e) {
         if (e0 + e >= V) continue;
-        const int q = (e % EPV) / (w16(DT) ? 2 : 1);
+        const int q = e / (w16(DT) ? 2 : 1);
         if (w16(DT)) {
             const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[e0 + e];
-            v[e / EPV][q] = (e & 1) ? ((v[e / EPV][q] & 0x0000FFFFu) | (h << 16))
-                                    : ((v[e / EPV][q] & 0xFFFF0000u) | h);
+            v[q] = (e & 1) ? ((v[q] & 0x0000FFFFu) | (h << 16)) : ((v[q] & 0xFFFF0000u) | h);
         } else {
-            v[e / EPV][q] = reinterpret_cast<const uint32_t*>(rowp)[e0 + e];
+            v[q] = reinterpret_cast<const uint32_t*>(rowp)[e0 + e];
         }
     }
+    return v;
 }
 
 // PRE: the caller already holds, per selection thread t, the maximum and
@@ -783,34 +776,70 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
         }
         __syncthreads();
         T = sh.thr[0];
-        if constexpr (PF) if (sh.thr[1] + sh.thr[2] <= (uint32_t)capb) {
-            // every block with key >= T is a candidate block: staged in LDS
-            // (sh.nblk counts the slots), then filtered by all threads
-            if (tid == 0) sh.ncand = 0;
-            uint32_t more = 0u;                          // bit j: block b0 + j >= T, not prefetched
+        if constexpr (PF) if (K <= capb && T != 0u) {   // T == 0 (all-NaN blocks) would keep empty slots
+            // the candidate blocks are staged in LDS (sh.nblk counts the
+            // slots), then filtered by all threads. They are the blocks with
+            // key >= T while those fit in capb slots; otherwise the blocks
+            // with key > T and the K - count(key > T) lowest-indexed blocks
+            // with key == T: the first K blocks under (key desc, index asc),
+            // whose maxima precede every entry of a dropped tied block
+            static_assert(KPT <= 32, "one bit per block of a selection thread");
+            uint32_t keep = 0u;                          // bit j: block b0 + j is a candidate
 #pragma unroll
             for (int j = 0; j < KPT; ++j)
-                if (kr[j] >= T && j != pf_j) more |= 1u << j;   // slots past nb hold 0 < T
+                if (kr[j] >= T) keep |= 1u << j;         // slots past nb hold 0 < T
+            if (sh.thr[1] + sh.thr[2] > (uint32_t)capb) {
+                uint32_t eqm = 0u;                       // bit j: block b0 + j has key == T
+#pragma unroll
+                for (int j = 0; j < KPT; ++j)
+                    if (kr[j] == T) eqm |= 1u << j;
+                uint32_t tot = 0u;
+                const int need = K - (int)sh.thr[1];
+                int ei = (int)block_exclusive_scan<NT>((uint32_t)__builtin_popcount(eqm), sh.swtot, tot);
+                while (eqm != 0u) {                      // ascending block index
+                    const int j = __builtin_ctz(eqm);
+                    eqm &= eqm - 1u;
+                    if (ei >= need) keep &= ~(1u << j);
+                    ++ei;
+                }
+            }
+            if (tid == 0) sh.ncand = 0;
+            const uint32_t more = keep & ~(pf_blk >= 0 ? 1u << pf_j : 0u);   // kept, not prefetched
             // staging slot t holds thread t's prefetched block (every part
             // is written; only the slots of candidate blocks are read), slots
             // NT + c the blocks loaded now
 #pragma unroll
             for (int i = 0; i < VPB; ++i) stage[((tid & ~63) + i * 8 + ((tid & 63) >> 3)) * VPB + (tid & 7)] = pf[i];
-            if (pf_blk >= 0 && pf_key >= T) {
+            if (pf_blk >= 0 && ((keep >> pf_j) & 1u)) {
                 const int c = atomicAdd(&sh.nblk, 1);
                 sh.blk[c] = pf_blk;
                 sh.cslot[c] = tid;
             }
-            while (more != 0u) {
-                const int j = __builtin_ctz(more);
-                more &= more - 1u;
-                u32x4 v[VPB];
-                load_block<DT>(rowp, V, b0 + j, v);
+            for (uint32_t mb = more; mb != 0u; mb &= mb - 1u) {
                 const int c = atomicAdd(&sh.nblk, 1);
-                sh.blk[c] = b0 + j;
+                sh.blk[c] = b0 + __builtin_ctz(mb);
                 sh.cslot[c] = NT + c;
+            }
+            __syncthreads();
+            // the candidate blocks not prefetched, loaded by all threads in
+            // one round (part i % VPB of candidate i / VPB: a thread's loads
+            // are all issued before its first wait)
+            {
+                constexpr int MQ = (MAXBLK * VPB + NT - 1) / NT;
+                const int nq = sh.nblk * VPB;
+                u32x4 q[MQ];
+                int qs[MQ];
 #pragma unroll
-                for (int i = 0; i < VPB; ++i) stage[(NT + c) * VPB + i] = v[i];
+                for (int i = 0; i < MQ; ++i) {
+                    const int v = tid + i * NT;
+                    const int c = v / VPB;
+                    qs[i] = v < nq && sh.cslot[c] >= NT ? sh.cslot[c] * VPB + v % VPB : -1;
+                    if (qs[i] >= 0)
+                        q[i] = load_part<DT>(rowp, V, (int64_t)sh.blk[c] * kBlock + (int64_t)(v % VPB) * EPV);
+                }
+#pragma unroll
+                for (int i = 0; i < MQ; ++i)
+                    if (qs[i] >= 0) stage[qs[i]] = q[i];
             }
             __syncthreads();
             const bool keep_all = T == 0u;
