@@ -239,7 +239,8 @@ def _prefetch_rows(V, dt, seed):
 @pytest.mark.parametrize("k", [1, 20, 128])
 def test_prefetched_candidate_paths(dt, k):
     """Oracle parity on every row, and bitwise equality with the split path
-    (which never prefetches), for rows built to take each branch."""
+    (its selection runs after a separate streaming launch, from block keys
+    in the workspace), for rows built to take each branch."""
     V = 248_280                                              # last block holds 24 entries
     print(f"prefetch paths dt={dt} k={k}", flush=True)
     data = _prefetch_rows(V, dt, 7700 + k)
