@@ -27,11 +27,12 @@
  *   [mlxcel]      mlxcel PR #1969, description: the head acts per position,
  *                 so the row projected from a gathered hidden row equals the
  *                 same row of the full projection.
- *   [MTPLX]       MTPLX PR #532, Change: one float32 logsumexp per row; the
- *                 vocabulary viewed as 64-logit blocks, the K blocks with
- *                 the largest maxima kept, the exact top-K taken among their
- *                 entries; float32(logit) - lse only at the survivors and the
- *                 scored token; exact ties by ascending token id.
+ *   [MTPLX]       MTPLX PR #532, Change: an fp32 logsumexp per row; a
+ *                 prefilter over 64-logit blocks that keeps the K blocks
+ *                 with the largest maxima and takes the exact top-K among
+ *                 what they hold; logprobs formed for the K results and the
+ *                 scored token alone; equal values ordered by token id,
+ *                 lowest first.
  *   [openinfer]   openinfer issue #719, Suggested direction and Acceptance
  *                 criteria: logsumexp, selected logprob and top-k computed
  *                 while the logits stay on the GPU, returned as an O(k+1)
@@ -221,7 +222,9 @@ size_t lmhead_logprobs_workspace_size(int64_t rows, int64_t vocab, int32_t k, in
  * most one chunk of logits is resident. selected_ids is indexed by logits
  * row (R entries). logits_debug, when not NULL, is an [R][vocab] fp32 buffer
  * that receives the logits that were reduced (tests use it); the workspace
- * then only holds the reduction's part.
+ * then only holds the reduction's part. A row without a valid source (flagged
+ * in device_error) has NaN logits, so its lse, selected logprob and top-K
+ * logprobs come out NaN and its top-K ids -1.
  */
 lmh_status lmhead_logprobs(
     const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,

@@ -17,8 +17,8 @@
  *     compacted logits layout.
  *   - mlxcel PR #1969, description: the head acts per position, so the
  *     projected row of a gathered hidden row equals the full forward's row.
- *   - MTPLX PR #532, Motivation and Change: the result is the full
- *     log-softmax restricted to the top-K survivors and the scored token;
+ *   - MTPLX PR #532, Motivation and Change: the result equals the full
+ *     log-softmax read at the top-K entries and at the scored token;
  *     exact ties list by ascending token id; the 64-logit block-max
  *     prefilter keeps the K blocks with the largest maxima.
  *   - openinfer issue #719, Description: the host routine makes a

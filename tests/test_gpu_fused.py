@@ -127,3 +127,36 @@ def test_chunk_sizes_agree():
     for o in outs[1:]:
         assert torch.equal(o.topk_ids, outs[0].topk_ids)
         assert torch.equal(o.lse.view(torch.int32), outs[0].lse.view(torch.int32))
+
+
+def test_flagged_rows_fused():
+    """A logits row whose source index is out of range is flagged and written
+    in full: NaN lse, selected and top-K logprobs, -1 ids; every other row is
+    bitwise what it is when that index is valid. Rows 3 and 270 sit in the
+    first 256-row chunk (one workgroup per row on a 256-CU device) and in
+    the 44-row second chunk (the two-launch path)."""
+    g = synth.rng(5005)
+    T, H, V, K = 300, 256, 3000, 7
+    hid = bf16_tensor(synth.normal_bf16(g, (T, H)))
+    w = bf16_tensor(synth.normal_bf16(g, (V, H), H ** -0.5))
+    sel = i32_tensor(g.integers(0, V, size=T))
+    good = np.arange(T, dtype=np.int32)
+    bad = good.copy()
+    bad[[3, 270]] = [T + 5, -1]
+    runs = [lmh.lmhead_logprobs(hid, w, i32_tensor([0, T]), 0, sel, K, logits_indices=i32_tensor(ex))
+            for ex in (good, bad)]
+    torch.cuda.synchronize()
+    ok, fl = runs
+    assert int(ok.device_error.item()) == 0
+    assert int(fl.device_error.item()) & lmh.LMH_DEVERR_INDEX
+    flagged = np.zeros(T, dtype=bool)
+    flagged[[3, 270]] = True
+    assert np.all(np.isnan(fl.lse.cpu().numpy()[flagged]))
+    assert np.all(np.isnan(fl.selected_logprob.cpu().numpy()[flagged]))
+    assert np.all(fl.topk_ids.cpu().numpy()[flagged] == -1)
+    assert np.all(np.isnan(fl.topk_logprobs.cpu().numpy()[flagged]))
+    assert np.array_equal(fl.gather_indices.cpu().numpy()[flagged], [-1, -1])
+    for a, b in ((ok.lse, fl.lse), (ok.selected_logprob, fl.selected_logprob),
+                 (ok.topk_logprobs, fl.topk_logprobs)):
+        assert np.array_equal(a.cpu().numpy()[~flagged].view(np.uint32), b.cpu().numpy()[~flagged].view(np.uint32))
+    assert np.array_equal(ok.topk_ids.cpu().numpy()[~flagged], fl.topk_ids.cpu().numpy()[~flagged])

@@ -249,6 +249,35 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
 
 }  // namespace
 
+namespace lmh {
+
+lmh_status reduce_validate(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
+                           int64_t logits_ld, const int32_t* selected_ids, int32_t k, const float* lse,
+                           const float* selected_logprob, const int32_t* topk_ids,
+                           const float* topk_logprobs, size_t* workspace_bytes) {
+    const lmh_status st = check_reduce_shape(logits_dt, rows, vocab, logits_ld, k);
+    if (st != LMH_OK) return st;
+    *workspace_bytes = plan_reduce(rows, vocab, k).bytes;
+    if (rows == 0) return LMH_OK;
+    if (!logits || !lse) return LMH_ERR_NULL;
+    if (selected_ids && !selected_logprob) return LMH_ERR_NULL;
+    if (k > 0 && (!topk_ids || !topk_logprobs)) return LMH_ERR_NULL;
+    if (!aligned(logits, 16)) return LMH_ERR_ALIGN;
+    return LMH_OK;
+}
+
+lmh_status reduce_enqueue(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
+                          int64_t logits_ld, const int32_t* selected_ids, int32_t k, float* lse,
+                          float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+                          void* workspace, int32_t* device_error, hipStream_t s) {
+    const ReducePlan p = plan_reduce(rows, vocab, k);
+    ReduceArgs a{logits, (int32_t)logits_dt, logits_ld, selected_ids, lse, selected_logprob,
+                 topk_ids, topk_logprobs, workspace, device_error};
+    return from_hip(launch_reduce(p, a, s));
+}
+
+}  // namespace lmh
+
 extern "C" {
 
 const char* lmh_status_string(lmh_status st) {
@@ -343,20 +372,15 @@ lmh_status logprob_reduce(const void* logits, lmh_dtype logits_dt, int64_t rows,
                           float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
                           void* workspace, size_t workspace_bytes, int32_t* device_error,
                           void* stream) {
-    const lmh_status st = check_reduce_shape(logits_dt, rows, vocab, logits_ld, k);
+    size_t need = 0;
+    const lmh_status st = lmh::reduce_validate(logits, logits_dt, rows, vocab, logits_ld, selected_ids, k,
+                                               lse, selected_logprob, topk_ids, topk_logprobs, &need);
     if (st != LMH_OK) return st;
     if (rows == 0) return LMH_OK;   // nothing is read or written
-    if (!logits || !lse) return LMH_ERR_NULL;
-    if (selected_ids && !selected_logprob) return LMH_ERR_NULL;
-    if (k > 0 && (!topk_ids || !topk_logprobs)) return LMH_ERR_NULL;
-    if (!aligned(logits, 16)) return LMH_ERR_ALIGN;
-    const ReducePlan p = plan_reduce(rows, vocab, k);
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.bytes) return LMH_ERR_WORKSPACE;
-    if (rows == 0) return LMH_OK;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    ReduceArgs a{logits, (int32_t)logits_dt, logits_ld, selected_ids, lse, selected_logprob,
-                 topk_ids, topk_logprobs, workspace, device_error};
-    return from_hip(launch_reduce(p, a, s));
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return LMH_ERR_WORKSPACE;
+    return lmh::reduce_enqueue(logits, logits_dt, rows, vocab, logits_ld, selected_ids, k, lse,
+                               selected_logprob, topk_ids, topk_logprobs, workspace, device_error,
+                               static_cast<hipStream_t>(stream));
 }
 
 lmh_status lmh_debug_reduce_stage1(const void* logits, lmh_dtype logits_dt, int64_t rows,

@@ -173,4 +173,16 @@ bool reduce_row_path(const ReducePlan& p);
 // The whole reduction (either path).
 hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
 
+// logprob_reduce's host-side checks (everything but the workspace), in its
+// order; *workspace_bytes gets the workspace the shape needs. Then the
+// enqueue of the reduction on a workspace of at least that size.
+lmh_status reduce_validate(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
+                           int64_t logits_ld, const int32_t* selected_ids, int32_t k, const float* lse,
+                           const float* selected_logprob, const int32_t* topk_ids,
+                           const float* topk_logprobs, size_t* workspace_bytes);
+lmh_status reduce_enqueue(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
+                          int64_t logits_ld, const int32_t* selected_ids, int32_t k, float* lse,
+                          float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+                          void* workspace, int32_t* device_error, hipStream_t s);
+
 }  // namespace lmh

@@ -596,6 +596,13 @@ __device__ __forceinline__ void rank_topk(int64_t row, int32_t K, uint64_t* cand
             topk_lp[row * K + rank] = elem_value<DT>((uint32_t)(c >> 32)) - lse;
         }
     }
+    // fewer candidates than K only when no entry compares (a row of NaN, the
+    // head's mark for a row without a valid source): the places left are -1
+    // and NaN, so every output of the row is written
+    for (int r = nlist + tid; r < K; r += NT) {
+        topk_ids[row * K + r] = -1;
+        topk_lp[row * K + r] = __builtin_nanf("");
+    }
 }
 
 // The 16-byte part of a row starting at entry e0 (a multiple of the entries
@@ -1013,7 +1020,9 @@ __device__ inline float lse_tree16(float m, float s) {
     level(std::integral_constant<int, 0x4E>{}, 2);
     level(std::integral_constant<int, 0x141>{}, 4);
     level(std::integral_constant<int, 0x140>{}, 8);
-    return (m == kNegInf) ? kNegInf : m + logf(s);
+    // m = -inf: every entry is -inf (sum 0, lse -inf) or NaN (the sum is NaN
+    // and so is the lse)
+    return (m == kNegInf) ? (s == s ? kNegInf : s) : m + logf(s);
 }
 
 // The selected token's logit (a5), loaded long before its logprob is
