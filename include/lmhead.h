@@ -180,6 +180,28 @@ lmh_status logprob_reduce(
     void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
 
 /*
+ * logprob_reduce_noalloc -- logprob_reduce for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc. There is no workspace argument; the
+ * scratch lives in a static device array of LMH_NOALLOC_SCRATCH_BYTES per
+ * GPU that the library holds until the process ends (its device address is
+ * looked up on the first call on each device, with that device current).
+ * The call allocates and frees nothing.
+ * Arguments, outputs, results (bitwise) and status codes are those of
+ * logprob_reduce; a shape whose logprob_reduce_workspace_size exceeds
+ * LMH_NOALLOC_SCRATCH_BYTES returns LMH_ERR_WORKSPACE before any HIP call.
+ * All calls on one GPU share that GPU's array: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be ordered by the
+ * caller. Nothing in the array needs clearing between calls.
+ */
+#define LMH_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+lmh_status logprob_reduce_noalloc(
+    const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab, int64_t logits_ld,
+    const int32_t* selected_ids, int32_t k,
+    float* lse, float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+    int32_t* device_error, void* stream);
+
+/*
  * lmhead_apply_bitmask -- token bitmask on the compacted logits, in place
  * [vllm-metal, Testing: bitmask application under the compacted layout].
  *

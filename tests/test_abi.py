@@ -160,6 +160,40 @@ def test_reduce_k0_needs_no_topk_buffers(L):
     assert _reduce(L, k=0, ids=None, lps=None, wsb=16) == WS
 
 
+def _reduce_noalloc(L, **kw):
+    a = dict(logits=A, dt=BF16, rows=256, vocab=248320, ld=248320, sel=A, k=20, lse=A, slp=A,
+             ids=A, lps=A, err=None)
+    a.update(kw)
+    return L.logprob_reduce_noalloc(a["logits"], a["dt"], a["rows"], a["vocab"], a["ld"], a["sel"], a["k"],
+                                    a["lse"], a["slp"], a["ids"], a["lps"], a["err"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(logits=None), NULL), (dict(lse=None), NULL), (dict(slp=None), NULL),
+    (dict(ids=None), NULL), (dict(lps=None), NULL),
+    (dict(rows=-1), SHAPE), (dict(vocab=0), SHAPE), (dict(ld=248319), SHAPE),
+    (dict(dt=BAD_DT), DTYPE), (dict(logits=A + 8), ALIGN),
+    (dict(k=-1), K), (dict(k=129), K),
+    # a shape whose reduction workspace is above the static scratch
+    (dict(rows=3000), WS), (dict(rows=600, k=0), WS),
+])
+def test_reduce_noalloc_rejects(L, kw, want):
+    """The no-allocation reduction applies logprob_reduce's rules and refuses
+    shapes whose scratch exceeds LMH_NOALLOC_SCRATCH_BYTES, all before any
+    HIP call."""
+    assert _reduce_noalloc(L, **kw) == want
+
+
+def test_reduce_noalloc_limit(L):
+    limit = 8 << 20
+    text = open(HEADER).read()
+    assert re.search(r"#define LMH_NOALLOC_SCRATCH_BYTES \(\(size_t\)8 << 20\)", text)
+    assert L.logprob_reduce_workspace_size(3000, 248320, 20) > limit
+    assert L.logprob_reduce_workspace_size(600, 248320, 0) > limit
+    assert L.logprob_reduce_workspace_size(32, 151936, 5) <= limit
+    assert _reduce_noalloc(L, rows=0, logits=None, lse=None, slp=None, ids=None, lps=None) == OK
+
+
 def test_workspace_sizes(L):
     for rows, V, k in [(256, 248320, 128), (32, 151936, 5), (1, 1000, 0), (0, 64, 0)]:
         n = L.logprob_reduce_workspace_size(rows, V, k)

@@ -74,6 +74,7 @@ def lib():
         L.logprob_reduce_workspace_size.argtypes = [i64, i64, i32]
         L.logprob_reduce_workspace_size.restype = sz
         L.logprob_reduce.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p, p, sz, p, p]
+        L.logprob_reduce_noalloc.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p, p, p]
         L.lmh_debug_reduce_stage1.argtypes = [p, ctypes.c_int, i64, i64, i64, i32, p, sz, p]
         L.lmh_debug_reduce_path.argtypes = [i64, i64, i32]
         L.lmh_debug_reduce_path.restype = i32
@@ -95,6 +96,7 @@ def lib():
         L.lmh_status_string.argtypes = [ctypes.c_int]
         L.lmh_status_string.restype = ctypes.c_char_p
         for name in ("lmhead_gather_project", "lmh_debug_gather_project", "logprob_reduce",
+                     "logprob_reduce_noalloc",
                      "lmh_debug_reduce_stage1", "lmhead_logprobs", "lmhead_gather_project_q",
                      "lmh_debug_gather_project_q", "lmhead_logprobs_q", "lmhead_gather_project_ex",
                      "lmhead_logprobs_ex", "lmhead_selfcheck", "lmhead_apply_bitmask"):
@@ -271,6 +273,29 @@ def logprob_reduce(logits: torch.Tensor, selected_ids: Optional[torch.Tensor] = 
                           _ptr(out.topk_ids) if k else None, _ptr(out.topk_logprobs) if k else None,
                           _ptr(ws), ws.numel(), _ptr(out.device_error), _stream())
     _check(st, "logprob_reduce")
+    return out
+
+
+def logprob_reduce_noalloc(logits: torch.Tensor, selected_ids: Optional[torch.Tensor] = None,
+                           k: int = 0, out: Optional[Reduction] = None) -> Reduction:
+    """logprob_reduce on the library's static per-device scratch (no
+    workspace argument; the call itself allocates nothing -- pass `out` to
+    keep this wrapper from allocating the outputs)."""
+    L = lib()
+    R, V, ld = _matrix(logits, "logits")
+    sel = _i32(selected_ids, "selected_ids")
+    dev = logits.device
+    if out is None:
+        out = Reduction(torch.empty(R, dtype=torch.float32, device=dev),
+                        torch.empty(R, dtype=torch.float32, device=dev) if sel is not None else None,
+                        torch.empty((R, k), dtype=torch.int32, device=dev),
+                        torch.empty((R, k), dtype=torch.float32, device=dev),
+                        torch.zeros(1, dtype=torch.int32, device=dev))
+    st = L.logprob_reduce_noalloc(_ptr(logits), _dt(logits), R, V, ld, _ptr(sel), int(k),
+                                  _ptr(out.lse), _ptr(out.selected_logprob),
+                                  _ptr(out.topk_ids) if k else None, _ptr(out.topk_logprobs) if k else None,
+                                  _ptr(out.device_error), _stream())
+    _check(st, "logprob_reduce_noalloc")
     return out
 
 

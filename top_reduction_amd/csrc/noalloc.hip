@@ -1,0 +1,71 @@
+// noalloc.hip -- logprob_reduce without a workspace argument, for callers
+// that cannot allocate device memory (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc).
+//
+// The reduction's scratch (the two-launch path's per-item partials and block
+// keys) lives in one file-scope device array per GPU, `scratch`, held until
+// the process ends. Host code never passes the array's name to a kernel (in
+// host code it stands for a host-side shadow, not a device address): the
+// first call on a device, with that device current, asks the runtime for the
+// array's device address on that device and keeps it; every later call on
+// that device passes the kept pointer. No call allocates or frees memory.
+//
+// Every call on one GPU shares that GPU's array, and the array keeps what the
+// last call left in it. Nothing in it needs to start at zero: the first launch
+// writes every partial and key the second one reads (keys past a row's block
+// count are masked, not read as data). Calls that overlap on one GPU (on
+// different streams, or from different host threads without ordering) race on
+// the array; callers order them.
+#include <mutex>
+
+#include "lmh_internal.h"
+
+namespace {
+
+constexpr size_t kScratchBytes = LMH_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// The device address of `scratch` on the current device, looked up once.
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+lmh_status logprob_reduce_noalloc(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
+                                  int64_t logits_ld, const int32_t* selected_ids, int32_t k, float* lse,
+                                  float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+                                  int32_t* device_error, void* stream) {
+    size_t need = 0;
+    const lmh_status st = lmh::reduce_validate(logits, logits_dt, rows, vocab, logits_ld, selected_ids, k,
+                                               lse, selected_logprob, topk_ids, topk_logprobs, &need);
+    if (st != LMH_OK) return st;
+    if (rows == 0) return LMH_OK;   // nothing is read or written
+    if (need > kScratchBytes) return LMH_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return LMH_ERR_HIP;
+    return lmh::reduce_enqueue(logits, logits_dt, rows, vocab, logits_ld, selected_ids, k, lse,
+                               selected_logprob, topk_ids, topk_logprobs, ws, device_error,
+                               static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
