@@ -267,3 +267,51 @@ def test_prefetched_candidate_paths(dt, k):
     assert torch.equal(a.topk_logprobs.view(torch.int32), cat("topk_logprobs").view(torch.int32))
     ids = a.topk_ids.cpu().numpy()
     assert np.all(ids[0::4, 0] == V - 1)                     # the partial block's entry leads
+
+
+def _order_rows(V, seed):
+    """Rows whose block maxima are ordered along the row: rising (the top
+    blocks are the row's last), falling (its first), a saw-tooth repeated
+    every 4096 logits (equal maxima in every streaming item), rows rounded
+    to integers (many equal maxima), the top values in the row's first and
+    last blocks, and plain normal rows."""
+    g = synth.rng(seed)
+    x = synth.normal_f32(g, (256, V), 1.0)
+    ramp = np.linspace(-20.0, 20.0, V, dtype=np.float32)
+    for r in range(256):
+        kind = r % 8
+        if kind == 0:
+            x[r] = ramp + 0.01 * x[r]
+        elif kind == 1:
+            x[r] = -ramp + 0.01 * x[r]
+        elif kind == 2:
+            x[r] = np.tile(np.linspace(0.0, 8.0, 4096, dtype=np.float32), V // 4096 + 1)[:V]
+        elif kind == 3:
+            x[r] = np.round(x[r])                       # few distinct values: equal block maxima
+        elif kind == 4:
+            x[r, :64] += 30.0
+            x[r, -64:] += 30.0
+    return synth.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("k", [1, 7, 32, 33])
+def test_selection_on_ordered_rows(k):
+    """The one-workgroup-per-row reduction on rows whose block maxima are
+    ordered along the row: oracle parity on every row and bitwise equality
+    with the split path."""
+    V = 248_320
+    print(f"ordered rows k={k}", flush=True)
+    data = _order_rows(V, 7900 + k)
+    g = synth.rng(7950 + k)
+    sel = g.integers(0, V, size=256).astype(np.int32)
+    t = bf16_tensor(data)
+    if torch.cuda.get_device_properties(0).multi_processor_count <= 256:
+        assert lmh.reduce_row_path(256, V, k)
+    a = lmh.logprob_reduce(t, i32_tensor(sel), k)
+    check_reduce(a, data, sel, k, *oracle.reduce(data, sel, k))
+    parts = [lmh.logprob_reduce(t[i:i + 100], i32_tensor(sel[i:i + 100]), k) for i in range(0, 256, 100)]
+    torch.cuda.synchronize()
+    cat = lambda f: torch.cat([getattr(p, f) for p in parts])
+    assert torch.equal(a.lse.view(torch.int32), cat("lse").view(torch.int32))
+    assert torch.equal(a.topk_ids, cat("topk_ids"))
+    assert torch.equal(a.topk_logprobs.view(torch.int32), cat("topk_logprobs").view(torch.int32))
