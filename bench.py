@@ -350,14 +350,18 @@ def main():
                                            vp(cu), R, 0, None, 0, vp(out), lmh.LMH_F32, Vq, vp(lcu),
                                            None, None, stream)
 
-        def sel_kernel():
-            return L.lmhead_gather_project(vp(hid), lmh.LMH_BF16, T, H, H, vp(w), lmh.LMH_BF16, Vq, H,
+        # three copies of the 311 MB head (933 MB, well above the 256 MB MALL),
+        # rotated so that no launch finds its weights in the cache
+        wcopies = [w] + [w.clone() for _ in range(2)]
+
+        def sel_kernel(wc):
+            return L.lmhead_gather_project(vp(hid), lmh.LMH_BF16, T, H, H, vp(wc), lmh.LMH_BF16, Vq, H,
                                            vp(cu), R, 0, None, 0, vp(out), lmh.LMH_F32, Vq, None,
                                            None, None, stream)
         assert sel_call() == 0
         hs = max(steps // 4, 10)
         m_sel = timer.loop([sel_call], hs, warmup)
-        tk = timer.loop_median([sel_kernel], hs, warmup)
+        tk = timer.loop_median([lambda wc=wc: sel_kernel(wc) for wc in wcopies], hs, warmup)
         head_bytes = Vq * H * 2 + R * H * 2 + R * Vq * 4
         ach = head_bytes / (tk * 1e-3) / 1e9
         log(f"selective head: call {m_sel * 1e3:.1f} us, kernel {tk * 1e3:.1f} us -> {ach:.0f} GB/s")
@@ -381,7 +385,7 @@ def main():
             "selective_ms": round(m_sel, 4), "selective_kernel_us": round(tk * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                         "bytes_per_launch": head_bytes,
+                         "bytes_per_launch": head_bytes, "weight_copies_rotated": len(wcopies),
                          "kernel": "k_head_pipe (k-pipelined weight stream, 16-wave chain per CU)",
                          "traffic": load_traffic("head_pipe_bf16",
                                                  os.path.join(ROOT, "top_reduction_amd", "csrc", "pipe.hip"))},
@@ -406,7 +410,7 @@ def main():
         tm = timer.loop([lambda i=i: mask_call(i) for i in range(4)], hs, warmup)
         result["head"]["bitmask_us"] = round(tm * 1e3, 2)
         log(f"bitmask on 40 x {Vq} fp32 logits: {tm * 1e3:.1f} us")
-        del hid, w, full, out, outs, masks
+        del hid, w, wcopies, full, out, outs, masks
 
     # ------------------------------------------------------------------
     # quantised selective head (Qwen3-0.6B shape, 4- and 8-bit codes, group 64)
@@ -427,6 +431,10 @@ def main():
             sc = lmh_bf16(torch, qd["scales"], dev)
             bi = lmh_bf16(torch, qd["biases"], dev)
             qld, sld = q.shape[1], sc.shape[1]
+            # copies of codes, scales and biases rotated so that together they
+            # exceed the 256 MB MALL (4-bit: 4 x 112 MB; 8-bit: 3 x 190 MB)
+            ncop = 4 if bits == 4 else 3
+            qcopies = [(q, sc, bi)] + [(q.clone(), sc.clone(), bi.clone()) for _ in range(ncop - 1)]
 
             def sel_q(q=q, sc=sc, bi=bi, qld=qld, sld=sld, bits=bits):
                 return L.lmhead_gather_project_q(vp(hid), lmh.LMH_BF16, T, H, H, vp(q), qld, vp(sc),
@@ -439,7 +447,7 @@ def main():
                                                  2048, vp(full), lmh.LMH_F32, Vq, None, None, None,
                                                  stream)
             assert sel_q() == 0 and full_q() == 0
-            tk = timer.loop_median([sel_q], max(steps // 4, 10), warmup)
+            tk = timer.loop_median([lambda c=c: sel_q(*c) for c in qcopies], max(steps // 4, 10), warmup)
             qbytes = Vq * H * bits // 8 + Vq * (H // G) * 4 + R * H * 2 + R * Vq * 4
             ach = qbytes / (tk * 1e-3) / 1e9
             tf = timer.loop([full_q], max(steps // 20, 5), 2)
@@ -452,7 +460,7 @@ def main():
                 "selective_kernel_us": round(tk * 1e3, 2),
                 "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                             "bytes_per_launch": qbytes,
+                             "bytes_per_launch": qbytes, "weight_copies_rotated": ncop,
                              "traffic": load_traffic(f"head_stream_q{bits}",
                                                      os.path.join(ROOT, "top_reduction_amd", "csrc",
                                                                   "head.hip"))},
@@ -461,7 +469,7 @@ def main():
                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(tfl / BF16_PEAK_TFLOPS, 4)},
             }
-            del q, sc, bi
+            del q, sc, bi, qcopies
         del hid, out, full
 
     # ------------------------------------------------------------------
@@ -474,6 +482,8 @@ def main():
         Vl, H = w.shape
         kk = 20
         fused = {}
+        # two copies of the 1.05 GB head, rotated in the mixed-batch loops
+        wl = [w, w.clone()]
         for mode in ("mixed", "prompt"):
             d = synth.mixed_batch(7301) if mode == "mixed" else synth.prompt_batch(7302)
             hid = lmh_bf16(torch, d["hidden"], dev)
@@ -488,21 +498,40 @@ def main():
             o = (torch.empty(R, device=dev), torch.empty(R, device=dev),
                  torch.empty((R, kk), dtype=torch.int32, device=dev), torch.empty((R, kk), device=dev))
 
-            def call(hid=hid, cu=cu, sel=sel, ex=ex, T=T, S=S, R=R, ws=ws, o=o, nd=d["num_decode"]):
-                return L.lmhead_logprobs(vp(hid), lmh.LMH_BF16, T, H, H, vp(w), lmh.LMH_BF16, Vl, H,
+            def call(wc=w, hid=hid, cu=cu, sel=sel, ex=ex, T=T, S=S, R=R, ws=ws, o=o, nd=d["num_decode"]):
+                return L.lmhead_logprobs(vp(hid), lmh.LMH_BF16, T, H, H, vp(wc), lmh.LMH_BF16, Vl, H,
                                          vp(cu), S, nd, None if ex is None else vp(ex),
                                          0 if ex is None else R, vp(sel), kk, vp(o[0]), vp(o[1]),
                                          vp(o[2]), vp(o[3]), None, None, 256, None, vp(ws),
                                          ws.numel(), None, stream)
             assert call() == 0
             n = max(steps // 10, 5)
-            m = timer.loop([call], n, 3)
+            fns = [lambda wc=wc: call(wc) for wc in wl] if mode == "mixed" else [call]
+            m = timer.loop(fns, n, 3)
             entry = {"ms": round(m, 4), "rows": R, "rows_per_s": round(R / (m * 1e-3))}
             if mode == "mixed":
                 entry["workload"] = ("32 decode rows + prefills 512/2048 x4 (10272 tokens), 40 sampled "
                                      "rows, hidden 4096, vocab 128256, K=20")
                 wb = Vl * H * 2
                 entry["weight_stream_gbps"] = round(wb / (m * 1e-3) / 1e9, 1)
+                entry["weight_copies_rotated"] = len(wl)
+                # the head stage alone: the same 40 rows projected to fp32 logits
+                zout = torch.empty((R, Vl), device=dev)
+
+                def head_only(wc, hid=hid, cu=cu, T=T, S=S, nd=d["num_decode"]):
+                    return L.lmhead_gather_project(vp(hid), lmh.LMH_BF16, T, H, H, vp(wc), lmh.LMH_BF16, Vl,
+                                                   H, vp(cu), S, nd, None, 0, vp(zout), lmh.LMH_F32, Vl,
+                                                   None, None, None, stream)
+                assert head_only(w) == 0
+                th = timer.loop_median([lambda wc=wc: head_only(wc) for wc in wl], max(n, 10), 3)
+                hb = Vl * H * 2 + R * H * 2 + R * Vl * 4
+                ha = hb / (th * 1e-3) / 1e9
+                entry["head_kernel_us"] = round(th * 1e3, 2)
+                entry["head_roofline"] = {"bound": "hbm", "achieved": round(ha, 1), "peak": HBM_PEAK_GBS,
+                                          "unit": "GB/s", "frac": round(ha / HBM_PEAK_GBS, 4),
+                                          "bytes_per_launch": hb}
+                log(f"fused mixed head stage alone: {th * 1e3:.1f} us -> {ha:.0f} GB/s")
+                del zout
             else:
                 entry["workload"] = "one 1024-token prompt, all positions, 256-row chunks, K=20"
                 entry["tflops"] = round(2.0 * R * H * Vl / (m * 1e-3) / 1e12, 1)
@@ -510,7 +539,7 @@ def main():
             log(f"fused {mode}: {m:.3f} ms")
             del hid, ws
         result["fused"] = fused
-        del w
+        del w, wl
 
     # ------------------------------------------------------------------
     # a plain elementwise copy of known size: the reference that scales the

@@ -73,7 +73,7 @@ typedef enum {
     LMH_ERR_SHAPE = 2,     /* a size is negative/zero where it must not be, a   */
                            /* row pitch is below the row width, or a size limit */
                            /* below is exceeded                                 */
-    LMH_ERR_K = 3,         /* K < 0, K > vocab, or min(K, nb) * 64 > 8192       */
+    LMH_ERR_K = 3,         /* K < -1, K > vocab, or min(K, nb) * 64 > 8192      */
     LMH_ERR_DTYPE = 4,     /* unsupported dtype or dtype combination           */
     LMH_ERR_ALIGN = 5,     /* a base pointer or row pitch is not 16-B aligned   */
     LMH_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the size function  */
@@ -90,6 +90,10 @@ typedef enum { LMH_F32 = 0, LMH_BF16 = 1, LMH_F16 = 2 } lmh_dtype;
 #define LMH_DEVERR_LAYOUT 2 /* cu_seqlens[0] != 0, cu_seqlens decreasing, cu_seqlens[S] */
                             /* beyond num_tokens, a decode segment not one token long,   */
                             /* or an empty segment in sampled mode                       */
+
+/* k = LMH_K_FULL asks for every token's logprob instead of a top-K
+ * [openinfer, Acceptance criteria: -1 = full vocabulary] */
+#define LMH_K_FULL (-1)
 
 /* logits per prefilter block [MTPLX, Change] and the candidate bound */
 #define LMH_BLOCK 64
@@ -154,7 +158,11 @@ size_t logprob_reduce_workspace_size(int64_t rows, int64_t vocab, int32_t k);
  * selected_ids [rows] int32 or NULL (then selected_logprob is not written).
  * k       0 <= k <= vocab and min(k, ceil(vocab/64)) * 64 <= 8192 (so k <= 128
  *         at vocabularies above 8192). k = 0 computes lse and the selected
- *         logprob only; topk_* may then be NULL.
+ *         logprob only; topk_* may then be NULL. k = LMH_K_FULL (-1) writes
+ *         every token's logprob instead of a top-K: topk_logprobs is then
+ *         [rows][vocab] fp32 (row pitch vocab, element v the logprob of
+ *         token v, float32(logit) - lse like every other logprob) and
+ *         topk_ids is not used (may be NULL).
  * lse [rows], selected_logprob [rows], topk_ids [rows][k] (int32),
  * topk_logprobs [rows][k] (fp32): outputs, written in full.
  * Method: one coalesced pass over each row produces online (max, sum-exp)
@@ -244,7 +252,9 @@ size_t lmhead_logprobs_workspace_size(int64_t rows, int64_t vocab, int32_t k, in
  * most one chunk of logits is resident. selected_ids is indexed by logits
  * row (R entries). logits_debug, when not NULL, is an [R][vocab] fp32 buffer
  * that receives the logits that were reduced (tests use it); the workspace
- * then only holds the reduction's part. A row without a valid source (flagged
+ * then only holds the reduction's part. k = LMH_K_FULL writes every token's
+ * logprob of each logits row into topk_logprobs [R][vocab] (row pitch vocab),
+ * as logprob_reduce does. A row without a valid source (flagged
  * in device_error) has NaN logits, so its lse, selected logprob and top-K
  * logprobs come out NaN and its top-K ids -1.
  */
@@ -361,8 +371,22 @@ lmh_status lmhead_gather_project_ex(
 
 /*
  * lmhead_logprobs_ex -- lmhead_logprobs with the head given by `head` (dense
- * or quantised, with output scaling: the reduction sees the scaled logits).
- * vocab_mask must be NULL (reserved).
+ * or quantised, with output scaling: the reduction sees the scaled logits)
+ * and an optional token bitmask [vllm-metal, Testing: bitmask application
+ * under the compacted layout].
+ * vocab_mask [num_segments][vocab_mask_ld] 32-bit words or NULL (no mask):
+ *         the layout lmhead_apply_bitmask takes (bit v % 32 of word v / 32 of
+ *         row s set keeps token v in segment s's logits rows, clear makes it
+ *         -inf; bits past vocab ignored), vocab_mask_ld >= ceil(vocab/32),
+ *         4-B aligned. Each chunk's fp32 logits are masked before they are
+ *         reduced, so lse, the selected logprob and the top-K are those of
+ *         the masked rows (a fully masked row: lse -inf, NaN logprobs; a
+ *         masked selected token: logprob -inf). Segment s owns the logits
+ *         rows logits_cu_seqlens[s] .. [s+1]-1: with logits_indices the call
+ *         computes those bounds into logits_cu_seqlens, which must then be
+ *         non-NULL (else LMH_ERR_NULL); in sampled mode segment s is row s.
+ *         A segment whose bounds are malformed is left unmasked and sets
+ *         LMH_DEVERR_LAYOUT. vocab_mask_ld is ignored when vocab_mask is NULL.
  */
 lmh_status lmhead_logprobs_ex(
     const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,

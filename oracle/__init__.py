@@ -183,6 +183,18 @@ def reduce(logits: np.ndarray, selected=None, k: int = 0, lib=None):
     return lse, sel_lp, ids, lp
 
 
+def full_logprobs(logits: np.ndarray, lib=None) -> np.ndarray:
+    """Every token's logprob, f64 [rows][V]: x - lse of its row (openinfer
+    issue #719, Acceptance criteria: -1 asks for the full vocabulary), with
+    lse from the plain reduction above; a row of -inf gives NaN (-inf minus
+    -inf)."""
+    lib = lib or load()
+    x = np.ascontiguousarray(widen(logits, lib))
+    lse = reduce(logits, None, 0, lib)[0]
+    with np.errstate(invalid="ignore"):
+        return x - lse[:, None]
+
+
 def apply_bitmask(logits: np.ndarray, mask: np.ndarray, logits_cu_seqlens=None, lib=None):
     """f64 copy of ``logits`` [rows][V] with segment s's token bitmask (uint32
     words [S][ceil(V/32)], bit set = token kept) applied to its rows

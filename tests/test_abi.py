@@ -137,7 +137,8 @@ def _reduce(L, **kw):
     (dict(dt=BAD_DT), DTYPE),
     (dict(logits=A + 8), ALIGN), (dict(ld=248324), ALIGN),
     (dict(dt=F16, wsb=1024), WS), (dict(dt=F16, ld=248324), ALIGN),   # f16 logits are accepted
-    (dict(k=-1), K), (dict(k=129), K), (dict(vocab=100, ld=104, k=101), K),
+    (dict(k=-2), K), (dict(k=129), K), (dict(vocab=100, ld=104, k=101), K),
+    (dict(k=-1, lps=None), NULL), (dict(k=-1, ids=None, wsb=16), WS),   # full-vocabulary mode
     (dict(vocab=9 * 8192 * 64, ld=9 * 8192 * 64, k=1), SHAPE),
     (dict(ws=None), WS), (dict(wsb=1024), WS), (dict(ws=A + 16), WS),
 ])
@@ -173,7 +174,7 @@ def _reduce_noalloc(L, **kw):
     (dict(ids=None), NULL), (dict(lps=None), NULL),
     (dict(rows=-1), SHAPE), (dict(vocab=0), SHAPE), (dict(ld=248319), SHAPE),
     (dict(dt=BAD_DT), DTYPE), (dict(logits=A + 8), ALIGN),
-    (dict(k=-1), K), (dict(k=129), K),
+    (dict(k=-2), K), (dict(k=129), K), (dict(k=-1, lps=None), NULL),
     # a shape whose reduction workspace is above the static scratch
     (dict(rows=3000), WS), (dict(rows=600, k=0), WS),
 ])
@@ -262,11 +263,22 @@ def test_gather_project_ex_null_head_and_variant(L):
     assert _project_ex(L, _head(), S=100, D=0, variant=1) == SHAPE
 
 
-def test_logprobs_ex_mask_reserved(L):
+def test_logprobs_ex_mask_rules(L):
+    """The token bitmask of the fused call: a pitch below ceil(vocab/32)
+    words, a misaligned mask, and explicit rows without logits_cu_seqlens
+    (the segment bounds the mask needs) are refused; a valid mask passes its
+    checks (the too-small workspace is what stops the call)."""
     h = _head()
-    args = [A, BF16, 23, 64, 64, ctypes.byref(h), 1000, A, 5, 2, None, 0, A, 5, A, A, A, A, None,
-            None, 0, None]
-    assert L.lmhead_logprobs_ex(*args, A, 32, A, 1 << 30, None, None) == SHAPE
+
+    def call(mask, mask_ld, ex=None, nex=0, lcu=None, wsb=1 << 30):
+        return L.lmhead_logprobs_ex(A, BF16, 23, 64, 64, ctypes.byref(h), 1000, A, 5, 2, ex, nex, A, 5,
+                                    A, A, A, A, lcu, None, 0, None, mask, mask_ld, A, wsb, None, None)
+    assert call(A, 31) == SHAPE
+    assert call(A + 2, 32) == ALIGN
+    assert call(A, 32, ex=A, nex=5) == NULL
+    assert call(A, 32, wsb=16) == WS
+    assert call(A, 32, ex=A, nex=5, lcu=A, wsb=16) == WS
+    assert call(None, 0, wsb=16) == WS
     assert L.lmhead_logprobs_ex(None, BF16, 23, 64, 64, ctypes.byref(h), 1000, A, 5, 2, None, 0,
                                 A, 5, A, A, A, A, None, None, 0, None, None, 0, A, 1 << 30, None,
                                 None) == NULL

@@ -128,3 +128,58 @@ def test_compacted_chain_matches_oracle_chain():
     assert rows3.size > 0
     assert np.all(out.topk_ids.cpu().numpy()[rows3, 0] == 4097)
     assert np.all(out.topk_logprobs.cpu().numpy()[rows3, 0] == 0.0)
+
+
+@pytest.mark.parametrize("mode", ["explicit", "sampled"])
+def test_fused_logprobs_with_mask(mode):
+    """lmhead_logprobs_ex with a token bitmask: each chunk's logits are masked
+    before they are reduced. The reduced logits (logits_debug) are the
+    unmasked logits of the same call without a mask, masked by the oracle
+    (exact); the reduction matches the oracle's on them (ids exact, 1e-5).
+    Explicit mode: three segments owning 200, 250 and 250 rows, reduced in
+    256-row chunks that straddle them; the middle segment's mask clears every
+    token (lse -inf, NaN logprobs). Sampled mode: 40 one-row segments, one
+    selected token masked."""
+    g = synth.rng(9100 + len(mode))
+    H, V, K = 256, 3000, 7
+    w = bf16_tensor(synth.normal_bf16(g, (V, H), H ** -0.5))
+    if mode == "explicit":
+        T = 700
+        cu = np.array([0, 200, 450, 700], dtype=np.int32)
+        ex = np.arange(T, dtype=np.int32)
+        S, R = 3, T
+    else:
+        T = 40 * 37
+        cu = (37 * np.arange(41)).astype(np.int32)
+        ex = None
+        S, R = 40, 40
+    hid = bf16_tensor(synth.normal_bf16(g, (T, H)))
+    sel = g.integers(0, V, size=R).astype(np.int32)
+    mask = _mask_words(g, S, V)
+    if mode == "explicit":
+        mask[1, :] = 0                                        # a fully masked segment
+    else:
+        mask[5, sel[5] // 32] &= ~np.uint32(1 << (sel[5] % 32))   # row 5's selected token masked
+    head = lmh.HeadSpec(w)
+    kw = dict(selected_ids=i32_tensor(sel), k=K, chunk_rows=256, return_logits=True,
+              logits_indices=None if ex is None else i32_tensor(ex))
+    plain = lmh.lmhead_logprobs_ex(hid, head, i32_tensor(cu), 0, **kw)
+    masked = lmh.lmhead_logprobs_ex(hid, head, i32_tensor(cu), 0,
+                                    vocab_mask=torch.from_numpy(mask.view(np.int32)).cuda(), **kw)
+    torch.cuda.synchronize()
+    assert int(masked.device_error.item()) == 0
+    lcu = masked.logits_cu_seqlens.cpu().numpy()
+    z_plain = np.ascontiguousarray(plain.logits.cpu().numpy())
+    z = np.ascontiguousarray(masked.logits.cpu().numpy())
+    st, z_ref = oracle.apply_bitmask(z_plain, mask, None if ex is None else lcu)
+    assert st == oracle.OK
+    assert np.array_equal(np.isneginf(z), np.isneginf(z_ref))
+    assert np.array_equal(z.astype(np.float64), z_ref)
+    ref = oracle.reduce(z, sel, K)
+    check_reduce(masked, z, sel, K, *ref)
+    lse = masked.lse.cpu().numpy()
+    if mode == "explicit":
+        assert np.all(np.isneginf(lse[200:450])) and np.all(np.isfinite(lse[:200]))
+        assert np.all(np.isnan(masked.topk_logprobs.cpu().numpy()[200:450]))
+    else:
+        assert np.isneginf(masked.selected_logprob.cpu().numpy()[5])

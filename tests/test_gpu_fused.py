@@ -177,3 +177,25 @@ def test_flagged_rows_fused():
                  (ok.topk_logprobs, fl.topk_logprobs)):
         assert np.array_equal(a.cpu().numpy()[~flagged].view(np.uint32), b.cpu().numpy()[~flagged].view(np.uint32))
     assert np.array_equal(ok.topk_ids.cpu().numpy()[~flagged], fl.topk_ids.cpu().numpy()[~flagged])
+
+
+def test_full_vocabulary_fused():
+    """lmhead_logprobs with k = -1 over 300 explicit rows in 256-row chunks:
+    every token's logprob of every row, bitwise float32(z) - lse of the fp32
+    logits the call reduced, and within 1e-5 of the oracle on those logits."""
+    g = synth.rng(5007)
+    T, H, V = 300, 256, 3000
+    hid = bf16_tensor(synth.normal_bf16(g, (T, H)))
+    w = bf16_tensor(synth.normal_bf16(g, (V, H), H ** -0.5))
+    sel = g.integers(0, V, size=T).astype(np.int32)
+    out = lmh.lmhead_logprobs(hid, w, i32_tensor([0, T]), 0, i32_tensor(sel), lmh.LMH_K_FULL,
+                              logits_indices=i32_tensor(np.arange(T)), chunk_rows=256, return_logits=True)
+    torch.cuda.synchronize()
+    z = np.ascontiguousarray(out.logits.cpu().numpy())
+    lp = out.topk_logprobs.cpu().numpy()
+    lse = out.lse.cpu().numpy()
+    assert lp.shape == (T, V)
+    want = (z - lse[:, None]).astype(np.float32)
+    assert np.array_equal(lp.view(np.uint32), want.view(np.uint32))
+    ref = oracle.full_logprobs(z)
+    assert np.max(np.abs(lp - ref)) <= 1e-5

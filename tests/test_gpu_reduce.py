@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 import top_reduction_amd as lmh
-from helpers import bf16_tensor, check_reduce, f32_tensor, i32_tensor
+from helpers import as_f32, bf16_tensor, check_reduce, f32_tensor, i32_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -315,3 +315,56 @@ def test_selection_on_ordered_rows(k):
     assert torch.equal(a.lse.view(torch.int32), cat("lse").view(torch.int32))
     assert torch.equal(a.topk_ids, cat("topk_ids"))
     assert torch.equal(a.topk_logprobs.view(torch.int32), cat("topk_logprobs").view(torch.int32))
+
+
+@pytest.mark.parametrize("case", ["chunk_bf16", "ragged_bf16", "f16", "f32"])
+def test_full_vocabulary_logprobs(case):
+    """k = -1: every token's logprob (openinfer issue #719, Acceptance
+    criteria). Each is bitwise float32(x) - lse of the same call, within
+    1e-5 of the f64 oracle, and equal to the top-K logprobs of a k = 20 call
+    at its ids."""
+    print(f"full vocabulary {case}", flush=True)
+    g = synth.rng(8200 + len(case))
+    if case == "chunk_bf16":
+        bits, sel = synth.scoring_chunk(8201, "gumbel", 20)
+        host, t = bits, bf16_tensor(bits)
+    elif case == "ragged_bf16":
+        host = synth.f32_to_bf16_bits(synth.normal_f32(g, (7, 1003), 2.0))
+        host[3] = 0xFF80                                  # an all -inf row: NaN logprobs
+        padded = np.zeros((7, 1008), dtype=np.uint16)     # 16-byte row pitch
+        padded[:, :1003] = host
+        t = bf16_tensor(padded)[:, :1003]
+        sel = g.integers(0, 1003, size=7).astype(np.int32)
+    elif case == "f16":
+        host = (synth.normal_f32(g, (40, 151_936), 2.0)).astype(np.float16)
+        t = torch.from_numpy(host).cuda()
+        sel = g.integers(0, 151_936, size=40).astype(np.int32)
+    else:
+        host = synth.normal_f32(g, (9, 4100), 3.0)
+        t = torch.from_numpy(host).cuda()
+        sel = g.integers(0, 4100, size=9).astype(np.int32)
+    R, V = host.shape
+    full = lmh.logprob_reduce(t, i32_tensor(sel), lmh.LMH_K_FULL)
+    top = lmh.logprob_reduce(t, i32_tensor(sel), 20)
+    torch.cuda.synchronize()
+    lp = full.topk_logprobs.cpu().numpy()
+    assert lp.shape == (R, V)
+    lse = full.lse.cpu().numpy()
+    assert np.array_equal(lse.view(np.uint32), top.lse.cpu().numpy().view(np.uint32))
+    x = as_f32(host)
+    want = (x - lse[:, None].astype(np.float32)).astype(np.float32)
+    same = np.isnan(want) == np.isnan(lp)
+    assert np.all(same)
+    assert np.array_equal(lp.view(np.uint32)[~np.isnan(want)], want.view(np.uint32)[~np.isnan(want)])
+    ref = oracle.full_logprobs(host)
+    lse_ref = oracle.reduce(host, None, 0)[0]
+    fin = np.isfinite(lse_ref)
+    assert np.all(np.abs(lse[fin] - lse_ref[fin]) <= np.maximum(1e-5, np.abs(lse_ref[fin]) * 2.0 ** -23))
+    finite = np.isfinite(ref)
+    err = np.abs(lp[finite].astype(np.float64) - ref[finite])
+    assert np.all(err <= np.maximum(1e-5, np.abs(ref[finite]) * 2.0 ** -23)), float(err.max())
+    rows = np.arange(R)[:, None]
+    ids = top.topk_ids.cpu().numpy()
+    tl = top.topk_logprobs.cpu().numpy()
+    ok = ~np.isnan(tl)
+    assert np.array_equal(lp[rows, ids][ok].view(np.uint32), tl[ok].view(np.uint32))

@@ -38,6 +38,7 @@ LMH_F32, LMH_BF16, LMH_F16 = 0, 1, 2
 LMH_HEAD_AUTO, LMH_HEAD_STREAM, LMH_HEAD_TILED, LMH_HEAD_PIPE = 0, 1, 2, 3
 LMH_SCALE_NONE, LMH_SCALE_MUL, LMH_SCALE_DIV = 0, 1, 2
 LMH_DEVERR_INDEX, LMH_DEVERR_LAYOUT = 1, 2
+LMH_K_FULL = -1   # k: every token's logprob ([rows, vocab] in topk_logprobs) instead of a top-K
 STATUS = {0: "LMH_OK", 1: "LMH_ERR_NULL", 2: "LMH_ERR_SHAPE", 3: "LMH_ERR_K",
           4: "LMH_ERR_DTYPE", 5: "LMH_ERR_ALIGN", 6: "LMH_ERR_WORKSPACE", 7: "LMH_ERR_HIP"}
 
@@ -144,6 +145,22 @@ def _i32(t: Optional[torch.Tensor], name: str):
     if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous int32 device tensor")
     return t
+
+
+def _topk_out(R: int, V: int, k: int, dev):
+    """Top-K outputs: ids [R, k] and logprobs [R, k]; for k = LMH_K_FULL no
+    ids and every token's logprob [R, V]."""
+    if k == LMH_K_FULL:
+        return (torch.empty((R, 0), dtype=torch.int32, device=dev),
+                torch.empty((R, V), dtype=torch.float32, device=dev))
+    return (torch.empty((R, max(k, 0)), dtype=torch.int32, device=dev),
+            torch.empty((R, max(k, 0)), dtype=torch.float32, device=dev))
+
+
+def _topk_ptrs(k: int, ids: torch.Tensor, lps: torch.Tensor):
+    if k == LMH_K_FULL:
+        return None, _ptr(lps)
+    return (_ptr(ids), _ptr(lps)) if k else (None, None)
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
@@ -263,14 +280,13 @@ def logprob_reduce(logits: torch.Tensor, selected_ids: Optional[torch.Tensor] = 
     if ws is None:
         ws = workspace(need, dev)
     if out is None:
+        ids, lps = _topk_out(R, V, k, dev)
         out = Reduction(torch.empty(R, dtype=torch.float32, device=dev),
                         torch.empty(R, dtype=torch.float32, device=dev) if sel is not None else None,
-                        torch.empty((R, k), dtype=torch.int32, device=dev),
-                        torch.empty((R, k), dtype=torch.float32, device=dev),
-                        torch.zeros(1, dtype=torch.int32, device=dev))
+                        ids, lps, torch.zeros(1, dtype=torch.int32, device=dev))
+    pi, pl = _topk_ptrs(k, out.topk_ids, out.topk_logprobs)
     st = L.logprob_reduce(_ptr(logits), _dt(logits), R, V, ld, _ptr(sel), int(k),
-                          _ptr(out.lse), _ptr(out.selected_logprob),
-                          _ptr(out.topk_ids) if k else None, _ptr(out.topk_logprobs) if k else None,
+                          _ptr(out.lse), _ptr(out.selected_logprob), pi, pl,
                           _ptr(ws), ws.numel(), _ptr(out.device_error), _stream())
     _check(st, "logprob_reduce")
     return out
@@ -286,14 +302,13 @@ def logprob_reduce_noalloc(logits: torch.Tensor, selected_ids: Optional[torch.Te
     sel = _i32(selected_ids, "selected_ids")
     dev = logits.device
     if out is None:
+        ids, lps = _topk_out(R, V, k, dev)
         out = Reduction(torch.empty(R, dtype=torch.float32, device=dev),
                         torch.empty(R, dtype=torch.float32, device=dev) if sel is not None else None,
-                        torch.empty((R, k), dtype=torch.int32, device=dev),
-                        torch.empty((R, k), dtype=torch.float32, device=dev),
-                        torch.zeros(1, dtype=torch.int32, device=dev))
+                        ids, lps, torch.zeros(1, dtype=torch.int32, device=dev))
+    pi, pl = _topk_ptrs(k, out.topk_ids, out.topk_logprobs)
     st = L.logprob_reduce_noalloc(_ptr(logits), _dt(logits), R, V, ld, _ptr(sel), int(k),
-                                  _ptr(out.lse), _ptr(out.selected_logprob),
-                                  _ptr(out.topk_ids) if k else None, _ptr(out.topk_logprobs) if k else None,
+                                  _ptr(out.lse), _ptr(out.selected_logprob), pi, pl,
                                   _ptr(out.device_error), _stream())
     _check(st, "logprob_reduce_noalloc")
     return out
@@ -344,15 +359,13 @@ def _logprobs(fn, name, hidden, weight_args, V, cu_seqlens, num_decode, selected
     dbg = torch.empty((R, ld), dtype=torch.float32, device=dev) if return_logits else None
     lse = torch.empty(R, dtype=torch.float32, device=dev)
     slp = torch.empty(R, dtype=torch.float32, device=dev) if sel is not None else None
-    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
-    lps = torch.empty((R, k), dtype=torch.float32, device=dev)
+    ids, lps = _topk_out(R, V, k, dev)
     lcu = torch.empty(S + 1, dtype=torch.int32, device=dev)
     gidx = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     st = fn(_ptr(hidden), _dt(hidden), T, H, hld, *weight_args,
             _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
-            _ptr(sel), int(k), _ptr(lse), _ptr(slp),
-            _ptr(ids) if k else None, _ptr(lps) if k else None,
+            _ptr(sel), int(k), _ptr(lse), _ptr(slp), *_topk_ptrs(k, ids, lps),
             _ptr(lcu), _ptr(gidx), int(chunk_rows), _ptr(dbg),
             _ptr(ws), ws.numel(), _ptr(err), _stream())
     _check(st, name)
@@ -435,8 +448,12 @@ def lmhead_gather_project_ex(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: t
 def lmhead_logprobs_ex(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: torch.Tensor,
                        num_decode: int = 0, selected_ids: Optional[torch.Tensor] = None, k: int = 0,
                        logits_indices: Optional[torch.Tensor] = None, chunk_rows: int = 0,
-                       return_logits: bool = False, ws: Optional[torch.Tensor] = None) -> Logprobs:
-    """lmhead_logprobs with a HeadSpec (the reduction sees the scaled logits)."""
+                       return_logits: bool = False, ws: Optional[torch.Tensor] = None,
+                       vocab_mask: Optional[torch.Tensor] = None) -> Logprobs:
+    """lmhead_logprobs with a HeadSpec (the reduction sees the scaled logits)
+    and an optional token bitmask ([segments, words] int32, bit v % 32 of
+    word v // 32 set = token v kept in that segment's rows), applied to each
+    chunk's logits before it is reduced."""
     L = lib()
     V, h = _head_struct(head, hidden.shape[1])
     T, H, hld = _matrix(hidden, "hidden")
@@ -452,16 +469,19 @@ def lmhead_logprobs_ex(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: torch.T
     dbg = torch.empty((R, ld), dtype=torch.float32, device=dev) if return_logits else None
     lse = torch.empty(R, dtype=torch.float32, device=dev)
     slp = torch.empty(R, dtype=torch.float32, device=dev) if sel is not None else None
-    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
-    lps = torch.empty((R, k), dtype=torch.float32, device=dev)
+    ids, lps = _topk_out(R, V, k, dev)
     lcu = torch.empty(S + 1, dtype=torch.int32, device=dev)
     gidx = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
+    mld = 0
+    if vocab_mask is not None:
+        Sm, _, mld = _matrix(vocab_mask, "vocab_mask")
+        if vocab_mask.dtype != torch.int32 or Sm != S:
+            raise ValueError("vocab_mask must be int32 words, one row per segment")
     st = L.lmhead_logprobs_ex(_ptr(hidden), _dt(hidden), T, H, hld, ctypes.byref(h), V,
                               _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
-                              _ptr(sel), int(k), _ptr(lse), _ptr(slp),
-                              _ptr(ids) if k else None, _ptr(lps) if k else None,
-                              _ptr(lcu), _ptr(gidx), int(chunk_rows), _ptr(dbg), None, 0,
+                              _ptr(sel), int(k), _ptr(lse), _ptr(slp), *_topk_ptrs(k, ids, lps),
+                              _ptr(lcu), _ptr(gidx), int(chunk_rows), _ptr(dbg), _ptr(vocab_mask), mld,
                               _ptr(ws), ws.numel(), _ptr(err), _stream())
     _check(st, "lmhead_logprobs_ex")
     return Logprobs(lse, slp, ids, lps, lcu, gidx[:R], err, None if dbg is None else dbg[:, :V])

@@ -105,10 +105,10 @@ lmh_status check_reduce_shape(lmh_dtype dt, int64_t rows, int64_t vocab, int64_t
     if (!valid_logits_dtype(dt)) return LMH_ERR_DTYPE;
     if (((size_t)ld * esize(dt)) % 16) return LMH_ERR_ALIGN;
     const int64_t nb = ceil_div(vocab, kBlock);
-    if (k < 0 || k > vocab) return LMH_ERR_K;
+    if (k < LMH_K_FULL || k > vocab) return LMH_ERR_K;
     if ((k < nb ? k : nb) * (int64_t)kBlock > kMaxCandidates) return LMH_ERR_K;
     if (k > 0 && nb > kMaxCandidates) return LMH_ERR_SHAPE;
-    const ReducePlan p = plan_reduce(rows, vocab, k);
+    const ReducePlan p = plan_reduce(rows, vocab, k > 0 ? k : 0);
     if (p.wgs >= ((int64_t)1 << 30)) return LMH_ERR_SHAPE;   // stage-1 item index fits 32 bits
     return LMH_OK;
 }
@@ -188,7 +188,8 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
                          float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
                          int32_t* logits_cu_seqlens, int32_t* gather_indices, int32_t chunk_rows,
                          float* logits_debug, void* workspace, size_t workspace_bytes,
-                         int32_t* device_error, void* stream) {
+                         int32_t* device_error, void* stream, const uint32_t* vocab_mask = nullptr,
+                         int64_t vocab_mask_ld = 0) {
     const ProjectCheck c = check_project_inputs(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
                                                 w, vocab, cu_seqlens, num_segments, num_decode,
                                                 logits_indices, num_indices);
@@ -197,6 +198,15 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
         if (!lse) return LMH_ERR_NULL;
         if (selected_ids && !selected_logprob) return LMH_ERR_NULL;
         if (k > 0 && (!topk_ids || !topk_logprobs)) return LMH_ERR_NULL;
+        if (k == LMH_K_FULL && !topk_logprobs) return LMH_ERR_NULL;
+    }
+    const int32_t kr = k > 0 ? k : 0;   // the top-K of the reduction (K = -1: none)
+    if (vocab_mask != nullptr) {
+        // explicit rows: the segment -> rows map is the logits_cu_seqlens
+        // this call writes, so the caller must ask for it
+        if (logits_indices != nullptr && !logits_cu_seqlens) return LMH_ERR_NULL;
+        if (vocab_mask_ld < ceil_div(vocab, 32)) return LMH_ERR_SHAPE;
+        if (!aligned(vocab_mask, 4)) return LMH_ERR_ALIGN;
     }
     if (chunk_rows < 0) return LMH_ERR_SHAPE;
     const int64_t R = c.rows;
@@ -208,7 +218,7 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
         const lmh_status st = check_reduce_shape(LMH_F32, chunk, vocab, ld, k);
         if (st != LMH_OK) return st;
     }
-    const ReducePlan pc = plan_reduce(chunk, vocab, k);
+    const ReducePlan pc = plan_reduce(chunk, vocab, kr);
     const size_t logits_bytes = logits_debug ? 0 : up256((size_t)chunk * (size_t)ld * sizeof(float));
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < logits_bytes + pc.bytes)
         return LMH_ERR_WORKSPACE;
@@ -232,17 +242,31 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
                                      device_error);
         lmh_status st = launch_head(h, hidden_dt == LMH_BF16, LMH_HEAD_AUTO, s);
         if (st != LMH_OK) return st;
+        if (vocab_mask != nullptr && num_segments > 0) {
+            // each segment's mask on this chunk's rows, before they are reduced
+            MaskArgs m{out, LMH_F32, n, vocab, ld, reinterpret_cast<const int32_t*>(vocab_mask),
+                       vocab_mask_ld, logits_indices ? logits_cu_seqlens : nullptr, num_segments,
+                       device_error};
+            m.win0 = r0;
+            m.total_rows = R;
+            st = from_hip(launch_apply_bitmask(m, s));
+            if (st != LMH_OK) return st;
+        }
         // this chunk's decomposition, inside the workspace layout sized for a full chunk
-        ReducePlan q = plan_reduce(n, vocab, k);
+        ReducePlan q = plan_reduce(n, vocab, kr);
         q.part_off = pc.part_off;
         q.keys_off = pc.keys_off;
         q.bytes = pc.bytes;
         ReduceArgs a{out, LMH_F32, ld, selected_ids ? selected_ids + r0 : nullptr, lse + r0,
                      selected_ids ? selected_logprob + r0 : nullptr,
-                     k > 0 ? topk_ids + r0 * k : nullptr, k > 0 ? topk_logprobs + r0 * k : nullptr,
+                     kr > 0 ? topk_ids + r0 * kr : nullptr, kr > 0 ? topk_logprobs + r0 * kr : nullptr,
                      ws_reduce, device_error};
         st = from_hip(launch_reduce(q, a, s));
         if (st != LMH_OK) return st;
+        if (k == LMH_K_FULL) {
+            st = from_hip(launch_full_logprobs(out, LMH_F32, n, vocab, ld, lse + r0, topk_logprobs + r0 * vocab, s));
+            if (st != LMH_OK) return st;
+        }
     }
     return LMH_OK;
 }
@@ -257,11 +281,12 @@ lmh_status reduce_validate(const void* logits, lmh_dtype logits_dt, int64_t rows
                            const float* topk_logprobs, size_t* workspace_bytes) {
     const lmh_status st = check_reduce_shape(logits_dt, rows, vocab, logits_ld, k);
     if (st != LMH_OK) return st;
-    *workspace_bytes = plan_reduce(rows, vocab, k).bytes;
+    *workspace_bytes = plan_reduce(rows, vocab, k > 0 ? k : 0).bytes;
     if (rows == 0) return LMH_OK;
     if (!logits || !lse) return LMH_ERR_NULL;
     if (selected_ids && !selected_logprob) return LMH_ERR_NULL;
     if (k > 0 && (!topk_ids || !topk_logprobs)) return LMH_ERR_NULL;
+    if (k == LMH_K_FULL && !topk_logprobs) return LMH_ERR_NULL;
     if (!aligned(logits, 16)) return LMH_ERR_ALIGN;
     return LMH_OK;
 }
@@ -270,10 +295,13 @@ lmh_status reduce_enqueue(const void* logits, lmh_dtype logits_dt, int64_t rows,
                           int64_t logits_ld, const int32_t* selected_ids, int32_t k, float* lse,
                           float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
                           void* workspace, int32_t* device_error, hipStream_t s) {
-    const ReducePlan p = plan_reduce(rows, vocab, k);
+    const int32_t kr = k > 0 ? k : 0;   // K = -1: lse first, then every logprob
+    const ReducePlan p = plan_reduce(rows, vocab, kr);
     ReduceArgs a{logits, (int32_t)logits_dt, logits_ld, selected_ids, lse, selected_logprob,
-                 topk_ids, topk_logprobs, workspace, device_error};
-    return from_hip(launch_reduce(p, a, s));
+                 kr > 0 ? topk_ids : nullptr, kr > 0 ? topk_logprobs : nullptr, workspace, device_error};
+    const lmh_status st = from_hip(launch_reduce(p, a, s));
+    if (st != LMH_OK || k != LMH_K_FULL) return st;
+    return from_hip(launch_full_logprobs(logits, (int32_t)logits_dt, rows, vocab, logits_ld, lse, topk_logprobs, s));
 }
 
 }  // namespace lmh
@@ -285,7 +313,7 @@ const char* lmh_status_string(lmh_status st) {
         case LMH_OK: return "LMH_OK";
         case LMH_ERR_NULL: return "LMH_ERR_NULL: a required pointer is NULL";
         case LMH_ERR_SHAPE: return "LMH_ERR_SHAPE: invalid size, pitch or size limit";
-        case LMH_ERR_K: return "LMH_ERR_K: k < 0, k > vocab or min(k, blocks) * 64 > 8192";
+        case LMH_ERR_K: return "LMH_ERR_K: k < -1, k > vocab or min(k, blocks) * 64 > 8192";
         case LMH_ERR_DTYPE: return "LMH_ERR_DTYPE: unsupported dtype";
         case LMH_ERR_ALIGN: return "LMH_ERR_ALIGN: pointer or row pitch not aligned";
         case LMH_ERR_WORKSPACE: return "LMH_ERR_WORKSPACE: workspace missing or too small";
@@ -390,7 +418,7 @@ lmh_status lmh_debug_reduce_stage1(const void* logits, lmh_dtype logits_dt, int6
     const lmh_status st = check_reduce_shape(logits_dt, rows, vocab, logits_ld, k);
     if (st != LMH_OK) return st;
     if (!aligned(logits, 16)) return LMH_ERR_ALIGN;
-    const ReducePlan p = plan_reduce(rows, vocab, k);
+    const ReducePlan p = plan_reduce(rows, vocab, k > 0 ? k : 0);
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.bytes) return LMH_ERR_WORKSPACE;
     if (rows == 0) return LMH_OK;
     ReduceArgs a{logits, (int32_t)logits_dt, logits_ld, nullptr, nullptr, nullptr,
@@ -420,8 +448,8 @@ lmh_status lmhead_apply_bitmask(void* logits, lmh_dtype logits_dt, int64_t rows,
 }
 
 int32_t lmh_debug_reduce_path(int64_t rows, int64_t vocab, int32_t k) {
-    if (rows <= 0 || vocab <= 0 || k < 0) return 0;
-    return reduce_row_path(plan_reduce(rows, vocab, k)) ? 1 : 0;
+    if (rows <= 0 || vocab <= 0 || k < LMH_K_FULL) return 0;
+    return reduce_row_path(plan_reduce(rows, vocab, k > 0 ? k : 0)) ? 1 : 0;
 }
 
 size_t lmhead_logprobs_workspace_size(int64_t rows, int64_t vocab, int32_t k, int32_t chunk_rows) {
@@ -496,12 +524,11 @@ lmh_status lmhead_logprobs_ex(const void* hidden, lmh_dtype hidden_dt, int64_t n
                               const uint32_t* vocab_mask, int64_t vocab_mask_ld, void* workspace,
                               size_t workspace_bytes, int32_t* device_error, void* stream) {
     if (!head) return LMH_ERR_NULL;
-    if (vocab_mask != nullptr || vocab_mask_ld != 0) return LMH_ERR_SHAPE;
     return logprobs_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld, head_weight(*head),
                          vocab, cu_seqlens, num_segments, num_decode, logits_indices, num_indices,
                          selected_ids, k, lse, selected_logprob, topk_ids, topk_logprobs,
                          logits_cu_seqlens, gather_indices, chunk_rows, logits_debug, workspace,
-                         workspace_bytes, device_error, stream);
+                         workspace_bytes, device_error, stream, vocab_mask, vocab_mask_ld);
 }
 
 size_t lmhead_selfcheck_workspace_size(int64_t rows, int64_t vocab) {

@@ -136,6 +136,10 @@ struct MaskArgs {
     const int32_t* lcu;   // [segments + 1] or nullptr (segment s is row s)
     int32_t segments;
     int32_t* err;         // may be nullptr
+    // the buffer's rows are compacted rows win0 .. win0 + rows - 1 of
+    // total_rows (0: the buffer holds them all)
+    int64_t win0 = 0;
+    int64_t total_rows = 0;
 };
 hipError_t launch_apply_bitmask(const MaskArgs& a, hipStream_t s);
 
@@ -172,6 +176,10 @@ hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStr
 bool reduce_row_path(const ReducePlan& p);
 // The whole reduction (either path).
 hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
+// Full-vocabulary logprobs out[r][v] = fp32(x[r][v]) - lse[r] (out pitch:
+// vocab), after a reduction has written lse.
+hipError_t launch_full_logprobs(const void* logits, int32_t dt, int64_t rows, int64_t vocab, int64_t ld,
+                                const float* lse, float* out, hipStream_t s);
 
 // logprob_reduce's host-side checks (everything but the workspace), in its
 // order; *workspace_bytes gets the workspace the shape needs. Then the

@@ -1334,6 +1334,33 @@ __global__ __launch_bounds__(kRowThreads) void k_rowreduce(const uint8_t* __rest
                                                 reinterpret_cast<u32x4*>(cand + cap + ((K + 1) & ~1)), s_tkey);
 }
 
+// ---------------------------------------------------------------------------
+// Full-vocabulary logprobs (K = -1; openinfer issue #719, Acceptance
+// criteria): out[r][v] = fp32(x[r][v]) - lse[r], one rounding, the same
+// value the top-K path writes for the ids it returns. One thread per 16-byte
+// group of a row; entries past the vocabulary are not written.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_full_logprobs(const uint8_t* __restrict__ logits, int64_t ld,
+                                                            int64_t V, uint32_t chunks,
+                                                            const float* __restrict__ lse,
+                                                            float* __restrict__ out) {
+    constexpr int EPV = w16(DT) ? 8 : 4;
+    constexpr size_t ESZ = w16(DT) ? 2 : 4;
+    const uint32_t r = blockIdx.x / chunks;
+    const int64_t e0 = ((int64_t)(blockIdx.x - r * chunks) * kThreads + threadIdx.x) * EPV;
+    if (e0 >= V) return;
+    const float l = lse[r];
+    const u32x4 w = load_part<DT>(logits + (size_t)r * (size_t)ld * ESZ, V, e0);
+    float* o = out + (int64_t)r * V + e0;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+        const uint32_t wd = w[e / (w16(DT) ? 2 : 1)];
+        const float x = w16(DT) ? ((e & 1) ? hi16<DT>(wd) : lo16<DT>(wd)) : __uint_as_float(wd);
+        if (e0 + e < V) o[e] = x - l;
+    }
+}
+
 }  // namespace
 
 ReducePlan plan_reduce(int64_t rows, int64_t vocab, int32_t k) {
@@ -1358,6 +1385,23 @@ ReducePlan plan_reduce(int64_t rows, int64_t vocab, int32_t k) {
     p.bytes = p.keys_off + up((size_t)rows * p.kld * sizeof(uint32_t));
     if (p.bytes == 0) p.bytes = 256;
     return p;
+}
+
+hipError_t launch_full_logprobs(const void* logits, int32_t dt, int64_t rows, int64_t vocab, int64_t ld,
+                                const float* lse, float* out, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    const int epv = w16(dt) ? 8 : 4;
+    const int64_t groups = (vocab + epv - 1) / epv;
+    const uint32_t chunks = (uint32_t)((groups + kThreads - 1) / kThreads);
+    const dim3 grid((unsigned)(chunks * rows));
+    const uint8_t* lg = static_cast<const uint8_t*>(logits);
+    if (dt == kDtBf16)
+        hipLaunchKernelGGL((k_full_logprobs<kDtBf16>), grid, dim3(kThreads), 0, s, lg, ld, vocab, chunks, lse, out);
+    else if (dt == kDtF16)
+        hipLaunchKernelGGL((k_full_logprobs<kDtF16>), grid, dim3(kThreads), 0, s, lg, ld, vocab, chunks, lse, out);
+    else
+        hipLaunchKernelGGL((k_full_logprobs<kDtF32>), grid, dim3(kThreads), 0, s, lg, ld, vocab, chunks, lse, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_reduce_stage1(const ReducePlan& p, const ReduceArgs& a, hipStream_t s) {
