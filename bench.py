@@ -535,6 +535,20 @@ def main():
             else:
                 entry["workload"] = "one 1024-token prompt, all positions, 256-row chunks, K=20"
                 entry["tflops"] = round(2.0 * R * H * Vl / (m * 1e-3) / 1e12, 1)
+                entry["reduce_first_pass"] = "tiled head epilogue (per-block partials)"
+                # the same call with the reduction's first pass as its own
+                # stream over each chunk's logits
+                _, hs = lmh._head_struct(lmh.HeadSpec(w), H)
+
+                def call_unfused(hid=hid, cu=cu, sel=sel, ex=ex, T=T, S=S, R=R, ws=ws, o=o, hs=hs):
+                    return L.lmh_debug_logprobs_ex(vp(hid), lmh.LMH_BF16, T, H, H, ctypes.byref(hs), Vl,
+                                                   vp(cu), S, 0, vp(ex), R, vp(sel), kk, vp(o[0]), vp(o[1]),
+                                                   vp(o[2]), vp(o[3]), None, None, 256, None, None, 0, vp(ws),
+                                                   ws.numel(), None, stream, 1)
+                assert call_unfused() == 0
+                mu = timer.loop([call_unfused], n, 3)
+                entry["unfused_ms"] = round(mu, 4)
+                log(f"fused prompt with the reduction's own first pass: {mu:.3f} ms")
             fused[mode] = entry
             log(f"fused {mode}: {m:.3f} ms")
             del hid, ws

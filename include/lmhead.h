@@ -252,7 +252,17 @@ size_t lmhead_logprobs_workspace_size(int64_t rows, int64_t vocab, int32_t k, in
  * most one chunk of logits is resident. selected_ids is indexed by logits
  * row (R entries). logits_debug, when not NULL, is an [R][vocab] fp32 buffer
  * that receives the logits that were reduced (tests use it); the workspace
- * then only holds the reduction's part. k = LMH_K_FULL writes every token's
+ * then only holds the reduction's part. Chunks of more than 64 rows of a dense
+ * bf16 head whose hidden size is a multiple of 128 are projected by the
+ * tiled kernel, whose epilogue also writes, per row and 64-logit block, the
+ * block maximum and its (max, sum of exp) partial [MTPLX PR #532,
+ * Motivation: no second full pass over a chunk's logits]; the reduction then
+ * merges those partials (one per block: partial i to thread i mod 256 in
+ * ascending order, each wave's lanes as a pairwise tree, then the four waves
+ * in order) and takes the top-K from them, with no pass of its own over the
+ * logits. Ids and selected values are those of the unfused reduction of the
+ * same logits; lse may differ from it in the last bits (another summation
+ * order). k = LMH_K_FULL writes every token's
  * logprob of each logits row into topk_logprobs [R][vocab] (row pitch vocab),
  * as logprob_reduce does. A row without a valid source (flagged
  * in device_error) has NaN logits, so its lse, selected logprob and top-K
@@ -477,6 +487,27 @@ lmh_status lmh_debug_gather_project_q(
     void* logits, lmh_dtype logits_dt, int64_t logits_ld,
     int32_t* logits_cu_seqlens, int32_t* gather_indices,
     int32_t* device_error, void* stream, int32_t variant);
+
+/*
+ * lmh_debug_logprobs_ex -- lmhead_logprobs_ex with the reduction's first pass
+ * chosen: epilogue 0 lets chunks of more than 64 rows of a dense bf16 head
+ * (hidden size a multiple of 128, no vocab_mask) take it in the tiled head's
+ * epilogue, as lmhead_logprobs_ex does; 1 always runs it as its own pass over
+ * the chunk's logits (tests and measurement compare the two). Any other
+ * value returns LMH_ERR_SHAPE.
+ */
+lmh_status lmh_debug_logprobs_ex(
+    const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens, int64_t hidden_dim,
+    int64_t hidden_ld, const lmh_head* head, int64_t vocab,
+    const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
+    const int32_t* logits_indices, int32_t num_indices,
+    const int32_t* selected_ids, int32_t k,
+    float* lse, float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+    int32_t* logits_cu_seqlens, int32_t* gather_indices,
+    int32_t chunk_rows, float* logits_debug,
+    const uint32_t* vocab_mask, int64_t vocab_mask_ld,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream,
+    int32_t epilogue);
 
 /*
  * lmh_debug_reduce_stage1 -- only the streaming pass of logprob_reduce

@@ -131,19 +131,33 @@ def test_prompt_mode_chunks(llama_weight):
 
 
 def test_chunk_sizes_agree():
+    """Chunks of at most 64 rows reduce with their own streaming pass, larger
+    chunks from the tiled head's per-block partials (so with 256-row chunks
+    the first 256 rows take the partials and the last 44 their own pass):
+    per row, results are bitwise independent of the chunking within each
+    kind; across the two, ids are equal and lse agrees to fp32 rounding."""
     g = synth.rng(5004)
     T, H, V = 300, 256, 3000
     hid = synth.normal_bf16(g, (T, H))
     w = synth.normal_bf16(g, (V, H), H ** -0.5)
     ex = np.arange(T, dtype=np.int32)
     sel = g.integers(0, V, size=T).astype(np.int32)
-    outs = [lmh.lmhead_logprobs(bf16_tensor(hid), bf16_tensor(w), i32_tensor([0, T]), 0,
-                                i32_tensor(sel), 7, logits_indices=i32_tensor(ex), chunk_rows=c)
-            for c in (0, 1, 64, 100, 300)]
+    outs = {c: lmh.lmhead_logprobs(bf16_tensor(hid), bf16_tensor(w), i32_tensor([0, T]), 0,
+                                   i32_tensor(sel), 7, logits_indices=i32_tensor(ex), chunk_rows=c)
+            for c in (0, 1, 64, 100, 300)}
     torch.cuda.synchronize()
-    for o in outs[1:]:
-        assert torch.equal(o.topk_ids, outs[0].topk_ids)
-        assert torch.equal(o.lse.view(torch.int32), outs[0].lse.view(torch.int32))
+    lse = {c: o.lse.view(torch.int32).cpu().numpy() for c, o in outs.items()}
+    for c in (0, 64, 100, 300):
+        assert torch.equal(outs[c].topk_ids, outs[1].topk_ids)
+    partials = {0: np.arange(256), 100: np.arange(T), 300: np.arange(T)}
+    own_pass = {0: np.arange(256, T), 1: np.arange(T), 64: np.arange(T)}
+    for kind in (partials, own_pass):
+        rows = set.intersection(*(set(v.tolist()) for v in kind.values()))
+        rows = np.array(sorted(rows))
+        first = next(iter(kind))
+        for c in kind:
+            assert np.array_equal(lse[c][rows], lse[first][rows])
+    assert float((outs[100].lse - outs[1].lse).abs().max()) <= 1e-5
 
 
 def test_flagged_rows_fused():
@@ -199,3 +213,50 @@ def test_full_vocabulary_fused():
     assert np.array_equal(lp.view(np.uint32), want.view(np.uint32))
     ref = oracle.full_logprobs(z)
     assert np.max(np.abs(lp - ref)) <= 1e-5
+
+
+@pytest.mark.parametrize("k,scale", [(20, 0), (0, 0), (5, 2)])
+def test_epilogue_partials_match_unfused(llama_weight, k, scale):
+    """The Llama-3-8B-shaped prompt (1024 rows in 256-row chunks) with the
+    reduction's first pass in the tiled head's epilogue, against the same
+    call with that pass run on its own: the reduced logits are bitwise
+    equal, ids equal, lse and logprobs within 1e-5; both against the oracle
+    on those logits (ids exact, 1e-5). With a divided head the partials are
+    those of the scaled logits."""
+    d = synth.prompt_batch(5003)
+    hid = bf16_tensor(d["hidden"])
+    head = lmh.HeadSpec(bf16_tensor(llama_weight), lmh.LMH_SCALE_DIV if scale else lmh.LMH_SCALE_NONE,
+                        float(scale) if scale else 1.0)
+    kw = dict(selected_ids=i32_tensor(d["selected"]), k=k, logits_indices=i32_tensor(d["logits_indices"]),
+              chunk_rows=256, return_logits=True)
+    fused = lmh.lmhead_logprobs_ex(hid, head, i32_tensor(d["cu_seqlens"]), 0, epilogue=0, **kw)
+    plain = lmh.lmhead_logprobs_ex(hid, head, i32_tensor(d["cu_seqlens"]), 0, epilogue=1, **kw)
+    torch.cuda.synchronize()
+    assert int(fused.device_error.item()) == 0
+    assert torch.equal(fused.logits.view(torch.int32), plain.logits.view(torch.int32))
+    assert torch.equal(fused.topk_ids, plain.topk_ids)
+    assert float((fused.lse - plain.lse).abs().max()) <= 1e-5
+    assert float((fused.selected_logprob - plain.selected_logprob).abs().max()) <= 1e-5
+    if k:
+        assert float((fused.topk_logprobs - plain.topk_logprobs).abs().max()) <= 1e-5
+    z = np.ascontiguousarray(fused.logits.cpu().numpy())
+    ref = oracle.reduce(z, d["selected"], k)
+    check_reduce(fused, z, d["selected"], k, *ref)
+
+
+def test_epilogue_partials_full_vocabulary():
+    """k = -1 on 300 rows (a 256-row chunk from the epilogue partials, then a
+    44-row chunk with its own pass): every logprob bitwise float32(z) - lse
+    of the call, lse within 1e-5 of the oracle."""
+    g = synth.rng(5008)
+    T, H, V = 300, 256, 3000
+    hid = bf16_tensor(synth.normal_bf16(g, (T, H)))
+    w = bf16_tensor(synth.normal_bf16(g, (V, H), H ** -0.5))
+    out = lmh.lmhead_logprobs(hid, w, i32_tensor([0, T]), 0, None, lmh.LMH_K_FULL,
+                              logits_indices=i32_tensor(np.arange(T)), chunk_rows=256, return_logits=True)
+    torch.cuda.synchronize()
+    z = np.ascontiguousarray(out.logits.cpu().numpy())
+    lse = out.lse.cpu().numpy()
+    assert np.array_equal(out.topk_logprobs.cpu().numpy().view(np.uint32),
+                          (z - lse[:, None]).astype(np.float32).view(np.uint32))
+    assert np.max(np.abs(lse - oracle.reduce(z, None, 0)[0])) <= 1e-5

@@ -90,6 +90,7 @@ def lib():
         projx = [p, ctypes.c_int, i64, i64, i64, hp, i64, p, i32, i32, p, i32]
         L.lmhead_gather_project_ex.argtypes = projx + [p, ctypes.c_int, i64, p, p, p, p, i32]
         L.lmhead_logprobs_ex.argtypes = projx + [p, i32, p, p, p, p, p, p, i32, p, p, i64, p, sz, p, p]
+        L.lmh_debug_logprobs_ex.argtypes = projx + [p, i32, p, p, p, p, p, p, i32, p, p, i64, p, sz, p, p, i32]
         L.lmhead_selfcheck_workspace_size.argtypes = [i64, i64]
         L.lmhead_selfcheck_workspace_size.restype = sz
         L.lmhead_selfcheck.argtypes = projx + [p, i64, p, sz, p, p, p]
@@ -100,7 +101,7 @@ def lib():
                      "logprob_reduce_noalloc",
                      "lmh_debug_reduce_stage1", "lmhead_logprobs", "lmhead_gather_project_q",
                      "lmh_debug_gather_project_q", "lmhead_logprobs_q", "lmhead_gather_project_ex",
-                     "lmhead_logprobs_ex", "lmhead_selfcheck", "lmhead_apply_bitmask"):
+                     "lmhead_logprobs_ex", "lmh_debug_logprobs_ex", "lmhead_selfcheck", "lmhead_apply_bitmask"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -449,11 +450,13 @@ def lmhead_logprobs_ex(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: torch.T
                        num_decode: int = 0, selected_ids: Optional[torch.Tensor] = None, k: int = 0,
                        logits_indices: Optional[torch.Tensor] = None, chunk_rows: int = 0,
                        return_logits: bool = False, ws: Optional[torch.Tensor] = None,
-                       vocab_mask: Optional[torch.Tensor] = None) -> Logprobs:
+                       vocab_mask: Optional[torch.Tensor] = None, epilogue: Optional[int] = None) -> Logprobs:
     """lmhead_logprobs with a HeadSpec (the reduction sees the scaled logits)
     and an optional token bitmask ([segments, words] int32, bit v % 32 of
     word v // 32 set = token v kept in that segment's rows), applied to each
-    chunk's logits before it is reduced."""
+    chunk's logits before it is reduced. `epilogue` (diagnostic): None as
+    the library chooses; 0 lets the tiled head's epilogue take the
+    reduction's first pass where it can, 1 never (lmh_debug_logprobs_ex)."""
     L = lib()
     V, h = _head_struct(head, hidden.shape[1])
     T, H, hld = _matrix(hidden, "hidden")
@@ -478,12 +481,15 @@ def lmhead_logprobs_ex(hidden: torch.Tensor, head: HeadSpec, cu_seqlens: torch.T
         Sm, _, mld = _matrix(vocab_mask, "vocab_mask")
         if vocab_mask.dtype != torch.int32 or Sm != S:
             raise ValueError("vocab_mask must be int32 words, one row per segment")
-    st = L.lmhead_logprobs_ex(_ptr(hidden), _dt(hidden), T, H, hld, ctypes.byref(h), V,
-                              _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
-                              _ptr(sel), int(k), _ptr(lse), _ptr(slp), *_topk_ptrs(k, ids, lps),
-                              _ptr(lcu), _ptr(gidx), int(chunk_rows), _ptr(dbg), _ptr(vocab_mask), mld,
-                              _ptr(ws), ws.numel(), _ptr(err), _stream())
-    _check(st, "lmhead_logprobs_ex")
+    args = (_ptr(hidden), _dt(hidden), T, H, hld, ctypes.byref(h), V,
+            _ptr(cu), S, int(num_decode), _ptr(ex), R if ex is not None else 0,
+            _ptr(sel), int(k), _ptr(lse), _ptr(slp), *_topk_ptrs(k, ids, lps),
+            _ptr(lcu), _ptr(gidx), int(chunk_rows), _ptr(dbg), _ptr(vocab_mask), mld,
+            _ptr(ws), ws.numel(), _ptr(err), _stream())
+    if epilogue is None:
+        _check(L.lmhead_logprobs_ex(*args), "lmhead_logprobs_ex")
+    else:
+        _check(L.lmh_debug_logprobs_ex(*args, int(epilogue)), "lmh_debug_logprobs_ex")
     return Logprobs(lse, slp, ids, lps, lcu, gidx[:R], err, None if dbg is None else dbg[:, :V])
 
 

@@ -180,6 +180,14 @@ lmh_status gather_project_impl(const void* hidden, lmh_dtype hidden_dt, int64_t 
     return launch_head(h, hidden_dt == LMH_BF16, variant, s);
 }
 
+// Workspace of the reduction when the tiled head's epilogue takes its
+// streaming pass: per row of a chunk, one (max, sum) per 64-logit block and
+// the block keys in the second kernel's layout.
+size_t blocks_ws_bytes(int64_t chunk, int64_t vocab, int32_t k) {
+    const ReducePlan p = plan_reduce(chunk, vocab, k > 0 ? k : 0);
+    return up256((size_t)chunk * (size_t)p.nb * sizeof(float2)) + up256((size_t)chunk * (size_t)p.kld * 4);
+}
+
 lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
                          int64_t hidden_dim, int64_t hidden_ld, const WeightSpec& w, int64_t vocab,
                          const int32_t* cu_seqlens, int32_t num_segments, int32_t num_decode,
@@ -189,7 +197,7 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
                          int32_t* logits_cu_seqlens, int32_t* gather_indices, int32_t chunk_rows,
                          float* logits_debug, void* workspace, size_t workspace_bytes,
                          int32_t* device_error, void* stream, const uint32_t* vocab_mask = nullptr,
-                         int64_t vocab_mask_ld = 0) {
+                         int64_t vocab_mask_ld = 0, bool allow_epilogue = true) {
     const ProjectCheck c = check_project_inputs(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld,
                                                 w, vocab, cu_seqlens, num_segments, num_decode,
                                                 logits_indices, num_indices);
@@ -222,6 +230,13 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
     const size_t logits_bytes = logits_debug ? 0 : up256((size_t)chunk * (size_t)ld * sizeof(float));
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < logits_bytes + pc.bytes)
         return LMH_ERR_WORKSPACE;
+    // chunks of more rows than the weight-streaming kernels take run on the
+    // tiled kernel; with a dense bf16 head of a hidden size it tiles in 64-wide
+    // stages, its epilogue does the reduction's streaming pass (unless a token
+    // mask must change the logits first, or the workspace has no room for the
+    // per-block partials)
+    const bool epi = allow_epilogue && hidden_dt == LMH_BF16 && w.bits == 0 && hidden_dim % 128 == 0 &&
+                     vocab_mask == nullptr && workspace_bytes >= logits_bytes + blocks_ws_bytes(chunk, vocab, kr);
     if (logits_debug && !aligned(logits_debug, 16)) return LMH_ERR_ALIGN;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -237,9 +252,33 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
     for (int64_t r0 = 0; r0 < R; r0 += chunk) {
         const int32_t n = (int32_t)((R - r0) < chunk ? (R - r0) : chunk);
         float* out = logits_debug ? logits_debug + r0 * ld : ws_logits;
-        const HeadArgs h = head_args(hidden, num_tokens, hidden_dim, hidden_ld, w, vocab, cu_seqlens,
-                                     num_decode, logits_indices, (int32_t)r0, n, out, ld, false,
-                                     device_error);
+        HeadArgs h = head_args(hidden, num_tokens, hidden_dim, hidden_ld, w, vocab, cu_seqlens, num_decode,
+                               logits_indices, (int32_t)r0, n, out, ld, false, device_error);
+        if (epi && n > kStreamMaxRows) {
+            // the head writes the logits and, per block, the partials and keys;
+            // the second reduction kernel finishes each row from them
+            ReducePlan q = plan_reduce(n, vocab, kr);
+            q.splits = q.nb;
+            q.part_off = 0;
+            q.keys_off = up256((size_t)chunk * (size_t)q.nb * sizeof(float2));
+            h.part = reinterpret_cast<float2*>(static_cast<char*>(ws_reduce) + q.part_off);
+            h.bkeys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws_reduce) + q.keys_off);
+            h.part_nb = q.nb;
+            h.keys_ld = q.kld;
+            lmh_status st = launch_head(h, true, LMH_HEAD_AUTO, s);
+            if (st != LMH_OK) return st;
+            ReduceArgs a{out, LMH_F32, ld, selected_ids ? selected_ids + r0 : nullptr, lse + r0,
+                         selected_ids ? selected_logprob + r0 : nullptr,
+                         kr > 0 ? topk_ids + r0 * kr : nullptr, kr > 0 ? topk_logprobs + r0 * kr : nullptr,
+                         ws_reduce, device_error};
+            st = from_hip(launch_reduce_stage2_blocks(q, a, s));
+            if (st != LMH_OK) return st;
+            if (k == LMH_K_FULL) {
+                st = from_hip(launch_full_logprobs(out, LMH_F32, n, vocab, ld, lse + r0, topk_logprobs + r0 * vocab, s));
+                if (st != LMH_OK) return st;
+            }
+            continue;
+        }
         lmh_status st = launch_head(h, hidden_dt == LMH_BF16, LMH_HEAD_AUTO, s);
         if (st != LMH_OK) return st;
         if (vocab_mask != nullptr && num_segments > 0) {
@@ -457,7 +496,9 @@ size_t lmhead_logprobs_workspace_size(int64_t rows, int64_t vocab, int32_t k, in
     const int64_t chunk_cfg = chunk_rows > 0 ? chunk_rows : 256;
     const int64_t chunk = rows < chunk_cfg ? (rows > 0 ? rows : 1) : chunk_cfg;
     const int64_t ld = ceil_div(vocab, 4) * 4;
-    return up256((size_t)chunk * (size_t)ld * sizeof(float)) + plan_reduce(chunk, vocab, k < 0 ? 0 : k).bytes;
+    const size_t red = plan_reduce(chunk, vocab, k < 0 ? 0 : k).bytes;
+    const size_t blk = blocks_ws_bytes(chunk, vocab, k);
+    return up256((size_t)chunk * (size_t)ld * sizeof(float)) + (red > blk ? red : blk);
 }
 
 lmh_status lmhead_logprobs(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
@@ -529,6 +570,26 @@ lmh_status lmhead_logprobs_ex(const void* hidden, lmh_dtype hidden_dt, int64_t n
                          selected_ids, k, lse, selected_logprob, topk_ids, topk_logprobs,
                          logits_cu_seqlens, gather_indices, chunk_rows, logits_debug, workspace,
                          workspace_bytes, device_error, stream, vocab_mask, vocab_mask_ld);
+}
+
+lmh_status lmh_debug_logprobs_ex(const void* hidden, lmh_dtype hidden_dt, int64_t num_tokens,
+                                 int64_t hidden_dim, int64_t hidden_ld, const lmh_head* head,
+                                 int64_t vocab, const int32_t* cu_seqlens, int32_t num_segments,
+                                 int32_t num_decode, const int32_t* logits_indices,
+                                 int32_t num_indices, const int32_t* selected_ids, int32_t k,
+                                 float* lse, float* selected_logprob, int32_t* topk_ids,
+                                 float* topk_logprobs, int32_t* logits_cu_seqlens,
+                                 int32_t* gather_indices, int32_t chunk_rows, float* logits_debug,
+                                 const uint32_t* vocab_mask, int64_t vocab_mask_ld, void* workspace,
+                                 size_t workspace_bytes, int32_t* device_error, void* stream,
+                                 int32_t epilogue) {
+    if (!head) return LMH_ERR_NULL;
+    if (epilogue != 0 && epilogue != 1) return LMH_ERR_SHAPE;
+    return logprobs_impl(hidden, hidden_dt, num_tokens, hidden_dim, hidden_ld, head_weight(*head),
+                         vocab, cu_seqlens, num_segments, num_decode, logits_indices, num_indices,
+                         selected_ids, k, lse, selected_logprob, topk_ids, topk_logprobs,
+                         logits_cu_seqlens, gather_indices, chunk_rows, logits_debug, workspace,
+                         workspace_bytes, device_error, stream, vocab_mask, vocab_mask_ld, epilogue == 0);
 }
 
 size_t lmhead_selfcheck_workspace_size(int64_t rows, int64_t vocab) {

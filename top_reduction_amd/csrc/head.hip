@@ -751,6 +751,52 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
     }
 }
 
+// The reduction partial of one 64-logit block of logits row r, from the 16
+// lanes of a DPP row that hold its columns (4 each, lane order = column
+// order): the block maximum M (exact), S = the sum of exp(x - M) computed as
+// in the reduction's stream (2^(x log2e + c) with c = -RN(M log2e), scaled
+// once by 2^-e, e = M log2e + c exactly), the four terms of a lane added in
+// column order and the lanes by a fixed pairwise tree. Columns past the
+// vocabulary count as -inf. A row without a source (NaN logits) gives M =
+// -inf and S = NaN, and the key of NaN, as the stream does on NaN logits.
+// Called by every lane (the DPP exchanges need the whole row); one lane writes.
+__device__ inline void block_partial(const HeadParams& p, int32_t r, bool has_src, int64_t v, const f32x4& val,
+                                     int64_t blk) {
+    constexpr float kLog2eF = 1.4426950408889634f;
+    constexpr float kNegInfF = -__builtin_inff();
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = v + e < p.V ? val[e] : kNegInfF;
+    auto dpp = [](float a, auto ctl) {
+        constexpr int C = decltype(ctl)::value;
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), C, 0xF, 0xF, false));
+    };
+    using q1 = std::integral_constant<int, 0xB1>;    // quad_perm [1,0,3,2]
+    using q2 = std::integral_constant<int, 0x4E>;    // quad_perm [2,3,0,1]
+    using hm = std::integral_constant<int, 0x141>;   // row_half_mirror
+    using rm = std::integral_constant<int, 0x140>;   // row_mirror
+    float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    m = fmaxf(m, dpp(m, q1{}));
+    m = fmaxf(m, dpp(m, q2{}));
+    m = fmaxf(m, dpp(m, hm{}));
+    m = fmaxf(m, dpp(m, rm{}));
+    const float mr = m == kNegInfF ? 0.f : m;
+    const float c = -(mr * kLog2eF);
+    const float ee = fmaf(mr, kLog2eF, c);
+    float sm = (__builtin_amdgcn_exp2f(fmaf(x[0], kLog2eF, c)) + __builtin_amdgcn_exp2f(fmaf(x[1], kLog2eF, c))) +
+               (__builtin_amdgcn_exp2f(fmaf(x[2], kLog2eF, c)) + __builtin_amdgcn_exp2f(fmaf(x[3], kLog2eF, c)));
+    sm += dpp(sm, q1{});
+    sm += dpp(sm, q2{});
+    sm += dpp(sm, hm{});
+    sm += dpp(sm, rm{});
+    sm *= __builtin_amdgcn_exp2f(-ee);
+    if ((threadIdx.x & 15) == 0 && r < p.R && blk < p.nb) {
+        const float nan = __builtin_nanf("");
+        p.part[(int64_t)r * p.nb + blk] = has_src ? make_float2(m, sm) : make_float2(kNegInfF, nan);
+        p.bkeys[(int64_t)r * p.kld + blk] = f32_key(has_src ? m : nan);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 tiled kernel with 64-wide k stages (hidden size a multiple of 128):
 // the same 256 x 256 tile, waves, MFMA sequence and epilogue as k_head_tiled,
@@ -769,12 +815,18 @@ constexpr int kT64Waves = 8;
 
 // NW waves: 8 (two per SIMD, 128 x 64 each) or 4 (one per SIMD, 128 x 128
 // each, accumulators in the AGPRs a lone wave may use).
-template <bool OUT_BF16, int NW>
+// FUSED (fp32 logits, eight waves): each wave's 64 columns are one 64-logit
+// block of the vocabulary, and the epilogue also writes, per row, that
+// block's maximum as a key and its (max, sum of exp(x - max)) partial -- the
+// reduction's streaming pass, done on the values while they are in registers
+// (MTPLX PR #532, Motivation: no second pass over a chunk's logits).
+template <bool OUT_BF16, int NW, bool FUSED = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
     constexpr int NTH = NW * 64;
     constexpr int WN = kTileN / (NW / 2);              // columns per wave
     constexpr int NF = WN / 16;                         // B fragments per wave
+    static_assert(!FUSED || (WN == 64 && !OUT_BF16), "a wave's columns are one block; fp32 logits");
     constexpr int L = kTileM * (kT64K / 8) / NTH;       // chunks per thread per stage (A and B each)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int32_t* sIdx = reinterpret_cast<int32_t*>(lds + 2 * kT64Stage);
@@ -914,6 +966,7 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
                 f32x4 val = *reinterpret_cast<const f32x4*>(&stg[rr * 68 + cl]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) val[e] = scale_logit(val[e], p.scale_mode, p.scale);
+                if constexpr (FUSED) block_partial(p, r, sIdx[rl] >= 0, v, val, (n0 + wn) >> 6);
                 if (r < p.R) {
                     const bool valid = sIdx[rl] >= 0;
                     if (vec_ok && v + 4 <= p.V) {
@@ -1047,14 +1100,14 @@ hipError_t launch_tiled_q(const HeadParams& p, int32_t mtiles, int32_t ntiles, h
     return launch_tiled<OUT_BF16, BITS, false>(p, mtiles, ntiles, s);
 }
 
-template <bool OUT_BF16, int NW = kT64Waves>
+template <bool OUT_BF16, int NW = kT64Waves, bool FUSED = false>
 hipError_t launch_tiled64(const HeadParams& p, int32_t mtiles, int32_t ntiles, hipStream_t s) {
-    const void* fn = (const void*)k_head_tiled64<OUT_BF16, NW>;
+    const void* fn = (const void*)k_head_tiled64<OUT_BF16, NW, FUSED>;
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kT64Lds);
     if (e != hipSuccess) return e;
     const int64_t total = (int64_t)mtiles * ntiles;
     const dim3 grid((unsigned)(((total + 7) / 8) * 8));
-    hipLaunchKernelGGL((k_head_tiled64<OUT_BF16, NW>), grid, dim3(NW * 64), kT64Lds, s, p, mtiles, ntiles);
+    hipLaunchKernelGGL((k_head_tiled64<OUT_BF16, NW, FUSED>), grid, dim3(NW * 64), kT64Lds, s, p, mtiles, ntiles);
     return hipGetLastError();
 }
 
@@ -1063,8 +1116,12 @@ hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
     const HeadParams p = to_params(a);
     const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
     const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
-    if (p.H % 128 == 0)
+    if (p.H % 128 == 0) {
+        if (a.part != nullptr)
+            return a.out_bf16 ? hipErrorInvalidValue : launch_tiled64<false, kT64Waves, true>(p, mtiles, ntiles, s);
         return a.out_bf16 ? launch_tiled64<true>(p, mtiles, ntiles, s) : launch_tiled64<false>(p, mtiles, ntiles, s);
+    }
+    if (a.part != nullptr) return hipErrorInvalidValue;
     return a.out_bf16 ? launch_tiled<true, 16, false>(p, mtiles, ntiles, s)
                       : launch_tiled<false, 16, false>(p, mtiles, ntiles, s);
 }

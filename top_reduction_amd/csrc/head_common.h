@@ -50,6 +50,12 @@ struct HeadParams {
     int64_t old;
     int32_t scale_mode;       // 0 none, 1 multiply by scale, 2 divide by scale
     float scale;
+    // reduction partials from the tiled epilogue (nullptr: none): per logits
+    // row and 64-logit block, the block's (max, sum of exp(x - max)) at
+    // part[row * nb + b] and its key at bkeys[row * kld + b]
+    float2* part;
+    uint32_t* bkeys;
+    int32_t nb, kld;
 };
 
 // Head output scaling on the fp32 accumulator, before any output rounding
@@ -144,6 +150,10 @@ HeadParams to_params(const HeadArgs& a) {
     p.qw.biases = a.biases;
     p.qw.sld = a.s_ld;
     p.qw.gshift = a.gshift;
+    p.part = a.part;
+    p.bkeys = a.bkeys;
+    p.nb = a.part_nb;
+    p.kld = a.keys_ld;
     return p;
 }
 

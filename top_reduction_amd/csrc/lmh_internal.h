@@ -99,6 +99,14 @@ struct HeadArgs {
     // output scaling on the fp32 accumulator: 0 none, 1 multiply, 2 divide
     int32_t scale_mode = 0;
     float scale = 1.0f;
+    // the reduction's first pass done by the tiled kernel's epilogue (fp32
+    // logits, hidden size a multiple of 128, more than kStreamMaxRows rows):
+    // per row and 64-logit block, (max, sum of exp(x - max)) at
+    // part[row * part_nb + b] and the block-max key at bkeys[row * keys_ld + b]
+    float2* part = nullptr;
+    uint32_t* bkeys = nullptr;
+    int32_t part_nb = 0;
+    int32_t keys_ld = 0;
 };
 // Compute units of the current device (0 if it cannot be queried).
 int cu_count();
@@ -170,6 +178,11 @@ struct ReduceArgs {
 };
 hipError_t launch_reduce_stage1(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
+// Stage 2 on partials written by the tiled head's epilogue: one (max, sum)
+// per 64-logit block (p.splits == p.nb), merged in their own fixed order
+// (partial i to thread i mod 256 in ascending order, each wave's lanes as a
+// pairwise tree, then the four waves in order); fp32 logits.
+hipError_t launch_reduce_stage2_blocks(const ReducePlan& p, const ReduceArgs& a, hipStream_t s);
 // True when the one-workgroup-per-row kernel serves this plan on the current
 // device (rows fill the CUs evenly); the split path otherwise. Both give
 // bitwise-identical results.

@@ -1043,11 +1043,44 @@ __device__ inline void write_selected(int64_t V, int32_t sel_id, float xsel, flo
     }
 }
 
+// The (max, sum) of a wave's 64 lanes as a pairwise tree (partner lane ^ 1,
+// ^ 2, the mirror lane in the half row and in the row, then lane ^ 16 and
+// lane ^ 32; the lower half always the left operand); every lane ends with
+// the wave's partial.
+__device__ inline void lse_tree64(float& m, float& s) {
+    const int lane = threadIdx.x & 63;
+    auto merge_with = [&](float m2, float s2, int d) {
+        const bool left = (lane & d) == 0;
+        float mL = left ? m : m2, sL = left ? s : s2;
+        lse_merge(mL, sL, left ? m2 : m, left ? s2 : s);
+        m = mL;
+        s = sL;
+    };
+    auto level = [&](auto ctl, int d) {
+        constexpr int C = decltype(ctl)::value;
+        merge_with(__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), C, 0xF, 0xF, false)),
+                   __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), C, 0xF, 0xF, false)), d);
+    };
+    level(std::integral_constant<int, 0xB1>{}, 1);
+    level(std::integral_constant<int, 0x4E>{}, 2);
+    level(std::integral_constant<int, 0x141>{}, 4);
+    level(std::integral_constant<int, 0x140>{}, 8);
+    merge_with(__int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (16 << 10))),
+               __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(s), 0x1F | (16 << 10))), 16);
+    const int x32 = ((lane ^ 32) << 2);
+    merge_with(__int_as_float(__builtin_amdgcn_ds_bpermute(x32, __float_as_int(m))),
+               __int_as_float(__builtin_amdgcn_ds_bpermute(x32, __float_as_int(s))), 32);
+}
+
 // ---------------------------------------------------------------------------
 // Split path, second kernel: one workgroup of 256 threads per row reads the
-// row's item partials and block keys from the workspace.
+// row's item partials and block keys from the workspace. BLOCKS: the
+// partials are one per 64-logit block, written by the tiled head's epilogue
+// (fp32 logits), and merge in their own fixed order: partial i goes to thread
+// i mod 256, which merges its partials in ascending order; each wave's lanes
+// then merge as a pairwise tree and the four waves in order.
 // ---------------------------------------------------------------------------
-template <int DT, int KPT>
+template <int DT, int KPT, bool BLOCKS = false>
 __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__ logits, int64_t ld,
                                                      int64_t V, int32_t nb, int32_t kld, int32_t splits,
                                                      const float2* __restrict__ part,
@@ -1117,19 +1150,40 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
     int32_t sel_id = 0;
     if (sel_thread) sel_id = sel[row];
 
-    // logsumexp: lanes 0..15 of wave 0 merge their groups' partials, then
-    // the wave merges the groups
-    if (tid < 64) {
+    if constexpr (BLOCKS) {
+        __shared__ float2 swave[kThreads / 64];
         float m = kNegInf, sm = 0.f;
-        if (tid < kGroups)
-            for (int i = tid; i < splits; i += kGroups) {
-                const float2 pp = part[row * splits + i];
-                lse_merge(m, sm, pp.x, pp.y);
-            }
-        const float l = lse_tree16(m, sm);
+        for (int i = tid; i < splits; i += kThreads) {
+            const float2 pp = part[row * splits + i];
+            lse_merge(m, sm, pp.x, pp.y);
+        }
+        lse_tree64(m, sm);
+        if ((tid & 63) == 0) swave[tid >> 6] = make_float2(m, sm);
+        __syncthreads();
         if (tid == 0) {
+            float mm = swave[0].x, ss = swave[0].y;
+#pragma unroll
+            for (int w = 1; w < kThreads / 64; ++w) lse_merge(mm, ss, swave[w].x, swave[w].y);
+            // m = -inf: every entry -inf (lse -inf) or NaN (lse NaN)
+            const float l = (mm == kNegInf) ? (ss == ss ? kNegInf : ss) : mm + logf(ss);
             sh.lse = l;
             lse_out[row] = l;
+        }
+    } else {
+        // logsumexp: lanes 0..15 of wave 0 merge their groups' partials, then
+        // the wave merges the groups
+        if (tid < 64) {
+            float m = kNegInf, sm = 0.f;
+            if (tid < kGroups)
+                for (int i = tid; i < splits; i += kGroups) {
+                    const float2 pp = part[row * splits + i];
+                    lse_merge(m, sm, pp.x, pp.y);
+                }
+            const float l = lse_tree16(m, sm);
+            if (tid == 0) {
+                sh.lse = l;
+                lse_out[row] = l;
+            }
         }
     }
     __syncthreads();
@@ -1430,29 +1484,57 @@ hipError_t launch_reduce_stage1(const ReducePlan& p, const ReduceArgs& a, hipStr
     return hipGetLastError();
 }
 
-template <int DT, int KPT>
+template <int DT, int KPT, bool BLOCKS>
 hipError_t launch_stage2_kpt(const ReducePlan& p, const ReduceArgs& a, hipStream_t s, const float2* part,
                              const void* keys, int32_t cap, size_t lds) {
-    const void* fn = (const void*)k_stage2<DT, KPT>;
+    const void* fn = (const void*)k_stage2<DT, KPT, BLOCKS>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_stage2<DT, KPT>), dim3((unsigned)p.rows), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((k_stage2<DT, KPT, BLOCKS>), dim3((unsigned)p.rows), dim3(kThreads), lds, s,
                        static_cast<const uint8_t*>(a.logits), a.ld, p.vocab, p.nb, p.kld, p.splits, part,
                        keys, a.sel, p.k, a.lse, a.sel_lp, a.topk_ids, a.topk_lp, a.err, cap);
     return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool BLOCKS = false>
 hipError_t launch_stage2_dt(const ReducePlan& p, const ReduceArgs& a, hipStream_t s, const float2* part,
                             const void* keys, int32_t cap, size_t lds) {
     switch (p.kpt) {
-        case 4: return launch_stage2_kpt<DT, 4>(p, a, s, part, keys, cap, lds);
-        case 8: return launch_stage2_kpt<DT, 8>(p, a, s, part, keys, cap, lds);
-        case 16: return launch_stage2_kpt<DT, 16>(p, a, s, part, keys, cap, lds);
-        default: return launch_stage2_kpt<DT, 32>(p, a, s, part, keys, cap, lds);
+        case 4: return launch_stage2_kpt<DT, 4, BLOCKS>(p, a, s, part, keys, cap, lds);
+        case 8: return launch_stage2_kpt<DT, 8, BLOCKS>(p, a, s, part, keys, cap, lds);
+        case 16: return launch_stage2_kpt<DT, 16, BLOCKS>(p, a, s, part, keys, cap, lds);
+        default: return launch_stage2_kpt<DT, 32, BLOCKS>(p, a, s, part, keys, cap, lds);
     }
+}
+
+// candidates and LDS of the second kernel (fp32 logits: no staging)
+void stage2_sizes(const ReducePlan& p, int32_t dt, int32_t& cap, size_t& lds) {
+    cap = 0;
+    lds = 0;
+    if (p.k > 0) {
+        // 16-bit logits: room for up to 2K candidate blocks (at most 128) and
+        // their staging slots, so that the prefetched-candidate path also
+        // takes blocks tied at T
+        const int32_t kb2 = w16(dt) ? std::min(std::max(p.k, std::min(2 * p.k, kMaxCandidates / kBlock)), p.nb)
+                                    : std::min(p.k, p.nb);
+        cap = kb2 * kBlock;
+        // (the staging path exists only when K <= nb)
+        const size_t stage = w16(dt) && p.k <= p.nb ? ((size_t)kThreads * kBlock + (size_t)cap) * 2 : 0;
+        lds = ((size_t)cap + (size_t)((p.k + 1) & ~1)) * sizeof(uint64_t) + stage;
+    }
+}
+
+hipError_t launch_reduce_stage2_blocks(const ReducePlan& p, const ReduceArgs& a, hipStream_t s) {
+    if (p.rows == 0) return hipSuccess;
+    if (a.dt != kDtF32 || p.splits != p.nb) return hipErrorInvalidValue;
+    char* ws = static_cast<char*>(a.ws);
+    int32_t cap;
+    size_t lds;
+    stage2_sizes(p, a.dt, cap, lds);
+    return launch_stage2_dt<kDtF32, true>(p, a, s, reinterpret_cast<const float2*>(ws + p.part_off),
+                                          ws + p.keys_off, cap, lds);
 }
 
 hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStream_t s) {
