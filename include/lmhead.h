@@ -83,7 +83,14 @@ typedef enum {
 /* LMH_F16 (IEEE binary16) is accepted for the logits of logprob_reduce only
  * [MTPLX PR #532, Tests: bf16/f16 logits]; every other dtype argument takes
  * LMH_F32 or LMH_BF16. */
-typedef enum { LMH_F32 = 0, LMH_BF16 = 1, LMH_F16 = 2 } lmh_dtype;
+typedef enum {
+    LMH_F32 = 0,
+    LMH_BF16 = 1,
+    LMH_F16 = 2,
+    /* not a dtype: makes every 32-bit value a value of the type, so an
+     * unknown code from a caller is checked (LMH_ERR_DTYPE), not undefined */
+    LMH_DTYPE_MAX_ENUM = 0x7FFFFFFF
+} lmh_dtype;
 
 /* device_error bits */
 #define LMH_DEVERR_INDEX 1  /* a row index or selected id outside its range            */

@@ -29,7 +29,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_TEST_LIBRARY: another build of oracle.c to load instead (the
+# sanitizer test runs the pins against an instrumented build)
+_LIB_PATH = os.environ.get("ORACLE_TEST_LIBRARY", os.path.join(_HERE, "liboracle.so"))
 _SRC = os.path.join(_HERE, "oracle.c")
 
 F32, BF16, F64, F16 = 0, 1, 2, 3

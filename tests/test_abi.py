@@ -2,6 +2,7 @@
 point the header declares, and rejects bad host-visible arguments with the
 documented status before any HIP call (so no GPU is touched)."""
 import ctypes
+import importlib.util
 import os
 import re
 
@@ -9,7 +10,20 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lmhead.h")
-LIB = os.path.join(ROOT, "top_reduction_amd", "liblmhead.so")
+# the library under test: the build's, or another build of the same sources
+# (the sanitizer test runs this module against a host-instrumented build)
+LIB = os.environ.get("LMH_TEST_LIBRARY", os.path.join(ROOT, "top_reduction_amd", "liblmhead.so"))
+
+
+def _abi_module():
+    """top_reduction_amd/_abi.py loaded by path: the prototypes without torch."""
+    spec = importlib.util.spec_from_file_location("lmh_abi", os.path.join(ROOT, "top_reduction_amd", "_abi.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+ABI = _abi_module()
 
 OK, NULL, SHAPE, K, DTYPE, ALIGN, WS, HIP = range(8)
 F32, BF16, F16, BAD_DT = 0, 1, 2, 7
@@ -26,8 +40,7 @@ def declared_functions():
 def L():
     if not os.path.exists(LIB):
         pytest.skip("liblmhead.so is not built")
-    import top_reduction_amd
-    return top_reduction_amd.lib()
+    return ABI.load(LIB)
 
 
 def test_header_declares_the_boundary():
@@ -224,8 +237,7 @@ def test_fused_rejects(L):
 
 
 def _head(**kw):
-    import top_reduction_amd as lmh
-    h = lmh.LmhHead()
+    h = ABI.LmhHead()
     h.weight, h.weight_dt, h.weight_ld, h.bits, h.group_size = A, BF16, 64, 0, 0
     h.weight_q, h.weight_q_ld, h.scales, h.biases, h.scales_ld = None, 0, None, None, 0
     h.scale_mode, h.scale = 0, 1.0
@@ -302,8 +314,7 @@ def test_head_struct_layout_matches_c(tmp_path):
     """The ctypes mirror of lmh_head has C's size and field offsets (compiled
     against include/lmhead.h with the host C compiler)."""
     import subprocess
-    import top_reduction_amd as lmh
-    fields = [f for f, _ in lmh.LmhHead._fields_]
+    fields = [f for f, _ in ABI.LmhHead._fields_]
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lmhead.h"\nint main(void){\n'
                    + 'printf("%zu\\n", sizeof(lmh_head));\n'
@@ -312,8 +323,8 @@ def test_head_struct_layout_matches_c(tmp_path):
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
-    assert out[0] == ctypes.sizeof(lmh.LmhHead)
-    assert out[1:] == [getattr(lmh.LmhHead, f).offset for f in fields]
+    assert out[0] == ctypes.sizeof(ABI.LmhHead)
+    assert out[1:] == [getattr(ABI.LmhHead, f).offset for f in fields]
 
 
 def _bitmask(L, **kw):
