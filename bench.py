@@ -49,8 +49,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-    WRITE_SIZE, both with --sections copycal,head,headq) into HBM bytes per
-    launch.
+    WRITE_SIZE, both with --sections copycal,reduce,head,headq,fused) into HBM
+    bytes per launch.
     Each counter is scaled by what it reads for the plain elementwise copy of
     known size that the copycal section runs."""
     import csv
@@ -77,8 +77,15 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
               "head_stream_bf16": ("k_head_stream<", "head.hip", 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
               "head_pipe_bf16": ("k_head_pipe<3, 2, 4, false, false, true>", "pipe.hip",
                                  151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
-              "head_tiled_bf16": ("k_head_tiled64<false, 8>", "head.hip",
-                                  151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4)}
+              "head_tiled_bf16": ("k_head_tiled64<false, 8, false>", "head.hip",
+                                  151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4),
+              # the prompt chunks' tiled head with the reduction's first pass in
+              # its epilogue (Llama-3-8B shape, 256 rows): W, hidden rows, fp32
+              # logits, and per block an 8-byte partial and a 4-byte key
+              "head_tiled_epilogue_bf16": ("k_head_tiled64<false, 8, true>", "head.hip",
+                                           128256 * 4096 * 2 + 256 * 4096 * 2 + 256 * 128256 * 4
+                                           + 256 * 2004 * 12),
+              "reduce_stage2_blocks": ("k_stage2<0, 8, true>", "reduce.hip", None)}
     for bits in (4, 8):
         qbytes = 151936 * 1024 * bits // 8 + 151936 * 16 * 4
         wanted[f"head_stream_q{bits}"] = (f"k_head_stream_q<3, 1, {bits}, ", "head.hip",

@@ -317,6 +317,72 @@ def test_selection_on_ordered_rows(k):
     assert torch.equal(a.topk_logprobs.view(torch.int32), cat("topk_logprobs").view(torch.int32))
 
 
+def _fp32_bin_rows(V, seed):
+    """fp32 rows for the threshold search, which first bins the block-max
+    keys on their top 16 bits: 200 blocks with distinct maxima inside one
+    16-bit bin above the rest (more than the gather holds: the search goes
+    on inside the bin); 300 blocks tied exactly at the top (the same, with
+    the tie cut by block index); five finite blocks in a row of -inf (the
+    K-th key is -inf's, a bin that does not decode to a finite edge); 100
+    distinct maxima in one bin (all of that bin's blocks kept, more than K);
+    rows near -60 (negative keys); rows of values near 1e-30 with exact zeros of both
+    signs; a rising ramp; plain normal rows."""
+    g = synth.rng(seed)
+    x = synth.normal_f32(g, (256, V), 2.0)
+    nb = -(-V // 64)
+    step = np.float32(2.0 ** -19)                   # 16-bit bins at 10.0 are 2^-4 wide
+    for r in range(256):
+        kind = r % 8
+        if kind == 1:
+            blocks = g.choice(nb - 1, size=200, replace=False)
+            x[r, blocks * 64 + 5] = np.float32(10.0) + step * np.arange(200, dtype=np.float32)
+        elif kind == 2:
+            blocks = g.choice(nb - 1, size=300, replace=False)
+            x[r, blocks * 64 + 11] = 12.0
+        elif kind == 3:
+            keep = g.choice(nb - 1, size=5, replace=False)
+            row = np.full(V, -np.inf, dtype=np.float32)
+            for b in keep:
+                row[b * 64:b * 64 + 64] = x[r, b * 64:b * 64 + 64]
+            x[r] = row
+        elif kind == 4:
+            blocks = g.choice(nb - 1, size=100, replace=False)
+            x[r, blocks * 64 + 30] = np.float32(10.0) + step * g.permutation(100).astype(np.float32)
+        elif kind == 5:
+            x[r] = np.float32(-60.0) + x[r]          # |lse| stays where an fp32 ulp is below 1e-5
+        elif kind == 6:
+            x[r] = x[r] * np.float32(1e-30)
+            x[r, ::97] = 0.0
+            x[r, 1::89] = -0.0
+        elif kind == 7:
+            x[r] = np.linspace(-30.0, 30.0, V, dtype=np.float32) + np.float32(0.001) * x[r]
+    return x
+
+
+@pytest.mark.parametrize("k", [1, 20, 128])
+def test_fp32_threshold_bins(k):
+    """fp32 logits of the Llama-3-8B prompt chunk shape (256 x 128,256) on
+    rows built for each branch of the threshold search: oracle parity on
+    every row, and bitwise equality between the one-workgroup-per-row path
+    and the split path."""
+    V = 128_256
+    print(f"fp32 threshold bins k={k}", flush=True)
+    data = _fp32_bin_rows(V, 8100 + k)
+    g = synth.rng(8150 + k)
+    sel = g.integers(0, V, size=256).astype(np.int32)
+    t = f32_tensor(data)
+    if torch.cuda.get_device_properties(0).multi_processor_count <= 256:
+        assert lmh.reduce_row_path(256, V, k)
+    a = lmh.logprob_reduce(t, i32_tensor(sel), k)
+    check_reduce(a, data, sel, k, *oracle.reduce(data, sel, k))
+    parts = [lmh.logprob_reduce(t[i:i + 100], i32_tensor(sel[i:i + 100]), k) for i in range(0, 256, 100)]
+    torch.cuda.synchronize()
+    cat = lambda f: torch.cat([getattr(p, f) for p in parts])
+    assert torch.equal(a.lse.view(torch.int32), cat("lse").view(torch.int32))
+    assert torch.equal(a.topk_ids, cat("topk_ids"))
+    assert torch.equal(a.topk_logprobs.view(torch.int32), cat("topk_logprobs").view(torch.int32))
+
+
 @pytest.mark.parametrize("case", ["chunk_bf16", "ragged_bf16", "f16", "f32"])
 def test_full_vocabulary_logprobs(case):
     """k = -1: every token's logprob (openinfer issue #719, Acceptance

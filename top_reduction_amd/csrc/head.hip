@@ -966,7 +966,7 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
                 f32x4 val = *reinterpret_cast<const f32x4*>(&stg[rr * 68 + cl]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) val[e] = scale_logit(val[e], p.scale_mode, p.scale);
-                if constexpr (FUSED) block_partial(p, r, sIdx[rl] >= 0, v, val, (n0 + wn) >> 6);
+                if constexpr (FUSED) block_partial(p, r, sIdx[rl] >= 0, v, val, (n0 + wn + cb * 64) >> 6);
                 if (r < p.R) {
                     const bool valid = sIdx[rl] >= 0;
                     if (vec_ok && v + 4 <= p.V) {

@@ -509,6 +509,14 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wtot, uint
 //    smallest per-thread maximum (at least K keys reach it whenever K threads
 //    hold blocks), finished by a 256-bin LDS histogram; the kept blocks are
 //    all keys above T plus the lowest-indexed keys equal to T, K in all;
+//  * the search runs on the keys' top 16 bits (all of a 16-bit key). For
+//    fp32 logits, when the blocks with keys at or above the 16-bit bin of
+//    the K-th key fit the candidate list whole (at most 2K blocks, 128 at
+//    most) and that bin holds finite values, T is the bin's
+//    lower edge and all of those blocks are kept (K or more); otherwise a
+//    second search inside the bin on full keys gives the exact T. Every
+//    bin-wide search step is a barrier round, so this skips the several
+//    rounds that full 32-bit keys take to narrow;
 //  * one round of 16-byte loads gathers the kept blocks; entries with key
 //    >= T become candidates, compacted by a prefix scan;
 //  * with PF (16-bit logits), each thread loads the block holding its own
@@ -681,8 +689,15 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
     int phase = 0;
     int nblk;
     uint32_t T = 0;                                     // key threshold (0: keep everything)
+    bool coarse = false;                                // fp32: every block of T's 16-bit bin and above kept
     if (K <= nb) {
-        const int ksh = w16(DT) ? 16 : 0;
+        // The search runs on the top 16 bits of every key first (the whole
+        // key for 16-bit logits). For fp32 logits that gives the 16-bit bin
+        // holding the K-th key; when the blocks of that bin and above are
+        // few, all of them are kept (a superset of the K blocks, whose
+        // entries the candidate filter and the rank below still order
+        // exactly), else the search goes on inside the bin on full keys.
+        constexpr int ksh = 16;
         // Largest t with count(key >= t) >= K; count(>= lo) >= K > count(>= hi).
         // one max-reduction gives the maximum and (complemented) two minima:
         // of all keys, and of the per-thread maxima of threads holding blocks
@@ -715,74 +730,93 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
             block_reduce<1, 3, NT>(mm, sh.sred, phase);
         }
         const int nth = (nb + KPT - 1) / KPT;           // threads holding blocks
-        uint64_t lo = (uint64_t)((K <= nth ? ~mm[2] : ~mm[1]) >> ksh);
-        uint64_t hi = (uint64_t)(mm[0] >> ksh) + 1;
-        uint32_t c_hi = 0u;                              // count(key >= hi)
-        // 5-way narrowing with exact counts until at most 256 key values remain
-        while (hi - lo > kHistBins) {
-            const uint64_t span = hi - lo;
-            uint32_t t[4];
+        // one search over key values [lo, hi) shifted right by `shift`:
+        // sh.thr = {T << shift, count(key > T), count(key == T)} in shifted keys
+        auto search = [&](uint64_t lo, uint64_t hi, uint32_t c_hi, int shift) {
+            // 5-way narrowing with exact counts until at most 256 key values remain
+            while (hi - lo > kHistBins) {
+                const uint64_t span = hi - lo;
+                uint32_t t[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint64_t d = (span * (uint64_t)(i + 1)) / 5;
-                t[i] = (uint32_t)(lo + (d < 1 ? 1 : d));
-            }
-            uint32_t c[4] = {0u, 0u, 0u, 0u};
+                for (int i = 0; i < 4; ++i) {
+                    const uint64_t d = (span * (uint64_t)(i + 1)) / 5;
+                    t[i] = (uint32_t)(lo + (d < 1 ? 1 : d));
+                }
+                uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int j = 0; j < KPT; ++j) {
-                const uint32_t kv = kr[j] >> ksh;
+                for (int j = 0; j < KPT; ++j) {
+                    const uint32_t kv = kr[j] >> shift;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) c[i] += (kv >= t[i]) ? 1u : 0u;
-            }
-            uint32_t pk[2] = {c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
-            block_reduce<0, 2, NT>(pk, sh.sred, phase);
-            const uint32_t cc[4] = {pk[0] & 0xFFFFu, pk[0] >> 16, pk[1] & 0xFFFFu, pk[1] >> 16};
+                    for (int i = 0; i < 4; ++i) c[i] += (kv >= t[i]) ? 1u : 0u;
+                }
+                uint32_t pk[2] = {c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
+                block_reduce<0, 2, NT>(pk, sh.sred, phase);
+                const uint32_t cc[4] = {pk[0] & 0xFFFFu, pk[0] >> 16, pk[1] & 0xFFFFu, pk[1] >> 16};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (cc[i] >= (uint32_t)K) {
-                    if (t[i] > lo) lo = t[i];
-                } else if (t[i] < hi) {
-                    hi = t[i];
-                    c_hi = cc[i];
+                for (int i = 0; i < 4; ++i) {
+                    if (cc[i] >= (uint32_t)K) {
+                        if (t[i] > lo) lo = t[i];
+                    } else if (t[i] < hi) {
+                        hi = t[i];
+                        c_hi = cc[i];
+                    }
                 }
             }
-        }
-        // histogram of the keys in [lo, hi), then a suffix scan in wave 0:
-        // T is the largest key value v with count(key >= v) >= K
+            // histogram of the keys in [lo, hi) (cleared before the call),
+            // then a suffix scan in wave 0: T is the largest key value v with
+            // count(key >= v) >= K
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const uint64_t kv = kr[j] >> shift;
+                if (kv >= lo && kv < hi) atomicAdd(&sh.hist[(int)(kv - lo)], 1u);
+            }
+            __syncthreads();
+            if (tid < 64) {
+                const uint32_t h0 = sh.hist[4 * tid], h1 = sh.hist[4 * tid + 1];
+                const uint32_t h2 = sh.hist[4 * tid + 2], h3 = sh.hist[4 * tid + 3];
+                const uint32_t sum4 = h0 + h1 + h2 + h3;
+                const uint32_t incl = wave_scan<0>(sum4);
+                const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+                // count(key >= bin 4l + 4) and the four suffix counts inside the lane
+                const uint32_t above = c_hi + total - incl;
+                const uint32_t s3 = above + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+                const uint32_t k = (uint32_t)K;
+                int b = -1;
+                uint32_t gt = 0u, eqc = 0u;
+                if (s3 >= k && above < k) { b = 4 * tid + 3; gt = above; eqc = h3; }
+                else if (s2 >= k && s3 < k) { b = 4 * tid + 2; gt = s3; eqc = h2; }
+                else if (s1 >= k && s2 < k) { b = 4 * tid + 1; gt = s2; eqc = h1; }
+                else if (s0 >= k && s1 < k) { b = 4 * tid; gt = s1; eqc = h0; }
+                if (b >= 0) {
+                    sh.thr[0] = (uint32_t)((lo + (uint64_t)b) << shift);
+                    sh.thr[1] = gt;
+                    sh.thr[2] = eqc;
+                }
+            }
+            __syncthreads();
+        };
         if constexpr (!PRE) {
             if (tid < kHistBins) sh.hist[tid] = 0u;
             __syncthreads();
         }
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const uint64_t kv = kr[j] >> ksh;
-            if (kv >= lo && kv < hi) atomicAdd(&sh.hist[(int)(kv - lo)], 1u);
-        }
-        __syncthreads();
-        if (tid < 64) {
-            const uint32_t h0 = sh.hist[4 * tid], h1 = sh.hist[4 * tid + 1];
-            const uint32_t h2 = sh.hist[4 * tid + 2], h3 = sh.hist[4 * tid + 3];
-            const uint32_t sum4 = h0 + h1 + h2 + h3;
-            const uint32_t incl = wave_scan<0>(sum4);
-            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-            // count(key >= bin 4l + 4) and the four suffix counts inside the lane
-            const uint32_t above = c_hi + total - incl;
-            const uint32_t s3 = above + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
-            const uint32_t k = (uint32_t)K;
-            int b = -1;
-            uint32_t gt = 0u, eqc = 0u;
-            if (s3 >= k && above < k) { b = 4 * tid + 3; gt = above; eqc = h3; }
-            else if (s2 >= k && s3 < k) { b = 4 * tid + 2; gt = s3; eqc = h2; }
-            else if (s1 >= k && s2 < k) { b = 4 * tid + 1; gt = s2; eqc = h1; }
-            else if (s0 >= k && s1 < k) { b = 4 * tid; gt = s1; eqc = h0; }
-            if (b >= 0) {
-                sh.thr[0] = (uint32_t)((lo + (uint64_t)b) << ksh);
-                sh.thr[1] = gt;
-                sh.thr[2] = eqc;
+        search((uint64_t)((K <= nth ? ~mm[2] : ~mm[1]) >> ksh), (uint64_t)(mm[0] >> ksh) + 1, 0u, ksh);
+        T = sh.thr[0];
+        if constexpr (!w16(DT)) {
+            // the bin's blocks and those above, when all their entries fit
+            // the candidate list and the bin holds finite values only (its
+            // lower edge decodes to a finite float)
+            const uint32_t bin = T >> 16;
+            const uint32_t nkeep = sh.thr[1] + sh.thr[2];
+            if (nkeep <= (uint32_t)MAXBLK && nkeep * kBlock <= (uint32_t)cap && bin >= 0x0080u && bin < 0xFF80u) {
+                coarse = true;
+            } else {
+                const uint32_t c_above = sh.thr[1];
+                if (tid < kHistBins) sh.hist[tid] = 0u;   // wave 0's scan read it before the barrier
+                __syncthreads();
+                search((uint64_t)T, (uint64_t)T + 0x10000u, c_above, 0);
+                T = sh.thr[0];
             }
         }
-        __syncthreads();
-        T = sh.thr[0];
         if constexpr (PF) if (K <= capb && T != 0u) {   // T == 0 (all-NaN blocks) would keep empty slots
             // the candidate blocks are staged in LDS (sh.nblk counts the
             // slots), then filtered by all threads. They are the blocks with
@@ -880,7 +914,7 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
             return;
         }
         const int need = K - (int)sh.thr[1];             // blocks equal to T that are kept
-        const bool all_ties = (uint32_t)need == sh.thr[2];
+        const bool all_ties = coarse || (uint32_t)need == sh.thr[2];
         if (all_ties) {
             // every key >= T is kept: placement order does not matter
 #pragma unroll
@@ -915,7 +949,7 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
                 }
             }
         }
-        nblk = min(K, MAXBLK);
+        nblk = coarse ? (int)(sh.thr[1] + sh.thr[2]) : min(K, MAXBLK);
     } else {
         for (int b = tid; b < nb; b += NT) sh.blk[b] = b;
         nblk = nb;
@@ -1106,43 +1140,32 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
         sh.nblk = 0;
     }
 
-    // this thread's block keys, blocks [b0, b0 + KPT); 0 past nb
+    // this thread's block keys, blocks [b0, b0 + KPT): the raw 32-bit words
+    // now (two 16-bit keys per word for 16-bit logits), unpacked after the
+    // partials' loads are issued
     const int b0 = tid * KPT;
-    uint32_t kr[KPT];
+    constexpr int KW = w16(DT) ? KPT / 2 : KPT;
+    uint32_t kw[KW];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) kr[j] = 0u;
+    for (int j = 0; j < KW; ++j) kw[j] = 0u;
     if (K > 0 && K <= nb && b0 < nb) {
-        if (w16(DT)) {
-            const uint16_t* kp = reinterpret_cast<const uint16_t*>(keys) + row * kld + b0;
-            if (KPT == 4) {
-                const uint2 q = *reinterpret_cast<const uint2*>(kp);
-                const uint32_t wq[2] = {q.x, q.y};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kr[j] = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
-            } else {
-#pragma unroll
-                for (int c = 0; c < KPT / 8; ++c) {
-                    const u32x4 q = reinterpret_cast<const u32x4*>(kp)[c];
-                    const uint32_t wq[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        kr[c * 8 + j] = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
-                }
-            }
+        const uint32_t* kp = w16(DT)
+            ? reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(keys) + row * kld + b0)
+            : reinterpret_cast<const uint32_t*>(keys) + row * kld + b0;
+        if constexpr (KW == 2) {
+            const uint2 q = *reinterpret_cast<const uint2*>(kp);
+            kw[0] = q.x;
+            kw[1] = q.y;
         } else {
-            const uint32_t* kp = reinterpret_cast<const uint32_t*>(keys) + row * kld + b0;
 #pragma unroll
-            for (int c = 0; c < KPT / 4; ++c) {
+            for (int c = 0; c < KW / 4; ++c) {
                 const u32x4 q = reinterpret_cast<const u32x4*>(kp)[c];
-                kr[c * 4 + 0] = q.x;
-                kr[c * 4 + 1] = q.y;
-                kr[c * 4 + 2] = q.z;
-                kr[c * 4 + 3] = q.w;
+                kw[c * 4 + 0] = q.x;
+                kw[c * 4 + 1] = q.y;
+                kw[c * 4 + 2] = q.z;
+                kw[c * 4 + 3] = q.w;
             }
         }
-#pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if (b0 + j >= nb) kr[j] = 0u;
     }
 
     // the selected token's id, issued now (thread 64: off the lse wave)
@@ -1152,10 +1175,20 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
 
     if constexpr (BLOCKS) {
         __shared__ float2 swave[kThreads / 64];
+        // rounds of KPT partials per thread, all loaded before the first
+        // merge of the round (one round when the row has at most KPT * 256
+        // blocks); the merge order is the loop's ascending i either way
         float m = kNegInf, sm = 0.f;
-        for (int i = tid; i < splits; i += kThreads) {
-            const float2 pp = part[row * splits + i];
-            lse_merge(m, sm, pp.x, pp.y);
+        for (int i0 = tid; i0 < splits; i0 += KPT * kThreads) {
+            float2 pp[KPT];
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const int i = i0 + j * kThreads;
+                pp[j] = i < splits ? part[row * splits + i] : make_float2(kNegInf, 0.f);
+            }
+#pragma unroll
+            for (int j = 0; j < KPT; ++j)
+                if (i0 + j * kThreads < splits) lse_merge(m, sm, pp[j].x, pp[j].y);
         }
         lse_tree64(m, sm);
         if ((tid & 63) == 0) swave[tid >> 6] = make_float2(m, sm);
@@ -1173,11 +1206,21 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
         // logsumexp: lanes 0..15 of wave 0 merge their groups' partials, then
         // the wave merges the groups
         if (tid < 64) {
+            // a group's partials in rounds of four, each round's loads issued
+            // before its first merge (merge order: ascending i)
+            constexpr int kRound = 4;
             float m = kNegInf, sm = 0.f;
             if (tid < kGroups)
-                for (int i = tid; i < splits; i += kGroups) {
-                    const float2 pp = part[row * splits + i];
-                    lse_merge(m, sm, pp.x, pp.y);
+                for (int i0 = tid; i0 < splits; i0 += kRound * kGroups) {
+                    float2 pp[kRound];
+#pragma unroll
+                    for (int j = 0; j < kRound; ++j) {
+                        const int i = i0 + j * kGroups;
+                        pp[j] = i < splits ? part[row * splits + i] : make_float2(kNegInf, 0.f);
+                    }
+#pragma unroll
+                    for (int j = 0; j < kRound; ++j)
+                        if (i0 + j * kGroups < splits) lse_merge(m, sm, pp[j].x, pp[j].y);
                 }
             const float l = lse_tree16(m, sm);
             if (tid == 0) {
@@ -1185,6 +1228,13 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
                 lse_out[row] = l;
             }
         }
+    }
+    // the keys, 0 past nb
+    uint32_t kr[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        kr[j] = !w16(DT) ? kw[j] : ((j & 1) ? (kw[j >> 1] & 0xFFFF0000u) : (kw[j >> 1] << 16));
+        if (b0 + j >= nb) kr[j] = 0u;
     }
     __syncthreads();
     const float lse = sh.lse;
@@ -1509,17 +1559,20 @@ hipError_t launch_stage2_dt(const ReducePlan& p, const ReduceArgs& a, hipStream_
     }
 }
 
+// Candidate entries a row's selection can hold: up to 2K candidate blocks
+// (at most 128), so that the prefetched-candidate path of 16-bit logits also
+// takes blocks tied at T, and fp32 logits keep a whole 16-bit bin of blocks.
+int32_t cand_cap(const ReducePlan& p) {
+    if (p.k <= 0) return 0;
+    return std::min(std::max(p.k, std::min(2 * p.k, kMaxCandidates / kBlock)), p.nb) * kBlock;
+}
+
 // candidates and LDS of the second kernel (fp32 logits: no staging)
 void stage2_sizes(const ReducePlan& p, int32_t dt, int32_t& cap, size_t& lds) {
     cap = 0;
     lds = 0;
     if (p.k > 0) {
-        // 16-bit logits: room for up to 2K candidate blocks (at most 128) and
-        // their staging slots, so that the prefetched-candidate path also
-        // takes blocks tied at T
-        const int32_t kb2 = w16(dt) ? std::min(std::max(p.k, std::min(2 * p.k, kMaxCandidates / kBlock)), p.nb)
-                                    : std::min(p.k, p.nb);
-        cap = kb2 * kBlock;
+        cap = cand_cap(p);
         // (the staging path exists only when K <= nb)
         const size_t stage = w16(dt) && p.k <= p.nb ? ((size_t)kThreads * kBlock + (size_t)cap) * 2 : 0;
         lds = ((size_t)cap + (size_t)((p.k + 1) & ~1)) * sizeof(uint64_t) + stage;
@@ -1544,17 +1597,7 @@ hipError_t launch_reduce_stage2(const ReducePlan& p, const ReduceArgs& a, hipStr
     const void* keys = ws + p.keys_off;
     int32_t cap = 0;
     size_t lds = 0;
-    if (p.k > 0) {
-        // 16-bit logits: room for up to 2K candidate blocks (at most 128) and
-        // their staging slots, so that the prefetched-candidate path also
-        // takes blocks tied at T
-        const int32_t kb2 = w16(a.dt) ? std::min(std::max(p.k, std::min(2 * p.k, kMaxCandidates / kBlock)), p.nb)
-                                      : std::min(p.k, p.nb);
-        cap = kb2 * kBlock;
-        // (the staging path exists only when K <= nb)
-        const size_t stage = w16(a.dt) && p.k <= p.nb ? ((size_t)kThreads * kBlock + (size_t)cap) * 2 : 0;
-        lds = ((size_t)cap + (size_t)((p.k + 1) & ~1)) * sizeof(uint64_t) + stage;
-    }
+    stage2_sizes(p, a.dt, cap, lds);
     if (a.dt == kDtBf16) return launch_stage2_dt<kDtBf16>(p, a, s, part, keys, cap, lds);
     if (a.dt == kDtF16) return launch_stage2_dt<kDtF16>(p, a, s, part, keys, cap, lds);
     return launch_stage2_dt<kDtF32>(p, a, s, part, keys, cap, lds);
@@ -1610,11 +1653,7 @@ hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s
     int32_t cap = 0;
     size_t lds = 0;
     if (p.k > 0) {
-        // 16-bit logits: room for up to 2K candidate blocks (at most 128), so
-        // that the prefetched-candidate path also takes blocks tied at T
-        const int32_t kb2 = w16(a.dt) ? std::min(std::max(p.k, std::min(2 * p.k, kMaxCandidates / kBlock)), p.nb)
-                                      : std::min(p.k, p.nb);
-        cap = kb2 * kBlock;
+        cap = cand_cap(p);
         const size_t kbytes = (size_t)p.kpt * kThreads * (w16(a.dt) ? 2 : 4);
         // staged blocks: one per selection thread, then the candidate blocks
         // (the staging path exists only when K <= nb)
