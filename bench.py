@@ -334,8 +334,26 @@ def main():
         m = timer.loop(f, steps, warmup)
         result["decode"] = {"workload": "32 x 151936 bf16 decode rows, K=5", "us": round(m * 1e3, 2),
                             "rows_per_s": round(32 / (m * 1e-3)),
-                            "gbps": round(32 * synth.VOCAB_QWEN3 * 2 / (m * 1e-3) / 1e9, 1)}
+                            "gbps": round(32 * synth.VOCAB_QWEN3 * 2 / (m * 1e-3) / 1e9, 1),
+                            "path": "split: streaming launch + selection launch"}
         log(f"decode: {m * 1e3:.1f} us")
+        # K = 1 and K = 0: the two launches (logprob_reduce) against the single
+        # launch the no-workspace entry point takes for them
+        for kk in (1, 0):
+            def two(t, kk=kk):
+                return L.logprob_reduce(vp(t), lmh.LMH_BF16, 32, synth.VOCAB_QWEN3, synth.VOCAB_QWEN3, vp(s), kk,
+                                        vp(o[0]), vp(o[1]), vp(o[2]) if kk else None,
+                                        vp(o[3]) if kk else None, vp(ws), ws.numel(), None, stream)
+
+            def one(t, kk=kk):
+                return L.logprob_reduce_noalloc(vp(t), lmh.LMH_BF16, 32, synth.VOCAB_QWEN3, synth.VOCAB_QWEN3,
+                                                vp(s), kk, vp(o[0]), vp(o[1]), vp(o[2]) if kk else None,
+                                                vp(o[3]) if kk else None, None, stream)
+            assert two(copies[0]) == 0 and one(copies[0]) == 0
+            m2 = timer.loop([lambda t=t: two(t) for t in copies], steps, warmup)
+            m1 = timer.loop([lambda t=t: one(t) for t in copies], steps, warmup)
+            result["decode"][f"k{kk}"] = {"split_us": round(m2 * 1e3, 2), "single_launch_us": round(m1 * 1e3, 2)}
+            log(f"decode K={kk}: two launches {m2 * 1e3:.1f} us, single launch {m1 * 1e3:.1f} us")
         del copies
 
     # ------------------------------------------------------------------

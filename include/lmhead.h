@@ -198,16 +198,23 @@ lmh_status logprob_reduce(
  * logprob_reduce_noalloc -- logprob_reduce for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops and
  * harnesses that forbid hipMalloc. There is no workspace argument; the
- * scratch lives in a static device array of LMH_NOALLOC_SCRATCH_BYTES per
- * GPU that the library holds until the process ends (its device address is
- * looked up on the first call on each device, with that device current).
+ * scratch (LMH_NOALLOC_SCRATCH_BYTES of workspace plus one 32-bit counter
+ * per row for up to 4096 rows) lives in a static device array per GPU that
+ * the library holds until the process ends (its device address is looked up
+ * on the first call on each device, with that device current, and that call
+ * also enqueues a small kernel on `stream` that clears the counters).
  * The call allocates and frees nothing.
  * Arguments, outputs, results (bitwise) and status codes are those of
  * logprob_reduce; a shape whose logprob_reduce_workspace_size exceeds
  * LMH_NOALLOC_SCRATCH_BYTES returns LMH_ERR_WORKSPACE before any HIP call.
- * All calls on one GPU share that GPU's array: calls that overlap on one GPU
- * (other streams, other host threads) race and must be ordered by the
- * caller. Nothing in the array needs clearing between calls.
+ * Few rows (decode steps, openinfer issue #719, Description: rows that leave
+ * most compute units idle) with K <= 1 and vocab <= 262,144 take a single
+ * launch: each row is spread over several workgroups that each reduce a
+ * slice to its exact top-K, and the last workgroup of the row to arrive (a
+ * per-row counter in the array, back at zero when the launch ends) merges
+ * the slices (larger K take the two launches, which measured faster there). All calls on one GPU share that GPU's array: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller. Nothing in the array needs clearing between calls.
  */
 #define LMH_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
 lmh_status logprob_reduce_noalloc(
@@ -515,6 +522,24 @@ lmh_status lmh_debug_logprobs_ex(
     const uint32_t* vocab_mask, int64_t vocab_mask_ld,
     void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream,
     int32_t epilogue);
+
+/*
+ * lmh_debug_reduce_single -- logprob_reduce through the single-launch path
+ * that logprob_reduce_noalloc takes for few rows, at any k it supports
+ * (-1 <= k <= 32; logprob_reduce_noalloc takes it only for k <= 1, where it
+ * measured faster than the two launches), on a caller workspace (the size
+ * logprob_reduce_workspace_size gives) and caller counters: 4096 32-bit
+ * words, zero before the first call, which every call leaves zero. Shapes
+ * the path does not take (rows that fill the compute units, k > 32, vocab >
+ * 64 * 4096 or rows > 4096) return LMH_ERR_SHAPE; counters NULL returns
+ * LMH_ERR_NULL. Results are bitwise those of logprob_reduce. Calls sharing
+ * counters must not overlap.
+ */
+lmh_status lmh_debug_reduce_single(
+    const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab, int64_t logits_ld,
+    const int32_t* selected_ids, int32_t k,
+    float* lse, float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+    void* workspace, size_t workspace_bytes, uint32_t* counters, int32_t* device_error, void* stream);
 
 /*
  * lmh_debug_reduce_stage1 -- only the streaming pass of logprob_reduce

@@ -208,6 +208,26 @@ def test_reduce_noalloc_limit(L):
     assert _reduce_noalloc(L, rows=0, logits=None, lse=None, slp=None, ids=None, lps=None) == OK
 
 
+def _reduce_single(L, **kw):
+    a = dict(logits=A, dt=BF16, rows=32, vocab=151936, ld=151936, sel=A, k=5, lse=A, slp=A,
+             ids=A, lps=A, ws=A, wsb=1 << 30, cnt=A, err=None)
+    a.update(kw)
+    return L.lmh_debug_reduce_single(a["logits"], a["dt"], a["rows"], a["vocab"], a["ld"], a["sel"], a["k"],
+                                     a["lse"], a["slp"], a["ids"], a["lps"], a["ws"], a["wsb"], a["cnt"],
+                                     a["err"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(logits=None), NULL), (dict(lse=None), NULL), (dict(dt=BAD_DT), DTYPE),
+    (dict(logits=A + 8), ALIGN), (dict(k=-2), K), (dict(ws=None), WS), (dict(wsb=16), WS),
+    (dict(cnt=None), NULL),
+])
+def test_reduce_single_rejects(L, kw, want):
+    """The forcing entry point of the single-launch path applies
+    logprob_reduce's rules, then needs its counters, before any HIP call."""
+    assert _reduce_single(L, **kw) == want
+
+
 def test_workspace_sizes(L):
     for rows, V, k in [(256, 248320, 128), (32, 151936, 5), (1, 1000, 0), (0, 64, 0)]:
         n = L.logprob_reduce_workspace_size(rows, V, k)

@@ -48,8 +48,9 @@ def _same(a, b):
 def test_noalloc_matches_logprob_reduce():
     L = lmh.lib()
     dev = torch.device("cuda:0")
-    # call 1: 32 decode rows x 151,936 (the two-launch path, which uses the
-    # scratch); call 2: a smaller input, 5 rows x 40,000 with K = 3
+    # call 1: 32 decode rows x 151,936; call 2: a smaller input, 5 rows x
+    # 40,000 with K = 3 (both take the single-launch path, which uses the
+    # scratch and its per-row counters)
     bits1, sel1 = synth.decode_logits(8100, sel_mode="uniform")
     g = synth.rng(8101)
     bits2 = synth.normal_bf16(g, (5, 40000), 2.0)

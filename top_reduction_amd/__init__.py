@@ -255,6 +255,28 @@ def logprob_reduce_noalloc(logits: torch.Tensor, selected_ids: Optional[torch.Te
     return out
 
 
+def reduce_single(logits: torch.Tensor, selected_ids: Optional[torch.Tensor], k: int,
+                  counters: torch.Tensor) -> Reduction:
+    """logprob_reduce through the single-launch few-row path at any k it
+    supports (lmh_debug_reduce_single); `counters` is an int32 tensor of 4096
+    zeros that every call leaves zero."""
+    L = lib()
+    R, V, ld = _matrix(logits, "logits")
+    sel = _i32(selected_ids, "selected_ids")
+    dev = logits.device
+    ws = workspace(L.logprob_reduce_workspace_size(R, V, k), dev)
+    ids, lps = _topk_out(R, V, k, dev)
+    out = Reduction(torch.empty(R, dtype=torch.float32, device=dev),
+                    torch.empty(R, dtype=torch.float32, device=dev) if sel is not None else None,
+                    ids, lps, torch.zeros(1, dtype=torch.int32, device=dev))
+    pi, pl = _topk_ptrs(k, out.topk_ids, out.topk_logprobs)
+    st = L.lmh_debug_reduce_single(_ptr(logits), _dt(logits), R, V, ld, _ptr(sel), int(k),
+                                   _ptr(out.lse), _ptr(out.selected_logprob), pi, pl, _ptr(ws), ws.numel(),
+                                   _ptr(counters), _ptr(out.device_error), _stream())
+    _check(st, "lmh_debug_reduce_single")
+    return out
+
+
 def reduce_stage1(logits: torch.Tensor, k: int, ws: torch.Tensor) -> None:
     """Only the streaming pass of logprob_reduce (for timing that kernel)."""
     L = lib()

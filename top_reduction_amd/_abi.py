@@ -48,6 +48,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.logprob_reduce_workspace_size.restype = sz
     L.logprob_reduce.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p, p, sz, p, p]
     L.logprob_reduce_noalloc.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p, p, p]
+    L.lmh_debug_reduce_single.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, p, p, p, p, sz, p, p, p]
     L.lmh_debug_reduce_stage1.argtypes = [p, ctypes.c_int, i64, i64, i64, i32, p, sz, p]
     L.lmh_debug_reduce_path.argtypes = [i64, i64, i32]
     L.lmh_debug_reduce_path.restype = i32
@@ -70,7 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.lmh_status_string.argtypes = [ctypes.c_int]
     L.lmh_status_string.restype = ctypes.c_char_p
     for name in ("lmhead_gather_project", "lmh_debug_gather_project", "logprob_reduce",
-                 "logprob_reduce_noalloc",
+                 "logprob_reduce_noalloc", "lmh_debug_reduce_single",
                  "lmh_debug_reduce_stage1", "lmhead_logprobs", "lmhead_gather_project_q",
                  "lmh_debug_gather_project_q", "lmhead_logprobs_q", "lmhead_gather_project_ex",
                  "lmhead_logprobs_ex", "lmh_debug_logprobs_ex", "lmhead_selfcheck", "lmhead_apply_bitmask"):

@@ -333,12 +333,15 @@ lmh_status reduce_validate(const void* logits, lmh_dtype logits_dt, int64_t rows
 lmh_status reduce_enqueue(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
                           int64_t logits_ld, const int32_t* selected_ids, int32_t k, float* lse,
                           float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
-                          void* workspace, int32_t* device_error, hipStream_t s) {
+                          void* workspace, int32_t* device_error, hipStream_t s, uint32_t* single_counters,
+                          int single) {
     const int32_t kr = k > 0 ? k : 0;   // K = -1: lse first, then every logprob
     const ReducePlan p = plan_reduce(rows, vocab, kr);
     ReduceArgs a{logits, (int32_t)logits_dt, logits_ld, selected_ids, lse, selected_logprob,
                  kr > 0 ? topk_ids : nullptr, kr > 0 ? topk_logprobs : nullptr, workspace, device_error};
-    const lmh_status st = from_hip(launch_reduce(p, a, s));
+    const bool one = single_counters != nullptr && single_ok(p) && single_bytes(p) <= p.bytes &&
+                     (single == 1 || p.k <= kSingleRouteK);
+    const lmh_status st = from_hip(one ? launch_reduce_single(p, a, single_counters, s) : launch_reduce(p, a, s));
     if (st != LMH_OK || k != LMH_K_FULL) return st;
     return from_hip(launch_full_logprobs(logits, (int32_t)logits_dt, rows, vocab, logits_ld, lse, topk_logprobs, s));
 }
@@ -448,6 +451,24 @@ lmh_status logprob_reduce(const void* logits, lmh_dtype logits_dt, int64_t rows,
     return lmh::reduce_enqueue(logits, logits_dt, rows, vocab, logits_ld, selected_ids, k, lse,
                                selected_logprob, topk_ids, topk_logprobs, workspace, device_error,
                                static_cast<hipStream_t>(stream));
+}
+
+lmh_status lmh_debug_reduce_single(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
+                                   int64_t logits_ld, const int32_t* selected_ids, int32_t k, float* lse,
+                                   float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
+                                   void* workspace, size_t workspace_bytes, uint32_t* counters,
+                                   int32_t* device_error, void* stream) {
+    size_t need = 0;
+    const lmh_status st = lmh::reduce_validate(logits, logits_dt, rows, vocab, logits_ld, selected_ids, k,
+                                               lse, selected_logprob, topk_ids, topk_logprobs, &need);
+    if (st != LMH_OK) return st;
+    if (rows == 0) return LMH_OK;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return LMH_ERR_WORKSPACE;
+    if (!counters) return LMH_ERR_NULL;
+    if (!single_ok(plan_reduce(rows, vocab, k > 0 ? k : 0))) return LMH_ERR_SHAPE;
+    return lmh::reduce_enqueue(logits, logits_dt, rows, vocab, logits_ld, selected_ids, k, lse,
+                               selected_logprob, topk_ids, topk_logprobs, workspace, device_error,
+                               static_cast<hipStream_t>(stream), counters, 1);
 }
 
 lmh_status lmh_debug_reduce_stage1(const void* logits, lmh_dtype logits_dt, int64_t rows,

@@ -194,6 +194,18 @@ hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s
 hipError_t launch_full_logprobs(const void* logits, int32_t dt, int64_t rows, int64_t vocab, int64_t ld,
                                 const float* lse, float* out, hipStream_t s);
 
+// Single-launch path for a few rows (k_single): rows that take the split
+// path, K <= LMH_SINGLE_MAX_K, at most 64 items per row, at most
+// LMH_SINGLE_MAX_ROWS rows. It needs `counters`, one 32-bit word per row
+// (LMH_SINGLE_MAX_ROWS words) that are zero before the launch and that the
+// launch leaves zero; launches sharing counters must not overlap. Its scratch
+// (a.ws) takes single_bytes(p) bytes, never more than p.bytes.
+#define LMH_SINGLE_MAX_K 32
+#define LMH_SINGLE_MAX_ROWS 4096
+bool single_ok(const ReducePlan& p);
+size_t single_bytes(const ReducePlan& p);
+hipError_t launch_reduce_single(const ReducePlan& p, const ReduceArgs& a, uint32_t* counters, hipStream_t s);
+
 // logprob_reduce's host-side checks (everything but the workspace), in its
 // order; *workspace_bytes gets the workspace the shape needs. Then the
 // enqueue of the reduction on a workspace of at least that size.
@@ -201,9 +213,15 @@ lmh_status reduce_validate(const void* logits, lmh_dtype logits_dt, int64_t rows
                            int64_t logits_ld, const int32_t* selected_ids, int32_t k, const float* lse,
                            const float* selected_logprob, const int32_t* topk_ids,
                            const float* topk_logprobs, size_t* workspace_bytes);
+// With counters (see launch_reduce_single): single = 0 routes the shapes
+// that single_ok accepts with K <= kSingleRouteK to the single-launch path
+// (where it measured faster than the split path), single = 1 sends every
+// shape that single_ok accepts there.
+constexpr int32_t kSingleRouteK = 1;
 lmh_status reduce_enqueue(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
                           int64_t logits_ld, const int32_t* selected_ids, int32_t k, float* lse,
                           float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,
-                          void* workspace, int32_t* device_error, hipStream_t s);
+                          void* workspace, int32_t* device_error, hipStream_t s,
+                          uint32_t* single_counters = nullptr, int single = 0);
 
 }  // namespace lmh

@@ -1248,6 +1248,294 @@ __global__ __launch_bounds__(kThreads) void k_stage2(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Single-launch path for a few rows (rows that leave most CUs idle; openinfer
+// issue #719, Description: decode steps of a few rows): each row is spread
+// over S = ceil(P / 4) workgroups of four waves, wave w of workgroup j
+// streaming item 4j + w exactly as the split path's first kernel does (the
+// same partials and block keys). Each workgroup then takes the exact top-K of
+// its own slice: wave 0 finds the K-th largest of the slice's block keys by
+// repeated wave maxima (counted with multiplicity, ties cut by ascending
+// block index), the kept blocks' entries at or above it are gathered (the
+// slice was just read: L2 hits), ranked, and the slice's K (id, value) pairs
+// go to the scratch. A row's top-K lies in the union of its slices' top-K.
+// The last workgroup of a row to arrive (one device-scope counter per row,
+// incremented once per workgroup after a device-scope release of its writes)
+// merges the row's item partials in the canonical order, ranks the union and
+// writes the row's outputs, then puts the counter back to zero. No workgroup
+// waits for another, so the results are bitwise those of the other paths.
+// ---------------------------------------------------------------------------
+constexpr int kSingleMaxK = LMH_SINGLE_MAX_K;
+constexpr int kSingleMaxSlices = 16;   // P <= 64 items per row
+constexpr int64_t kSingleMaxRows = LMH_SINGLE_MAX_ROWS;
+static_assert(kSingleMaxK * kSingleMaxSlices <= 2 * kThreads, "the final union is read in two rounds");
+
+template <int DT, bool KEYS>
+__global__ __launch_bounds__(kThreads) void k_single(const uint8_t* __restrict__ logits, int64_t ld, int64_t V,
+                                                     int32_t P, int32_t S, const int32_t* __restrict__ sel,
+                                                     int32_t K, float* __restrict__ lse_out,
+                                                     float* __restrict__ sel_out, int32_t* __restrict__ topk_ids,
+                                                     float* __restrict__ topk_lp, int32_t* __restrict__ err,
+                                                     float2* __restrict__ part, int32_t* __restrict__ loc_ids,
+                                                     float* __restrict__ loc_vals,
+                                                     uint32_t* __restrict__ counters) {
+    using I = Stage1Item<DT>;
+    constexpr size_t ESZ = w16(DT) ? 2 : 4;
+    constexpr int EPV = I::EPV;
+    constexpr int VPB = kBlock / EPV;
+    __shared__ RowShared<kThreads> sh;
+    __shared__ uint32_t skey[kThreads];                                 // the slice's block keys (0: none)
+    __shared__ __attribute__((aligned(16))) uint64_t cand[kSingleMaxK * kBlock];
+    __shared__ uint64_t list2[kSingleMaxK];
+    __shared__ int32_t lids[kSingleMaxK];                              // the slice's top-K
+    __shared__ float lvals[kSingleMaxK];
+    __shared__ int32_t s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const uint32_t g = blockIdx.x;
+    const uint32_t rowu = g / (uint32_t)S;
+    const int64_t row = rowu;
+    const int32_t j = (int32_t)(g - rowu * (uint32_t)S);
+    const int32_t seg = 4 * j + wave;
+    const uint8_t* rowp = logits + (size_t)row * (size_t)ld * ESZ;
+    if (tid == 0) {
+        sh.nlist = 0;
+        sh.ncand = 0;
+        sh.nblk = 0;
+        sh.lse = 0.f;
+    }
+
+    // (1) this wave's item, as in the split path's first kernel
+    uint32_t kb = 0u;
+    if (seg < P) {
+        u32x4 buf[I::VPL];
+        float M, Sm;
+        if (stage1_load<DT>(rowp, V, seg, lane, buf)) {
+            __builtin_amdgcn_sched_barrier(0);
+            stage1_item<DT, KEYS>(buf, lane, M, Sm, kb);
+        } else {
+            stage1_item<DT, KEYS>(buf, lane, M, Sm, kb);
+        }
+        if (lane == 0)
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(part) + row * P + seg,
+                               ((uint64_t)__float_as_uint(Sm) << 32) | __float_as_uint(M), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        if (((int64_t)seg * (kSeg / kBlock) + lane) * kBlock >= V) kb = 0u;   // a block past V has no key
+    }
+
+    if constexpr (KEYS) {
+        skey[tid] = kb;                  // local block tid = block 4j*64 + tid of the row
+        __syncthreads();
+        // (2) wave 0: the slice's K-th largest key T and its kept blocks (all
+        // keys above T, then the lowest-indexed keys equal to T up to K); a
+        // slice with fewer than K blocks keeps all of them (T = 0)
+        if (wave == 0) {
+            uint32_t kk[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kk[i] = skey[i * 64 + lane];
+            uint32_t T = 0u, gt = 0u;
+            if (K <= 4) {
+                // the distinct key values from the top, one per round
+                uint32_t rem[4] = {kk[0], kk[1], kk[2], kk[3]};
+                uint32_t before = 0u;
+                for (int it = 0; it < K; ++it) {
+                    const uint32_t m = wave_reduce<1>(max(max(rem[0], rem[1]), max(rem[2], rem[3])));
+                    if (m == 0u) break;
+                    uint32_t c = 0u;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) c += (uint32_t)__popcll(__ballot(rem[i] == m));
+                    if (before + c >= (uint32_t)K) {
+                        T = m;
+                        gt = before;
+                        break;
+                    }
+                    before += c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) rem[i] = rem[i] == m ? 0u : rem[i];
+                }
+            } else {
+                // bitwise search from the top bit: T is the largest value
+                // with at least K keys at or above it (16-bit keys occupy the
+                // top half); keys 0 are empty slots
+                uint32_t real = 0u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) real += (uint32_t)__popcll(__ballot(kk[i] != 0u));
+                if (real >= (uint32_t)K) {
+                    uint32_t prefix = 0u, k_left = (uint32_t)K;
+                    constexpr int lo_bit = w16(DT) ? 16 : 0;
+                    for (int bit = 31; bit >= lo_bit; --bit) {
+                        const uint32_t hi_mask = 0xFFFFFFFFu << bit;       // bits bit..31
+                        const uint32_t want = prefix | (1u << bit);
+                        uint32_t c = 0u;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) c += (uint32_t)__popcll(__ballot((kk[i] & hi_mask) == want));
+                        if (c >= k_left)
+                            prefix = want;
+                        else
+                            k_left -= c;
+                    }
+                    T = prefix;
+                    gt = (uint32_t)K - k_left;                  // keys above T
+                }
+            }
+            const uint32_t need = (uint32_t)K - gt;      // keys equal to T that are kept
+            const uint64_t below = (1ull << lane) - 1ull;
+            uint32_t eq_seen = 0u;
+            int nk = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool eq = T != 0u && kk[i] == T;
+                const uint64_t eqm = __ballot(eq);
+                const bool keep = kk[i] != 0u &&
+                                  (T == 0u || kk[i] > T || (eq && eq_seen + (uint32_t)__popcll(eqm & below) < need));
+                const uint64_t km = __ballot(keep);
+                if (keep) sh.blk[nk + __popcll(km & below)] = i * 64 + lane;
+                nk += __popcll(km);
+                eq_seen += (uint32_t)__popcll(eqm);
+            }
+            if (lane == 0) {
+                sh.nblk = nk;
+                sh.thr[0] = T;
+            }
+        }
+        __syncthreads();
+
+        // (3) the kept blocks' entries at or above T (all of them for T = 0),
+        // then the slice's top-K as (id, value) pairs
+        {
+            const int nkb = sh.nblk;
+            const uint32_t T = sh.thr[0];
+            const bool keep_all = T == 0u;
+            const float Tf = keep_all ? kNegInf : block_value<DT>(T);
+            const int64_t blk0 = (int64_t)j * 4 * (kSeg / kBlock);
+            for (int v = tid; v < nkb * VPB; v += kThreads) {
+                const int64_t e0 = (blk0 + sh.blk[v / VPB]) * kBlock + (int64_t)(v % VPB) * EPV;
+                const u32x4 w = load_part<DT>(rowp, V, e0);
+                uint32_t m = 0u;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const uint32_t wd = w[e / (w16(DT) ? 2 : 1)];
+                    const float x = w16(DT) ? ((e & 1) ? hi16<DT>(wd) : lo16<DT>(wd)) : __uint_as_float(wd);
+                    if (e0 + e < V && (keep_all || x >= Tf)) m |= 1u << e;
+                }
+                if (m != 0u) {
+                    int pos = atomicAdd(&sh.ncand, __builtin_popcount(m));
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        if ((m >> e) & 1u) {
+                            const uint32_t wd = w[e / (w16(DT) ? 2 : 1)];
+                            const float x = w16(DT) ? ((e & 1) ? hi16<DT>(wd) : lo16<DT>(wd)) : __uint_as_float(wd);
+                            cand[pos++] = ((uint64_t)elem_key<DT>(x) << 32) |
+                                          (uint64_t)(0xFFFFFFFFu - (uint32_t)(e0 + e));
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            // sh.lse is 0 here: the values are written as they are, to LDS
+            rank_topk<DT, kThreads>(0, K, cand, sh.ncand, list2, sh, lids, lvals, &sh.lse, nullptr);
+            __syncthreads();
+            if (tid < K) {
+                const int64_t at = (int64_t)g * K + tid;
+                __hip_atomic_store(reinterpret_cast<uint32_t*>(loc_ids) + at, (uint32_t)lids[tid],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(reinterpret_cast<uint32_t*>(loc_vals) + at, __float_as_uint(lvals[tid]),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+
+    // (4) arrival. Everything another workgroup reads (the partials and the
+    // top-K lists) was written with device-scope stores, which the caches
+    // pass through to the device's point of coherence, and is read back with
+    // device-scope loads, which do not hit a stale cached copy; so the
+    // publication needs no cache write-back or invalidation (a device-scope
+    // fence, measured at about 9 us per workgroup here), only that every
+    // such store has completed before the workgroup's one increment of the
+    // row's counter: each wave waits for its stores, then the barrier.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&counters[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == (uint32_t)(S - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) {
+        sh.ncand = 0;
+        sh.nlist = 0;
+    }
+    __syncthreads();
+
+    // (5) the last workgroup of the row: lse from the item partials in the
+    // canonical order (as stage 2), the union of the slices' top-K ranked
+    const bool sel_thread = sel != nullptr && sel_out != nullptr && tid == 64;
+    int32_t sel_id = 0;
+    if (sel_thread) sel_id = sel[row];
+    if (tid < 64) {
+        constexpr int kRound = 4;
+        float m = kNegInf, sm = 0.f;
+        if (tid < kGroups)
+            for (int i0 = tid; i0 < P; i0 += kRound * kGroups) {
+                float2 pp[kRound];
+#pragma unroll
+                for (int u = 0; u < kRound; ++u) {
+                    const int i = i0 + u * kGroups;
+                    const uint64_t b = i < P ? __hip_atomic_load(reinterpret_cast<const uint64_t*>(part) + row * P + i,
+                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                             : ((uint64_t)__float_as_uint(0.f) << 32) | __float_as_uint(kNegInf);
+                    pp[u] = make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+                }
+#pragma unroll
+                for (int u = 0; u < kRound; ++u)
+                    if (i0 + u * kGroups < P) lse_merge(m, sm, pp[u].x, pp[u].y);
+            }
+        const float l = lse_tree16(m, sm);
+        if (tid == 0) {
+            sh.lse = l;
+            lse_out[row] = l;
+        }
+    }
+    if constexpr (KEYS) {
+        // (n <= 16 * 32 = 2 * kThreads: every thread's loads in one round)
+        const int n = S * K;
+        int32_t id[2];
+        float val[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int i = tid + r * kThreads;
+            const int64_t at = row * (int64_t)n + (i < n ? i : 0);
+            id[r] = (int32_t)__hip_atomic_load(reinterpret_cast<const uint32_t*>(loc_ids) + at, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+            val[r] = __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(loc_vals) + at,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (i >= n) id[r] = -1;
+        }
+        // one LDS atomic per wave and round: lanes place their entries by
+        // their rank among the wave's valid lanes
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const bool ok = id[r] >= 0;
+            const uint64_t vm = __ballot(ok);
+            int base = 0;
+            if (lane == 0 && vm != 0ull) base = atomicAdd(&sh.ncand, __popcll(vm));
+            base = __shfl(base, 0);
+            if (ok)
+                cand[base + __popcll(vm & ((1ull << lane) - 1ull))] =
+                    ((uint64_t)elem_key<DT>(val[r]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id[r]);
+        }
+    }
+    __syncthreads();
+    const float lse = sh.lse;
+    const float xsel = sel_thread ? load_selected<DT>(rowp, V, sel_id) : 0.f;
+    if constexpr (KEYS)
+        rank_topk<DT, kThreads>(row, K, cand, sh.ncand, list2, sh, topk_ids, topk_lp, &sh.lse, nullptr);
+    if (sel_thread) write_selected(V, sel_id, xsel, lse, sel_out + row, err);
+    if (tid == 0) counters[row] = 0u;                    // ready for the next call
+}
+
+// ---------------------------------------------------------------------------
 // One-workgroup-per-row path (rows that fill the CUs evenly): 8 waves stream
 // the row's items, handed out from an LDS counter (bf16 items double-
 // buffered: the next item's loads are in flight while the current one is
@@ -1641,6 +1929,49 @@ bool reduce_row_path(const ReducePlan& p) {
     // one workgroup per CU at a time: the rows must fill the CUs evenly
     const int64_t rounds = (p.rows + ncu - 1) / ncu;
     return p.rows * 4 >= rounds * ncu * 3;
+}
+
+bool single_ok(const ReducePlan& p) {
+    return p.rows > 0 && p.rows <= kSingleMaxRows && p.k >= 0 && p.k <= kSingleMaxK &&
+           p.splits <= 4 * kSingleMaxSlices && !reduce_row_path(p);
+}
+
+size_t single_bytes(const ReducePlan& p) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t S = (size_t)(p.splits + 3) / 4;
+    return up((size_t)p.rows * p.splits * sizeof(float2)) + 2 * up((size_t)p.rows * S * p.k * 4);
+}
+
+hipError_t launch_reduce_single(const ReducePlan& p, const ReduceArgs& a, uint32_t* counters, hipStream_t s) {
+    if (p.rows == 0) return hipSuccess;
+    if (!single_ok(p) || counters == nullptr) return hipErrorInvalidValue;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const int32_t S = (p.splits + 3) / 4;
+    char* ws = static_cast<char*>(a.ws);
+    float2* part = reinterpret_cast<float2*>(ws);
+    const size_t lb = up((size_t)p.rows * S * p.k * 4);
+    int32_t* loc_ids = reinterpret_cast<int32_t*>(ws + up((size_t)p.rows * p.splits * sizeof(float2)));
+    float* loc_vals = reinterpret_cast<float*>(reinterpret_cast<char*>(loc_ids) + lb);
+    const dim3 grid((unsigned)(p.rows * S));
+    auto go = [&](auto dt) {
+        constexpr int DT = decltype(dt)::value;
+        const uint8_t* lg = static_cast<const uint8_t*>(a.logits);
+        if (p.k > 0)
+            hipLaunchKernelGGL((k_single<DT, true>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.splits, S,
+                               a.sel, p.k, a.lse, a.sel_lp, a.topk_ids, a.topk_lp, a.err, part, loc_ids,
+                               loc_vals, counters);
+        else
+            hipLaunchKernelGGL((k_single<DT, false>), grid, dim3(kThreads), 0, s, lg, a.ld, p.vocab, p.splits, S,
+                               a.sel, 0, a.lse, a.sel_lp, a.topk_ids, a.topk_lp, a.err, part, loc_ids,
+                               loc_vals, counters);
+    };
+    if (a.dt == kDtBf16)
+        go(std::integral_constant<int, kDtBf16>{});
+    else if (a.dt == kDtF16)
+        go(std::integral_constant<int, kDtF16>{});
+    else
+        go(std::integral_constant<int, kDtF32>{});
+    return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReducePlan& p, const ReduceArgs& a, hipStream_t s) {
