@@ -56,52 +56,60 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
     import csv
     import statistics
 
+    # medians per (kernel, grid size): one kernel name serves several shapes
     def per_kernel(path, counter):
         d = {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] == counter:
-                d.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                d.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
         return {k: statistics.median(v) for k, v in d.items()}
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    copy = [k for k in fetch if "vectorized_elementwise_kernel" in k]
+    copy = [k for k in fetch if "vectorized_elementwise_kernel" in k[0]]
     if len(copy) != 1:
         raise SystemExit(f"expected one elementwise copy kernel, found {copy}")
     nbytes = 256 * 248320 * 2
     f_fetch = fetch[copy[0]] * 1024 / nbytes
     f_write = write[copy[0]] * 1024 / nbytes
     csrc = os.path.join(ROOT, "top_reduction_amd", "csrc")
-    wanted = {"reduce_row_bf16": ("k_rowreduce<1, 16, true>", "reduce.hip", nbytes),
-              "reduce_stage1_bf16": ("k_stage1<1, true>", "reduce.hip", nbytes),
-              "reduce_stage2_bf16": ("k_stage2<1", "reduce.hip", None),
-              "head_stream_bf16": ("k_head_stream<", "head.hip", 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
+    # (kernel name part, source, algorithmic bytes per launch, grid size in
+    # threads or None for any)
+    llama_w = 128256 * 4096 * 2
+    wanted = {"reduce_row_bf16": ("k_rowreduce<1, 16, true>", "reduce.hip", nbytes, None),
+              "reduce_stage1_bf16": ("k_stage1<1, true>", "reduce.hip", nbytes, None),
+              "reduce_stage2_bf16": ("k_stage2<1", "reduce.hip", None, None),
+              # the Llama-3-8B mixed batch's 40 sampled rows (hidden 4096)
+              "head_stream_bf16": ("k_head_stream<", "head.hip", llama_w + 40 * 4096 * 2 + 40 * 128256 * 4, None),
               "head_pipe_bf16": ("k_head_pipe<3, 2, 4, false, false, true>", "pipe.hip",
-                                 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4),
+                                 151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4, None),
+              # the Qwen3-0.6B 2048-row projection (4752 workgroups of 512)
               "head_tiled_bf16": ("k_head_tiled64<false, 8, false>", "head.hip",
-                                  151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4),
-              # the prompt chunks' tiled head with the reduction's first pass in
-              # its epilogue (Llama-3-8B shape, 256 rows): W, hidden rows, fp32
-              # logits, and per block an 8-byte partial and a 4-byte key
+                                  151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4, 4752 * 512),
+              # a Llama-3-8B prompt chunk of 256 rows, without and with the
+              # reduction's first pass in the epilogue (then per block an
+              # 8-byte partial and a 4-byte key as well)
+              "head_tiled_chunk_bf16": ("k_head_tiled64<false, 8, false>", "head.hip",
+                                        llama_w + 256 * 4096 * 2 + 256 * 128256 * 4, 504 * 512),
               "head_tiled_epilogue_bf16": ("k_head_tiled64<false, 8, true>", "head.hip",
-                                           128256 * 4096 * 2 + 256 * 4096 * 2 + 256 * 128256 * 4
-                                           + 256 * 2004 * 12),
-              "reduce_stage2_blocks": ("k_stage2<0, 8, true>", "reduce.hip", None)}
+                                           llama_w + 256 * 4096 * 2 + 256 * 128256 * 4 + 256 * 2004 * 12,
+                                           504 * 512),
+              "reduce_stage2_blocks": ("k_stage2<0, 8, true>", "reduce.hip", None, None)}
     for bits in (4, 8):
         qbytes = 151936 * 1024 * bits // 8 + 151936 * 16 * 4
         wanted[f"head_stream_q{bits}"] = (f"k_head_stream_q<3, 1, {bits}, ", "head.hip",
-                                          qbytes + 40 * 1024 * 2 + 40 * 151936 * 4)
+                                          qbytes + 40 * 1024 * 2 + 40 * 151936 * 4, None)
         wanted[f"head_tiled_q{bits}"] = (f"k_head_tiled<false, {bits}, ", "head.hip",
-                                         qbytes + 2048 * 1024 * 2 + 2048 * 151936 * 4)
-    res = {"calibration": {"kernel": copy[0][:80], "bytes_read": nbytes, "bytes_written": nbytes,
+                                         qbytes + 2048 * 1024 * 2 + 2048 * 151936 * 4, None)
+    res = {"calibration": {"kernel": copy[0][0][:80], "bytes_read": nbytes, "bytes_written": nbytes,
                            "fetch_kib": fetch[copy[0]], "write_kib": write[copy[0]],
                            "fetch_factor": round(f_fetch, 5), "write_factor": round(f_write, 5)}}
-    for key, (pat, src, algo) in wanted.items():
-        names = [k for k in fetch if pat in k]
+    for key, (pat, src, algo, grid) in wanted.items():
+        names = [k for k in fetch if pat in k[0] and (grid is None or k[1] == grid)]
         if not names:
             continue
         k = names[0]
         t = fetch[k] * 1024 / f_fetch + write.get(k, 0.0) * 1024 / f_write
-        res[key] = {"kernel": k[:80], "fetch_kib_per_dispatch": fetch[k],
+        res[key] = {"kernel": k[0][:80], "grid_threads": k[1], "fetch_kib_per_dispatch": fetch[k],
                     "write_kib_per_dispatch": write.get(k), "bytes_per_launch": round(t),
                     "algorithmic_bytes": algo,
                     "source_sha256": source_sha(os.path.join(csrc, src))}
@@ -259,6 +267,7 @@ def main():
     ms = timer.loop(fns, steps, warmup)
     log(f"reduce K={K}: {ms * 1e3:.1f} us/step")
     red_src = os.path.join(ROOT, "top_reduction_amd", "csrc", "reduce.hip")
+    head_src = os.path.join(ROOT, "top_reduction_amd", "csrc", "head.hip")
     row_path = lmh.reduce_row_path(rows, V, K)
     # back-to-back launches of the step's kernel(s): per-step time over the
     # whole timed loop (an event pair around each launch would add its own
@@ -416,7 +425,9 @@ def main():
                                                  os.path.join(ROOT, "top_reduction_amd", "csrc", "pipe.hip"))},
             "full_2048_ms": round(tf, 4),
             "full_roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
-                              "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4)},
+                              "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4),
+                              "traffic": load_traffic("head_tiled_bf16", head_src),
+                              "algorithmic_bytes": Vq * H * 2 + 2048 * H * 2 + 2048 * Vq * 4},
         }
         # token bitmask on the 40 selective rows (one segment per row): mask
         # words read once, masked logits written as -inf, nothing else touched
@@ -554,13 +565,18 @@ def main():
                 entry["head_kernel_us"] = round(th * 1e3, 2)
                 entry["head_roofline"] = {"bound": "hbm", "achieved": round(ha, 1), "peak": HBM_PEAK_GBS,
                                           "unit": "GB/s", "frac": round(ha / HBM_PEAK_GBS, 4),
-                                          "bytes_per_launch": hb}
+                                          "bytes_per_launch": hb,
+                                          "traffic": load_traffic("head_stream_bf16", head_src)}
                 log(f"fused mixed head stage alone: {th * 1e3:.1f} us -> {ha:.0f} GB/s")
                 del zout
             else:
                 entry["workload"] = "one 1024-token prompt, all positions, 256-row chunks, K=20"
                 entry["tflops"] = round(2.0 * R * H * Vl / (m * 1e-3) / 1e12, 1)
                 entry["reduce_first_pass"] = "tiled head epilogue (per-block partials)"
+                # HBM bytes of one 256-row chunk's head launch (counters), against
+                # W + hidden rows + fp32 logits + partials and keys
+                entry["chunk_head_traffic"] = load_traffic("head_tiled_epilogue_bf16", head_src)
+                entry["chunk_head_algorithmic_bytes"] = Vl * H * 2 + 256 * H * 2 + 256 * Vl * 4 + 256 * (-(-Vl // 64)) * 12
                 # the same call with the reduction's first pass as its own
                 # stream over each chunk's logits
                 _, hs = lmh._head_struct(lmh.HeadSpec(w), H)
