@@ -515,15 +515,13 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int32_t* sIdx = reinterpret_cast<int32_t*>(lds + 72 * 1024);
 
-    // XCD-aware order: hardware places workgroup i on XCD i % 8; give each
-    // XCD a contiguous run of logical tiles, row tiles fastest, so the row
-    // tiles of one W slab share that XCD's L2.
+    // XCD-aware order (tile_of)
     const int32_t total = mtiles * ntiles;
     const int32_t per_xcd = (int32_t)((gridDim.x + 7) / 8);
     const int32_t logical = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
     if (logical >= total) return;
-    const int32_t mt = logical % mtiles;
-    const int32_t nt = logical / mtiles;
+    int32_t mt, nt;
+    tile_of(logical, mtiles, ntiles, mt, nt);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -835,8 +833,8 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
     const int32_t per_xcd = (int32_t)((gridDim.x + 7) / 8);
     const int32_t logical = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
     if (logical >= total) return;
-    const int32_t mt = logical % mtiles;
-    const int32_t nt = logical / mtiles;
+    int32_t mt, nt;
+    tile_of(logical, mtiles, ntiles, mt, nt);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;

@@ -83,6 +83,25 @@ struct QOrder {
     static constexpr int QQ = QB / 4;       // elements per lane quarter per run
 };
 
+// Tile order of the tiled heads. The hardware places workgroup i on XCD
+// i % 8, and each XCD gets a contiguous run of the logical tile order. The
+// order takes the row tiles in bands of LMH_TILE_MBAND (the vocabulary
+// tiles of one band in turn, the band's row tiles fastest), so an XCD's
+// concurrent tiles share a few hidden-row tiles, which stay in its L2, and
+// each W slab is read by the band's row tiles together.
+#ifndef LMH_TILE_MBAND
+#define LMH_TILE_MBAND 4
+#endif
+__device__ inline void tile_of(int32_t logical, int32_t mtiles, int32_t ntiles, int32_t& mt, int32_t& nt) {
+    constexpr int32_t MB = LMH_TILE_MBAND;
+    const int32_t band_tiles = MB * ntiles;
+    const int32_t b = logical / band_tiles;
+    const int32_t rem = logical - b * band_tiles;
+    const int32_t mb = mtiles - b * MB < MB ? mtiles - b * MB : MB;   // row tiles of this band
+    nt = rem / mb;
+    mt = b * MB + (rem - nt * mb);
+}
+
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef float f32x2 __attribute__((ext_vector_type(2)));
