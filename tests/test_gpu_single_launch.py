@@ -182,3 +182,26 @@ def test_rejects_shapes_off_the_path():
         with pytest.raises(lmh.LmhError) as e:
             lmh.reduce_single(t, None, k, _counters())
         assert e.value.status == 2                       # LMH_ERR_SHAPE
+
+
+def test_many_calls_back_to_back():
+    """Sixty single-launch calls of varying rows, vocabularies and K queued
+    back to back with no synchronisation between them, each compared
+    bitwise with the two-launch path afterwards: the device-scope stores,
+    the per-row counters and their return to zero hold across consecutive
+    launches."""
+    print("single launch many calls", flush=True)
+    g = synth.rng(8300)
+    shapes = [(int(g.integers(1, 65)), int(g.choice([4096, 12_289, 50_000, 151_936])), int(g.integers(0, 33)))
+              for _ in range(60)]
+    data = {V: synth.normal_bf16(g, (64, V), 2.0) for V in {s[1] for s in shapes}}
+    tens = {V: _padded(b, "bf16") for V, b in data.items()}
+    runs = []
+    for R, V, k in shapes:
+        k = min(k, V)
+        t = tens[V][:R]
+        sel = g.integers(0, V, size=R).astype(np.int32)
+        runs.append((t, sel, k, lmh.reduce_single(t, i32_tensor(sel), k, _counters())))
+    for t, sel, k, a in runs:
+        _bitwise(a, lmh.logprob_reduce(t, i32_tensor(sel), k), k)
+    assert int(_counters().abs().sum().item()) == 0
