@@ -57,9 +57,9 @@ constexpr int kStreamQThreads = 64 * LMH_STREAMQ_WAVES;   // threads per quantis
 template <bool OUT_BF16>
 __device__ inline void store_out(void* out, int64_t off, float v) {
     if (OUT_BF16)
-        reinterpret_cast<uint16_t*>(out)[off] = f32_to_bf16_rne(v);
+        __builtin_nontemporal_store(f32_to_bf16_rne(v), reinterpret_cast<uint16_t*>(out) + off);
     else
-        reinterpret_cast<float*>(out)[off] = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<float*>(out) + off);
 }
 
 // Drives step(PF, c, current, next) over chunks 0..n-1 with two weight
@@ -738,7 +738,7 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
                 const bool valid = sIdx[rl] >= 0;
                 if (vec_ok && v + 4 <= p.V) {
                     const f32x4 o = valid ? val : f32x4{kNaN, kNaN, kNaN, kNaN};
-                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v) = o;
+                    __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v));
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -942,7 +942,9 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
 
     // Epilogue through LDS (free after the last barrier): per pass, each wave
     // stages 32 rows x 64 columns of its tile (fp32, rows padded by 16 B),
-    // then stores whole 16-byte row segments.
+    // then stores whole 16-byte row segments, non-temporal (the logits are
+    // not read again by this launch; measured 2 % faster on the 2048-row
+    // projection and the 256-row chunk).
     const int lq = lane >> 4;
     float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 68);
     const bool vec_ok = !OUT_BF16 && (p.old % 4 == 0) &&
@@ -978,7 +980,7 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
                     const bool valid = sIdx[rl] >= 0;
                     if (vec_ok && v + 4 <= p.V) {
                         const f32x4 o = valid ? val : f32x4{kNaN, kNaN, kNaN, kNaN};
-                        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v) = o;
+                        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v));
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
