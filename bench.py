@@ -346,22 +346,26 @@ def main():
                             "gbps": round(32 * synth.VOCAB_QWEN3 * 2 / (m * 1e-3) / 1e9, 1),
                             "path": "split: streaming launch + selection launch"}
         log(f"decode: {m * 1e3:.1f} us")
-        # K = 1 and K = 0: the two launches (logprob_reduce) against the single
-        # launch the no-workspace entry point takes for them
-        for kk in (1, 0):
+        # K = 5, 1 and 0: the two launches (logprob_reduce) against the single
+        # launch (forced through lmh_debug_reduce_single; the no-workspace
+        # entry point takes it at K = 0 only, where it measured faster)
+        counters = torch.zeros(4096, dtype=torch.int32, device=dev)
+        for kk in (5, 1, 0):
             def two(t, kk=kk):
                 return L.logprob_reduce(vp(t), lmh.LMH_BF16, 32, synth.VOCAB_QWEN3, synth.VOCAB_QWEN3, vp(s), kk,
                                         vp(o[0]), vp(o[1]), vp(o[2]) if kk else None,
                                         vp(o[3]) if kk else None, vp(ws), ws.numel(), None, stream)
 
             def one(t, kk=kk):
-                return L.logprob_reduce_noalloc(vp(t), lmh.LMH_BF16, 32, synth.VOCAB_QWEN3, synth.VOCAB_QWEN3,
-                                                vp(s), kk, vp(o[0]), vp(o[1]), vp(o[2]) if kk else None,
-                                                vp(o[3]) if kk else None, None, stream)
+                return L.lmh_debug_reduce_single(vp(t), lmh.LMH_BF16, 32, synth.VOCAB_QWEN3, synth.VOCAB_QWEN3,
+                                                 vp(s), kk, vp(o[0]), vp(o[1]), vp(o[2]) if kk else None,
+                                                 vp(o[3]) if kk else None, vp(ws), ws.numel(), vp(counters), None,
+                                                 stream)
             assert two(copies[0]) == 0 and one(copies[0]) == 0
             m2 = timer.loop([lambda t=t: two(t) for t in copies], steps, warmup)
             m1 = timer.loop([lambda t=t: one(t) for t in copies], steps, warmup)
-            result["decode"][f"k{kk}"] = {"split_us": round(m2 * 1e3, 2), "single_launch_us": round(m1 * 1e3, 2)}
+            result["decode"][f"k{kk}"] = {"split_us": round(m2 * 1e3, 2), "single_launch_us": round(m1 * 1e3, 2),
+                                          "noalloc_path": "single launch" if kk <= 0 else "split"}
             log(f"decode K={kk}: two launches {m2 * 1e3:.1f} us, single launch {m1 * 1e3:.1f} us")
         del copies
 

@@ -208,13 +208,14 @@ lmh_status logprob_reduce(
  * logprob_reduce; a shape whose logprob_reduce_workspace_size exceeds
  * LMH_NOALLOC_SCRATCH_BYTES returns LMH_ERR_WORKSPACE before any HIP call.
  * Few rows (decode steps, openinfer issue #719, Description: rows that leave
- * most compute units idle) with K <= 1 and vocab <= 262,144 take a single
- * launch: each row is spread over several workgroups that each reduce a
- * slice to its exact top-K, and the last workgroup of the row to arrive (a
- * per-row counter in the array, back at zero when the launch ends) merges
- * the slices (larger K take the two launches, which measured faster there). All calls on one GPU share that GPU's array: calls that
- * overlap on one GPU (other streams, other host threads) race and must be
- * ordered by the caller. Nothing in the array needs clearing between calls.
+ * most compute units idle) with K = 0 (or -1) and vocab <= 262,144 take a
+ * single launch: each row is spread over several workgroups that each reduce
+ * a slice, and the last workgroup of the row to arrive (a per-row counter in
+ * the array, back at zero when the launch ends) merges the slices; K >= 1
+ * takes the two launches, which measured faster there. All calls on one GPU
+ * share that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be ordered by the caller. Nothing in the
+ * array needs clearing between calls.
  */
 #define LMH_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
 lmh_status logprob_reduce_noalloc(
@@ -526,7 +527,7 @@ lmh_status lmh_debug_logprobs_ex(
 /*
  * lmh_debug_reduce_single -- logprob_reduce through the single-launch path
  * that logprob_reduce_noalloc takes for few rows, at any k it supports
- * (-1 <= k <= 32; logprob_reduce_noalloc takes it only for k <= 1, where it
+ * (-1 <= k <= 32; logprob_reduce_noalloc takes it only for k <= 0, where it
  * measured faster than the two launches), on a caller workspace (the size
  * logprob_reduce_workspace_size gives) and caller counters: 4096 32-bit
  * words, zero before the first call, which every call leaves zero. Shapes

@@ -434,3 +434,73 @@ def test_full_vocabulary_logprobs(case):
     tl = top.topk_logprobs.cpu().numpy()
     ok = ~np.isnan(tl)
     assert np.array_equal(lp[rows, ids][ok].view(np.uint32), tl[ok].view(np.uint32))
+
+
+def _top1_rows(V, seed):
+    """Rows for K = 1, whose answer is the first entry equal to the row
+    maximum: the maximum planted in several blocks of different selection
+    threads, in two blocks of one thread, twice in one block, in block 0, in
+    the partial last block only, in both block 0 and the partial last block;
+    constant rows; rows of -inf; -0/+0 rows; plain rows."""
+    g = synth.rng(seed)
+    x = synth.normal_f32(g, (256, V), 2.0)
+    nb = -(-V // 64)
+    for r in range(256):
+        kind = r % 10
+        if kind == 0:
+            blocks = np.sort(g.choice(nb - 1, size=5, replace=False))
+            x[r, blocks * 64 + g.integers(0, 64, size=5)] = 20.0
+        elif kind == 1:
+            b0 = 16 * int(g.integers(1, (nb - 1) // 16))          # two blocks of one thread
+            x[r, b0 * 64 + 40] = 20.0
+            x[r, (b0 + 3) * 64 + 2] = 20.0
+        elif kind == 2:
+            b = int(g.integers(0, nb - 1))
+            x[r, b * 64 + 50] = 20.0
+            x[r, b * 64 + 9] = 20.0
+        elif kind == 3:
+            x[r, 5] = 20.0
+        elif kind == 4:
+            x[r, V - 3] = 20.0
+        elif kind == 5:
+            x[r, 63] = 20.0
+            x[r, V - 1] = 20.0
+        elif kind == 6:
+            x[r, :] = 1.5
+        elif kind == 7:
+            x[r, :] = -np.inf
+        elif kind == 8:
+            x[r] = np.where(np.arange(V) % 3 == 0, -0.0, 0.0)
+            x[r, ::7] = -1.0
+    return x
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_top1_rows(dt):
+    """K = 1 on rows built for the top-entry shortcut (the prefetched block
+    of the lowest thread holding the row maximum) and its fallback (the
+    maximum in the partial last block): oracle parity on every row, and
+    bitwise equality of the one-workgroup-per-row and split paths."""
+    V = 248_280                                              # the last block holds 24 entries
+    print(f"top-1 rows dt={dt}", flush=True)
+    x = _top1_rows(V, 8400 + (dt == "f16"))
+    data = synth.f32_to_bf16_bits(x) if dt == "bf16" else x.astype(np.float16)
+    g = synth.rng(8410)
+    sel = g.integers(0, V, size=256).astype(np.int32)
+    ld = (V + 7) // 8 * 8
+    full = np.zeros((256, ld), dtype=data.dtype)
+    full[:, :V] = data
+    t = (bf16_tensor(full) if dt == "bf16" else torch.from_numpy(full).cuda())[:, :V]
+    if torch.cuda.get_device_properties(0).multi_processor_count <= 256:
+        assert lmh.reduce_row_path(256, V, 1)
+    a = lmh.logprob_reduce(t, i32_tensor(sel), 1)
+    check_reduce(a, data, sel, 1, *oracle.reduce(data, sel, 1))
+    parts = [lmh.logprob_reduce(t[i:i + 100], i32_tensor(sel[i:i + 100]), 1) for i in range(0, 256, 100)]
+    torch.cuda.synchronize()
+    cat = lambda f: torch.cat([getattr(p, f) for p in parts])
+    assert torch.equal(a.lse.view(torch.int32), cat("lse").view(torch.int32))
+    assert torch.equal(a.topk_ids, cat("topk_ids"))
+    assert torch.equal(a.topk_logprobs.view(torch.int32), cat("topk_logprobs").view(torch.int32))
+    ids = a.topk_ids.cpu().numpy()[:, 0]
+    assert np.all(ids[3::10] == 5) and np.all(ids[4::10] == V - 3) and np.all(ids[5::10] == 63)
+    assert np.all(ids[6::10] == 0) and np.all(ids[7::10] == 0)

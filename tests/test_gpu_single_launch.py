@@ -1,7 +1,7 @@
 """The single-launch reduction for a few rows (each row spread over several
 workgroups, the last one to arrive merging the slices; openinfer issue #719,
 Description and Suggested direction), forced at every K it supports through
-lmh_debug_reduce_single and taken by logprob_reduce_noalloc at K <= 1,
+lmh_debug_reduce_single and taken by logprob_reduce_noalloc at K <= 0,
 against logprob_reduce on a workspace (the two-launch split path): lse,
 selected logprobs, top-K ids and logprobs bitwise equal, on decode rows, the
 Llama-3-8B mixed-batch shape, f16, ragged vocabularies, rows built for the
@@ -47,7 +47,7 @@ def _both(t, sel, k):
     a = lmh.reduce_single(t, s, k, _counters())
     b = lmh.logprob_reduce(t, s, k)
     _bitwise(a, b, k)
-    if k <= 1:                                         # the no-workspace entry point's own choice
+    if k <= 1:                                         # the no-workspace entry point (single launch at K <= 0)
         _bitwise(lmh.logprob_reduce_noalloc(t, s, k), b, k)
     return a
 

@@ -217,7 +217,7 @@ lmh_status reduce_validate(const void* logits, lmh_dtype logits_dt, int64_t rows
 // that single_ok accepts with K <= kSingleRouteK to the single-launch path
 // (where it measured faster than the split path), single = 1 sends every
 // shape that single_ok accepts there.
-constexpr int32_t kSingleRouteK = 1;
+constexpr int32_t kSingleRouteK = 0;
 lmh_status reduce_enqueue(const void* logits, lmh_dtype logits_dt, int64_t rows, int64_t vocab,
                           int64_t logits_ld, const int32_t* selected_ids, int32_t k, float* lse,
                           float* selected_logprob, int32_t* topk_ids, float* topk_logprobs,

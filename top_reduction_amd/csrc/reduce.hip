@@ -685,6 +685,78 @@ __device__ __forceinline__ void row_topk(const uint8_t* __restrict__ rowp, int64
         }
     }
 
+    // K = 1 with prefetched blocks (16-bit logits): the top entry is the
+    // first entry equal to the row's largest block maximum T, and the block
+    // holding it is the lowest-indexed block with key T -- the prefetched
+    // block of the lowest selection thread whose largest key is T. So the
+    // owner's wave reads the answer out of its prefetch registers, with no
+    // threshold search, staging or rank. The partial last block is not
+    // prefetched: when the winning thread holds it, the general path runs.
+    if constexpr (PF) if (K == 1) {
+        const int lane = tid & 63;
+        uint32_t T1 = 0u;
+        int tstar = NT;
+        if constexpr (PRE) {
+            // every wave reads the per-thread maxima itself (no barrier)
+            uint32_t m = 0u;
+#pragma unroll
+            for (int i = 0; i < NT / 64; ++i) m = max(m, tkey[0][lane + 64 * i]);
+            T1 = wave_reduce<1>(m);
+#pragma unroll
+            for (int i = 0; i < NT / 64; ++i) {
+                const uint64_t b = __ballot(tkey[0][lane + 64 * i] == T1);
+                if (tstar == NT && b != 0ull) tstar = 64 * i + __builtin_ctzll(b);
+            }
+        } else {
+            uint32_t tmax = 0u;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) tmax = max(tmax, kr[j]);
+            int fphase = 0;
+            uint32_t mx[1] = {tmax};
+            block_reduce<1, 1, NT>(mx, sh.sred, fphase);
+            T1 = mx[0];
+            uint32_t who[1] = {tmax == T1 ? (uint32_t)tid : (uint32_t)NT};
+            block_reduce<2, 1, NT>(who, sh.sred, fphase);
+            tstar = (int)who[0];
+        }
+        const bool partial_last = (int64_t)nb * kBlock > V;
+        if (T1 != 0u && !(partial_last && tstar == (nb - 1) / KPT)) {
+            if ((tstar >> 6) == (tid >> 6)) {            // the owner's wave
+                const int o = tstar & 63;
+                const int32_t bstar = __shfl(pf_blk, o);
+                // lanes 8 (o % 8) .. +7 hold its eight 16-byte parts in pf[o / 8]
+                u32x4 w = pf[0];
+#pragma unroll
+                for (int i = 1; i < VPB; ++i)
+                    if ((o >> 3) == i) w = pf[i];
+                const float Tf = block_value<DT>(T1);
+                uint32_t m = 0u;
+                if ((lane >> 3) == (o & 7)) {
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        const float x = (e & 1) ? hi16<DT>(w[e >> 1]) : lo16<DT>(w[e >> 1]);
+                        if (x == Tf) m |= 1u << e;
+                    }
+                }
+                const uint64_t bal = __ballot(m != 0u);
+                if (lse_ready != nullptr)
+                    while (__hip_atomic_load(lse_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+                    }
+                const float lse = lse_ready != nullptr
+                                      ? __hip_atomic_load(lse_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                                      : *lse_p;
+                // no entry equals T only for a NaN T (a row of NaN): -1 and NaN
+                const int lw = bal != 0ull ? __builtin_ctzll(bal) : o;
+                if (lane == lw) {
+                    topk_ids[row] = bal != 0ull ? bstar * kBlock + (lane & 7) * EPV + __builtin_ctz(m) : -1;
+                    topk_lp[row] = bal != 0ull ? Tf - lse : __builtin_nanf("");
+                }
+            }
+            return;
+        }
+        if constexpr (!PRE) __syncthreads();             // the general path's first reduction reuses sred
+    }
+
     // (3) threshold and kept blocks
     int phase = 0;
     int nblk;
