@@ -308,6 +308,23 @@ def main():
                             "gbps": round(nbytes / (m * 1e-3) / 1e9, 1)}
             log(f"reduce K={k}: {m * 1e3:.1f} us")
         result["reduce_by_k"] = by_k
+        # K = -1 (openinfer issue #719, Acceptance criteria): every token's
+        # logprob, a [256][248320] fp32 output; bytes = the reduction's read,
+        # the second read of the logits and the output write
+        full_out = torch.empty((rows, V), device=dev)
+        fullf = []
+        for (t, s_, _, _), ws in zip(chunks, wss):
+            o = (torch.empty(rows, device=dev), torch.empty(rows, device=dev))
+            a = (vp(t), lmh.LMH_BF16, rows, V, V, vp(s_), lmh.LMH_K_FULL, vp(o[0]), vp(o[1]), None,
+                 vp(full_out), vp(ws), ws.numel(), None, stream)
+            fullf.append(lambda a=a, o=o: L.logprob_reduce(*a))
+        assert all(f() == 0 for f in fullf)
+        m = timer.loop(fullf, max(steps // 4, 10), warmup)
+        fb = 2 * nbytes + rows * V * 4
+        by_k["-1"] = {"us": round(m * 1e3, 2), "rows_per_s": round(rows / (m * 1e-3)),
+                      "gbps": round(fb / (m * 1e-3) / 1e9, 1), "bytes_per_call": fb}
+        log(f"reduce K=-1 (full-vocabulary logprobs): {m * 1e3:.1f} us -> {fb / (m * 1e-3) / 1e9:.0f} GB/s")
+        del full_out, fullf
         # the same chunks as f16 logits (MTPLX PR #532, Tests: bf16/f16), K = 20
         f16 = [(t.to(torch.float16), s_) for (t, s_, _, _) in chunks]
         fns16 = []

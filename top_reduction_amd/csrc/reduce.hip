@@ -36,6 +36,7 @@ constexpr int kHistBins = 256;     // key values resolved by one stage-2 histogr
 constexpr int kSeg = 4096;          // logits per streaming work item (one wave)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -1817,11 +1818,25 @@ __global__ __launch_bounds__(kThreads) void k_full_logprobs(const uint8_t* __res
     const float l = lse[r];
     const u32x4 w = load_part<DT>(logits + (size_t)r * (size_t)ld * ESZ, V, e0);
     float* o = out + (int64_t)r * V + e0;
+    float y[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
         const uint32_t wd = w[e / (w16(DT) ? 2 : 1)];
         const float x = w16(DT) ? ((e & 1) ? hi16<DT>(wd) : lo16<DT>(wd)) : __uint_as_float(wd);
-        if (e0 + e < V) o[e] = x - l;
+        y[e] = x - l;
+    }
+    // whole groups on a 16-byte aligned output: 16-byte non-temporal stores
+    // (scalar stores, each lane writing 4 of every 32 bytes, ran at a third
+    // of the HBM rate)
+    if (e0 + EPV <= V && (reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+#pragma unroll
+        for (int q = 0; q < EPV / 4; ++q)
+            __builtin_nontemporal_store(f32x4{y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]},
+                                        reinterpret_cast<f32x4*>(o) + q);
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+            if (e0 + e < V) o[e] = y[e];
     }
 }
 
