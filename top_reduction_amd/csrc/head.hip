@@ -814,21 +814,22 @@ constexpr int kT64Lds = 2 * kT64Stage + kTileM * 4;
 // 0.76 ms on the 2048-row Qwen3-0.6B projection
 constexpr int kT64Waves = 8;
 
-// NW waves: 8 (two per SIMD, 128 x 64 each) or 4 (one per SIMD, 128 x 128
-// each, accumulators in the AGPRs a lone wave may use).
-// FUSED (fp32 logits, eight waves): each wave's 64 columns are one 64-logit
-// block of the vocabulary, and the epilogue also writes, per row, that
-// block's maximum as a key and its (max, sum of exp(x - max)) partial -- the
-// reduction's streaming pass, done on the values while they are in registers
-// (MTPLX PR #532, Motivation: no second pass over a chunk's logits).
+// NW waves: 8 (two per SIMD, 128 x 64 each).
+// FUSED (fp32 logits): each wave's 64 columns are one 64-logit block of the
+// vocabulary, and the epilogue also writes, per row, that block's maximum as
+// a key and its (max, sum of exp(x - max)) partial -- the reduction's
+// streaming pass, done on the values while they are in registers (MTPLX PR
+// #532, Motivation: no second pass over a chunk's logits).
 template <bool OUT_BF16, int NW, bool FUSED = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
     constexpr int NTH = NW * 64;
     constexpr int WN = kTileN / (NW / 2);              // columns per wave
     constexpr int NF = WN / 16;                         // B fragments per wave
-    static_assert(!FUSED || (WN == 64 && !OUT_BF16), "a wave's columns are one block; fp32 logits");
+    static_assert(NW == 8 && NF == 4, "eight waves of 128 x 64");
+    static_assert(!FUSED || !OUT_BF16, "partials of fp32 logits");
     constexpr int L = kTileM * (kT64K / 8) / NTH;       // chunks per thread per stage (A and B each)
+    static_assert(L == 4, "eight chunk writes per stage, one per 16-row group of its first k-step");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int32_t* sIdx = reinterpret_cast<int32_t*>(lds + 2 * kT64Stage);
 
@@ -841,7 +842,7 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = (wave / (NW / 2)) * 128;
     const int wn = (wave % (NW / 2)) * WN;
     const int32_t m0 = mt * kTileM;
@@ -881,21 +882,24 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
 #pragma unroll
         for (int j = 0; j < L; ++j) rb[j] = *reinterpret_cast<const u32x4*>(p.W + gb[j] + k);
     };
-    auto lwrite = [&](int buf, const u32x4 (&ra)[L], const u32x4 (&rb)[L]) {
-        uint8_t* base = lds + buf * kT64Stage;
-#pragma unroll
-        for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(base + wofs[j]) = ra[j];
-#pragma unroll
-        for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(base + kTileM * 128 + wofs[j]) = rb[j];
-    };
     f32x4 acc[8][NF];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto mma = [&](int buf) {
-        const uint8_t* base = lds + buf * kT64Stage;
+    // One stage: the MFMAs of the stage held in rd (two k-steps), the next
+    // stage's chunks (wa, wb: A rows, then W rows) written to wr one per
+    // 16-row group of the first k-step, and the loads of stage st into
+    // (la, lb) issued after the first group. Scheduling barriers keep the
+    // writes and loads at those places: the compiler otherwise gathers the
+    // writes after the last MFMA and the loads before the barrier, where
+    // they leave the MFMA pipe idle (the interleaving measured 5 % faster on
+    // the 2048-row Qwen3-0.6B projection and the 256-row Llama-3-8B chunk).
+    // rd and wr are the two LDS buffers, never the same one.
+    auto step = [&](const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr, int st, u32x4 (&la)[L],
+                    u32x4 (&lb)[L], const u32x4 (&wa)[L], const u32x4 (&wb)[L]) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t rofs = h == 0 ? rofs0 : rofs1;
@@ -903,20 +907,26 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
             const uint32_t bofs = (uint32_t)((kTileM + wn) * 128) + rofs;
             u32x4 fb[NF];
 #pragma unroll
-            for (int j = 0; j < NF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(base + bofs + j * 16 * 128);
+            for (int j = 0; j < NF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(rd + bofs + j * 16 * 128);
             // A fragments read two 16-row groups ahead of their MFMAs (one
-            // ahead measured 2-3 % slower: 790 against 763 us on the 2048-row
-            // Qwen3-0.6B projection, 297 against 294 us on a 256-row
-            // Llama-3-8B chunk)
-            u32x4 fa0 = *reinterpret_cast<const u32x4*>(base + aofs);
-            u32x4 fa1 = *reinterpret_cast<const u32x4*>(base + aofs + 16 * 128);
+            // ahead measured 2-3 % slower)
+            u32x4 fa0 = *reinterpret_cast<const u32x4*>(rd + aofs);
+            u32x4 fa1 = *reinterpret_cast<const u32x4*>(rd + aofs + 16 * 128);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const u32x4 cur = fa0;
                 fa0 = fa1;
-                if (i < 6) fa1 = *reinterpret_cast<const u32x4*>(base + aofs + (i + 2) * 16 * 128);
+                if (i < 6) fa1 = *reinterpret_cast<const u32x4*>(rd + aofs + (i + 2) * 16 * 128);
 #pragma unroll
                 for (int j = 0; j < NF; ++j) acc[i][j] = mfma16(cur, fb[j], acc[i][j]);
+                if (h == 0) {
+                    if (i < L)
+                        *reinterpret_cast<u32x4*>(wr + wofs[i]) = wa[i];
+                    else
+                        *reinterpret_cast<u32x4*>(wr + kTileM * 128 + wofs[i - L]) = wb[i - L];
+                    if (i == 0) gload(st, la, lb);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
@@ -927,16 +937,15 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
     u32x4 ra0[L], ra1[L], rb0[L], rb1[L];
     gload(0, ra0, rb0);
     gload(1, ra1, rb1);
-    lwrite(0, ra0, rb0);
+#pragma unroll
+    for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(lds + wofs[j]) = ra0[j];
+#pragma unroll
+    for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(lds + kTileM * 128 + wofs[j]) = rb0[j];
     __syncthreads();
     for (int s = 0; s < nst; s += 2) {
-        gload(s + 2, ra0, rb0);
-        mma(0);
-        lwrite(1, ra1, rb1);
+        step(lds, lds + kT64Stage, s + 2, ra0, rb0, ra1, rb1);
         __syncthreads();
-        gload(s + 3, ra1, rb1);
-        mma(1);
-        lwrite(0, ra0, rb0);
+        step(lds + kT64Stage, lds, s + 3, ra1, rb1, ra0, rb0);
         __syncthreads();
     }
 
@@ -944,13 +953,21 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
     // stages 32 rows x 64 columns of its tile (fp32, rows padded by 16 B),
     // then stores whole 16-byte row segments, non-temporal (the logits are
     // not read again by this launch; measured 2 % faster on the 2048-row
-    // projection and the 256-row chunk).
+    // projection and the 256-row chunk). The scale mode is resolved once per
+    // launch; a wave whose 128 x 64 block lies inside the logits matrix with
+    // every row sourced stores with no per-element checks.
     const int lq = lane >> 4;
     float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 68);
     const bool vec_ok = !OUT_BF16 && (p.old % 4 == 0) &&
                         ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
-#pragma unroll
-    for (int cb = 0; cb < NF / 4; ++cb) {
+    const bool rows_sourced = __all(sIdx[wm + lane] >= 0 && sIdx[wm + 64 + lane] >= 0);
+    const bool fast = vec_ok && rows_sourced && m0 + wm + 128 <= p.R && n0 + wn + WN <= p.V;
+    // this lane's store position in the wave's block: row lq (+ 4q + 32h),
+    // columns 4fr .. 4fr + 3
+    float* const wout = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + wm) * p.old + (n0 + wn);
+    const int64_t lofs = (int64_t)lq * p.old + 4 * fr;
+    auto epilogue = [&](auto mode_c) {
+        constexpr int MODE = decltype(mode_c)::value;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
 #pragma unroll
@@ -959,41 +976,57 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) stg[(ii * 16 + lq * 4 + e) * 68 + j * 16 + fr] = acc[i][cb * 4 + j][e];
+                    for (int e = 0; e < 4; ++e) stg[(ii * 16 + lq * 4 + e) * 68 + j * 16 + fr] = acc[i][j][e];
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // lane l stores columns 4*(l%16) .. +3 of rows l/16 + 4q, q = 0..7
+            f32x4 val[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int rr = lq + 4 * q;                      // row within the pass
-                const int rl = wm + h * 32 + rr;
-                const int32_t r = m0 + rl;
-                const int cl = 4 * fr;
-                const int64_t v = n0 + wn + cb * 64 + cl;
-                f32x4 val = *reinterpret_cast<const f32x4*>(&stg[rr * 68 + cl]);
+                val[q] = *reinterpret_cast<const f32x4*>(&stg[(lq + 4 * q) * 68 + 4 * fr]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = scale_logit(val[e], p.scale_mode, p.scale);
-                if constexpr (FUSED) block_partial(p, r, sIdx[rl] >= 0, v, val, (n0 + wn + cb * 64) >> 6);
-                if (r < p.R) {
-                    const bool valid = sIdx[rl] >= 0;
-                    if (vec_ok && v + 4 <= p.V) {
-                        const f32x4 o = valid ? val : f32x4{kNaN, kNaN, kNaN, kNaN};
-                        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v));
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (v + e < p.V)
-                                store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v + e, valid ? val[e] : kNaN);
-                    }
-                }
+                for (int e = 0; e < 4; ++e) val[q][e] = scale_logit(val[q][e], MODE, p.scale);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (fast && !FUSED) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    __builtin_nontemporal_store(val[q], reinterpret_cast<f32x4*>(wout + (int64_t)(h * 32 + 4 * q) * p.old + lofs));
+                continue;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int rl = wm + h * 32 + lq + 4 * q;
+                const int32_t r = m0 + rl;
+                const int64_t v = n0 + wn + 4 * fr;
+                const bool valid = sIdx[rl] >= 0;
+                if constexpr (FUSED) block_partial(p, r, valid, v, val[q], (n0 + wn) >> 6);
+                const f32x4 ov = valid ? val[q] : f32x4{kNaN, kNaN, kNaN, kNaN};
+                float* o = reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v;
+                if (fast) {
+                    __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(o));
+                } else if (r < p.R) {
+                    if (vec_ok && v + 4 <= p.V) {
+                        __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(o));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (v + e < p.V) store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v + e, ov[e]);
+                    }
+                }
+            }
         }
-    }
+    };
+    if (p.scale_mode == 1)
+        epilogue(std::integral_constant<int, 1>{});
+    else if (p.scale_mode == 2)
+        epilogue(std::integral_constant<int, 2>{});
+    else
+        epilogue(std::integral_constant<int, 0>{});
 }
 
 // ---------------------------------------------------------------------------
