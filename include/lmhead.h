@@ -268,8 +268,9 @@ size_t lmhead_logprobs_workspace_size(int64_t rows, int64_t vocab, int32_t k, in
  * row (R entries). logits_debug, when not NULL, is an [R][vocab] fp32 buffer
  * that receives the logits that were reduced (tests use it); the workspace
  * then only holds the reduction's part. Chunks of more than 64 rows of a dense
- * bf16 head whose hidden size is a multiple of 128 are projected by the
- * tiled kernel, whose epilogue also writes, per row and 64-logit block, the
+ * bf16 head whose hidden size is a multiple of 128 (hidden matrix and 256
+ * weight rows each at most 4 GiB) are projected by the tiled kernel, whose
+ * epilogue also writes, per row and 64-logit block, the
  * block maximum and its (max, sum of exp) partial [MTPLX PR #532,
  * Motivation: no second full pass over a chunk's logits]; the reduction then
  * merges those partials (one per block: partial i to thread i mod 256 in
@@ -506,8 +507,9 @@ lmh_status lmh_debug_gather_project_q(
 /*
  * lmh_debug_logprobs_ex -- lmhead_logprobs_ex with the reduction's first pass
  * chosen: epilogue 0 lets chunks of more than 64 rows of a dense bf16 head
- * (hidden size a multiple of 128, no vocab_mask) take it in the tiled head's
- * epilogue, as lmhead_logprobs_ex does; 1 always runs it as its own pass over
+ * (hidden size a multiple of 128, hidden matrix and 256 weight rows each at
+ * most 4 GiB, no vocab_mask) take it in the tiled head's epilogue, as
+ * lmhead_logprobs_ex does; 1 always runs it as its own pass over
  * the chunk's logits (tests and measurement compare the two). Any other
  * value returns LMH_ERR_SHAPE.
  */

@@ -164,6 +164,48 @@ def test_invalid_rows_are_nan_tiled(H, out):
         _close(z[good], oracle.head(hid, w, ex[good]))
 
 
+@pytest.mark.parametrize("mode,s", [(lmh.LMH_SCALE_NONE, 1.0), (lmh.LMH_SCALE_MUL, 0.3), (lmh.LMH_SCALE_DIV, 6.0)])
+def test_tiled_walk_ragged(mode, s):
+    """600 rows x (151,936 - 37) vocabulary at hidden 256: more than four row
+    x vocab tiles per CU, so each workgroup walks several tiles and loads
+    the next tile's first stages before its epilogue; the last row tile and
+    the last vocab tile are partial and four rows have no source. Those rows
+    are NaN and flagged; 12 rows (the partial row tile included) match the
+    scaled oracle at every column; 40 rows equal, bit for bit, the same rows
+    projected by the weight-streaming kernel; scaled logits are one fp32
+    multiply or IEEE division of the unscaled ones."""
+    g = synth.rng(40 + mode)
+    T, H, V, R = 700, 256, 151_936 - 37, 600
+    hid = synth.normal_bf16(g, (T, H))
+    w = synth.normal_bf16(g, (V, H), H ** -0.5)
+    ex = g.integers(0, T, size=R).astype(np.int32)
+    bad = np.array([5, 300, 513, 599])
+    ex[bad] = [T, -2, T + 1, -1]
+    head = lmh.HeadSpec(bf16_tensor(w), mode, s)
+    hid_t, cu_t = bf16_tensor(hid), i32_tensor([0, T])
+    p = lmh.lmhead_gather_project_ex(hid_t, head, cu_t, 0, logits_indices=i32_tensor(ex),
+                                     variant=lmh.LMH_HEAD_TILED)
+    print(f"tiled walk {R} x {V} x {H} mode {mode}", flush=True)
+    torch.cuda.synchronize()
+    z = p.logits.cpu().numpy()
+    good = np.setdiff1d(np.arange(R), bad)
+    assert np.all(np.isnan(z[bad])) and np.all(np.isfinite(z[good]))
+    assert int(p.device_error.item()) & lmh.LMH_DEVERR_INDEX
+    rows = np.concatenate([g.choice(good[good < 512], size=8, replace=False), good[good >= 512][-4:]])
+    _close(z[rows], oracle.head(hid, w, ex[rows], scale_mode=mode, scale=s))
+    sel = g.choice(good, size=40, replace=False)
+    q = lmh.lmhead_gather_project_ex(hid_t, head, cu_t, 0, logits_indices=i32_tensor(ex[sel]),
+                                     variant=lmh.LMH_HEAD_STREAM)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.logits.cpu().numpy().view(np.uint32), z[sel].view(np.uint32))
+    if mode != lmh.LMH_SCALE_NONE:
+        u = lmh.lmhead_gather_project_ex(hid_t, lmh.HeadSpec(head.weight), cu_t, 0,
+                                         logits_indices=i32_tensor(ex), variant=lmh.LMH_HEAD_TILED)
+        zu = u.logits.cpu().numpy()[good].astype(np.float32)
+        want = zu * np.float32(s) if mode == lmh.LMH_SCALE_MUL else zu / np.float32(s)
+        assert np.array_equal(z[good].view(np.uint32), want.view(np.uint32))
+
+
 @pytest.fixture(scope="module")
 def qwen_batch():
     return synth.selective_head_batch(4000)

@@ -235,7 +235,8 @@ lmh_status logprobs_impl(const void* hidden, lmh_dtype hidden_dt, int64_t num_to
     // stages, its epilogue does the reduction's streaming pass (unless a token
     // mask must change the logits first, or the workspace has no room for the
     // per-block partials)
-    const bool epi = allow_epilogue && hidden_dt == LMH_BF16 && w.bits == 0 && hidden_dim % 128 == 0 &&
+    const bool epi = allow_epilogue && hidden_dt == LMH_BF16 && w.bits == 0 &&
+                     tiled64_fits(num_tokens, hidden_ld, hidden_dim, w.ld) &&
                      vocab_mask == nullptr && workspace_bytes >= logits_bytes + blocks_ws_bytes(chunk, vocab, kr);
     if (logits_debug && !aligned(logits_debug, 16)) return LMH_ERR_ALIGN;
 

@@ -809,94 +809,102 @@ __device__ inline void block_partial(const HeadParams& p, int32_t r, bool has_sr
 // ---------------------------------------------------------------------------
 constexpr int kT64K = 64;
 constexpr int kT64Stage = (kTileM + kTileN) * kT64K * 2;         // 64 KB
-constexpr int kT64Lds = 2 * kT64Stage + kTileM * 4;
+constexpr int kT64Lds = 2 * kT64Stage + 2 * kTileM * 4;   // two stages, two row-source lists
 // eight waves: four (one per SIMD, 128 x 128 each) measured 1.23 ms against
 // 0.76 ms on the 2048-row Qwen3-0.6B projection
-constexpr int kT64Waves = 8;
 
-// NW waves: 8 (two per SIMD, 128 x 64 each).
+// Eight waves (two per SIMD), each 128 x 64 of the tile. The workgroups of an
+// XCD take its share of the tiles in the banded order (tile_of): with as many
+// workgroups as tiles each takes one; with PERSIST and fewer workgroups (one
+// per CU), each walks its XCD's share, and the last two stages of a tile load
+// the next tile's first two stages (its row sources resolved at the start of
+// the tile), so those loads overlap the tile's epilogue and no workgroup is
+// dispatched per tile (measured 726 -> 685 us on the 2048-row Qwen3-0.6B
+// projection). The epilogue stages 16 rows per pass in the LDS buffer the
+// last stage was read from.
 // FUSED (fp32 logits): each wave's 64 columns are one 64-logit block of the
 // vocabulary, and the epilogue also writes, per row, that block's maximum as
 // a key and its (max, sum of exp(x - max)) partial -- the reduction's
 // streaming pass, done on the values while they are in registers (MTPLX PR
 // #532, Motivation: no second pass over a chunk's logits).
-template <bool OUT_BF16, int NW, bool FUSED = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+template <bool OUT_BF16, bool FUSED, bool PERSIST>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
+    constexpr int NW = 8;
     constexpr int NTH = NW * 64;
     constexpr int WN = kTileN / (NW / 2);              // columns per wave
     constexpr int NF = WN / 16;                         // B fragments per wave
-    static_assert(NW == 8 && NF == 4, "eight waves of 128 x 64");
+    static_assert(NF == 4, "a wave's 64 columns are one 64-logit block");
     static_assert(!FUSED || !OUT_BF16, "partials of fp32 logits");
     constexpr int L = kTileM * (kT64K / 8) / NTH;       // chunks per thread per stage (A and B each)
     static_assert(L == 4, "eight chunk writes per stage, one per 16-row group of its first k-step");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    int32_t* sIdx = reinterpret_cast<int32_t*>(lds + 2 * kT64Stage);
+    int32_t* const sIdx2 = reinterpret_cast<int32_t*>(lds + 2 * kT64Stage);   // [2][kTileM] with PERSIST
 
     const int32_t total = mtiles * ntiles;
-    const int32_t per_xcd = (int32_t)((gridDim.x + 7) / 8);
-    const int32_t logical = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
-    if (logical >= total) return;
-    int32_t mt, nt;
-    tile_of(logical, mtiles, ntiles, mt, nt);
+    const int32_t per_xcd = (total + 7) / 8;
+    const int32_t xcd = (int32_t)(blockIdx.x % 8);
+    const int32_t wgs = (int32_t)(gridDim.x / 8);       // workgroups per XCD
+    const int32_t lo = xcd * per_xcd;
+    const int32_t hi = lo + per_xcd < total ? lo + per_xcd : total;
+    int32_t logical = lo + (int32_t)(blockIdx.x / 8);
+    if (logical >= hi) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = (wave / (NW / 2)) * 128;
     const int wn = (wave % (NW / 2)) * WN;
-    const int32_t m0 = mt * kTileM;
-    const int64_t n0 = (int64_t)nt * kTileN;
-
-    for (int t = tid; t < kTileM; t += NTH) {
-        const int32_t r = m0 + t;
-        sIdx[t] = (r < p.R) ? row_source(p.row0 + r, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
-    }
-    __syncthreads();
-
-    // this thread's staging chunks: rows tid/8 + (NTH/8)j, chunk tid%8
     const int c = tid & 7;
-    int64_t ga[L], gb[L];
+    const int fr = lane & 15;
+    const int lq = lane >> 4;
+    const uint32_t rofs0 = (uint32_t)(fr * 128 + ((((lane >> 4) + 0) ^ (fr & 7)) << 4));
+    const uint32_t rofs1 = (uint32_t)(fr * 128 + ((((lane >> 4) + 4) ^ (fr & 7)) << 4));
+    const int nst = (int)(p.H / kT64K);                  // even: H is a multiple of 128
     uint32_t wofs[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) {
         const int row = (tid >> 3) + (NTH / 8) * j;
-        const int32_t t = sIdx[row];
-        ga[j] = (int64_t)(t < 0 ? 0 : t) * p.hld + c * 8;
-        const int64_t n = n0 + row < p.V ? n0 + row : p.V - 1;
-        gb[j] = n * p.wld + c * 8;
         wofs[j] = (uint32_t)(row * 128 + ((c ^ (row & 7)) << 4));
     }
-    // fragment reads of k-step h of a stage: row l%16 of a 16-row group,
-    // chunk l/16 + 4h
-    const int fr = lane & 15;
-    const uint32_t rofs0 = (uint32_t)(fr * 128 + ((((lane >> 4) + 0) ^ (fr & 7)) << 4));
-    const uint32_t rofs1 = (uint32_t)(fr * 128 + ((((lane >> 4) + 4) ^ (fr & 7)) << 4));
-    const int nst = (int)(p.H / kT64K);                  // even: H is a multiple of 128
-
-    // loads of stages past the last read k = 0 (never written to LDS)
+    auto sources = [&](int32_t lg, int32_t* dst) {
+        int32_t mt_, nt_;
+        tile_of(lg, mtiles, ntiles, mt_, nt_);
+        for (int t = tid; t < kTileM; t += NTH) {
+            const int32_t r = mt_ * kTileM + t;
+            dst[t] = (r < p.R) ? row_source(p.row0 + r, p.cu, p.num_decode, p.num_tokens, p.ex) : -1;
+        }
+    };
+    // this thread's staging chunks of tile lg (rows tid/8 + 64j, chunk tid%8)
+    // as 32-bit byte offsets from the hidden matrix and from the tile's first
+    // W row
+    uint32_t ga[L], gb[L];
+    const uint8_t* wtile;
+    auto addresses = [&](int32_t lg, const int32_t* src) {
+        int32_t mt_, nt_;
+        tile_of(lg, mtiles, ntiles, mt_, nt_);
+        const int64_t nb0 = (int64_t)nt_ * kTileN;
+        wtile = reinterpret_cast<const uint8_t*>(p.W + nb0 * p.wld);
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const int row = (tid >> 3) + (NTH / 8) * j;
+            const int32_t t = src[row];
+            ga[j] = (uint32_t)(((int64_t)(t < 0 ? 0 : t) * p.hld + c * 8) * 2);
+            const int64_t n = nb0 + row < p.V ? row : p.V - 1 - nb0;
+            gb[j] = (uint32_t)((n * p.wld + c * 8) * 2);
+        }
+    };
+    // stage st of the tile whose addresses are set (st >= nst: stage st - nst)
     auto gload = [&](int st, u32x4 (&ra)[L], u32x4 (&rb)[L]) {
-        const int64_t k = st < nst ? (int64_t)st * kT64K : 0;
+        const int64_t kb = (int64_t)(st < nst ? st : st - nst) * kT64K * 2;
+        const uint8_t* const hk = reinterpret_cast<const uint8_t*>(p.hidden) + kb;
+        const uint8_t* const wk = wtile + kb;
 #pragma unroll
-        for (int j = 0; j < L; ++j) ra[j] = *reinterpret_cast<const u32x4*>(p.hidden + ga[j] + k);
+        for (int j = 0; j < L; ++j) ra[j] = *reinterpret_cast<const u32x4*>(hk + ga[j]);
 #pragma unroll
-        for (int j = 0; j < L; ++j) rb[j] = *reinterpret_cast<const u32x4*>(p.W + gb[j] + k);
+        for (int j = 0; j < L; ++j) rb[j] = *reinterpret_cast<const u32x4*>(wk + gb[j]);
     };
     f32x4 acc[8][NF];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // One stage: the MFMAs of the stage held in rd (two k-steps), the next
-    // stage's chunks (wa, wb: A rows, then W rows) written to wr one per
-    // 16-row group of the first k-step, and the loads of stage st into
-    // (la, lb) issued after the first group. Scheduling barriers keep the
-    // writes and loads at those places: the compiler otherwise gathers the
-    // writes after the last MFMA and the loads before the barrier, where
-    // they leave the MFMA pipe idle (the interleaving measured 5 % faster on
-    // the 2048-row Qwen3-0.6B projection and the 256-row Llama-3-8B chunk).
-    // rd and wr are the two LDS buffers, never the same one.
     auto step = [&](const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr, int st, u32x4 (&la)[L],
                     u32x4 (&lb)[L], const u32x4 (&wa)[L], const u32x4 (&wb)[L]) {
         __builtin_amdgcn_sched_barrier(0);
@@ -908,8 +916,6 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
             u32x4 fb[NF];
 #pragma unroll
             for (int j = 0; j < NF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(rd + bofs + j * 16 * 128);
-            // A fragments read two 16-row groups ahead of their MFMAs (one
-            // ahead measured 2-3 % slower)
             u32x4 fa0 = *reinterpret_cast<const u32x4*>(rd + aofs);
             u32x4 fa1 = *reinterpret_cast<const u32x4*>(rd + aofs + 16 * 128);
 #pragma unroll
@@ -931,9 +937,11 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
         }
     };
 
-    // stage s is multiplied from LDS buffer s%2 while stage s+1 is written to
-    // the other buffer and stage s+2 is loaded into the register set that
-    // stage s came from
+    // the first tile: its row sources, its first two stages
+    int cur = 0;
+    sources(logical, sIdx2);
+    __syncthreads();
+    addresses(logical, sIdx2);
     u32x4 ra0[L], ra1[L], rb0[L], rb1[L];
     gload(0, ra0, rb0);
     gload(1, ra1, rb1);
@@ -942,91 +950,103 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
 #pragma unroll
     for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(lds + kTileM * 128 + wofs[j]) = rb0[j];
     __syncthreads();
-    for (int s = 0; s < nst; s += 2) {
-        step(lds, lds + kT64Stage, s + 2, ra0, rb0, ra1, rb1);
-        __syncthreads();
-        step(lds + kT64Stage, lds, s + 3, ra1, rb1, ra0, rb0);
-        __syncthreads();
-    }
 
-    // Epilogue through LDS (free after the last barrier): per pass, each wave
-    // stages 32 rows x 64 columns of its tile (fp32, rows padded by 16 B),
-    // then stores whole 16-byte row segments, non-temporal (the logits are
-    // not read again by this launch; measured 2 % faster on the 2048-row
-    // projection and the 256-row chunk). The scale mode is resolved once per
-    // launch; a wave whose 128 x 64 block lies inside the logits matrix with
-    // every row sourced stores with no per-element checks.
-    const int lq = lane >> 4;
-    float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 68);
-    const bool vec_ok = !OUT_BF16 && (p.old % 4 == 0) &&
-                        ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
-    const bool rows_sourced = __all(sIdx[wm + lane] >= 0 && sIdx[wm + 64 + lane] >= 0);
-    const bool fast = vec_ok && rows_sourced && m0 + wm + 128 <= p.R && n0 + wn + WN <= p.V;
-    // this lane's store position in the wave's block: row lq (+ 4q + 32h),
-    // columns 4fr .. 4fr + 3
-    float* const wout = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + wm) * p.old + (n0 + wn);
-    const int64_t lofs = (int64_t)lq * p.old + 4 * fr;
-    auto epilogue = [&](auto mode_c) {
-        constexpr int MODE = decltype(mode_c)::value;
+    while (true) {
+        int32_t mt, nt;
+        tile_of(logical, mtiles, ntiles, mt, nt);
+        const int32_t m0 = mt * kTileM;
+        const int64_t n0 = (int64_t)nt * kTileN;
+        const int32_t next = logical + wgs;
+        const bool has_next = PERSIST && next < hi;
+        int32_t* const sIdx = sIdx2 + cur * kTileM;
+        int32_t* const sIdxN = sIdx2 + (cur ^ 1) * kTileM;
+        if (has_next) sources(next, sIdxN);   // visible after the first step's barrier
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-                const int i = h * 2 + ii;
+            for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < nst; s += 2) {
+            if (s == nst - 2 && has_next) {
+                if (nst == 2) __syncthreads();
+                addresses(next, sIdxN);   // the loads of stages nst, nst + 1: the next tile's 0, 1
+            }
+            step(lds, lds + kT64Stage, s + 2, ra0, rb0, ra1, rb1);
+            __syncthreads();
+            step(lds + kT64Stage, lds, s + 3, ra1, rb1, ra0, rb0);
+            __syncthreads();
+        }
+        // buffer 0 now holds the next tile's first stage; the epilogue stages
+        // through buffer 1 (16 rows x 64 columns per wave and pass, rows
+        // padded by 16 B)
+        float* stg = reinterpret_cast<float*>(lds + kT64Stage) + wave * (16 * 68);
+        const bool vec_ok = !OUT_BF16 && (p.old % 4 == 0) &&
+                            ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+        const bool rows_sourced = __all(sIdx[wm + lane] >= 0 && sIdx[wm + 64 + lane] >= 0);
+        const bool fast = vec_ok && rows_sourced && m0 + wm + 128 <= p.R && n0 + wn + WN <= p.V;
+        float* const wout = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + wm) * p.old + (n0 + wn);
+        const int64_t lofs = (int64_t)lq * p.old + 4 * fr;
+        auto epilogue = [&](auto mode_c) {
+            constexpr int MODE = decltype(mode_c)::value;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) stg[(ii * 16 + lq * 4 + e) * 68 + j * 16 + fr] = acc[i][j][e];
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // lane l stores columns 4*(l%16) .. +3 of rows l/16 + 4q, q = 0..7
-            f32x4 val[8];
+                    for (int e = 0; e < 4; ++e) stg[(lq * 4 + e) * 68 + j * 16 + fr] = acc[i][j][e];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                // lane l: columns 4*(l%16) .. +3 of rows l/16 + 4q, q = 0..3
+                f32x4 val[4];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                val[q] = *reinterpret_cast<const f32x4*>(&stg[(lq + 4 * q) * 68 + 4 * fr]);
+                for (int q = 0; q < 4; ++q) {
+                    val[q] = *reinterpret_cast<const f32x4*>(&stg[(lq + 4 * q) * 68 + 4 * fr]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[q][e] = scale_logit(val[q][e], MODE, p.scale);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (fast && !FUSED) {
+                    for (int e = 0; e < 4; ++e) val[q][e] = scale_logit(val[q][e], MODE, p.scale);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if (fast && !FUSED) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    __builtin_nontemporal_store(val[q], reinterpret_cast<f32x4*>(wout + (int64_t)(h * 32 + 4 * q) * p.old + lofs));
-                continue;
-            }
+                    for (int q = 0; q < 4; ++q)
+                        __builtin_nontemporal_store(val[q], reinterpret_cast<f32x4*>(wout + (int64_t)(i * 16 + 4 * q) * p.old + lofs));
+                    continue;
+                }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int rl = wm + h * 32 + lq + 4 * q;
-                const int32_t r = m0 + rl;
-                const int64_t v = n0 + wn + 4 * fr;
-                const bool valid = sIdx[rl] >= 0;
-                if constexpr (FUSED) block_partial(p, r, valid, v, val[q], (n0 + wn) >> 6);
-                const f32x4 ov = valid ? val[q] : f32x4{kNaN, kNaN, kNaN, kNaN};
-                float* o = reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v;
-                if (fast) {
-                    __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(o));
-                } else if (r < p.R) {
-                    if (vec_ok && v + 4 <= p.V) {
+                for (int q = 0; q < 4; ++q) {
+                    const int rl = wm + i * 16 + lq + 4 * q;
+                    const int32_t r = m0 + rl;
+                    const int64_t v = n0 + wn + 4 * fr;
+                    const bool valid = sIdx[rl] >= 0;
+                    if constexpr (FUSED) block_partial(p, r, valid, v, val[q], (n0 + wn) >> 6);
+                    const f32x4 ov = valid ? val[q] : f32x4{kNaN, kNaN, kNaN, kNaN};
+                    float* o = reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v;
+                    if (fast) {
                         __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(o));
-                    } else {
+                    } else if (r < p.R) {
+                        if (vec_ok && v + 4 <= p.V) {
+                            __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(o));
+                        } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (v + e < p.V) store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v + e, ov[e]);
+                            for (int e = 0; e < 4; ++e)
+                                if (v + e < p.V) store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v + e, ov[e]);
+                        }
                     }
                 }
             }
-        }
-    };
-    if (p.scale_mode == 1)
-        epilogue(std::integral_constant<int, 1>{});
-    else if (p.scale_mode == 2)
-        epilogue(std::integral_constant<int, 2>{});
-    else
-        epilogue(std::integral_constant<int, 0>{});
+        };
+        if (p.scale_mode == 1)
+            epilogue(std::integral_constant<int, 1>{});
+        else if (p.scale_mode == 2)
+            epilogue(std::integral_constant<int, 2>{});
+        else
+            epilogue(std::integral_constant<int, 0>{});
+        if (!has_next) break;
+        __syncthreads();   // staging done before the next tile writes buffer 1
+        logical = next;
+        cur ^= 1;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1142,14 +1162,28 @@ hipError_t launch_tiled_q(const HeadParams& p, int32_t mtiles, int32_t ntiles, h
     return launch_tiled<OUT_BF16, BITS, false>(p, mtiles, ntiles, s);
 }
 
-template <bool OUT_BF16, int NW = kT64Waves, bool FUSED = false>
+// Persistent walk when every CU gets at least four tiles, for plain fp32
+// logits (the bf16-output and partials epilogues do not fit the registers
+// beside the next tile's state); otherwise one workgroup per tile.
+template <bool OUT_BF16, bool FUSED = false>
 hipError_t launch_tiled64(const HeadParams& p, int32_t mtiles, int32_t ntiles, hipStream_t s) {
-    const void* fn = (const void*)k_head_tiled64<OUT_BF16, NW, FUSED>;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    const int cus = cu_count();
+    if constexpr (!OUT_BF16 && !FUSED) {
+        if (cus > 0 && total >= 4 * (int64_t)cus) {
+            const void* fn = (const void*)k_head_tiled64<false, false, true>;
+            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kT64Lds);
+            if (e != hipSuccess) return e;
+            const dim3 grid((unsigned)((cus + 7) / 8 * 8));
+            hipLaunchKernelGGL((k_head_tiled64<false, false, true>), grid, dim3(512), kT64Lds, s, p, mtiles, ntiles);
+            return hipGetLastError();
+        }
+    }
+    const void* fn = (const void*)k_head_tiled64<OUT_BF16, FUSED, false>;
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kT64Lds);
     if (e != hipSuccess) return e;
-    const int64_t total = (int64_t)mtiles * ntiles;
     const dim3 grid((unsigned)(((total + 7) / 8) * 8));
-    hipLaunchKernelGGL((k_head_tiled64<OUT_BF16, NW, FUSED>), grid, dim3(NW * 64), kT64Lds, s, p, mtiles, ntiles);
+    hipLaunchKernelGGL((k_head_tiled64<OUT_BF16, FUSED, false>), grid, dim3(512), kT64Lds, s, p, mtiles, ntiles);
     return hipGetLastError();
 }
 
@@ -1158,9 +1192,9 @@ hipError_t launch_head_tiled_bf16(const HeadArgs& a, hipStream_t s) {
     const HeadParams p = to_params(a);
     const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
     const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
-    if (p.H % 128 == 0) {
+    if (tiled64_fits(p.num_tokens, p.hld, p.H, p.wld)) {
         if (a.part != nullptr)
-            return a.out_bf16 ? hipErrorInvalidValue : launch_tiled64<false, kT64Waves, true>(p, mtiles, ntiles, s);
+            return a.out_bf16 ? hipErrorInvalidValue : launch_tiled64<false, true>(p, mtiles, ntiles, s);
         return a.out_bf16 ? launch_tiled64<true>(p, mtiles, ntiles, s) : launch_tiled64<false>(p, mtiles, ntiles, s);
     }
     if (a.part != nullptr) return hipErrorInvalidValue;

@@ -111,6 +111,15 @@ struct HeadArgs {
 // Compute units of the current device (0 if it cannot be queried).
 int cu_count();
 
+// The tiled kernel with 64-wide stages (and the reduction partials in its
+// epilogue) takes a dense bf16 head whose hidden size is a multiple of 128
+// and whose operand offsets fit 32 bits: the hidden matrix (num_tokens rows
+// of pitch hidden_ld) and 256 weight rows of pitch weight_ld, in bytes.
+inline bool tiled64_fits(int64_t num_tokens, int64_t hidden_ld, int64_t hidden_dim, int64_t weight_ld) {
+    constexpr int64_t kMax = (int64_t)1 << 32;
+    return hidden_dim % 128 == 0 && num_tokens * hidden_ld * 2 <= kMax && 256 * weight_ld * 2 <= kMax;
+}
+
 // bf16 MFMA heads. stream: R <= kStreamMaxRows; tiled: any R.
 hipError_t launch_head_stream_bf16(const HeadArgs& a, hipStream_t s);
 // The k-pipelined weight stream (bf16 or quantised weights), for the shapes
