@@ -908,6 +908,9 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
     auto step = [&](const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr, int st, u32x4 (&la)[L],
                     u32x4 (&lb)[L], const u32x4 (&wa)[L], const u32x4 (&wb)[L]) {
         __builtin_amdgcn_sched_barrier(0);
+        // the second k-step's first two fragments, read during the first
+        // k-step's seventh 16-row group (2 % on the 2048-row projection)
+        u32x4 pa, pb;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t rofs = h == 0 ? rofs0 : rofs1;
@@ -918,9 +921,16 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
             // fragments two 16-row groups ahead of their MFMAs (one ahead
             // measured 2-3 % slower)
             u32x4 fb[NF];
-            u32x4 fa0 = *reinterpret_cast<const u32x4*>(rd + aofs);
+            u32x4 fa0;
+            if (h == 1) {
+                fa0 = pa;
+                fb[0] = pb;
+            } else {
+                fa0 = *reinterpret_cast<const u32x4*>(rd + aofs);
+                fb[0] = *reinterpret_cast<const u32x4*>(rd + bofs);
+            }
 #pragma unroll
-            for (int j = 0; j < NF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(rd + bofs + j * 16 * 128);
+            for (int j = 1; j < NF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(rd + bofs + j * 16 * 128);
             u32x4 fa1 = *reinterpret_cast<const u32x4*>(rd + aofs + 16 * 128);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -935,6 +945,10 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
                     else
                         *reinterpret_cast<u32x4*>(wr + kTileM * 128 + wofs[i - L]) = wb[i - L];
                     if (i == 0) gload(st, la, lb);
+                    if (i == 6) {
+                        pa = *reinterpret_cast<const u32x4*>(rd + (uint32_t)(wm * 128) + rofs1);
+                        pb = *reinterpret_cast<const u32x4*>(rd + (uint32_t)((kTileM + wn) * 128) + rofs1);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
