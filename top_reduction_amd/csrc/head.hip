@@ -525,7 +525,7 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = (wave >> 2) * 128;
     const int wn = (wave & 3) * kWaveN;
     const int32_t m0 = mt * kTileM;
@@ -620,33 +620,34 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
             }
         }
     };
-    auto lwrite = [&](int buf, int st, const u32x4 (&ra)[kTileLA], const TileB<BITS>& rb) {
-        uint8_t* base = lds + buf * kTileStage;
+    // chunk j of a stage's A slice (j < kTileLA) or W slice (j - kTileLA),
+    // dequantised for quantised weights, zero past H
+    auto wchunk = [&](uint8_t* __restrict__ base, int st, int j, const u32x4 (&ra)[kTileLA], const TileB<BITS>& rb) {
         const bool z = QUANT ? (int64_t)st * kTileK >= p.H : (int64_t)st * kTileK + c * 8 + 8 > p.H;
         const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < kTileLA; ++j) *reinterpret_cast<u32x4*>(base + wofs[j]) = z ? zero : ra[j];
-#pragma unroll
-        for (int j = 0; j < kTileLB; ++j) {
-            u32x4 b;
-            if constexpr (!QUANT) {
-                b = rb.v[j];
-            } else {
-                float sf, bf;
-                if constexpr (STAB) {
-                    sf = __uint_as_float(rb.sb[j] << 16);
-                    bf = __uint_as_float(rb.sb[j] & 0xFFFF0000u);
-                } else {
-                    sf = __uint_as_float((uint32_t)rb.sc[j] << 16);
-                    bf = __uint_as_float((uint32_t)rb.bi[j] << 16);
-                }
-                if constexpr (BITS == 4)
-                    b = dequant8<4>(rb.q[j], 0u, sf, bf);
-                else
-                    b = dequant8<8>(rb.q0[j], rb.q1[j], sf, bf);
-            }
-            *reinterpret_cast<u32x4*>(base + kTileM * 64 + wofs[j]) = z ? zero : b;
+        if (j < kTileLA) {
+            *reinterpret_cast<u32x4*>(base + wofs[j]) = z ? zero : ra[j];
+            return;
         }
+        const int jb = j - kTileLA;
+        u32x4 b;
+        if constexpr (!QUANT) {
+            b = rb.v[jb];
+        } else {
+            float sf, bf;
+            if constexpr (STAB) {
+                sf = __uint_as_float(rb.sb[jb] << 16);
+                bf = __uint_as_float(rb.sb[jb] & 0xFFFF0000u);
+            } else {
+                sf = __uint_as_float((uint32_t)rb.sc[jb] << 16);
+                bf = __uint_as_float((uint32_t)rb.bi[jb] << 16);
+            }
+            if constexpr (BITS == 4)
+                b = dequant8<4>(rb.q[jb], 0u, sf, bf);
+            else
+                b = dequant8<8>(rb.q0[jb], rb.q1[jb], sf, bf);
+        }
+        *reinterpret_cast<u32x4*>(base + kTileM * 64 + wofs[jb]) = z ? zero : b;
     };
     f32x4 acc[8][NF];
 #pragma unroll
@@ -654,23 +655,31 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
 #pragma unroll
         for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // MFMAs of one stage; the A fragments are read from LDS one 16-row group
-    // ahead of their use
-    auto mma = [&](int buf) {
-        const uint8_t* base = lds + buf * kTileStage;
+    // One stage: its MFMAs from rd; stage sw's chunks (wa, wb) written to wr,
+    // one per 16-row group, and the loads of stage sl into (la, lb) issued
+    // after the first group, held there by scheduling barriers (the compiler
+    // otherwise gathers the writes, with their dequantisation, after the last
+    // MFMA). The first MFMA's two fragments are read first; A fragments two
+    // 16-row groups ahead of their MFMAs. rd and wr are the two LDS buffers.
+    static_assert(kTileLA + kTileLB <= 8, "one chunk write per 16-row group");
+    auto step = [&](const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr, int sw, const u32x4 (&wa)[kTileLA],
+                    const TileB<BITS>& wb, int sl, u32x4 (&la)[kTileLA], TileB<BITS>& lb) {
+        __builtin_amdgcn_sched_barrier(0);
         u32x4 fb[NF];
+        u32x4 fa0 = *reinterpret_cast<const u32x4*>(rd + aofs);
 #pragma unroll
-        for (int j = 0; j < NF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(base + bofs + j * 16 * 64);
-        // A fragments read two 16-row groups ahead of their MFMAs
-        u32x4 fa0 = *reinterpret_cast<const u32x4*>(base + aofs);
-        u32x4 fa1 = *reinterpret_cast<const u32x4*>(base + aofs + 16 * 64);
+        for (int j = 0; j < NF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(rd + bofs + j * 16 * 64);
+        u32x4 fa1 = *reinterpret_cast<const u32x4*>(rd + aofs + 16 * 64);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const u32x4 cur = fa0;
             fa0 = fa1;
-            if (i < 6) fa1 = *reinterpret_cast<const u32x4*>(base + aofs + (i + 2) * 16 * 64);
+            if (i < 6) fa1 = *reinterpret_cast<const u32x4*>(rd + aofs + (i + 2) * 16 * 64);
 #pragma unroll
             for (int j = 0; j < NF; ++j) acc[i][j] = mfma16(cur, fb[j], acc[i][j]);
+            if (i < kTileLA + kTileLB) wchunk(wr, sw, i, wa, wb);
+            if (i == 0) gload(sl, la, lb);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -682,74 +691,92 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
     gload(0, ra0, rb0);
     gload(1, ra1, rb1);
     gload(2, ra2, rb2);
-    lwrite(0, 0, ra0, rb0);
+#pragma unroll
+    for (int j = 0; j < kTileLA + kTileLB; ++j) wchunk(lds, 0, j, ra0, rb0);
     __syncthreads();
     int cur = 0;                                    // LDS buffer of stage s
     for (int s = 0; s < nst; s += 3) {
-        gload(s + 3, ra0, rb0);
-        mma(cur);
-        lwrite(cur ^ 1, s + 1, ra1, rb1);
+        step(lds + cur * kTileStage, lds + (cur ^ 1) * kTileStage, s + 1, ra1, rb1, s + 3, ra0, rb0);
         __syncthreads();
         cur ^= 1;
-        gload(s + 4, ra1, rb1);
-        mma(cur);
-        lwrite(cur ^ 1, s + 2, ra2, rb2);
+        step(lds + cur * kTileStage, lds + (cur ^ 1) * kTileStage, s + 2, ra2, rb2, s + 4, ra1, rb1);
         __syncthreads();
         cur ^= 1;
-        gload(s + 5, ra2, rb2);
-        mma(cur);
-        lwrite(cur ^ 1, s + 3, ra0, rb0);
+        step(lds + cur * kTileStage, lds + (cur ^ 1) * kTileStage, s + 3, ra0, rb0, s + 5, ra2, rb2);
         __syncthreads();
         cur ^= 1;
     }
 
     // Epilogue through LDS (free after the last barrier): per pass, each wave
     // stages 32 rows x 64 columns of its quarter (fp32, rows padded by 16 B),
-    // then stores whole 16-byte row segments.
+    // then stores whole 16-byte row segments, non-temporal. The scale mode is
+    // resolved once per launch; a wave whose 128 x 64 block lies inside the
+    // logits matrix with every row sourced stores with no per-element checks.
     const int lq = lane >> 4;
     float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 68);
     const bool vec_ok = !OUT_BF16 && (p.old % 4 == 0) &&
                         ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+    const bool rows_sourced = __all(sIdx[wm + lane] >= 0 && sIdx[wm + 64 + lane] >= 0);
+    const bool fast = vec_ok && rows_sourced && m0 + wm + 128 <= p.R && n0 + wn + kWaveN <= p.V;
+    float* const wout = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + wm) * p.old + (n0 + wn);
+    const int64_t lofs = (int64_t)lq * p.old + 4 * fr;
+    auto epilogue = [&](auto mode_c) {
+        constexpr int MODE = decltype(mode_c)::value;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+        for (int h = 0; h < 4; ++h) {
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-            const int i = h * 2 + ii;
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = h * 2 + ii;
 #pragma unroll
-            for (int j = 0; j < NF; ++j)
+                for (int j = 0; j < NF; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) stg[(ii * 16 + lq * 4 + e) * 68 + j * 16 + fr] = acc[i][j][e];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // lane l stores columns 4*(l%16) .. +3 of rows l/16 + 4q, q = 0..7
+                    for (int e = 0; e < 4; ++e) stg[(ii * 16 + lq * 4 + e) * 68 + j * 16 + fr] = acc[i][j][e];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // lane l stores columns 4*(l%16) .. +3 of rows l/16 + 4q, q = 0..7
+            f32x4 val[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int rr = lq + 4 * q;                      // row within the pass
-            const int rl = wm + h * 32 + rr;
-            const int32_t r = m0 + rl;
-            const int cl = 4 * fr;
-            const int64_t v = n0 + wn + cl;
-            f32x4 val = *reinterpret_cast<const f32x4*>(&stg[rr * 68 + cl]);
+            for (int q = 0; q < 8; ++q) {
+                val[q] = *reinterpret_cast<const f32x4*>(&stg[(lq + 4 * q) * 68 + 4 * fr]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) val[e] = scale_logit(val[e], p.scale_mode, p.scale);
-            if (r < p.R) {
-                const bool valid = sIdx[rl] >= 0;
-                if (vec_ok && v + 4 <= p.V) {
-                    const f32x4 o = valid ? val : f32x4{kNaN, kNaN, kNaN, kNaN};
-                    __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v));
-                } else {
+                for (int e = 0; e < 4; ++e) val[q][e] = scale_logit(val[q][e], MODE, p.scale);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (fast) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (v + e < p.V) store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v + e, valid ? val[e] : kNaN);
+                for (int q = 0; q < 8; ++q)
+                    __builtin_nontemporal_store(val[q], reinterpret_cast<f32x4*>(wout + (int64_t)(h * 32 + 4 * q) * p.old + lofs));
+                continue;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int rl = wm + h * 32 + lq + 4 * q;
+                const int32_t r = m0 + rl;
+                const int64_t v = n0 + wn + 4 * fr;
+                if (r < p.R) {
+                    const bool valid = sIdx[rl] >= 0;
+                    const f32x4 ov = valid ? val[q] : f32x4{kNaN, kNaN, kNaN, kNaN};
+                    if (vec_ok && v + 4 <= p.V) {
+                        __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (v + e < p.V) store_out<OUT_BF16>(p.out, (int64_t)r * p.old + v + e, ov[e]);
+                    }
                 }
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    };
+    if (p.scale_mode == 1)
+        epilogue(std::integral_constant<int, 1>{});
+    else if (p.scale_mode == 2)
+        epilogue(std::integral_constant<int, 2>{});
+    else
+        epilogue(std::integral_constant<int, 0>{});
 }
 
 // The reduction partial of one 64-logit block of logits row r, from the 16
