@@ -191,6 +191,36 @@ def test_bf16_output_and_invalid_rows():
     assert np.array_equal(bf16_bits(b.logits)[[0, 2, 4]], synth.f32_to_bf16_bits(zf[[0, 2, 4]]))
 
 
+@pytest.mark.parametrize("bits,group", [(4, 64), (4, 128), (8, 64)])
+def test_tiled_ragged_invalid_rows(bits, group):
+    """300 rows (a partial row tile) of a 5003-token vocabulary (a partial
+    vocab tile) through the tiled kernels (4-bit: the 64-wide stages with the
+    tile's scale/bias table): rows without a source are NaN and flagged,
+    bf16 output is the rounding of fp32, and 40 valid rows equal, bit for
+    bit, the same rows from the weight-streaming kernel."""
+    g = synth.rng(95 + bits + group)
+    H, V, T, R = 1024, 5003, 400, 300
+    hid = synth.normal_bf16(g, (T, H))
+    d = synth.quantized_head(96 + group, V, H, bits, group)
+    ex = g.integers(0, T, size=R).astype(np.int32)
+    bad = np.array([0, 150, 256, 299])
+    ex[bad] = [T, -1, T + 3, -2]
+    args = (bf16_tensor(hid), _qweight(d), i32_tensor([0, T]), 0)
+    f = lmh.lmhead_gather_project_q(*args, logits_indices=i32_tensor(ex), variant=lmh.LMH_HEAD_TILED)
+    b = lmh.lmhead_gather_project_q(*args, logits_indices=i32_tensor(ex), variant=lmh.LMH_HEAD_TILED,
+                                    out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    zf = f.logits.cpu().numpy()
+    good = np.setdiff1d(np.arange(R), bad)
+    assert np.all(np.isnan(zf[bad])) and np.all(np.isfinite(zf[good]))
+    assert int(f.device_error.item()) & lmh.LMH_DEVERR_INDEX
+    assert np.array_equal(bf16_bits(b.logits)[good], synth.f32_to_bf16_bits(zf[good]))
+    sel = g.choice(good, size=40, replace=False)
+    q = lmh.lmhead_gather_project_q(*args, logits_indices=i32_tensor(ex[sel]), variant=lmh.LMH_HEAD_STREAM)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.logits.cpu().numpy().view(np.uint32), zf[sel].view(np.uint32))
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 def test_fused_logprobs_q(bits):
     """lmhead_logprobs_q: the reduction of the projected rows matches the

@@ -840,6 +840,12 @@ constexpr int kT64Lds = 2 * kT64Stage + 2 * kTileM * 4;   // two stages, two row
 // eight waves: four (one per SIMD, 128 x 128 each) measured 1.23 ms against
 // 0.76 ms on the 2048-row Qwen3-0.6B projection
 
+// Staging registers of one 64-wide stage's W chunks (four per thread): bf16
+// chunks, or the 4-bit codes of the same elements with their group's
+// (scale, bias) pair from the tile's LDS table, dequantised on the LDS write.
+template <int BITS> struct T64B { u32x4 v[4]; };
+template <> struct T64B<4> { uint32_t q[4]; uint32_t sb[4]; };
+
 // Eight waves (two per SIMD), each 128 x 64 of the tile. The workgroups of an
 // XCD take its share of the tiles in the banded order (tile_of): with as many
 // workgroups as tiles each takes one; with PERSIST and fewer workgroups (one
@@ -854,7 +860,7 @@ constexpr int kT64Lds = 2 * kT64Stage + 2 * kTileM * 4;   // two stages, two row
 // a key and its (max, sum of exp(x - max)) partial -- the reduction's
 // streaming pass, done on the values while they are in registers (MTPLX PR
 // #532, Motivation: no second pass over a chunk's logits).
-template <bool OUT_BF16, bool FUSED, bool PERSIST>
+template <bool OUT_BF16, bool FUSED, bool PERSIST, int BITS = 16>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
     constexpr int NW = 8;
@@ -863,10 +869,16 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
     constexpr int NF = WN / 16;                         // B fragments per wave
     static_assert(NF == 4, "a wave's 64 columns are one 64-logit block");
     static_assert(!FUSED || !OUT_BF16, "partials of fp32 logits");
+    constexpr bool QUANT = BITS != 16;
+    static_assert(!QUANT || (BITS == 4 && !FUSED && !PERSIST), "4-bit weights: plain logits, one tile per workgroup");
+    using O = QOrder<QUANT ? BITS : 4>;
     constexpr int L = kTileM * (kT64K / 8) / NTH;       // chunks per thread per stage (A and B each)
     static_assert(L == 4, "eight chunk writes per stage, one per 16-row group of its first k-step");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int32_t* const sIdx2 = reinterpret_cast<int32_t*>(lds + 2 * kT64Stage);   // [2][kTileM] with PERSIST
+    // quantised: the tile's (scale, bias) pairs, [kTileN][groups + 1] dwords
+    uint32_t* const tab = reinterpret_cast<uint32_t*>(lds + 2 * kT64Stage + 2 * kTileM * 4);
+    const int tsp = QUANT ? (int)(p.H >> p.qw.gshift) + 1 : 0;
 
     const int32_t total = mtiles * ntiles;
     const int32_t per_xcd = (total + 7) / 8;
@@ -905,35 +917,74 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
     // this thread's staging chunks of tile lg (rows tid/8 + 64j, chunk tid%8)
     // as 32-bit byte offsets from the hidden matrix and from the tile's first
     // W row
+    // quantised: chunk c holds the 8 elements of lane quarter c % 4 for the
+    // stage's k-step c / 4, in the quantised order (step s of a code run
+    // gives lane quarter j the elements QB/4 j + 8 s of the run)
+    const int hc = QUANT ? c >> 2 : 0, jq = QUANT ? c & 3 : 0;
     uint32_t ga[L], gb[L];
     const uint8_t* wtile;
     auto addresses = [&](int32_t lg, const int32_t* src) {
         int32_t mt_, nt_;
         tile_of(lg, mtiles, ntiles, mt_, nt_);
         const int64_t nb0 = (int64_t)nt_ * kTileN;
-        wtile = reinterpret_cast<const uint8_t*>(p.W + nb0 * p.wld);
+        if constexpr (QUANT)
+            wtile = reinterpret_cast<const uint8_t*>(p.qw.q + nb0 * p.qw.qld);
+        else
+            wtile = reinterpret_cast<const uint8_t*>(p.W + nb0 * p.wld);
 #pragma unroll
         for (int j = 0; j < L; ++j) {
             const int row = (tid >> 3) + (NTH / 8) * j;
             const int32_t t = src[row];
-            ga[j] = (uint32_t)(((int64_t)(t < 0 ? 0 : t) * p.hld + c * 8) * 2);
-            const int64_t n = nb0 + row < p.V ? row : p.V - 1 - nb0;
-            gb[j] = (uint32_t)((n * p.wld + c * 8) * 2);
+            if constexpr (QUANT) {
+                const int64_t n = nb0 + row < p.V ? row : p.V - 1 - nb0;
+                ga[j] = (uint32_t)(((int64_t)(t < 0 ? 0 : t) * p.hld + O::QQ * jq) * 2);
+                gb[j] = (uint32_t)((n * p.qw.qld + 4 * jq) * 4);
+            } else {
+                ga[j] = (uint32_t)(((int64_t)(t < 0 ? 0 : t) * p.hld + c * 8) * 2);
+                const int64_t n = nb0 + row < p.V ? row : p.V - 1 - nb0;
+                gb[j] = (uint32_t)((n * p.wld + c * 8) * 2);
+            }
         }
     };
     // stage st of the tile whose addresses are set (st >= nst: stage st - nst)
-    auto gload = [&](int st, u32x4 (&ra)[L], u32x4 (&rb)[L]) {
-        const int64_t kb = (int64_t)(st < nst ? st : st - nst) * kT64K * 2;
-        const uint8_t* const hk = reinterpret_cast<const uint8_t*>(p.hidden) + kb;
-        const uint8_t* const wk = wtile + kb;
+    auto gload = [&](int st, u32x4 (&ra)[L], T64B<BITS>& rb) {
+        const int stt = st < nst ? st : st - nst;
+        if constexpr (!QUANT) {
+            const int64_t kb = (int64_t)stt * kT64K * 2;
+            const uint8_t* const hk = reinterpret_cast<const uint8_t*>(p.hidden) + kb;
+            const uint8_t* const wk = wtile + kb;
 #pragma unroll
-        for (int j = 0; j < L; ++j) ra[j] = *reinterpret_cast<const u32x4*>(hk + ga[j]);
+            for (int j = 0; j < L; ++j) ra[j] = *reinterpret_cast<const u32x4*>(hk + ga[j]);
 #pragma unroll
-        for (int j = 0; j < L; ++j) rb[j] = *reinterpret_cast<const u32x4*>(wk + gb[j]);
+            for (int j = 0; j < L; ++j) rb.v[j] = *reinterpret_cast<const u32x4*>(wk + gb[j]);
+        } else {
+            const int ks = 2 * stt + hc;                 // this thread's k-step
+            const int run = ks / O::SPB, sub = ks - run * O::SPB;
+            const uint8_t* const hk = reinterpret_cast<const uint8_t*>(p.hidden) + (run * O::QB + 8 * sub) * 2;
+            const uint8_t* const wk = wtile + (run * 16 + sub) * 4;
+            const int g = (run * O::QB + O::QQ * jq) >> p.qw.gshift;
+#pragma unroll
+            for (int j = 0; j < L; ++j) ra[j] = *reinterpret_cast<const u32x4*>(hk + ga[j]);
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                rb.q[j] = *reinterpret_cast<const uint32_t*>(wk + gb[j]);
+                rb.sb[j] = tab[((tid >> 3) + (NTH / 8) * j) * tsp + g];
+            }
+        }
+    };
+    // W chunk j of a stage, as written to LDS
+    auto wchunk = [&](const T64B<BITS>& rb, int j) -> u32x4 {
+        if constexpr (!QUANT) {
+            return rb.v[j];
+        } else {
+            const float sf = __uint_as_float(rb.sb[j] << 16);
+            const float bf = __uint_as_float(rb.sb[j] & 0xFFFF0000u);
+            return dequant8<4>(rb.q[j], 0u, sf, bf);
+        }
     };
     f32x4 acc[8][NF];
     auto step = [&](const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr, int st, u32x4 (&la)[L],
-                    u32x4 (&lb)[L], const u32x4 (&wa)[L], const u32x4 (&wb)[L]) {
+                    T64B<BITS>& lb, const u32x4 (&wa)[L], const T64B<BITS>& wb) {
         __builtin_amdgcn_sched_barrier(0);
         // the second k-step's first two fragments, read during the first
         // k-step's seventh 16-row group (2 % on the 2048-row projection)
@@ -970,7 +1021,7 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
                     if (i < L)
                         *reinterpret_cast<u32x4*>(wr + wofs[i]) = wa[i];
                     else
-                        *reinterpret_cast<u32x4*>(wr + kTileM * 128 + wofs[i - L]) = wb[i - L];
+                        *reinterpret_cast<u32x4*>(wr + kTileM * 128 + wofs[i - L]) = wchunk(wb, i - L);
                     if (i == 0) gload(st, la, lb);
                     if (i == 6) {
                         pa = *reinterpret_cast<const u32x4*>(rd + (uint32_t)(wm * 128) + rofs1);
@@ -982,18 +1033,32 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
         }
     };
 
-    // the first tile: its row sources, its first two stages
+    // the first tile: its row sources (and, quantised, its scale/bias
+    // table), its first two stages
     int cur = 0;
     sources(logical, sIdx2);
+    if constexpr (QUANT) {
+        int32_t mt_, nt_;
+        tile_of(logical, mtiles, ntiles, mt_, nt_);
+        const int64_t nb0 = (int64_t)nt_ * kTileN;
+        const int ng = tsp - 1;
+        for (int e = tid; e < kTileN * ng; e += NTH) {
+            const int row = e / ng;
+            const int g = e - row * ng;
+            const int64_t n = nb0 + row < p.V ? nb0 + row : p.V - 1;
+            tab[row * tsp + g] = (uint32_t)p.qw.scales[n * p.qw.sld + g] | ((uint32_t)p.qw.biases[n * p.qw.sld + g] << 16);
+        }
+    }
     __syncthreads();
     addresses(logical, sIdx2);
-    u32x4 ra0[L], ra1[L], rb0[L], rb1[L];
+    u32x4 ra0[L], ra1[L];
+    T64B<BITS> rb0, rb1;
     gload(0, ra0, rb0);
     gload(1, ra1, rb1);
 #pragma unroll
     for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(lds + wofs[j]) = ra0[j];
 #pragma unroll
-    for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(lds + kTileM * 128 + wofs[j]) = rb0[j];
+    for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(lds + kTileM * 128 + wofs[j]) = wchunk(rb0, j);
     __syncthreads();
 
     while (true) {
@@ -1210,10 +1275,21 @@ hipError_t launch_tiled_q(const HeadParams& p, int32_t mtiles, int32_t ntiles, h
 // Persistent walk when every CU gets at least four tiles, for plain fp32
 // logits (the bf16-output and partials epilogues do not fit the registers
 // beside the next tile's state); otherwise one workgroup per tile.
-template <bool OUT_BF16, bool FUSED = false>
+template <bool OUT_BF16, bool FUSED = false, int BITS = 16>
 hipError_t launch_tiled64(const HeadParams& p, int32_t mtiles, int32_t ntiles, hipStream_t s) {
     const int64_t total = (int64_t)mtiles * ntiles;
     const int cus = cu_count();
+    if constexpr (BITS != 16) {
+        // one tile per workgroup; the tile's (scale, bias) table after the
+        // row-source lists
+        const size_t lds = (size_t)kT64Lds + (size_t)kTileN * (size_t)((p.H >> p.qw.gshift) + 1) * 4;
+        const void* fn = (const void*)k_head_tiled64<OUT_BF16, false, false, BITS>;
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        const dim3 grid((unsigned)(((total + 7) / 8) * 8));
+        hipLaunchKernelGGL((k_head_tiled64<OUT_BF16, false, false, BITS>), grid, dim3(512), lds, s, p, mtiles, ntiles);
+        return hipGetLastError();
+    }
     if constexpr (!OUT_BF16 && !FUSED) {
         if (cus > 0 && total >= 4 * (int64_t)cus) {
             const void* fn = (const void*)k_head_tiled64<false, false, true>;
@@ -1288,10 +1364,28 @@ hipError_t launch_head_stream_q(const HeadArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+// The 4-bit tiled head takes the 64-wide-stage kernel when the tile's
+// (scale, bias) table fits beside its stage buffers (at most 29 groups per
+// row: hidden 1856 at group 64) and the hidden offsets fit 32 bits.
+bool tiled64_q_ok(const HeadParams& p) {
+    const int64_t groups = p.H >> p.qw.gshift;
+    return tiled64_fits(p.num_tokens, p.hld, p.H, 0) &&
+           (int64_t)kT64Lds + (int64_t)kTileN * (groups + 1) * 4 <= 160 * 1024;
+}
+
 hipError_t launch_head_tiled_q(const HeadArgs& a, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
     if (a.hidden_dim % 128) return hipErrorInvalidValue;
     const HeadParams p = to_params(a);
+    // 4-bit codes (2048-row Qwen3-0.6B projection: 830 -> 790 us); 8-bit codes
+    // keep the 32-wide kernel, whose registers hold their second code word
+    // without spilling (the 64-wide form measured 851 against 828 us)
+    if (a.bits == 4 && tiled64_q_ok(p)) {
+        const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
+        const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
+        return a.out_bf16 ? launch_tiled64<true, false, 4>(p, mtiles, ntiles, s)
+                          : launch_tiled64<false, false, 4>(p, mtiles, ntiles, s);
+    }
     const int32_t mtiles = (a.rows + kTileM - 1) / kTileM;
     const int32_t ntiles = (int32_t)((a.vocab + kTileN - 1) / kTileN);
     if (a.bits == 4)
