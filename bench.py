@@ -99,8 +99,9 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
         qbytes = 151936 * 1024 * bits // 8 + 151936 * 16 * 4
         wanted[f"head_stream_q{bits}"] = (f"k_head_stream_q<3, 1, {bits}, ", "head.hip",
                                           qbytes + 40 * 1024 * 2 + 40 * 151936 * 4, None)
-        wanted[f"head_tiled_q{bits}"] = (f"k_head_tiled<false, {bits}, ", "head.hip",
-                                         qbytes + 2048 * 1024 * 2 + 2048 * 151936 * 4, None)
+        # 4-bit: the 64-wide-stage kernel; 8-bit: the 32-wide one
+        pat = "k_head_tiled64<false, false, false, 4>" if bits == 4 else f"k_head_tiled<false, {bits}, "
+        wanted[f"head_tiled_q{bits}"] = (pat, "head.hip", qbytes + 2048 * 1024 * 2 + 2048 * 151936 * 4, None)
     res = {"calibration": {"kernel": copy[0][0][:80], "bytes_read": nbytes, "bytes_written": nbytes,
                            "fetch_kib": fetch[copy[0]], "write_kib": write[copy[0]],
                            "fetch_factor": round(f_fetch, 5), "write_factor": round(f_write, 5)}}
