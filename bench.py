@@ -84,14 +84,14 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> None:
                                  151936 * 1024 * 2 + 40 * 1024 * 2 + 40 * 151936 * 4, None),
               # the Qwen3-0.6B 2048-row projection (4752 tiles walked by one
               # workgroup of 512 per CU)
-              "head_tiled_bf16": ("k_head_tiled64<false, false, true>", "head.hip",
+              "head_tiled_bf16": ("k_head_tiled64<false, false, true, 16>", "head.hip",
                                   151936 * 1024 * 2 + 2048 * 1024 * 2 + 2048 * 151936 * 4, None),
               # a Llama-3-8B prompt chunk of 256 rows, without and with the
               # reduction's first pass in the epilogue (then per block an
               # 8-byte partial and a 4-byte key as well)
-              "head_tiled_chunk_bf16": ("k_head_tiled64<false, false, false>", "head.hip",
+              "head_tiled_chunk_bf16": ("k_head_tiled64<false, false, false, 16>", "head.hip",
                                         llama_w + 256 * 4096 * 2 + 256 * 128256 * 4, 504 * 512),
-              "head_tiled_epilogue_bf16": ("k_head_tiled64<false, true, false>", "head.hip",
+              "head_tiled_epilogue_bf16": ("k_head_tiled64<false, true, false, 16>", "head.hip",
                                            llama_w + 256 * 4096 * 2 + 256 * 128256 * 4 + 256 * 2004 * 12,
                                            504 * 512),
               "reduce_stage2_blocks": ("k_stage2<0, 8, true>", "reduce.hip", None, None)}
