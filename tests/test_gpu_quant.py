@@ -87,6 +87,9 @@ CASES = [  # (bits, group, H, V)
     (8, 128, 1024, 1024),
     # more than 86 groups per row: the tiled kernel loads scales per stage
     (4, 32, 3072, 700), (8, 32, 2816, 500),
+    # 4-bit on either side of the 64-wide-stage kernel's 29-group table limit
+    # (28 groups there, 32 and 48 on the 32-wide-stage kernel's LDS table)
+    (4, 32, 896, 1003), (4, 32, 1024, 1003), (4, 32, 1536, 515),
 ]
 
 
@@ -138,10 +141,13 @@ def test_quant_equals_dense_on_rounded_weights(bits, group, H, V, R):
     assert np.array_equal(zq.cpu().numpy().view(np.uint32), zd.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("bits,group", [(4, 64), (8, 128), (4, 32)])
-def test_stream_and_tiled_bitwise_equal(bits, group):
+@pytest.mark.parametrize("bits,group,H", [(4, 64, 512), (8, 128, 512), (4, 32, 512), (4, 32, 1024)])
+def test_stream_and_tiled_bitwise_equal(bits, group, H):
+    """The streaming and tiled kernels sum in one order: bitwise equal logits
+    (4-bit at 16 groups per row takes the 64-wide-stage tiled kernel, at 32
+    the 32-wide-stage one)."""
     g = synth.rng(77 + bits + group)
-    H, V, T = 512, 5003, 100
+    V, T = 5003, 100
     hid = synth.normal_bf16(g, (T, H))
     d = synth.quantized_head(78, V, H, bits, group)
     ex = i32_tensor(g.integers(0, T, size=64).astype(np.int32))
