@@ -53,11 +53,15 @@ def test_small_integers_exact(H, R):
 
 
 @pytest.mark.parametrize("H,R,V", [(1024, 40, 20011), (512, 5, 4097), (2048, 64, 9000),
-                                   (1536, 33, 16), (1024, 16, 100), (2048, 48, 50257)])
+                                   (1536, 33, 16), (1024, 16, 100), (2048, 48, 50257),
+                                   (1024, 40, 4100), (512, 64, 20012)])
 def test_bitwise_equal_to_stream_and_tiled(H, R, V):
     """Random bf16 rows: the pipelined, streaming and tiled kernels give the
     same bits; all within the head tolerance of the f64 oracle. V = 16 and
-    V = 100 give fewer 16-row tiles than workgroups."""
+    V = 100 give fewer 16-row tiles than workgroups; with fp32 logits and V a
+    multiple of 4 (9000, 100, 4100, 20012) tile pairs are stored as whole
+    rows, and runs of one or two tiles that start or end inside a pair store
+    their half alone (4100: a last tile of four columns)."""
     g = synth.rng(H + 7 * R + V)
     T = 300
     hid = synth.normal_bf16(g, (T, H))
