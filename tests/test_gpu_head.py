@@ -271,3 +271,43 @@ def test_pure_decode_identity():
     torch.cuda.synchronize()
     assert np.array_equal(p.gather_indices.cpu().numpy(), np.arange(33))
     assert torch.equal(p.logits.view(torch.int32), full.view(torch.int32))
+
+
+@pytest.mark.parametrize("weights", ["bf16", "q4"])
+@pytest.mark.parametrize("mode,s", [(lmh.LMH_SCALE_NONE, 1.0), (lmh.LMH_SCALE_MUL, 0.125), (lmh.LMH_SCALE_DIV, 3.0)])
+@pytest.mark.parametrize("pad", [0, 4, 1])
+def test_stream_row_segment_stores(weights, mode, s, pad):
+    """The streaming kernels' fp32 logits go out as whole row segments through
+    LDS when the vocabulary and the row pitch are multiples of 4 (pad 0, 4;
+    pad 1 takes the element stores): bitwise the tiled kernel's logits, NaN
+    on the rows without a source, the pitch padding untouched, with and
+    without output scaling; V = 5000 leaves the last workgroup's columns
+    partly past the vocabulary."""
+    g = synth.rng(4300 + pad + 7 * mode)
+    H, V, T, R = 1024, 5000, 200, 40
+    hid = synth.normal_bf16(g, (T, H))
+    if weights == "bf16":
+        wt = bf16_tensor(synth.normal_bf16(g, (V, H), H ** -0.5))
+    else:
+        d = synth.quantized_head(4301, V, H, 4, 64)
+        wt = lmh.QuantizedWeight(torch.from_numpy(d["q"].view(np.int32)).cuda(), bf16_tensor(d["scales"]),
+                                 bf16_tensor(d["biases"]), 4, 64)
+    head = lmh.HeadSpec(wt, mode, s)
+    ex = g.integers(0, T, size=R).astype(np.int32)
+    bad = np.array([2, 17, 39])
+    ex[bad] = T + 5                                            # no source: NaN rows
+    args = (bf16_tensor(hid), head, i32_tensor([0, T]), 0)
+    out = torch.full((R, V + pad), 7.0, dtype=torch.float32, device="cuda")
+    print(f"stream row segments {weights} mode {mode} pad {pad}", flush=True)
+    st = lmh.lmhead_gather_project_ex(*args, logits_indices=i32_tensor(ex), logits=out[:, :V],
+                                      variant=lmh.LMH_HEAD_STREAM)
+    ti = lmh.lmhead_gather_project_ex(*args, logits_indices=i32_tensor(ex), variant=lmh.LMH_HEAD_TILED)
+    torch.cuda.synchronize()
+    a = out[:, :V].cpu().numpy()
+    b = ti.logits.cpu().numpy()
+    good = np.setdiff1d(np.arange(R), bad)
+    assert np.all(np.isnan(a[bad]))
+    assert np.array_equal(a[good].view(np.uint32), b[good].view(np.uint32))
+    assert int(st.device_error.item()) & lmh.LMH_DEVERR_INDEX
+    if pad:
+        assert torch.all(out[:, V:] == 7.0)
