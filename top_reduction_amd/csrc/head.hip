@@ -134,11 +134,12 @@ __device__ inline void store_rows_staged(const HeadParams& p, float* __restrict_
 
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel: MT row tiles of 16 (R <= 16*MT) against a slab of
-// 64*NT W rows per workgroup (16*NT per wave), k in chunks of 128. Each wave
-// loads its W fragments straight from HBM into MFMA B operands a whole chunk
-// ahead; the gathered hidden rows come through double-buffered LDS, shared by
-// the 4 waves. Small slabs keep the last, partly filled round of workgroups
-// short.
+// 64*NT W rows per workgroup (16*NT per wave), k in chunks of KC (256). Each
+// wave loads its W fragments straight from HBM into MFMA B operands a whole
+// chunk ahead; the gathered hidden rows come through double-buffered LDS,
+// shared by the 4 waves. Small slabs keep the last, partly filled round of
+// workgroups short. fp32 logits leave as whole row segments through LDS
+// (store_rows_staged) where the vocabulary and the row pitch allow.
 // ---------------------------------------------------------------------------
 template <int MT, int NT, bool KFULL, bool OUT_BF16>
 __global__ __launch_bounds__(kStreamThreads) void k_head_stream(HeadParams p) {
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_head_stream(HeadParams p) {
 // lane per QB hidden elements plus the lane's group scale and bias, and
 // dequantised to bf16 in registers right before their MFMAs. The hidden size
 // is a multiple of 128, so every run is whole; runs past the hidden size (in
-// the last chunk) are skipped.
+// the last chunk) are skipped. The logits leave as in k_head_stream.
 // ---------------------------------------------------------------------------
 // NG > 0: the chunk's NG group scales (and biases) of a W row are read with
 // one vector load per lane (the hidden size is a multiple of KC = NG * group
