@@ -272,3 +272,33 @@ def test_decode_qwen3_shape_sampled_columns(bits):
     sub = dict(d, q=np.ascontiguousarray(d["q"][cols]), scales=np.ascontiguousarray(d["scales"][cols]),
                biases=np.ascontiguousarray(d["biases"][cols]))
     _check_vs_oracle(np.ascontiguousarray(z[:, cols]), hid, np.arange(R, dtype=np.int32), _exact_weights(sub))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_qwen3_shape_full_rows(bits):
+    """The launches the benchmark times at the Qwen3-0.6B head shape (hidden
+    1024, vocab 151,936, group 64): the 40 selected rows of 40 prefills of
+    2048 (the streaming kernel) and 8 seeded rows of segment 0's 2048-row
+    projection (the tiled kernel), every logit of every row against the
+    oracle; the selected rows equal, bit for bit, the same rows of the full
+    projection."""
+    d = synth.selective_head_batch(4100)
+    T, H = d["hidden"].shape
+    V = synth.VOCAB_QWEN3
+    q = synth.quantized_head(4101, V, H, bits, 64)
+    hid = bf16_tensor(d["hidden"])
+    qw = _qweight(q)
+    cu = i32_tensor(d["cu_seqlens"])
+    sel = lmh.lmhead_gather_project_q(hid, qw, cu, 0)
+    full = lmh.lmhead_gather_project_q(hid, qw, cu, 0, logits_indices=i32_tensor(np.arange(2048))).logits
+    torch.cuda.synchronize()
+    idx = (2047 + 2048 * np.arange(40)).astype(np.int32)
+    w_exact = _exact_weights(q)
+    print(f"oracle quantised head ({bits}-bit): 40 x 151936 x 1024", flush=True)
+    _check_vs_oracle(sel.logits.cpu().numpy(), d["hidden"], idx, w_exact)
+    rows = np.sort(synth.rng(4102).choice(2048, size=8, replace=False)).astype(np.int32)
+    rows[-1] = 2047
+    print(f"oracle quantised head ({bits}-bit): 8 rows of the 2048-row projection", flush=True)
+    zf = full.cpu().numpy()
+    _check_vs_oracle(np.ascontiguousarray(zf[rows]), d["hidden"], rows, w_exact)
+    assert np.array_equal(zf[2047].view(np.uint32), sel.logits.cpu().numpy()[0].view(np.uint32))
