@@ -161,3 +161,31 @@ def test_rejects_shapes_outside_its_range(H, R):
     with pytest.raises(RuntimeError, match="LMH_ERR_SHAPE"):
         lmh.lmhead_gather_project(hid, w, i32_tensor([0, R]), 0,
                                   logits_indices=i32_tensor(np.arange(R)), variant=PIPE)
+
+
+@pytest.mark.parametrize("V", [9000, 4104, 64, 5000])
+def test_bf16_logits_grouped_rows(V):
+    """bf16 logits with a vocabulary that is a multiple of 8 leave in groups
+    of four tiles as whole 128-byte rows (5000 = 8 * 625 too; runs that start
+    or end inside a group store their part alone): the round-to-nearest-even
+    of the fp32 logits, NaN on rows without a source, the pitch padding
+    untouched."""
+    g = synth.rng(4400 + V)
+    H, T, R = 1024, 120, 40
+    hid = synth.normal_bf16(g, (T, H))
+    w = synth.normal_bf16(g, (V, H), H ** -0.5)
+    ex = g.integers(0, T, size=R).astype(np.int32)
+    ex[[5, 33]] = T + 3                                      # no source
+    a = (bf16_tensor(hid), bf16_tensor(w), i32_tensor([0, T]), 0)
+    print(f"pipe bf16 grouped rows V={V}", flush=True)
+    ref = lmh.lmhead_gather_project(*a, logits_indices=i32_tensor(ex), variant=PIPE).logits
+    out = torch.full((R, V + 8), 7.0, dtype=torch.bfloat16, device="cuda")
+    lmh.lmhead_gather_project(*a, logits_indices=i32_tensor(ex), logits=out[:, :V], variant=PIPE)
+    torch.cuda.synchronize()
+    z = ref.cpu().numpy()
+    bits = bf16_bits(out[:, :V])
+    good = np.setdiff1d(np.arange(R), [5, 33])
+    assert np.all(np.isnan(z[[5, 33]]))
+    assert np.all(((bits[[5, 33]] & 0x7F80) == 0x7F80) & ((bits[[5, 33]] & 0x7F) != 0))   # NaN
+    assert np.array_equal(bits[good], synth.f32_to_bf16_bits(z[good]))
+    assert torch.all(out[:, V:] == 7.0)

@@ -36,15 +36,16 @@ constexpr int kPipeInflight = LMH_PIPE_INFLIGHT; // k-steps of weight fragments 
 // again by this launch; measured 2-5 % faster than default stores at 40 and
 // 64 rows of the Qwen3-0.6B head)
 constexpr int kNT = 2;
-// fp32 logits go out in groups of kStoreTiles tiles (whole 128-byte rows):
-// 68.2 against 70.2 us for 64-byte row pieces at 40 rows of the Qwen3-0.6B
-// head (groups of four 68.0, of eight 72.7)
-constexpr int kStoreTiles = 2;
+// Logits go out in groups of tiles that make whole 128-byte rows: two tiles
+// of fp32, four of bf16 (fp32: 68.2 against 70.2 us for 64-byte row pieces
+// at 40 rows of the Qwen3-0.6B head; groups of four 68.0, of eight 72.7)
+template <bool OUT_BF16> constexpr int store_tiles() { return OUT_BF16 ? 4 : 2; }
 
 // Logits output: the last wave stages each tile's logits in LDS and stores
-// every aligned pair of tiles as whole 128-byte rows with 16-byte stores
-// (VEC: fp32 logits, vocabulary a multiple of 4), or stores each tile right
-// away with 4-byte (2-byte for bf16) stores. Head output scaling: x /
+// every aligned group of tiles as whole 128-byte rows with 16-byte stores
+// (VEC: a vocabulary that is a multiple of 4 for fp32 logits, of 8 for
+// bf16), or stores each tile right away with 4-byte (2-byte for bf16)
+// stores. Head output scaling: x /
 // scale (DIV), else x * smul (1 without scaling: exact); the mode is a
 // template parameter because a branch around the stores would cost the
 // compiler its exact wait counts.
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(64 * kPipeWaves) void k_head_pipe(HeadParams p, int
     extern __shared__ __attribute__((aligned(16))) unsigned char pipe_smem[];
     f32x4* slot = reinterpret_cast<f32x4*>(pipe_smem);                        // [2][WAVES-1][MT][64]
     int32_t* sIdx = reinterpret_cast<int32_t*>(pipe_smem + 2 * SLOT * 16);    // [MT*16]
-    float* stage_out = reinterpret_cast<float*>(pipe_smem + 2 * SLOT * 16 + MT * 16 * 4);   // [MT*16][16*kStoreTiles]
+    float* stage_out = reinterpret_cast<float*>(pipe_smem + 2 * SLOT * 16 + MT * 16 * 4);   // [MT*16][16*store_tiles]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(64 * kPipeWaves) void k_head_pipe(HeadParams p, int
             // the P tiles of an aligned group are staged side by side and
             // stored as whole 64 * P-byte rows once the group's last tile of
             // this run is in (the run's first and last groups may be partial)
-            constexpr int P = kStoreTiles;
+            constexpr int P = store_tiles<OUT_BF16>();
             constexpr int CW = 16 * P;                       // staged columns
             const int32_t tg = t0 + j;
             const int part = tg % P;
@@ -137,19 +138,30 @@ __global__ __launch_bounds__(64 * kPipeWaves) void k_head_pipe(HeadParams p, int
                 for (int e = 0; e < 4; ++e) stage_out[(i * 16 + rl + e) * CW + part * 16 + l16] = value(i, e);
             if (part == P - 1 || j == n - 1) {
                 const int32_t g0 = tg - part;                // the group's first tile
-                constexpr int LPR = CW / 4;                  // lanes per row (16 bytes each)
+                constexpr int EPL = OUT_BF16 ? 8 : 4;        // logits per 16-byte store
+                constexpr int LPR = CW / EPL;                // lanes per row
                 constexpr int RPI = 64 / LPR;                // rows per store instruction
-                const int cq = (lane % LPR) * 4;
-                const int32_t tq = g0 + cq / 16;             // the tile of this lane's column
+                const int cq = (lane % LPR) * EPL;
+                const int32_t tq = g0 + cq / 16;             // the tile of this lane's columns
                 const bool part_ok = tq >= t0 && tq <= tg;
                 const int64_t col = (int64_t)g0 * 16 + cq;
 #pragma unroll
                 for (int i2 = 0; i2 < MT * 16 / RPI; ++i2) {
                     const int r = i2 * RPI + lane / LPR;
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(&stage_out[r * CW + cq]);
                     const bool ok = part_ok && col < p.V && r < p.R;
-                    const uint32_t off = ok ? (uint32_t)r * rowbytes + (uint32_t)col * 4u : 0x80000000u;
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), orsrc, off, 0, kNT);
+                    const uint32_t off = ok ? (uint32_t)r * rowbytes + (uint32_t)col * ES : 0x80000000u;
+                    u32x4 word;
+                    if constexpr (OUT_BF16) {
+                        const f32x4 v0 = *reinterpret_cast<const f32x4*>(&stage_out[r * CW + cq]);
+                        const f32x4 v1 = *reinterpret_cast<const f32x4*>(&stage_out[r * CW + cq + 4]);
+                        word = u32x4{(uint32_t)f32_to_bf16_rne(v0[0]) | ((uint32_t)f32_to_bf16_rne(v0[1]) << 16),
+                                     (uint32_t)f32_to_bf16_rne(v0[2]) | ((uint32_t)f32_to_bf16_rne(v0[3]) << 16),
+                                     (uint32_t)f32_to_bf16_rne(v1[0]) | ((uint32_t)f32_to_bf16_rne(v1[1]) << 16),
+                                     (uint32_t)f32_to_bf16_rne(v1[2]) | ((uint32_t)f32_to_bf16_rne(v1[3]) << 16)};
+                    } else {
+                        word = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(&stage_out[r * CW + cq]));
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(word, orsrc, off, 0, kNT);
                 }
             }
         } else {
@@ -252,7 +264,7 @@ hipError_t launch_pipe_k(const HeadParams& p, hipStream_t s) {
     int64_t g = (int64_t)cu_count();
     if (g <= 0) return hipErrorInvalidDevice;
     if (g > ntiles) g = ntiles;
-    const size_t lds = (size_t)2 * (W - 1) * MT * 64 * 16 + (size_t)MT * 16 * 4 + (VEC ? (size_t)MT * 16 * 16 * kStoreTiles * 4 : 0);
+    const size_t lds = (size_t)2 * (W - 1) * MT * 64 * 16 + (size_t)MT * 16 * 4 + (VEC ? (size_t)MT * 16 * 16 * store_tiles<OUT_BF16>() * 4 : 0);
     const void* fn = (const void*)k_head_pipe<MT, KSW, D, OUT_BF16, DIV, VEC>;
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -272,14 +284,14 @@ hipError_t launch_pipe_ksw(const HeadParams& p, int ksw, hipStream_t s) {
     }
 }
 
-// fp32 logits with a vocabulary that is a multiple of 4 store 16 bytes per
-// lane (the row pitch and base are 16-byte aligned by contract)
+// 16 bytes per lane when the vocabulary is a multiple of 4 fp32 or 8 bf16
+// logits (the row pitch and base are 16-byte aligned by contract)
 template <int MT, bool OUT_BF16>
 hipError_t launch_pipe_mt(const HeadParams& p, int ksw, hipStream_t s) {
     const bool div = p.scale_mode == 2;
-    if (!OUT_BF16 && p.V % 4 == 0)
-        return div ? launch_pipe_ksw<MT, false, true, true>(p, ksw, s)
-                   : launch_pipe_ksw<MT, false, false, true>(p, ksw, s);
+    if (p.V % (OUT_BF16 ? 8 : 4) == 0)
+        return div ? launch_pipe_ksw<MT, OUT_BF16, true, true>(p, ksw, s)
+                   : launch_pipe_ksw<MT, OUT_BF16, false, true>(p, ksw, s);
     return div ? launch_pipe_ksw<MT, OUT_BF16, true, false>(p, ksw, s)
                : launch_pipe_ksw<MT, OUT_BF16, false, false>(p, ksw, s);
 }
