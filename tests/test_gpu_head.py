@@ -311,3 +311,27 @@ def test_stream_row_segment_stores(weights, mode, s, pad):
     assert int(st.device_error.item()) & lmh.LMH_DEVERR_INDEX
     if pad:
         assert torch.all(out[:, V:] == 7.0)
+
+
+@pytest.mark.parametrize("H", [128, 96])
+@pytest.mark.parametrize("pad", [0, 1, 3, 9])
+def test_tiled_bf16_logits_pitches(H, pad):
+    """bf16 logits of the tiled kernels (64-wide stages at H = 128, 32-wide at
+    96) go out four per 8-byte store when the row pitch is a multiple of 4
+    (V + pad = 3000, 3008) and one by one otherwise (2999, 3002): the
+    round-to-nearest-even of the fp32 logits either way, the pitch padding
+    untouched; V = 2999 leaves a last group of three columns."""
+    g = synth.rng(4500 + H + pad)
+    T, V, R = 300, 2999, 270
+    hid = synth.normal_bf16(g, (T, H))
+    w = synth.normal_bf16(g, (V, H), H ** -0.5)
+    ex = g.integers(0, T, size=R).astype(np.int32)
+    args = (bf16_tensor(hid), bf16_tensor(w), i32_tensor([0, T]), 0)
+    print(f"tiled bf16 logits H={H} pad={pad}", flush=True)
+    f = lmh.lmhead_gather_project(*args, logits_indices=i32_tensor(ex), variant=lmh.LMH_HEAD_TILED).logits
+    out = torch.full((R, V + pad), 3.0, dtype=torch.bfloat16, device="cuda")
+    lmh.lmhead_gather_project(*args, logits_indices=i32_tensor(ex), logits=out[:, :V], variant=lmh.LMH_HEAD_TILED)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(out[:, :V]), synth.f32_to_bf16_bits(f.cpu().numpy()))
+    if pad:
+        assert torch.all(out[:, V:] == 3.0)

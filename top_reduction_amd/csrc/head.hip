@@ -62,6 +62,15 @@ __device__ inline void store_out(void* out, int64_t off, float v) {
         __builtin_nontemporal_store(v, reinterpret_cast<float*>(out) + off);
 }
 
+// Four consecutive bf16 logits (elements off .. off + 3, off a multiple of 4
+// on an 8-byte aligned output) as one 8-byte store.
+__device__ inline void store_bf16x4(void* out, int64_t off, const f32x4& v) {
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+    __builtin_nontemporal_store(((uint64_t)hi << 32) | lo,
+                                reinterpret_cast<uint64_t*>(reinterpret_cast<uint16_t*>(out) + off));
+}
+
 // Drives step(PF, c, current, next) over chunks 0..n-1 with two weight
 // register sets that alternate without copies (a copy of a prefetch
 // destination would wait for the prefetch). Inside the loop every step
@@ -780,6 +789,8 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
     float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 68);
     const bool vec_ok = !OUT_BF16 && (p.old % 4 == 0) &&
                         ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+    // bf16 logits: four per 8-byte store
+    const bool bf_ok = OUT_BF16 && (p.old % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.out) & 7) == 0);
     const bool rows_sourced = __all(sIdx[wm + lane] >= 0 && sIdx[wm + 64 + lane] >= 0);
     const bool fast = vec_ok && rows_sourced && m0 + wm + 128 <= p.R && n0 + wn + kWaveN <= p.V;
     float* const wout = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + wm) * p.old + (n0 + wn);
@@ -826,6 +837,8 @@ void k_head_tiled(HeadParams p, int32_t mtiles, int32_t ntiles) {
                     const f32x4 ov = valid ? val[q] : f32x4{kNaN, kNaN, kNaN, kNaN};
                     if (vec_ok && v + 4 <= p.V) {
                         __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + v));
+                    } else if (bf_ok && v + 4 <= p.V) {
+                        store_bf16x4(p.out, (int64_t)r * p.old + v, ov);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -1155,6 +1168,8 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
         float* stg = reinterpret_cast<float*>(lds + kT64Stage) + wave * (16 * 68);
         const bool vec_ok = !OUT_BF16 && (p.old % 4 == 0) &&
                             ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+        // bf16 logits: four per 8-byte store
+        const bool bf_ok = OUT_BF16 && (p.old % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.out) & 7) == 0);
         const bool rows_sourced = __all(sIdx[wm + lane] >= 0 && sIdx[wm + 64 + lane] >= 0);
         const bool fast = vec_ok && rows_sourced && m0 + wm + 128 <= p.R && n0 + wn + WN <= p.V;
         float* const wout = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + wm) * p.old + (n0 + wn);
@@ -1201,6 +1216,8 @@ void k_head_tiled64(HeadParams p, int32_t mtiles, int32_t ntiles) {
                     } else if (r < p.R) {
                         if (vec_ok && v + 4 <= p.V) {
                             __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(o));
+                        } else if (bf_ok && v + 4 <= p.V) {
+                            store_bf16x4(p.out, (int64_t)r * p.old + v, ov);
                         } else {
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
