@@ -275,14 +275,15 @@ def test_pure_decode_identity():
 
 @pytest.mark.parametrize("weights", ["bf16", "q4"])
 @pytest.mark.parametrize("mode,s", [(lmh.LMH_SCALE_NONE, 1.0), (lmh.LMH_SCALE_MUL, 0.125), (lmh.LMH_SCALE_DIV, 3.0)])
-@pytest.mark.parametrize("pad", [0, 4, 1])
-def test_stream_row_segment_stores(weights, mode, s, pad):
-    """The streaming kernels' fp32 logits go out as whole row segments through
-    LDS when the vocabulary and the row pitch are multiples of 4 (pad 0, 4;
-    pad 1 takes the element stores): bitwise the tiled kernel's logits, NaN
-    on the rows without a source, the pitch padding untouched, with and
-    without output scaling; V = 5000 leaves the last workgroup's columns
-    partly past the vocabulary."""
+@pytest.mark.parametrize("odt,pad", [("f32", 0), ("f32", 4), ("f32", 1), ("bf16", 0), ("bf16", 8), ("bf16", 4)])
+def test_stream_row_segment_stores(weights, mode, s, odt, pad):
+    """The streaming kernels' logits go out as whole row segments through LDS
+    when the vocabulary and the row pitch are multiples of 4 fp32 or 8 bf16
+    logits (fp32 pad 0, 4; bf16 pad 0, 8; the others take the element
+    stores): bitwise the tiled kernel's fp32 logits (bf16: their
+    round-to-nearest-even), NaN on the rows without a source, the pitch
+    padding untouched, with and without output scaling; V = 5000 leaves the
+    last workgroup's columns partly past the vocabulary."""
     g = synth.rng(4300 + pad + 7 * mode)
     H, V, T, R = 1024, 5000, 200, 40
     hid = synth.normal_bf16(g, (T, H))
@@ -297,17 +298,23 @@ def test_stream_row_segment_stores(weights, mode, s, pad):
     bad = np.array([2, 17, 39])
     ex[bad] = T + 5                                            # no source: NaN rows
     args = (bf16_tensor(hid), head, i32_tensor([0, T]), 0)
-    out = torch.full((R, V + pad), 7.0, dtype=torch.float32, device="cuda")
-    print(f"stream row segments {weights} mode {mode} pad {pad}", flush=True)
+    tdt = torch.float32 if odt == "f32" else torch.bfloat16
+    out = torch.full((R, V + pad), 7.0, dtype=tdt, device="cuda")
+    print(f"stream row segments {weights} mode {mode} {odt} pad {pad}", flush=True)
     st = lmh.lmhead_gather_project_ex(*args, logits_indices=i32_tensor(ex), logits=out[:, :V],
                                       variant=lmh.LMH_HEAD_STREAM)
     ti = lmh.lmhead_gather_project_ex(*args, logits_indices=i32_tensor(ex), variant=lmh.LMH_HEAD_TILED)
     torch.cuda.synchronize()
-    a = out[:, :V].cpu().numpy()
     b = ti.logits.cpu().numpy()
     good = np.setdiff1d(np.arange(R), bad)
-    assert np.all(np.isnan(a[bad]))
-    assert np.array_equal(a[good].view(np.uint32), b[good].view(np.uint32))
+    if odt == "f32":
+        a = out[:, :V].cpu().numpy()
+        assert np.all(np.isnan(a[bad]))
+        assert np.array_equal(a[good].view(np.uint32), b[good].view(np.uint32))
+    else:
+        bits = bf16_bits(out[:, :V])
+        assert np.all(((bits[bad] & 0x7F80) == 0x7F80) & ((bits[bad] & 0x7F) != 0))   # NaN
+        assert np.array_equal(bits[good], synth.f32_to_bf16_bits(b[good]))
     assert int(st.device_error.item()) & lmh.LMH_DEVERR_INDEX
     if pad:
         assert torch.all(out[:, V:] == 7.0)

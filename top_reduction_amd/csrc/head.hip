@@ -97,18 +97,22 @@ __device__ inline void chunk_loop(int n, Step& step, W& w0, W& w1) {
 // Logits of a streaming workgroup as whole row segments: each wave's MFMA
 // results (lane: rows 4*(lane/16)+e of column lane%16 of each 16-row tile)
 // go to an LDS staging tile of MT*16 rows x TPB/4*NT columns, then the
-// workgroup stores 16-byte pieces of consecutive columns -- fp32 logits,
-// vocabulary and row pitch multiples of 4, 16-byte aligned output. The
-// caller's barrier must precede it (`so` reuses the hidden-row buffers).
+// workgroup stores 16-byte pieces of consecutive columns (4 fp32 or 8 bf16
+// logits) -- vocabulary and row pitch multiples of that count, 16-byte
+// aligned output. The caller's barrier must precede it (`so` reuses the
+// hidden-row buffers).
+template <bool OUT_BF16>
 __device__ inline bool rows_vec_ok(const HeadParams& p) {
-    return p.V % 4 == 0 && p.old % 4 == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+    constexpr int E = OUT_BF16 ? 8 : 4;
+    return p.V % E == 0 && p.old % E == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
 }
-template <int MT, int NT, int TPB>
+template <int MT, int NT, int TPB, bool OUT_BF16>
 __device__ inline void store_rows_staged(const HeadParams& p, float* __restrict__ so,
                                          const f32x4 (&acc)[MT][NT], const int32_t* sIdx) {
     constexpr int ROWS = MT * 16;
     constexpr int CW = TPB / 4 * NT;            // the workgroup's columns
     constexpr int CWP = CW + 4;                 // staged row pitch (floats)
+    constexpr int E = OUT_BF16 ? 8 : 4;         // logits per 16-byte piece
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -124,18 +128,28 @@ __device__ inline void store_rows_staged(const HeadParams& p, float* __restrict_
             }
     __syncthreads();
     const int64_t col0 = (int64_t)blockIdx.x * CW;
-    constexpr int NCH = ROWS * (CW / 4);        // 16-byte pieces
+    constexpr int NCH = ROWS * (CW / E);        // 16-byte pieces
 #pragma unroll
     for (int c0 = 0; c0 < NCH; c0 += TPB) {
         const int c = c0 + tid;
         if (NCH % TPB == 0 || c < NCH) {
-            const int r = c / (CW / 4);
-            const int cc = (c % (CW / 4)) * 4;
+            const int r = c / (CW / E);
+            const int cc = (c % (CW / E)) * E;
             const int64_t col = col0 + cc;
             if (r < p.R && col < p.V) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&so[r * CWP + cc]);
-                __builtin_nontemporal_store(
-                    v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + col));
+                const f32x4 v0 = *reinterpret_cast<const f32x4*>(&so[r * CWP + cc]);
+                if constexpr (OUT_BF16) {
+                    const f32x4 v1 = *reinterpret_cast<const f32x4*>(&so[r * CWP + cc + 4]);
+                    const u32x4 wd{(uint32_t)f32_to_bf16_rne(v0[0]) | ((uint32_t)f32_to_bf16_rne(v0[1]) << 16),
+                                   (uint32_t)f32_to_bf16_rne(v0[2]) | ((uint32_t)f32_to_bf16_rne(v0[3]) << 16),
+                                   (uint32_t)f32_to_bf16_rne(v1[0]) | ((uint32_t)f32_to_bf16_rne(v1[1]) << 16),
+                                   (uint32_t)f32_to_bf16_rne(v1[2]) | ((uint32_t)f32_to_bf16_rne(v1[3]) << 16)};
+                    __builtin_nontemporal_store(
+                        wd, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)r * p.old + col));
+                } else {
+                    __builtin_nontemporal_store(
+                        v0, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)r * p.old + col));
+                }
             }
         }
     }
@@ -287,13 +301,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_head_stream(HeadParams p) {
     };
     chunk_loop(nchunks, step, w0, w1);
 
-    if constexpr (!OUT_BF16) {
-        // whole row segments (fp32 logits, aligned rows)
-        if (rows_vec_ok(p)) {
-            static_assert(sizeof(sA) >= (size_t)ROWS * (TPB / 4 * NT + 4) * 4, "the staging fits sA");
-            store_rows_staged<MT, NT, TPB>(p, reinterpret_cast<float*>(&sA[0][0][0]), acc, sIdx);
-            return;
-        }
+    // whole row segments (aligned rows)
+    if (rows_vec_ok<OUT_BF16>(p)) {
+        static_assert(sizeof(sA) >= (size_t)ROWS * (TPB / 4 * NT + 4) * 4, "the staging fits sA");
+        store_rows_staged<MT, NT, TPB, OUT_BF16>(p, reinterpret_cast<float*>(&sA[0][0][0]), acc, sIdx);
+        return;
     }
     // D fragment: lane holds rows 4*(lane/16)+e of column lane%16
 #pragma unroll
@@ -499,13 +511,11 @@ __global__ __launch_bounds__(kStreamQThreads) void k_head_stream_q(HeadParams p)
     };
     chunk_loop(nchunks, step, w0, w1);
 
-    if constexpr (!OUT_BF16) {
-        // whole row segments (fp32 logits, aligned rows)
-        if (rows_vec_ok(p)) {
-            static_assert(sizeof(sA) >= (size_t)ROWS * (TPB / 4 * NT + 4) * 4, "the staging fits sA");
-            store_rows_staged<MT, NT, TPB>(p, reinterpret_cast<float*>(&sA[0][0][0]), acc, sIdx);
-            return;
-        }
+    // whole row segments (aligned rows)
+    if (rows_vec_ok<OUT_BF16>(p)) {
+        static_assert(sizeof(sA) >= (size_t)ROWS * (TPB / 4 * NT + 4) * 4, "the staging fits sA");
+        store_rows_staged<MT, NT, TPB, OUT_BF16>(p, reinterpret_cast<float*>(&sA[0][0][0]), acc, sIdx);
+        return;
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
