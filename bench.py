@@ -452,6 +452,31 @@ def main():
                               "traffic": load_traffic("head_tiled_bf16", head_src),
                               "algorithmic_bytes": Vq * H * 2 + 2048 * H * 2 + 2048 * Vq * 4},
         }
+        # the same selective and full projections with bf16 logits (the
+        # output option of the head; half the logits bytes)
+        out16 = torch.empty((R, Vq), dtype=torch.bfloat16, device=dev)
+        full16 = torch.empty((2048, Vq), dtype=torch.bfloat16, device=dev)
+
+        def sel16(wc):
+            return L.lmhead_gather_project(vp(hid), lmh.LMH_BF16, T, H, H, vp(wc), lmh.LMH_BF16, Vq, H,
+                                           vp(cu), R, 0, None, 0, vp(out16), lmh.LMH_BF16, Vq, None,
+                                           None, None, stream)
+
+        def full16_call():
+            return L.lmhead_gather_project(vp(hid), lmh.LMH_BF16, T, H, H, vp(w), lmh.LMH_BF16, Vq, H,
+                                           vp(cu), R, 0, vp(full_idx), 2048, vp(full16), lmh.LMH_BF16, Vq,
+                                           None, None, None, stream)
+        assert sel16(w) == 0 and full16_call() == 0
+        t16 = timer.loop_median([lambda wc=wc: sel16(wc) for wc in wcopies], hs, warmup)
+        b16 = Vq * H * 2 + R * H * 2 + R * Vq * 2
+        tf16 = timer.loop([full16_call], fs, 2)
+        result["head"]["bf16_logits"] = {
+            "selective_kernel_us": round(t16 * 1e3, 2),
+            "selective_gbps": round(b16 / (t16 * 1e-3) / 1e9, 1),
+            "full_2048_ms": round(tf16, 4),
+            "full_tflops": round(flops / (tf16 * 1e-3) / 1e12, 1)}
+        log(f"bf16 logits: selective {t16 * 1e3:.1f} us, full 2048-row {tf16 * 1e3:.1f} us")
+        del out16, full16
         # token bitmask on the 40 selective rows (one segment per row): mask
         # words read once, masked logits written as -inf, nothing else touched
         g = synth.rng(7300)
